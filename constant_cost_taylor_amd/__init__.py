@@ -1,0 +1,232 @@
+"""Python binding of the MI355X SATA library (libsata.so, C ABI in include/sata.h).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels.  torch supplies device memory and the current HIP stream.  If the
+library is not built, importing works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsata.so")
+
+SATA_OK = 0
+SATA_ERR_INVALID_ARG = -1
+SATA_ERR_UNSUPPORTED = -2
+SATA_ERR_WORKSPACE = -3
+SATA_ERR_HIP = -4
+SATA_ERR_OOM = -5
+SATA_F32 = 0
+SATA_BF16 = 1
+
+_lib = None
+
+
+class SataError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+def _declare(lib):
+    c_int, c_i64, c_sz, c_dbl, c_vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double, ctypes.c_void_p
+    P = ctypes.POINTER
+    lib.sata_build_basis.argtypes = [c_int, c_int, c_dbl, P(c_vp)]
+    lib.sata_build_basis.restype = c_int
+    lib.sata_build_basis_host.argtypes = [c_int, c_int, c_dbl, P(c_vp)]
+    lib.sata_build_basis_host.restype = c_int
+    lib.sata_free_basis.argtypes = [c_vp]
+    lib.sata_free_basis.restype = None
+    lib.sata_basis_info.argtypes = [c_vp, P(c_int), P(c_int), P(c_dbl), P(c_i64)]
+    lib.sata_basis_info.restype = c_int
+    lib.sata_basis_rows.argtypes = [c_vp, c_int, P(c_i64)]
+    lib.sata_basis_rows.restype = c_int
+    lib.sata_basis_copy_tables.argtypes = [c_vp, c_int, c_vp, c_vp]
+    lib.sata_basis_copy_tables.restype = c_int
+    lib.sata_basis_download_rows.argtypes = [c_vp, c_vp, c_vp]
+    lib.sata_basis_download_rows.restype = c_int
+    lib.sata_state_floats.argtypes = [c_vp, c_int]
+    lib.sata_state_floats.restype = c_i64
+    lib.sata_state_stride.argtypes = [c_vp, c_int]
+    lib.sata_state_stride.restype = c_i64
+    lib.sata_prefill_workspace.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_int, P(c_sz)]
+    lib.sata_prefill_workspace.restype = c_int
+    lib.sata_prefill.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                 c_vp, c_sz, c_vp]
+    lib.sata_prefill.restype = c_int
+    lib.sata_decode_workspace.argtypes = [c_vp, c_int, c_int, c_int, P(c_sz)]
+    lib.sata_decode_workspace.restype = c_int
+    lib.sata_decode_step.argtypes = [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                     c_sz, c_vp]
+    lib.sata_decode_step.restype = c_int
+    lib.sata_status_string.argtypes = [c_int]
+    lib.sata_status_string.restype = ctypes.c_char_p
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m constant_cost_taylor_amd.build`"
+                               " (the SATA path has no fallback)")
+        _lib = ctypes.CDLL(LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sata_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != SATA_OK:
+        raise SataError(status, what)
+
+
+class Basis:
+    """Handle of the minimal-basis tables for (d_k, P, c) on the current device."""
+
+    def __init__(self, d_k: int, P: int, c: float = 1.0, host_only: bool = False):
+        h = ctypes.c_void_p()
+        fn = lib().sata_build_basis_host if host_only else lib().sata_build_basis
+        _check(fn(int(d_k), int(P), float(c), ctypes.byref(h)), "sata_build_basis")
+        self._h = h
+        self.d_k = int(d_k)
+        self.P = int(P)
+        self.c = float(c)
+        D = ctypes.c_int64()
+        _check(lib().sata_basis_info(h, None, None, None, ctypes.byref(D)), "sata_basis_info")
+        self.total_rows = int(D.value)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.sata_free_basis(h)
+            self._h = None
+
+    def rows(self, p: int) -> int:
+        r = ctypes.c_int64()
+        _check(lib().sata_basis_rows(self._h, int(p), ctypes.byref(r)), "sata_basis_rows")
+        return int(r.value)
+
+    def tables(self, p: int) -> Tuple[np.ndarray, np.ndarray]:
+        n = self.rows(p)
+        idx = np.zeros((n, p), dtype=np.int32)
+        mult = np.zeros(n, dtype=np.uint32)
+        _check(lib().sata_basis_copy_tables(self._h, int(p), idx.ctypes.data if p > 0 else None,
+                                            mult.ctypes.data), "sata_basis_copy_tables")
+        return idx, mult
+
+    def device_rows(self) -> Tuple[np.ndarray, np.ndarray]:
+        packed = np.zeros(self.total_rows, dtype=np.uint32)
+        weight = np.zeros(self.total_rows, dtype=np.float32)
+        _check(lib().sata_basis_download_rows(self._h, packed.ctypes.data, weight.ctypes.data),
+               "sata_basis_download_rows")
+        return packed, weight
+
+    def state_floats(self, d_v: Optional[int] = None) -> int:
+        return int(lib().sata_state_floats(self._h, int(self.d_k if d_v is None else d_v)))
+
+    def state_stride(self, d_v: Optional[int] = None) -> int:
+        return int(lib().sata_state_stride(self._h, int(self.d_k if d_v is None else d_v)))
+
+
+def build_basis(d_k: int, P: int, c: float = 1.0, host_only: bool = False) -> Basis:
+    return Basis(d_k, P, c, host_only)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SATA_F32
+    if t.dtype == torch.bfloat16:
+        return SATA_BF16
+    raise TypeError(f"unsupported input dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_ptr(device) -> int:
+    import torch
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def new_state(basis: Basis, count: int, device="cuda"):
+    """Zero states (empty prefix) for `count` heads: [count, state_stride] float32."""
+    import torch
+    return torch.zeros((count, basis.state_stride()), dtype=torch.float32, device=device)
+
+
+def prefill_workspace_bytes(basis: Basis, B: int, H: int, n: int, d_v: int, dtype_code: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().sata_prefill_workspace(basis.handle, B, H, n, d_v, dtype_code, ctypes.byref(b)),
+           "sata_prefill_workspace")
+    return int(b.value)
+
+
+def decode_workspace_bytes(basis: Basis, S: int, d_v: int, dtype_code: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().sata_decode_workspace(basis.handle, S, d_v, dtype_code, ctypes.byref(b)),
+           "sata_decode_workspace")
+    return int(b.value)
+
+
+def workspace(nbytes: int, device="cuda"):
+    """A 256-byte aligned device buffer of nbytes (torch's allocator aligns to 512)."""
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None):
+    """Causal prefill. q, k: [B, H, n, d_k], v: [B, H, n, d_v] (float32 or bfloat16,
+    contiguous, on the GPU). Returns (out [B, H, n, d_v] float32, state [B*H, stride])."""
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B, H, n, d_k] and v [B, H, n, d_v]")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, n, _ = q.shape
+    d_v = v.shape[3]
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if state is None:
+        state = new_state(basis, B * H, q.device)
+    if out is None:
+        out = torch.empty((B, H, n, d_v), dtype=torch.float32, device=q.device)
+    need = prefill_workspace_bytes(basis, B, H, n, d_v, code)
+    if ws is None:
+        ws = workspace(need, q.device)
+    st = lib().sata_prefill(basis.handle, B, H, n, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            out.data_ptr(), state.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                            _stream_ptr(q.device))
+    _check(st, "sata_prefill")
+    return out, state
+
+
+def decode_step(basis: Basis, q, k, v, state, out=None, ws=None):
+    """One decode step for S states: q, k [S, d_k], v [S, d_v]; state [S, stride] in/out.
+    Returns out [S, d_v] float32."""
+    import torch
+    if q.dim() != 2 or k.shape != q.shape or v.shape[0] != q.shape[0]:
+        raise ValueError("q, k must be [S, d_k] and v [S, d_v]")
+    S = q.shape[0]
+    d_v = v.shape[1]
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty((S, d_v), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(decode_workspace_bytes(basis, S, d_v, code), q.device)
+    st = lib().sata_decode_step(basis.handle, S, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), state.data_ptr(), ws.data_ptr(),
+                                ws.numel() * ws.element_size(), _stream_ptr(q.device))
+    _check(st, "sata_decode_step")
+    return out

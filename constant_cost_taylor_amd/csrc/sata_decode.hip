@@ -1,0 +1,182 @@
+// Decode step of causal SATA on gfx950: one new token per resident state.
+//
+// Each state takes its token's key into every basis row (S_m += phi_m(k) v,
+// z_m += phi_m(k)) and then reads out num = sum_m w_m phi_m(q) S_m and
+// den = sum_m w_m phi_m(q) z_m, so the token attends to itself
+// [SATA page, section "Engineering of constant compute cost": the per-token
+// step maps the key through the index matrix, accumulates, and forms the
+// output from the weighted sum over orders].
+//
+// The step is bound by HBM: every state value is read once and written once.
+// Layout of the work: grid = (row tiles of kDecodeRows rows) x (states).  A
+// block first builds the features of its rows in LDS (phi_k unweighted, phi_q
+// with the row weight), then streams its slice of S as float4 rows (d_v/4
+// threads per row), fusing the rank-1 update with the readout partial sums,
+// then streams z.  Per-tile partial sums go to the workspace and a second
+// kernel reduces them in a fixed order and divides.
+#include <hip/hip_runtime.h>
+
+#include "sata_internal.h"
+
+namespace sata {
+namespace {
+
+__device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+__device__ __forceinline__ float4 fma4(float s, float4 v, float4 acc) {
+  acc.x = fmaf(s, v.x, acc.x);
+  acc.y = fmaf(s, v.y, acc.y);
+  acc.z = fmaf(s, v.z, acc.z);
+  acc.w = fmaf(s, v.w, acc.w);
+  return acc;
+}
+
+template <int DK, typename IT>
+__global__ __launch_bounds__(kThreads) void decode_update_readout(DecodeArgs a) {
+  constexpr int DV = DK;
+  constexpr int TPR = DV / 4;          // threads per S row, one float4 each
+  constexpr int RPP = kThreads / TPR;  // rows per pass of the block
+  constexpr int DVP = padded_dv(DV);
+  constexpr int U = 4;                 // rows in flight per thread
+
+  __shared__ float xq[DK], xk[DK], xv[DV];
+  __shared__ float fk[kDecodeRows], fq[kDecodeRows];
+  __shared__ float red[RPP * DV];
+  __shared__ float dred[kThreads / 64];
+
+  const int tile = blockIdx.x;
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int r0 = tile * kDecodeRows;
+  const int nrows = min(kDecodeRows, a.D - r0);
+
+  const IT* q = static_cast<const IT*>(a.q) + static_cast<int64_t>(s) * DK;
+  const IT* k = static_cast<const IT*>(a.k) + static_cast<int64_t>(s) * DK;
+  const IT* v = static_cast<const IT*>(a.v) + static_cast<int64_t>(s) * DV;
+  if (tid < DK) {
+    xq[tid] = load_in(q, tid);
+    xk[tid] = load_in(k, tid);
+  }
+  if (tid < DV) xv[tid] = load_in(v, tid);
+  __syncthreads();
+
+  // Features of this tile's rows: phi_k = prod k[i_r], phi_q = w_m prod q[i_r].
+  for (int r = tid; r < nrows; r += kThreads) {
+    const uint32_t pk = a.rows[r0 + r];
+    const int p = static_cast<int>(pk >> 24);
+    float fkk = 1.f;
+    float fqq = a.weight[r0 + r];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      if (t < p) {
+        const int i = (pk >> (8 * t)) & 0xff;
+        fkk *= xk[i];
+        fqq *= xq[i];
+      }
+    }
+    fk[r] = fkk;
+    fq[r] = fqq;
+  }
+  __syncthreads();
+
+  float* st = a.state + static_cast<int64_t>(s) * a.stride;
+  float4* S4 = reinterpret_cast<float4*>(st + static_cast<int64_t>(r0) * DV);
+  const int c4 = tid % TPR;
+  const int rs = tid / TPR;
+  const float4 vv = make_float4(xv[4 * c4], xv[4 * c4 + 1], xv[4 * c4 + 2], xv[4 * c4 + 3]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  int r = rs;
+  for (; r + (U - 1) * RPP < nrows; r += U * RPP) {
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = S4[static_cast<int64_t>(r + u * RPP) * TPR + c4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      x[u] = fma4(fk[r + u * RPP], vv, x[u]);
+      S4[static_cast<int64_t>(r + u * RPP) * TPR + c4] = x[u];
+      acc = fma4(fq[r + u * RPP], x[u], acc);
+    }
+  }
+  for (; r < nrows; r += RPP) {
+    float4 x = S4[static_cast<int64_t>(r) * TPR + c4];
+    x = fma4(fk[r], vv, x);
+    S4[static_cast<int64_t>(r) * TPR + c4] = x;
+    acc = fma4(fq[r], x, acc);
+  }
+
+  // z rows of this tile.
+  float* z = st + static_cast<int64_t>(a.D) * DV + r0;
+  float dacc = 0.f;
+  for (int rr = tid; rr < nrows; rr += kThreads) {
+    const float zz = z[rr] + fk[rr];
+    z[rr] = zz;
+    dacc = fmaf(fq[rr], zz, dacc);
+  }
+
+  // Fixed-order reductions: over the row groups of a column, and over the block for den.
+  red[rs * DV + 4 * c4 + 0] = acc.x;
+  red[rs * DV + 4 * c4 + 1] = acc.y;
+  red[rs * DV + 4 * c4 + 2] = acc.z;
+  red[rs * DV + 4 * c4 + 3] = acc.w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) dacc += __shfl_xor(dacc, o);
+  if ((tid & 63) == 0) dred[tid >> 6] = dacc;
+  __syncthreads();
+  float* part = a.part + (static_cast<int64_t>(s) * a.n_tiles + tile) * DVP;
+  if (tid < DV) {
+    float sum = 0.f;
+    for (int j = 0; j < RPP; ++j) sum += red[j * DV + tid];
+    part[tid] = sum;
+  }
+  if (tid == DV) {
+    float sum = 0.f;
+    for (int j = 0; j < kThreads / 64; ++j) sum += dred[j];
+    part[DV] = sum;
+  }
+}
+
+template <int DV>
+__global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
+  constexpr int DVP = padded_dv(DV);
+  const int s = blockIdx.x;
+  const int c = threadIdx.x;
+  const float* part = a.part + static_cast<int64_t>(s) * a.n_tiles * DVP;
+  float den = 0.f;
+  for (int t = 0; t < a.n_tiles; ++t) den += part[static_cast<int64_t>(t) * DVP + DV];
+  if (c < DV) {
+    float num = 0.f;
+    for (int t = 0; t < a.n_tiles; ++t) num += part[static_cast<int64_t>(t) * DVP + c];
+    a.out[static_cast<int64_t>(s) * DV + c] = num / den;
+  }
+}
+
+template <int D>
+hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
+  dim3 grid(a.n_tiles, a.S);
+  if (bf16)
+    decode_update_readout<D, uint16_t><<<grid, kThreads, 0, st>>>(a);
+  else
+    decode_update_readout<D, float><<<grid, kThreads, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_reduce<D><<<a.S, 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(int d, bool bf16, const DecodeArgs& a, hipStream_t s) {
+  switch (d) {
+    case 8: return launch_d<8>(bf16, a, s);
+    case 16: return launch_d<16>(bf16, a, s);
+    case 32: return launch_d<32>(bf16, a, s);
+    case 64: return launch_d<64>(bf16, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sata

@@ -1,0 +1,474 @@
+// Host side of the SATA library: minimal-basis and coefficient tables, the
+// internal tile layout of the prefill scan, argument validation and dispatch.
+//
+// Basis (SATA page, section "Core insight: symmetric tensor decomposition"):
+// for every order p < P the rows are the multisets i1 <= ... <= ip over
+// [0, d) in lexicographic order, concatenated by ascending p; the number of
+// index tuples a multiset stands for is mult = p!/prod(count!), and its query
+// weight is w = mult / (p! c^p) = 1/(prod(count!) c^p).  The index matrices are
+// fixed once d and P are known, so they are built once per handle (section
+// "Hardware optimisation path and current limitations" notes they are
+// precomputable and nested: every order-p row extends an order-(p-1) row by
+// one index not below its last one).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/sata.h"
+#include "sata_internal.h"
+
+using sata::PrefillLayout;
+
+struct sata_basis {
+  int d = 0;
+  int P = 0;
+  double c = 1.0;
+  int64_t D = 0;
+  std::vector<int64_t> offset;               // first row of each order
+  std::vector<std::vector<int32_t>> idx;     // per order: rows * p
+  std::vector<std::vector<uint32_t>> mult;   // per order
+  std::vector<uint32_t> packed;              // per row: i1 | i2<<8 | i3<<16 | p<<24
+  std::vector<float> weight;                 // per row: w_m
+  int device = -1;
+  uint32_t* d_rows = nullptr;
+  float* d_weight = nullptr;
+  PrefillLayout lay[2];                      // [0] float32 inputs, [1] bfloat16 inputs
+  std::vector<void*> allocations;
+};
+
+namespace {
+
+bool supported_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64; }
+
+uint64_t factorial(int n) {
+  uint64_t f = 1;
+  for (int i = 2; i <= n; ++i) f *= static_cast<uint64_t>(i);
+  return f;
+}
+
+uint32_t pack_multiset(const int32_t* m, int p) {
+  uint32_t key = static_cast<uint32_t>(p) << 24;
+  for (int r = 0; r < p; ++r) key |= static_cast<uint32_t>(m[r]) << (8 * r);
+  return key;
+}
+
+// All multisets of size p over [0, d) in lexicographic order.
+std::vector<int32_t> enumerate_multisets(int d, int p, int64_t* count) {
+  std::vector<int32_t> out;
+  std::vector<int32_t> cur(p, 0);
+  int64_t n = 0;
+  while (true) {
+    out.insert(out.end(), cur.begin(), cur.end());
+    ++n;
+    int r = p - 1;
+    while (r >= 0 && cur[r] == d - 1) --r;
+    if (r < 0) break;
+    const int32_t nv = cur[r] + 1;
+    for (int t = r; t < p; ++t) cur[t] = nv;
+  }
+  *count = n;
+  return out;
+}
+
+template <typename T>
+int upload(sata_basis* b, const std::vector<T>& host, T** dev) {
+  *dev = nullptr;
+  if (host.empty()) return SATA_OK;
+  void* p = nullptr;
+  if (hipMalloc(&p, host.size() * sizeof(T)) != hipSuccess) return SATA_ERR_OOM;
+  b->allocations.push_back(p);
+  if (hipMemcpy(p, host.data(), host.size() * sizeof(T), hipMemcpyHostToDevice) != hipSuccess)
+    return SATA_ERR_HIP;
+  *dev = static_cast<T*>(p);
+  return SATA_OK;
+}
+
+struct Run {
+  uint32_t parent_key;   // packed parent multiset (order p-1)
+  float parent_weight;   // 1 / prod(count!) of the parent
+  int c0;                // first child index (multiple of 4)
+  int64_t row[4];        // canonical row of each child, -1 = masked
+  int cnt[4];            // multiplicity of the child index in the child row
+};
+
+// Runs of four children (P, c0..c0+3) over every parent of order 0..P-2,
+// in canonical row order.
+std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32_t, int64_t>& rank) {
+  std::vector<Run> runs;
+  for (int p = 1; p < b.P; ++p) {
+    const int pp = p - 1;
+    const int64_t nparents = static_cast<int64_t>(b.mult[pp].size());
+    for (int64_t r = 0; r < nparents; ++r) {
+      const int32_t* par = b.idx[pp].data() + r * pp;
+      const int lo = pp > 0 ? par[pp - 1] : 0;
+      uint64_t cf = 1;   // prod(count!) of the parent
+      for (int s = 0; s < pp;) {
+        int e = s;
+        while (e < pp && par[e] == par[s]) ++e;
+        cf *= factorial(e - s);
+        s = e;
+      }
+      for (int c0 = (lo / 4) * 4; c0 < b.d; c0 += 4) {
+        Run run;
+        run.parent_key = pack_multiset(par, pp);
+        run.parent_weight = static_cast<float>(1.0 / static_cast<double>(cf));
+        run.c0 = c0;
+        for (int j = 0; j < 4; ++j) {
+          const int c = c0 + j;
+          if (c < lo) {
+            run.row[j] = -1;
+            run.cnt[j] = 0;
+            continue;
+          }
+          int32_t child[4];
+          for (int s = 0; s < pp; ++s) child[s] = par[s];
+          child[pp] = c;
+          int cnt = 1;
+          for (int s = 0; s < pp; ++s) cnt += (par[s] == c);
+          run.row[j] = rank.at(pack_multiset(child, p));
+          run.cnt[j] = cnt;
+        }
+        runs.push_back(run);
+      }
+    }
+  }
+  return runs;
+}
+
+int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& rank, bool bf16,
+                 PrefillLayout* lay) {
+  const int rb = sata::prefill_rb(b->d, bf16);
+  const int per_tile = 4 * rb * sata::kWaves;
+  const int kstr = sata::kKStride;
+  const int xk_zero = 3 * b->d * kstr;
+  lay->rb = rb;
+  // With P = 1 there are no runs, but one (empty) tile still carries the
+  // order-0 row, so every layout has at least one tile.
+  const std::vector<Run> runs = build_runs(*b, rank);
+  const int n_tiles = std::max(1, static_cast<int>((runs.size() + per_tile - 1) / per_tile));
+  std::vector<uint32_t> kside(static_cast<size_t>(n_tiles) * sata::kWaves * rb * 16, 0);
+  std::vector<uint32_t> qside(static_cast<size_t>(n_tiles) * sata::kWaves * rb * 4, 0);
+  std::vector<uint32_t> rowinfo(static_cast<size_t>(n_tiles) * sata::kWaves * rb * 16, 0);
+  std::vector<uint32_t> parents(static_cast<size_t>(n_tiles) * per_tile, 0);
+  std::vector<float> pweight(static_cast<size_t>(n_tiles) * per_tile, 0.f);
+  std::vector<int32_t> nslot(n_tiles, 0);
+  for (int t = 0; t < n_tiles; ++t) {
+    std::unordered_map<uint32_t, int> slot_of;
+    for (int u = 0; u < per_tile; ++u) {
+      const size_t ri = static_cast<size_t>(t) * per_tile + u;
+      const int w = u / (4 * rb);
+      const int bl = (u / 4) % rb;
+      const int g = u % 4;
+      const size_t blk = (static_cast<size_t>(t) * sata::kWaves + w) * rb + bl;
+      if (ri >= runs.size()) {
+        // Empty run: masked children reading the zero row, parent slot 0.
+        for (int j = 0; j < 4; ++j) kside[blk * 16 + 4 * g + j] = static_cast<uint32_t>(xk_zero) << 16;
+        qside[blk * 4 + g] = 0;
+        continue;
+      }
+      const Run& run = runs[ri];
+      auto it = slot_of.find(run.parent_key);
+      int slot;
+      if (it == slot_of.end()) {
+        slot = static_cast<int>(slot_of.size());
+        slot_of.emplace(run.parent_key, slot);
+        parents[static_cast<size_t>(t) * per_tile + slot] =
+            (run.parent_key & 0xffffu) | (((run.parent_key >> 24) & 3u) << 16);
+        pweight[static_cast<size_t>(t) * per_tile + slot] = run.parent_weight;
+      } else {
+        slot = it->second;
+      }
+      qside[blk * 4 + g] = static_cast<uint32_t>(slot) | (static_cast<uint32_t>(run.c0) << 16);
+      for (int j = 0; j < 4; ++j) {
+        const int code = run.cnt[j];
+        const uint32_t pko = static_cast<uint32_t>(slot * kstr);
+        const uint32_t xko = code == 0 ? static_cast<uint32_t>(xk_zero)
+                                       : static_cast<uint32_t>(((code - 1) * b->d + run.c0 + j) * kstr);
+        kside[blk * 16 + 4 * g + j] = pko | (xko << 16);
+        if (run.row[j] >= 0)
+          rowinfo[blk * 16 + 4 * g + j] =
+              static_cast<uint32_t>(run.row[j] + 1) | (static_cast<uint32_t>(code) << 28);
+      }
+    }
+    // Every tile has at least one parent slot so empty runs read finite features.
+    nslot[t] = std::max(1, static_cast<int32_t>(slot_of.size()));
+  }
+  lay->n_tiles = n_tiles;
+  int st;
+  if ((st = upload(b, kside, &lay->kside)) != SATA_OK) return st;
+  if ((st = upload(b, qside, &lay->qside)) != SATA_OK) return st;
+  if ((st = upload(b, rowinfo, &lay->rowinfo)) != SATA_OK) return st;
+  if ((st = upload(b, parents, &lay->parents)) != SATA_OK) return st;
+  if ((st = upload(b, pweight, &lay->pweight)) != SATA_OK) return st;
+  if ((st = upload(b, nslot, &lay->nslot)) != SATA_OK) return st;
+  return SATA_OK;
+}
+
+void release(sata_basis* b) {
+  if (!b) return;
+  if (b->device >= 0) {
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(b->device);
+    for (void* p : b->allocations) (void)hipFree(p);
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+  delete b;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_device(const sata_basis* b) {
+  if (b->device < 0 || !b->d_rows) return SATA_ERR_INVALID_ARG;  // host-only handle
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SATA_ERR_HIP;
+  return dev == b->device ? SATA_OK : SATA_ERR_INVALID_ARG;
+}
+
+// Tokens per prefill window and the workspace it needs.  The window bounds
+// the per-tile readout records kept in the workspace (at most kPrefillWsCap).
+constexpr size_t kPrefillWsCap = size_t(16) << 30;
+
+void prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype, int64_t* nw, size_t* bytes) {
+  const int nt = b->lay[dtype].n_tiles;
+  const int64_t per_token = BH * (nt + 1) * sata::padded_dv(b->d) * 4;
+  int64_t w = static_cast<int64_t>(kPrefillWsCap / static_cast<size_t>(per_token));
+  w = std::max<int64_t>(sata::kChunk, (w / sata::kChunk) * sata::kChunk);
+  const int64_t nround = (n + sata::kChunk - 1) / sata::kChunk * sata::kChunk;
+  w = std::min(w, std::max<int64_t>(nround, sata::kChunk));
+  *nw = w;
+  *bytes = static_cast<size_t>(per_token) * static_cast<size_t>(w);
+}
+
+int decode_tiles(const sata_basis* b) {
+  return static_cast<int>((b->D + sata::kDecodeRows - 1) / sata::kDecodeRows);
+}
+
+}  // namespace
+
+extern "C" {
+
+static int build_basis_impl(int d_k, int P, double c, bool upload_tables, sata_basis** out) {
+  if (!out) return SATA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!(std::isfinite(c) && c > 0.0)) return SATA_ERR_INVALID_ARG;
+  if (!supported_dim(d_k) || P < 1 || P > 4) return SATA_ERR_UNSUPPORTED;
+  sata_basis* b = new (std::nothrow) sata_basis;
+  if (!b) return SATA_ERR_OOM;
+  b->d = d_k;
+  b->P = P;
+  b->c = c;
+  std::unordered_map<uint32_t, int64_t> rank;
+  int64_t total = 0;
+  for (int p = 0; p < P; ++p) {
+    int64_t cnt = 0;
+    b->idx.push_back(enumerate_multisets(d_k, p, &cnt));
+    b->offset.push_back(total);
+    std::vector<uint32_t> mult(cnt);
+    const double scale = 1.0 / (static_cast<double>(factorial(p)) * std::pow(c, p));
+    for (int64_t r = 0; r < cnt; ++r) {
+      const int32_t* m = b->idx[p].data() + r * p;
+      uint64_t den = 1;
+      for (int s = 0; s < p;) {
+        int e = s;
+        while (e < p && m[e] == m[s]) ++e;
+        den *= factorial(e - s);
+        s = e;
+      }
+      mult[r] = static_cast<uint32_t>(factorial(p) / den);
+      const uint32_t key = pack_multiset(m, p);
+      rank.emplace(key, total + r);
+      b->packed.push_back(key);
+      b->weight.push_back(static_cast<float>(static_cast<double>(mult[r]) * scale));
+    }
+    b->mult.push_back(std::move(mult));
+    total += cnt;
+  }
+  b->D = total;
+  if (!upload_tables) {
+    *out = b;
+    return SATA_OK;
+  }
+  if (hipGetDevice(&b->device) != hipSuccess) {
+    b->device = -1;
+    release(b);
+    return SATA_ERR_HIP;
+  }
+  int st = upload(b, b->packed, &b->d_rows);
+  if (st == SATA_OK) st = upload(b, b->weight, &b->d_weight);
+  if (st == SATA_OK) st = build_layout(b, rank, false, &b->lay[0]);
+  if (st == SATA_OK) st = build_layout(b, rank, true, &b->lay[1]);
+  if (st != SATA_OK) {
+    release(b);
+    return st;
+  }
+  *out = b;
+  return SATA_OK;
+}
+
+int sata_build_basis(int d_k, int P, double c, sata_basis** out) {
+  try {
+    return build_basis_impl(d_k, P, c, true, out);
+  } catch (...) {
+    if (out) *out = nullptr;
+    return SATA_ERR_OOM;
+  }
+}
+
+int sata_build_basis_host(int d_k, int P, double c, sata_basis** out) {
+  try {
+    return build_basis_impl(d_k, P, c, false, out);
+  } catch (...) {
+    if (out) *out = nullptr;
+    return SATA_ERR_OOM;
+  }
+}
+
+void sata_free_basis(sata_basis* basis) { release(basis); }
+
+int sata_basis_info(const sata_basis* b, int* d_k, int* P, double* c, int64_t* total_rows) {
+  if (!b) return SATA_ERR_INVALID_ARG;
+  if (d_k) *d_k = b->d;
+  if (P) *P = b->P;
+  if (c) *c = b->c;
+  if (total_rows) *total_rows = b->D;
+  return SATA_OK;
+}
+
+int sata_basis_rows(const sata_basis* b, int p, int64_t* rows) {
+  if (!b || !rows || p < 0 || p >= b->P) return SATA_ERR_INVALID_ARG;
+  *rows = static_cast<int64_t>(b->mult[p].size());
+  return SATA_OK;
+}
+
+int sata_basis_copy_tables(const sata_basis* b, int p, int32_t* idx, uint32_t* mult) {
+  if (!b || p < 0 || p >= b->P) return SATA_ERR_INVALID_ARG;
+  if (idx && !b->idx[p].empty()) std::memcpy(idx, b->idx[p].data(), b->idx[p].size() * sizeof(int32_t));
+  if (mult) std::memcpy(mult, b->mult[p].data(), b->mult[p].size() * sizeof(uint32_t));
+  return SATA_OK;
+}
+
+int sata_basis_download_rows(const sata_basis* b, uint32_t* packed, float* weight) {
+  if (!b || !packed || !weight) return SATA_ERR_INVALID_ARG;
+  if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  if (hipMemcpy(packed, b->d_rows, b->D * sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return SATA_ERR_HIP;
+  if (hipMemcpy(weight, b->d_weight, b->D * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess)
+    return SATA_ERR_HIP;
+  return SATA_OK;
+}
+
+int64_t sata_state_floats(const sata_basis* b, int d_v) {
+  if (!b || d_v != b->d) return -1;
+  return static_cast<int64_t>(d_v + 1) * b->D;
+}
+
+int64_t sata_state_stride(const sata_basis* b, int d_v) {
+  const int64_t f = sata_state_floats(b, d_v);
+  return f < 0 ? -1 : sata::state_stride(f);
+}
+
+int sata_prefill_workspace(const sata_basis* b, int B, int H, int n, int d_v, int dtype, size_t* bytes) {
+  if (!b || !bytes || B < 1 || H < 1 || n < 0) return SATA_ERR_INVALID_ARG;
+  if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  int64_t nw = 0;
+  prefill_plan(b, static_cast<int64_t>(B) * H, n, dtype, &nw, bytes);
+  if (n == 0) *bytes = 0;
+  return SATA_OK;
+}
+
+int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,
+                 const void* k, const void* v, float* out, float* state, void* ws, size_t ws_bytes,
+                 void* stream) {
+  if (!b || B < 1 || H < 1 || n < 0) return SATA_ERR_INVALID_ARG;
+  if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  if (n == 0) return SATA_OK;
+  const size_t esz = dtype == SATA_BF16 ? 2 : 4;
+  if (!q || !k || !v || !out || !state) return SATA_ERR_INVALID_ARG;
+  if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) || !aligned(out, 16) ||
+      !aligned(state, 16))
+    return SATA_ERR_INVALID_ARG;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (BH > 65535) return SATA_ERR_UNSUPPORTED;  // grid y limit
+  int64_t nw = 0;
+  size_t need = 0;
+  prefill_plan(b, BH, n, dtype, &nw, &need);
+  if (need > 0 && (!ws || ws_bytes < need)) return SATA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
+  if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == SATA_BF16;
+  const PrefillLayout& lay = b->lay[dtype];
+  const int64_t stride = sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D);
+  for (int64_t t0 = 0; t0 < n; t0 += nw) {
+    const int w = static_cast<int>(std::min<int64_t>(nw, n - t0));
+    sata::IntraArgs ia{q, k, v, static_cast<float*>(ws), n, t0, w, lay.n_tiles, b->P,
+                       static_cast<float>(1.0 / b->c)};
+    if (sata::launch_prefill_intra(b->d, bf16, static_cast<int>(BH), ia, s) != hipSuccess)
+      return SATA_ERR_HIP;
+    sata::ScanArgs sa{q, k, v, state, stride, static_cast<float*>(ws), lay, n, t0, w,
+                      static_cast<int>(b->D), static_cast<float>(1.0 / b->c)};
+    if (sata::launch_prefill_scan(b->d, bf16, static_cast<int>(BH), sa, s) != hipSuccess)
+      return SATA_ERR_HIP;
+    sata::ReduceArgs ra{static_cast<const float*>(ws), out, n, t0, w, lay.n_tiles + 1};
+    if (sata::launch_prefill_reduce(b->d, static_cast<int>(BH), ra, s) != hipSuccess)
+      return SATA_ERR_HIP;
+  }
+  return SATA_OK;
+}
+
+int sata_decode_workspace(const sata_basis* b, int S, int d_v, int dtype, size_t* bytes) {
+  if (!b || !bytes || S < 0) return SATA_ERR_INVALID_ARG;
+  if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  *bytes = static_cast<size_t>(S) * decode_tiles(b) * sata::padded_dv(d_v) * sizeof(float);
+  return SATA_OK;
+}
+
+int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
+                     const void* v, float* out, float* state, void* ws, size_t ws_bytes, void* stream) {
+  if (!b || S < 0) return SATA_ERR_INVALID_ARG;
+  if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  if (S == 0) return SATA_OK;
+  if (S > 65535) return SATA_ERR_UNSUPPORTED;
+  const size_t esz = dtype == SATA_BF16 ? 2 : 4;
+  if (!q || !k || !v || !out || !state) return SATA_ERR_INVALID_ARG;
+  if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) || !aligned(out, 16) ||
+      !aligned(state, 16))
+    return SATA_ERR_INVALID_ARG;
+  size_t need = 0;
+  sata_decode_workspace(b, S, d_v, dtype, &need);
+  if (!ws || ws_bytes < need) return SATA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
+  if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  sata::DecodeArgs a{q, k, v, state,
+                     sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D),
+                     static_cast<float*>(ws), out, b->d_rows, b->d_weight, S,
+                     static_cast<int>(b->D), decode_tiles(b)};
+  if (sata::launch_decode(b->d, dtype == SATA_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SATA_ERR_HIP;
+  return SATA_OK;
+}
+
+const char* sata_status_string(int status) {
+  switch (status) {
+    case SATA_OK: return "SATA_OK";
+    case SATA_ERR_INVALID_ARG: return "SATA_ERR_INVALID_ARG: invalid argument";
+    case SATA_ERR_UNSUPPORTED: return "SATA_ERR_UNSUPPORTED: unsupported d_k, d_v or P";
+    case SATA_ERR_WORKSPACE: return "SATA_ERR_WORKSPACE: workspace too small";
+    case SATA_ERR_HIP: return "SATA_ERR_HIP: HIP runtime or launch failure";
+    case SATA_ERR_OOM: return "SATA_ERR_OOM: allocation failed";
+    default: return "unknown SATA status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+builds basis tables on the host that equal the oracle's enumeration bit for
+bit, and rejects invalid arguments before touching a GPU."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import constant_cost_taylor_amd as SA
+from oracle import sata_oracle as O
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sata.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sata_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = SA.lib()
+    names = _declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("d,P", [(8, 1), (8, 3), (16, 4), (32, 4), (64, 4), (64, 2)])
+def test_host_tables_bit_exact(d, P):
+    b = SA.build_basis(d, P, 1.0, host_only=True)
+    ref = O.enumerate_basis(d, P)
+    assert b.total_rows == sum(r[0].shape[0] for r in ref) == math.comb(d + P - 1, P - 1)
+    for p, (idx, mult, _) in enumerate(ref):
+        hi, hm = b.tables(p)
+        assert hi.dtype == np.int32 and hm.dtype == np.uint32
+        np.testing.assert_array_equal(hi, idx)
+        np.testing.assert_array_equal(hm, mult)
+
+
+@pytest.mark.parametrize("d,P", [(8, 3), (16, 4), (64, 4), (32, 4)])
+def test_state_size_matches_closed_form(d, P):
+    b = SA.build_basis(d, P, 1.0, host_only=True)
+    assert b.state_floats() == O.cost_model(d, d, P)[0]
+    assert b.state_stride() % 64 == 0 and 0 <= b.state_stride() - b.state_floats() < 64
+
+
+def test_invalid_builds():
+    h = ctypes.c_void_p()
+    L = SA.lib()
+    assert L.sata_build_basis_host(7, 3, 1.0, ctypes.byref(h)) == SA.SATA_ERR_UNSUPPORTED
+    assert L.sata_build_basis_host(16, 5, 1.0, ctypes.byref(h)) == SA.SATA_ERR_UNSUPPORTED
+    assert L.sata_build_basis_host(16, 0, 1.0, ctypes.byref(h)) == SA.SATA_ERR_UNSUPPORTED
+    assert L.sata_build_basis_host(16, 3, 0.0, ctypes.byref(h)) == SA.SATA_ERR_INVALID_ARG
+    assert L.sata_build_basis_host(16, 3, float("nan"), ctypes.byref(h)) == SA.SATA_ERR_INVALID_ARG
+    assert L.sata_build_basis_host(16, 3, 1.0, None) == SA.SATA_ERR_INVALID_ARG
+
+
+def test_host_only_handle_rejects_compute():
+    """Validation runs before any HIP call: a host-only handle, a null
+    pointer or a wrong size is refused on a machine without a GPU."""
+    b = SA.build_basis(16, 4, 1.0, host_only=True)
+    L = SA.lib()
+    buf = (ctypes.c_float * 8192)()
+    p = ctypes.c_void_p((ctypes.addressof(buf) + 255) // 256 * 256)   # 256-byte aligned
+    # n = 0 and S = 0 are valid no-ops
+    assert L.sata_prefill(b.handle, 1, 1, 0, 16, SA.SATA_F32, None, None, None, None, None, None, 0, None) == SA.SATA_OK
+    assert L.sata_decode_step(b.handle, 0, 16, SA.SATA_F32, None, None, None, None, None, None, 0, None) == SA.SATA_OK
+    assert L.sata_prefill(b.handle, 1, 1, 4, 16, SA.SATA_F32, None, p, p, p, p, p, 1 << 20, None) == SA.SATA_ERR_INVALID_ARG
+    assert L.sata_prefill(b.handle, 1, 1, 4, 8, SA.SATA_F32, p, p, p, p, p, p, 1 << 20, None) == SA.SATA_ERR_UNSUPPORTED
+    assert L.sata_prefill(b.handle, 1, 1, 4, 16, 7, p, p, p, p, p, p, 1 << 20, None) == SA.SATA_ERR_INVALID_ARG
+    assert L.sata_prefill(b.handle, 1, 1, -1, 16, SA.SATA_F32, p, p, p, p, p, p, 1 << 20, None) == SA.SATA_ERR_INVALID_ARG
+    assert L.sata_prefill(b.handle, 1, 1, 4, 16, SA.SATA_F32, p, p, p, p, p, p, 8, None) == SA.SATA_ERR_WORKSPACE
+    assert L.sata_decode_step(b.handle, 2, 16, SA.SATA_F32, p, p, p, p, p, p, 0, None) == SA.SATA_ERR_WORKSPACE
+    # a host-only handle is refused once everything else checks out
+    assert L.sata_decode_step(b.handle, 2, 16, SA.SATA_F32, p, p, p, p, p, p, 1 << 20, None) == SA.SATA_ERR_INVALID_ARG
+    assert SA.status_string(SA.SATA_ERR_HIP).startswith("SATA_ERR_HIP")
+
+
+def test_workspace_sizes():
+    b = SA.build_basis(64, 4, 1.0, host_only=True)
+    assert SA.prefill_workspace_bytes(b, 1, 4, 0, 64, SA.SATA_BF16) == 0
+    small = SA.prefill_workspace_bytes(b, 1, 4, 100, 64, SA.SATA_BF16)
+    big = SA.prefill_workspace_bytes(b, 1, 4, 16384, 64, SA.SATA_BF16)
+    assert 0 < small < big
+    assert SA.decode_workspace_bytes(b, 256, 64, SA.SATA_BF16) == 256 * math.ceil(47905 / 1024) * 68 * 4

@@ -1,0 +1,319 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Gate (row-normwise, max over rows of ||o_i - r_i||_inf / ||r_i||_inf):
+1e-5 for float32 inputs, 3e-3 for bfloat16 inputs with float32 state.
+Basis tables: bit-exact.  Every input comes from the seeded generators in
+workloads.py; every expected value from oracle/.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import sata_oracle as O
+
+torch = pytest.importorskip("torch")
+import constant_cost_taylor_amd as SA  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {W.F32: 1e-5, W.BF16: 3e-3}
+
+
+def note(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    SA.lib()
+
+
+def to_dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    t = t.to(torch.bfloat16) if dtype == W.BF16 else t
+    return t.to("cuda")
+
+
+def f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def oracle_rows(q, k, v, P, c, rows=None):
+    return O.direct_taylor(f64(q), f64(k), f64(v), P, c, rows=rows)
+
+
+def run_prefill(basis, q, k, v, dtype, state=None):
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    out, st = SA.prefill(basis, qd, kd, vd, state=state)
+    torch.cuda.synchronize()
+    return out, st
+
+
+# ----------------------------------------------------------------------------
+# Tables
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,P,c", [(8, 3, 1.0), (16, 4, 1.0), (32, 4, 0.5), (64, 4, 1.0), (64, 1, 2.0)])
+def test_device_tables_bit_exact(d, P, c):
+    note(f"device tables d={d} P={P} c={c}")
+    b = SA.build_basis(d, P, c)
+    packed, weight = b.device_rows()
+    ref = O.enumerate_basis(d, P, c)
+    exp_packed = []
+    exp_weight = []
+    for p, (idx, mult, scale) in enumerate(ref):
+        for r in range(idx.shape[0]):
+            key = p << 24
+            for j in range(p):
+                key |= int(idx[r, j]) << (8 * j)
+            exp_packed.append(key)
+        exp_weight.append((mult.astype(np.float64) * scale).astype(np.float32))
+    np.testing.assert_array_equal(packed, np.array(exp_packed, dtype=np.uint32))
+    np.testing.assert_array_equal(weight, np.concatenate(exp_weight))
+
+
+# ----------------------------------------------------------------------------
+# Decode
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,P,dtype,steps", [(8, 3, W.F32, 80), (16, 4, W.BF16, 40), (64, 4, W.BF16, 12)])
+def test_decode_steps_from_empty_state(d, P, dtype, steps):
+    """Token-by-token decode from a zero state reproduces causal attention."""
+    note(f"decode from empty d={d} P={P} {dtype} steps={steps}")
+    S = 3
+    q, k, v = W.make_qkv(1, S, steps, d, d, dtype, 7000 + d)
+    b = SA.build_basis(d, P, 1.0)
+    state = SA.new_state(b, S)
+    got = np.zeros((S, steps, d))
+    qd, kd, vd = to_dev(q[0], dtype), to_dev(k[0], dtype), to_dev(v[0], dtype)
+    for t in range(steps):
+        out = SA.decode_step(b, qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(), state)
+        got[:, t] = out.cpu().numpy()
+    for s in range(S):
+        ref = oracle_rows(q[0, s], k[0, s], v[0, s], P, 1.0)
+        err = O.row_normwise_error(got[s], ref)
+        assert err <= TOL[dtype], (s, err)
+
+
+# ----------------------------------------------------------------------------
+# Prefill: small and ragged shapes (several chunks and tiles, ragged tail)
+# ----------------------------------------------------------------------------
+
+CASES = [
+    # name, B, H, n, d, P, c, dtype
+    ("c1_full", 1, 1, 256, 8, 3, 1.0, W.F32),
+    ("d8_P1", 1, 2, 100, 8, 1, 1.0, W.F32),
+    ("d8_P2_c2", 2, 1, 77, 8, 2, 2.0, W.F32),
+    ("d16_ragged", 1, 3, 1000, 16, 4, 1.0, W.F32),
+    ("d16_n1", 1, 2, 1, 16, 4, 1.0, W.F32),
+    ("d32_f32", 1, 1, 300, 32, 3, 1.0, W.F32),
+    ("d64_f32", 1, 1, 130, 64, 4, 1.0, W.F32),
+    ("d16_bf16", 2, 2, 513, 16, 4, 1.0, W.BF16),
+    ("d32_bf16", 1, 2, 777, 32, 4, 1.0, W.BF16),
+    ("d64_bf16", 1, 2, 333, 64, 4, 1.0, W.BF16),
+    ("d64_bf16_P3", 1, 1, 200, 64, 3, 0.75, W.BF16),
+    ("d8_bf16", 1, 1, 97, 8, 4, 1.0, W.BF16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_small(case):
+    name, B, H, n, d, P, c, dtype = case
+    note(f"prefill {name} B={B} H={H} n={n} d={d} P={P} c={c} {dtype}")
+    q, k, v = W.make_qkv(B, H, n, d, d, dtype, 9000 + 17 * d + n)
+    b = SA.build_basis(d, P, c)
+    out, _ = run_prefill(b, q, k, v, dtype)
+    got = out.cpu().numpy()
+    for bb in range(B):
+        for h in range(H):
+            ref = oracle_rows(q[bb, h], k[bb, h], v[bb, h], P, c)
+            err = O.row_normwise_error(got[bb, h], ref)
+            assert err <= TOL[dtype], (bb, h, err)
+
+
+def test_prefill_empty_is_noop():
+    note("prefill n=0")
+    b = SA.build_basis(16, 4, 1.0)
+    q = torch.zeros((1, 1, 0, 16), device="cuda")
+    out, st = SA.prefill(b, q, q, q)
+    assert out.shape == (1, 1, 0, 16) and float(st.abs().sum()) == 0.0
+
+
+@pytest.mark.parametrize("d,P,dtype,n", [(16, 4, W.F32, 300), (8, 3, W.F32, 70), (64, 4, W.BF16, 96),
+                                         (32, 4, W.BF16, 150)])
+def test_prefill_state_matches_direct_state(d, P, dtype, n):
+    """The state written back equals sum_j phi(k_j) v_j and sum_j phi(k_j)
+    (unweighted monomials, canonical row order)."""
+    note(f"prefill state d={d} P={P} {dtype} n={n}")
+    q, k, v = W.make_qkv(1, 2, n, d, d, dtype, 11000 + d)
+    b = SA.build_basis(d, P, 1.0)
+    _, st = run_prefill(b, q, k, v, dtype)
+    st = st.cpu().numpy()
+    basis = O.enumerate_basis(d, P)
+    D = b.total_rows
+    for h in range(2):
+        S, z = O.direct_state(f64(k[0, h]), f64(v[0, h]), basis)
+        gS = st[h, :D * d].reshape(D, d)
+        gz = st[h, D * d:D * (d + 1)]
+        tol = TOL[dtype]
+        # normwise per row block: max |err| / max |ref| over each order
+        off = 0
+        for p in range(P):
+            rows = math.comb(d + p - 1, p)
+            sl = slice(off, off + rows)
+            assert np.max(np.abs(gS[sl] - S[sl])) <= tol * np.max(np.abs(S[sl])) + 1e-30, (h, p)
+            assert np.max(np.abs(gz[sl] - z[sl])) <= tol * np.max(np.abs(z[sl])) + 1e-30, (h, p)
+            off += rows
+
+
+@pytest.mark.parametrize("d,P,dtype,n1,n2", [(16, 4, W.F32, 200, 333), (64, 4, W.BF16, 100, 161),
+                                             (8, 3, W.F32, 33, 64)])
+def test_prefill_continuation(d, P, dtype, n1, n2):
+    """prefill(a) then prefill(b | state) gives the rows of prefill(a + b)."""
+    note(f"continuation d={d} P={P} {dtype} {n1}+{n2}")
+    q, k, v = W.make_qkv(1, 2, n1 + n2, d, d, dtype, 12000 + d)
+    b = SA.build_basis(d, P, 1.0)
+    out1, st = run_prefill(b, q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], dtype)
+    out2, st = run_prefill(b, q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], dtype, state=st)
+    got = np.concatenate([out1.cpu().numpy(), out2.cpu().numpy()], axis=2)
+    for h in range(2):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
+        assert O.row_normwise_error(got[0, h], ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("d,P,dtype", [(16, 4, W.F32), (64, 4, W.BF16)])
+def test_prefill_then_decode(d, P, dtype):
+    note(f"prefill then decode d={d} P={P} {dtype}")
+    n, steps, H = 257, 9, 3
+    q, k, v = W.make_qkv(1, H, n + steps, d, d, dtype, 13000 + d)
+    b = SA.build_basis(d, P, 1.0)
+    _, st = run_prefill(b, q[:, :, :n], k[:, :, :n], v[:, :, :n], dtype)
+    qd, kd, vd = to_dev(q[0], dtype), to_dev(k[0], dtype), to_dev(v[0], dtype)
+    got = np.zeros((H, steps, d))
+    for s in range(steps):
+        t = n + s
+        got[:, s] = SA.decode_step(b, qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(),
+                                   st).cpu().numpy()
+    for h in range(H):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0, rows=np.arange(n, n + steps))
+        assert O.row_normwise_error(got[h], ref) <= TOL[dtype]
+
+
+def test_prefill_deterministic():
+    note("prefill run-twice bitwise")
+    d, P, dtype = 32, 4, W.BF16
+    q, k, v = W.make_qkv(1, 2, 400, d, d, dtype, 14000)
+    b = SA.build_basis(d, P, 1.0)
+    o1, s1 = run_prefill(b, q, k, v, dtype)
+    o2, s2 = run_prefill(b, q, k, v, dtype)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_workspace_too_small_changes_nothing():
+    note("workspace too small")
+    d = 16
+    b = SA.build_basis(d, 4, 1.0)
+    q = torch.randn(1, 1, 64, d, device="cuda")
+    out = torch.full((1, 1, 64, d), 7.0, device="cuda")
+    st = SA.new_state(b, 1)
+    with pytest.raises(SA.SataError) as e:
+        SA.prefill(b, q, q, q, state=st, out=out, ws=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == SA.SATA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert float(out.min()) == 7.0 and float(st.abs().sum()) == 0.0
+
+
+# ----------------------------------------------------------------------------
+# The study's workloads at full size (sampled rows where the oracle is O(n) per row)
+# ----------------------------------------------------------------------------
+
+def test_workload_c2_full():
+    w = W.WORKLOADS["c2_d16"]
+    note(f"workload {w.name} B={w.B} H={w.H} n={w.n}")
+    q, k, v = W.workload_inputs(w)
+    b = SA.build_basis(w.d_k, w.P, w.c)
+    out, _ = run_prefill(b, q, k, v, w.dtype)
+    got = out.cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(0, w.n, 97), np.arange(w.n - 64, w.n)]))
+    for bb in range(w.B):
+        for h in range(w.H):
+            full = (bb, h) in ((0, 0), (w.B - 1, w.H - 1))
+            rr = None if full else rows
+            ref = oracle_rows(q[bb, h], k[bb, h], v[bb, h], w.P, w.c, rows=rr)
+            g = got[bb, h] if full else got[bb, h][rows]
+            assert O.row_normwise_error(g, ref) <= TOL[w.dtype], (bb, h)
+
+
+def test_workload_c3_sampled():
+    w = W.WORKLOADS["c3_d64"]
+    note(f"workload {w.name} B={w.B} H={w.H} n={w.n}")
+    q, k, v = W.workload_inputs(w)
+    b = SA.build_basis(w.d_k, w.P, w.c)
+    out, _ = run_prefill(b, q, k, v, w.dtype)
+    got = out.cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(0, w.n, 61), np.arange(w.n - 40, w.n)]))
+    for h in range(w.H):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], w.P, w.c, rows=rows)
+        assert O.row_normwise_error(got[0, h][rows], ref) <= TOL[w.dtype], h
+
+
+def test_workload_c4_decode():
+    """256 resident states: 4096-token prefill, then decode steps; every
+    decode output and sampled prefill rows of 8 states are checked."""
+    w = W.WORKLOADS["c4_decode"]
+    steps = 16
+    note(f"workload {w.name} states={w.B * w.H} n={w.n} steps={steps}")
+    q, k, v = W.workload_inputs(w)
+    qs, ks, vs = W.decode_inputs(w, steps)
+    b = SA.build_basis(w.d_k, w.P, w.c)
+    out, st = run_prefill(b, q, k, v, w.dtype)
+    got_p = out.cpu().numpy().reshape(w.B * w.H, w.n, w.d_v)
+    del out
+    S = w.B * w.H
+    qd, kd, vd = to_dev(qs, w.dtype), to_dev(ks, w.dtype), to_dev(vs, w.dtype)
+    got_d = np.zeros((steps, S, w.d_v))
+    for s in range(steps):
+        got_d[s] = SA.decode_step(b, qd[s], kd[s], vd[s], st).cpu().numpy()
+    qf = q.reshape(S, w.n, w.d_k)
+    kf = k.reshape(S, w.n, w.d_k)
+    vf = v.reshape(S, w.n, w.d_v)
+    g = np.random.Generator(np.random.PCG64(4321))
+    for s in g.choice(S, size=8, replace=False):
+        rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(0, w.n, 127), [w.n - 1]]))
+        ref = oracle_rows(qf[s], kf[s], vf[s], w.P, w.c, rows=rows)
+        assert O.row_normwise_error(got_p[s][rows], ref) <= TOL[w.dtype], ("prefill", s)
+    for s in range(S):
+        qq = np.concatenate([qf[s], qs[:, s]])
+        kk = np.concatenate([kf[s], ks[:, s]])
+        vv = np.concatenate([vf[s], vs[:, s]])
+        ref = oracle_rows(qq, kk, vv, w.P, w.c, rows=np.arange(w.n, w.n + steps))
+        assert O.row_normwise_error(got_d[:, s], ref) <= TOL[w.dtype], ("decode", s)
+
+
+def test_workload_c5_sampled():
+    w = W.WORKLOADS["c5_long"]
+    note(f"workload {w.name} H={w.H} n={w.n}")
+    rows = W.sampled_rows(w.n)
+    b = SA.build_basis(w.d_k, w.P, w.c)
+    Q = torch.empty((1, w.H, w.n, w.d_k), dtype=torch.bfloat16, device="cuda")
+    K = torch.empty_like(Q)
+    V = torch.empty((1, w.H, w.n, w.d_v), dtype=torch.bfloat16, device="cuda")
+    host = []
+    for h in range(w.H):
+        q, k, v = W.head_inputs(w, h)
+        Q[0, h] = to_dev(q, w.dtype)
+        K[0, h] = to_dev(k, w.dtype)
+        V[0, h] = to_dev(v, w.dtype)
+        host.append((q, k, v))
+    out, _ = SA.prefill(b, Q, K, V)
+    torch.cuda.synchronize()
+    got = out[0][:, torch.from_numpy(rows).to("cuda")].cpu().numpy()
+    del out, Q, K, V
+    for h in range(w.H):
+        q, k, v = host[h]
+        ref = O.direct_taylor(f64(q), f64(k), f64(v), w.P, w.c, rows=rows, block=8)
+        assert O.row_normwise_error(got[h], ref) <= TOL[w.dtype], h
