@@ -1,0 +1,195 @@
+"""Benchmark of the causal SATA hot path on one MI355X.
+
+One step = the decode workload end to end: 256 resident states (batch 8 x 32
+heads), d_k = d_v = 64, P = 4, bf16 q/k/v with fp32 state: a 4096-token causal
+prefill from empty states, then 1024 single-token decode steps.  Inputs are
+seeded synthetic data (workloads.py), resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is head-tokens/s over the whole step (every
+prefill and decode token of every state).  The prefill and decode legs are
+also reported on their own, each against its roofline; `roofline` describes
+the dominant kernel (the decode update/readout, bound by HBM).  The CPU
+baseline is the float64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
+METRIC = "causal SATA tokens/sec/head (prefill, decode) + % of HBM/MFMA roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, qs, ks, vs, budget_s):
+    """The float64 oracle, as it stands, on a bounded sample: whole states'
+    prefill rows plus their decode rows, until the time budget is used."""
+    from oracle import sata_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    S = w.B * w.H
+    qf = q.reshape(S, w.n, w.d_k).astype(np.float64)
+    kf = k.reshape(S, w.n, w.d_k).astype(np.float64)
+    vf = v.reshape(S, w.n, w.d_v).astype(np.float64)
+    dsteps = qs.shape[0]
+    rows = 0
+    states = 0
+    t0 = time.perf_counter()
+    while states < S and (time.perf_counter() - t0) < budget_s:
+        s = states
+        O.direct_taylor(qf[s], kf[s], vf[s], w.P, w.c)
+        qq = np.concatenate([qf[s], qs[:, s].astype(np.float64)])
+        kk = np.concatenate([kf[s], ks[:, s].astype(np.float64)])
+        vv = np.concatenate([vf[s], vs[:, s].astype(np.float64)])
+        O.direct_taylor(qq, kk, vv, w.P, w.c, rows=np.arange(w.n, w.n + dsteps))
+        rows += w.n + dsteps
+        states += 1
+    el = time.perf_counter() - t0
+    return {"value": rows / el, "unit": "head-tokens/s", "cores": int(blas_threads),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{states} of {S} states: all {w.n} prefill rows and {dsteps} decode rows each "
+                      f"({rows} head-tokens, float64 numpy, {el:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (heads are independent; the multi-GPU "
+              "sharding is a design note only). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import constant_cost_taylor_amd as sa
+    import workloads as W
+    from oracle import sata_oracle as O
+
+    w = W.WORKLOADS["c4_decode"]
+    S = w.B * w.H
+    dsteps = args.decode_steps
+    q, k, v = W.workload_inputs(w)
+    qs, ks, vs = W.decode_inputs(w, dsteps)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    basis = sa.build_basis(w.d_k, w.P, w.c)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(dev)
+    Q, K, V = bf(q), bf(k), bf(v)
+    DQ, DK, DV = bf(qs), bf(ks), bf(vs)
+    state = sa.new_state(basis, S, dev)
+    out = torch.empty((w.B, w.H, w.n, w.d_v), dtype=torch.float32, device=dev)
+    dout = torch.empty((dsteps, S, w.d_v), dtype=torch.float32, device=dev)
+    pws = sa.workspace(sa.prefill_workspace_bytes(basis, w.B, w.H, w.n, w.d_v, sa.SATA_BF16), dev)
+    dws = sa.workspace(sa.decode_workspace_bytes(basis, S, w.d_v, sa.SATA_BF16), dev)
+    stream = torch.cuda.current_stream(dev)
+
+    ev_p = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev_d = [torch.cuda.Event(enable_timing=True) for _ in range(dsteps + 1)]
+    pre_ms, dec_ms = [], []
+
+    def step(record):
+        state.zero_()
+        if record:
+            ev_p[0].record(stream)
+        sa.prefill(basis, Q, K, V, state=state, out=out, ws=pws)
+        if record:
+            ev_p[1].record(stream)
+            ev_d[0].record(stream)
+        for t in range(dsteps):
+            sa.decode_step(basis, DQ[t], DK[t], DV[t], state, out=dout[t], ws=dws)
+            if record:
+                ev_d[t + 1].record(stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        pre_ms.append(ev_p[0].elapsed_time(ev_p[1]))
+        dec_ms.extend(ev_d[t].elapsed_time(ev_d[t + 1]) for t in range(dsteps))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # sanity check of the last step against the oracle on a few decode rows
+    s_chk = [0, S - 1]
+    got = dout[:, s_chk].cpu().numpy()
+    qf = q.reshape(S, w.n, w.d_k)
+    kf = k.reshape(S, w.n, w.d_k)
+    vf = v.reshape(S, w.n, w.d_v)
+    errs = []
+    for j, s in enumerate(s_chk):
+        rr = np.arange(w.n, w.n + dsteps, max(1, dsteps // 16))
+        ref = O.direct_taylor(np.concatenate([qf[s], qs[:, s]]).astype(np.float64),
+                              np.concatenate([kf[s], ks[:, s]]).astype(np.float64),
+                              np.concatenate([vf[s], vs[:, s]]).astype(np.float64), w.P, w.c, rows=rr)
+        errs.append(O.row_normwise_error(got[rr - w.n, j], ref))
+
+    ms_step = 1000.0 * wall / args.steps
+    pre = float(np.median(pre_ms))
+    dec = float(np.mean(dec_ms))
+    D = basis.total_rows
+    state_bytes = 2 * 4 * (w.d_v + 1) * D                  # read + write of one state
+    io_bytes = 3 * w.d_k * 2 + w.d_v * 4                   # q, k, v bf16 in, fp32 out
+    dec_bytes = S * (state_bytes + io_bytes)
+    dec_gbs = dec_bytes / (dec * 1e-3) / 1e9
+    _, page_flops = O.cost_model(w.d_k, w.d_v, w.P)
+    pre_tokens = S * w.n
+    pre_tflops = pre_tokens * page_flops / (pre * 1e-3) / 1e12
+    tokens = S * (w.n + dsteps)
+    value = tokens / (ms_step * 1e-3)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs, f32 state",
+        "data": "synthetic (seeded unit-norm Gaussian q,k; Gaussian v)",
+        "config": {"workload": f"decode workload: {S} states (batch {w.B} x {w.H} heads), d_k=d_v={w.d_k}, "
+                               f"P={w.P}, {w.n}-token prefill + {dsteps} decode steps",
+                   "global_batch": w.B, "heads": w.H, "seq_len": w.n, "decode_steps": dsteps,
+                   "parallelism": "single GPU"},
+        "prefill": {"head_tokens_per_s": pre_tokens / (pre * 1e-3), "ms": pre,
+                    "page_tflops": pre_tflops, "mfma_bf16_frac": pre_tflops / BF16_PEAK_TFLOPS},
+        "decode": {"head_tokens_per_s": S / (dec * 1e-3), "ms_per_step": dec,
+                   "first_last_ratio": float(np.mean(dec_ms[:8]) / np.mean(dec_ms[-8:])),
+                   "hbm_gbs": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": "decode_update_readout", "achieved": dec_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                     "traffic": None},
+        "check": {"decode_row_normwise_err": max(errs)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, qs, ks, vs, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

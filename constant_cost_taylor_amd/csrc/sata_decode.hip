@@ -139,18 +139,32 @@ __global__ __launch_bounds__(kThreads) void decode_update_readout(DecodeArgs a) 
   }
 }
 
+// One block per state: groups of DVP threads sum interleaved tiles, then the
+// groups are combined in a fixed order and num / den is written.
 template <int DV>
-__global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
   constexpr int DVP = padded_dv(DV);
+  constexpr int G = kThreads / DVP;
+  __shared__ float red[G * DVP];
   const int s = blockIdx.x;
-  const int c = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int grp = tid / DVP;
+  const int c = tid % DVP;
   const float* part = a.part + static_cast<int64_t>(s) * a.n_tiles * DVP;
-  float den = 0.f;
-  for (int t = 0; t < a.n_tiles; ++t) den += part[static_cast<int64_t>(t) * DVP + DV];
-  if (c < DV) {
-    float num = 0.f;
-    for (int t = 0; t < a.n_tiles; ++t) num += part[static_cast<int64_t>(t) * DVP + c];
-    a.out[static_cast<int64_t>(s) * DV + c] = num / den;
+  if (grp < G) {
+    float acc = 0.f;
+    for (int t = grp; t < a.n_tiles; t += G) acc += part[static_cast<int64_t>(t) * DVP + c];
+    red[grp * DVP + c] = acc;
+  }
+  __syncthreads();
+  if (tid < DV) {
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      num += red[gg * DVP + tid];
+      den += red[gg * DVP + DV];
+    }
+    a.out[static_cast<int64_t>(s) * DV + tid] = num / den;
   }
 }
 
@@ -163,7 +177,7 @@ hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
     decode_update_readout<D, float><<<grid, kThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_reduce<D><<<a.S, 64, 0, st>>>(a);
+  decode_reduce<D><<<a.S, kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

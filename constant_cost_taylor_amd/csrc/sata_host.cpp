@@ -391,9 +391,8 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
   if (n == 0) return SATA_OK;
-  const size_t esz = dtype == SATA_BF16 ? 2 : 4;
   if (!q || !k || !v || !out || !state) return SATA_ERR_INVALID_ARG;
-  if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) || !aligned(out, 16) ||
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
       !aligned(state, 16))
     return SATA_ERR_INVALID_ARG;
   const int64_t BH = static_cast<int64_t>(B) * H;

@@ -55,10 +55,47 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   return r;
 }
 
+// 16-byte LDS load at an offset the caller guarantees to be a multiple of 4 floats.
+__device__ __forceinline__ float4 lds4(const float* base, int off) {
+  return *reinterpret_cast<const float4*>(__builtin_assume_aligned(base + off, 16));
+}
+
 __device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
+
+// One thread's share of a chunk of q, k or v: EPT consecutive elements of one
+// token, fetched with 16-byte (or narrower) vector loads.
+template <typename IT, int EPT>
+struct ChunkRegs {
+  static constexpr int kBytes = EPT * static_cast<int>(sizeof(IT));
+  static constexpr int kVec = kBytes < 16 ? kBytes : 16;   // bytes per load
+  static constexpr int kLoads = kBytes / kVec;
+  struct alignas(kVec) Piece {
+    unsigned char b[kVec];
+  };
+  Piece p[kLoads];
+  __device__ __forceinline__ void load(const IT* src, bool valid) {
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      if (valid) {
+        p[j] = reinterpret_cast<const Piece*>(src)[j];
+      } else {
+#pragma unroll
+        for (int x = 0; x < kVec; ++x) p[j].b[x] = 0;
+      }
+    }
+  }
+  __device__ __forceinline__ IT raw(int e) const {
+    IT v;
+    __builtin_memcpy(&v, reinterpret_cast<const unsigned char*>(p) + e * sizeof(IT), sizeof(IT));
+    return v;
+  }
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
 template <int DK, bool BF16, int RB>
 struct ScanShape {
@@ -155,9 +192,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         S[b][nb][r] = val * inv_cnt;
       }
     }
+    // Move the block into accumulator registers right away, so the whole
+    // tile is never held in VGPRs at once.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(S[b][nb]));
+    __builtin_amdgcn_sched_barrier(0);  // one row block of loads in flight at a time
   }
-  // bf16 copy of the state used as the readout operand; refreshed after
-  // every update so the fp32 tile never has to leave the accumulators.
+  // bf16 copy of the state used as the readout operand; refreshed right
+  // after every update so the fp32 tile never has to leave the accumulators.
   uint32_t Sb[BF16 ? RB : 1][BF16 ? NB : 1][2];
   if constexpr (BF16) {
 #pragma unroll
@@ -176,35 +218,50 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   float* parth = a.part + static_cast<int64_t>(head) * (n_tiles + 1) * a.nw * DVP +
                  static_cast<int64_t>(tile) * a.nw * DVP;
 
+  // Each thread stages EPT consecutive elements of one token per tensor.
+  constexpr int EPT = L * DK / (kWaves * 64);
+  const int st_t = (tid * EPT) / DK;
+  const int st_i = (tid * EPT) % DK;
+  ChunkRegs<IT, EPT> rq, rk, rv;
+  {
+    const bool ok = st_t < min(L, a.nw);
+    rq.load(qh + (a.t0 + st_t) * DK + st_i, ok);
+    rk.load(kh + (a.t0 + st_t) * DK + st_i, ok);
+    rv.load(vh + (a.t0 + st_t) * DV + st_i, ok);
+  }
+
   const int nch = (a.nw + L - 1) / L;
   for (int ch = 0; ch < nch; ++ch) {
     const int64_t tb = a.t0 + static_cast<int64_t>(ch) * L;
     const int nvalid = min(L, a.nw - ch * L);
+    // Launder the run metadata so the LDS addresses derived from it are
+    // recomputed each chunk (a few integer ops) instead of held live.
+#pragma unroll
+    for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(ks[b]), "+v"(qs[b]));
     __syncthreads();  // previous chunk is done with every LDS buffer
 
-    // Stage the chunk: xq[t][i] = q/c, xk[code][i][t] = k/code, V' columns.
-    for (int e = tid; e < L * DK; e += kWaves * 64) {
-      const int t = e / DK;
-      const int i = e % DK;
-      float qv = 0.f, kv = 0.f;
-      if (t < nvalid) {
-        qv = load_in(qh, (tb + t) * DK + i) * a.inv_c;
-        kv = load_in(kh, (tb + t) * DK + i);
-      }
-      xq[t * XQSTR + i] = qv;
-      xk[i * KSTR + t] = kv;
-      xk[(DK + i) * KSTR + t] = kv * 0.5f;
-      xk[(2 * DK + i) * KSTR + t] = kv * (1.f / 3.f);
+    // Stage the chunk from the registers prefetched during the previous
+    // chunk: xq[t][i] = q/c, xk[code][i][t] = k/code, V' columns.
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const float qv = to_f32(rq.raw(e)) * a.inv_c;
+      const float kv = to_f32(rk.raw(e));
+      xq[st_t * XQSTR + st_i + e] = qv;
+      xk[(st_i + e) * KSTR + st_t] = kv;
+      xk[(DK + st_i + e) * KSTR + st_t] = kv * 0.5f;
+      xk[(2 * DK + st_i + e) * KSTR + st_t] = kv * (1.f / 3.f);
+      if constexpr (BF16)
+        vt[(st_i + e) * VSTR + st_t] = rv.raw(e);
+      else
+        vv[st_t * NC + st_i + e] = rv.raw(e);
     }
-    for (int e = tid; e < L * DV; e += kWaves * 64) {
-      const int t = e / DV;
-      const int c = e % DV;
-      if constexpr (BF16) {
-        const uint16_t* vb = reinterpret_cast<const uint16_t*>(vh);
-        vt[c * VSTR + t] = t < nvalid ? vb[(tb + t) * DV + c] : static_cast<uint16_t>(0);
-      } else {
-        vv[t * NC + c] = t < nvalid ? load_in(vh, (tb + t) * DV + c) : 0.f;
-      }
+    // Prefetch the next chunk; the loads stay in flight through this chunk.
+    if (ch + 1 < nch) {
+      const int64_t tn = tb + L + st_t;
+      const bool ok = st_t < min(L, a.nw - (ch + 1) * L);
+      rq.load(qh + tn * DK + st_i, ok);
+      rk.load(kh + tn * DK + st_i, ok);
+      rv.load(vh + tn * DV + st_i, ok);
     }
     __syncthreads();
 
@@ -253,12 +310,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         for (int mb = 0; mb < L / 16; ++mb) {
           const int t = mb * 16 + lr;
           const float p0 = pq[slot0 * QSTR + t];
-          const float4 x0 = *reinterpret_cast<const float4*>(&xq[t * XQSTR + c00]);
+          const float4 x0 = lds4(xq, t * XQSTR + c00);
           float p1 = 0.f;
           float4 x1 = make_float4(0.f, 0.f, 0.f, 0.f);
           if (has1) {
             p1 = pq[slot1 * QSTR + t];
-            x1 = *reinterpret_cast<const float4*>(&xq[t * XQSTR + c01]);
+            x1 = lds4(xq, t * XQSTR + c01);
           }
           A[mb][0] = static_cast<__bf16>(p0 * x0.x);
           A[mb][1] = static_cast<__bf16>(p0 * x0.y);
@@ -290,7 +347,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         for (int mb = 0; mb < L / 16; ++mb) {
           const int t = mb * 16 + lr;
           const float p = pq[slot * QSTR + t];
-          const float4 x = *reinterpret_cast<const float4*>(&xq[t * XQSTR + c0]);
+          const float4 x = lds4(xq, t * XQSTR + c0);
           const float av[4] = {p * x.x, p * x.y, p * x.z, p * x.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r)
@@ -337,8 +394,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
 
     // State update: S += phi_k(K)^T [V 1] for every row block.  Software
     // pipelined per row block (LDS loads of block b+1 in flight while block b
-    // runs on MFMA; block b-1's new state is repacked to bf16 meanwhile) with
-    // scheduling fences, so only a couple of blocks' temporaries are live.
+    // runs on MFMA) with scheduling fences, so only a couple of blocks'
+    // temporaries are live.
     if constexpr (BF16) {
       bf16x8 Bv[NB];
 #pragma unroll
@@ -348,10 +405,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
       {
         const int pko = ks[0] & 0xffff;
         const int xko = ks[0] >> 16;
-        cp0 = *reinterpret_cast<const float4*>(&pk[pko + 8 * g]);
-        cp1 = *reinterpret_cast<const float4*>(&pk[pko + 8 * g + 4]);
-        cx0 = *reinterpret_cast<const float4*>(&xk[xko + 8 * g]);
-        cx1 = *reinterpret_cast<const float4*>(&xk[xko + 8 * g + 4]);
+        cp0 = lds4(pk, pko + 8 * g);
+        cp1 = lds4(pk, pko + 8 * g + 4);
+        cx0 = lds4(xk, xko + 8 * g);
+        cx1 = lds4(xk, xko + 8 * g + 4);
       }
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
@@ -359,10 +416,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         if (b + 1 < RB) {
           const int pko = ks[b + 1 < RB ? b + 1 : b] & 0xffff;
           const int xko = ks[b + 1 < RB ? b + 1 : b] >> 16;
-          np0 = *reinterpret_cast<const float4*>(&pk[pko + 8 * g]);
-          np1 = *reinterpret_cast<const float4*>(&pk[pko + 8 * g + 4]);
-          nx0 = *reinterpret_cast<const float4*>(&xk[xko + 8 * g]);
-          nx1 = *reinterpret_cast<const float4*>(&xk[xko + 8 * g + 4]);
+          np0 = lds4(pk, pko + 8 * g);
+          np1 = lds4(pk, pko + 8 * g + 4);
+          nx0 = lds4(xk, xko + 8 * g);
+          nx1 = lds4(xk, xko + 8 * g + 4);
         }
         const u32x4 aw = {pack_bf16(cp0.x * cx0.x, cp0.y * cx0.y), pack_bf16(cp0.z * cx0.z, cp0.w * cx0.w),
                           pack_bf16(cp1.x * cx1.x, cp1.y * cx1.y), pack_bf16(cp1.z * cx1.z, cp1.w * cx1.w)};
@@ -373,8 +430,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         if (b > 0) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            Sb[b > 0 ? b - 1 : 0][nb][0] = pack_bf16(S[b > 0 ? b - 1 : 0][nb][0], S[b > 0 ? b - 1 : 0][nb][1]);
-            Sb[b > 0 ? b - 1 : 0][nb][1] = pack_bf16(S[b > 0 ? b - 1 : 0][nb][2], S[b > 0 ? b - 1 : 0][nb][3]);
+            const int bp = b > 0 ? b - 1 : 0;
+            Sb[bp][nb][0] = pack_bf16(S[bp][nb][0], S[bp][nb][1]);
+            Sb[bp][nb][1] = pack_bf16(S[bp][nb][2], S[bp][nb][3]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -433,6 +491,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (tile == 0) {
     __syncthreads();

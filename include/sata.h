@@ -106,8 +106,8 @@ int sata_prefill_workspace(const sata_basis* basis, int B, int H, int n, int d_v
                            size_t* bytes);
 
 /* Causal prefill of n tokens for B*H independent heads.
- *   q, k: [B, H, n, d_k], v: [B, H, n, d_v], contiguous, dtype as given
- *         (4-byte aligned for float32, 2-byte aligned for bfloat16).
+ *   q, k: [B, H, n, d_k], v: [B, H, n, d_v], contiguous, dtype as given,
+ *         16-byte aligned.
  *   out:  [B, H, n, d_v] float32, 16-byte aligned; row i receives
  *         sum_{j<=i} T_P(q_i.k_j/c) v_j / sum_{j<=i} T_P(q_i.k_j/c), where the
  *         sum also runs over the tokens already folded into `state`.
