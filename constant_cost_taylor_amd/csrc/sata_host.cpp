@@ -90,15 +90,19 @@ int upload(sata_basis* b, const std::vector<T>& host, T** dev) {
 }
 
 struct Run {
-  uint32_t parent_key;   // packed parent multiset (order p-1)
-  float parent_weight;   // 1 / prod(count!) of the parent
+  uint32_t parent_key;   // packed parent multiset (order p-1); bit 31 = key-side 1/3 slot
+  float parent_weight;   // 1 / prod(count!) of the parent (query side)
+  float kscale;          // factor of the key-side parent feature
   int c0;                // first child index (multiple of 4)
   int64_t row[4];        // canonical row of each child, -1 = masked
+  int code[4];           // key table of each child: 0 = masked, 1 = k, 2 = k/2
   int cnt[4];            // multiplicity of the child index in the child row
 };
 
-// Runs of four children (P, c0..c0+3) over every parent of order 0..P-2,
-// in canonical row order.
+// Runs of four children (P, c0..c0+3) over every parent of order 0..P-2, in
+// canonical row order.  A child whose index already occurs twice in the
+// parent (the (i, i, i) rows) gets a run of its own, fed by a parent slot
+// whose key feature carries the 1/3, so only the k and k/2 tables are needed.
 std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32_t, int64_t>& rank) {
   std::vector<Run> runs;
   for (int p = 1; p < b.P; ++p) {
@@ -114,27 +118,59 @@ std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32
         cf *= factorial(e - s);
         s = e;
       }
+      auto child_row = [&](int c, int* cnt) {
+        int32_t child[4];
+        for (int s = 0; s < pp; ++s) child[s] = par[s];
+        child[pp] = c;
+        int k = 1;
+        for (int s = 0; s < pp; ++s) k += (par[s] == c);
+        *cnt = k;
+        return rank.at(pack_multiset(child, p));
+      };
       for (int c0 = (lo / 4) * 4; c0 < b.d; c0 += 4) {
         Run run;
         run.parent_key = pack_multiset(par, pp);
         run.parent_weight = static_cast<float>(1.0 / static_cast<double>(cf));
+        run.kscale = 1.f;
         run.c0 = c0;
+        bool any = false;
         for (int j = 0; j < 4; ++j) {
           const int c = c0 + j;
-          if (c < lo) {
-            run.row[j] = -1;
-            run.cnt[j] = 0;
-            continue;
-          }
-          int32_t child[4];
-          for (int s = 0; s < pp; ++s) child[s] = par[s];
-          child[pp] = c;
-          int cnt = 1;
-          for (int s = 0; s < pp; ++s) cnt += (par[s] == c);
-          run.row[j] = rank.at(pack_multiset(child, p));
+          run.row[j] = -1;
+          run.code[j] = 0;
+          run.cnt[j] = 0;
+          if (c < lo) continue;
+          int cnt = 0;
+          const int64_t row = child_row(c, &cnt);
+          if (cnt > 2) continue;   // handled by its own run below
+          run.row[j] = row;
+          run.code[j] = cnt;
           run.cnt[j] = cnt;
+          any = true;
         }
-        runs.push_back(run);
+        if (any) runs.push_back(run);
+      }
+      // The child equal to a twice-repeated last index: k^3/3 = (k^2/3) * k.
+      int cnt = 0;
+      if (pp >= 2) {
+        const int64_t row = child_row(lo, &cnt);
+        if (cnt > 2) {
+          Run run;
+          run.parent_key = pack_multiset(par, pp) | (1u << 31);
+          run.parent_weight = static_cast<float>(1.0 / static_cast<double>(cf));
+          run.kscale = static_cast<float>(1.0 / cnt);
+          run.c0 = (lo / 4) * 4;
+          for (int j = 0; j < 4; ++j) {
+            run.row[j] = -1;
+            run.code[j] = 0;
+            run.cnt[j] = 0;
+          }
+          const int j = lo - run.c0;
+          run.row[j] = row;
+          run.code[j] = 1;
+          run.cnt[j] = cnt;
+          runs.push_back(run);
+        }
       }
     }
   }
@@ -142,70 +178,93 @@ std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32
 }
 
 int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& rank, bool bf16,
-                 PrefillLayout* lay) {
+                 bool upload_tables, PrefillLayout* lay) {
   const int rb = sata::prefill_rb(b->d, bf16);
-  const int per_tile = 4 * rb * sata::kWaves;
-  const int kstr = sata::kKStride;
-  const int xk_zero = 3 * b->d * kstr;
+  const int per_tile = sata::prefill_runs_per_tile(b->d, bf16);
+  const int max_slots = sata::prefill_slots(b->d, bf16);
+  const int kstr = sata::prefill_kstride(bf16);
+  const int xk_zero = 2 * b->d * kstr;
   lay->rb = rb;
-  // With P = 1 there are no runs, but one (empty) tile still carries the
-  // order-0 row, so every layout has at least one tile.
   const std::vector<Run> runs = build_runs(*b, rank);
-  const int n_tiles = std::max(1, static_cast<int>((runs.size() + per_tile - 1) / per_tile));
-  std::vector<uint32_t> kside(static_cast<size_t>(n_tiles) * sata::kWaves * rb * 16, 0);
-  std::vector<uint32_t> qside(static_cast<size_t>(n_tiles) * sata::kWaves * rb * 4, 0);
-  std::vector<uint32_t> rowinfo(static_cast<size_t>(n_tiles) * sata::kWaves * rb * 16, 0);
-  std::vector<uint32_t> parents(static_cast<size_t>(n_tiles) * per_tile, 0);
-  std::vector<float> pweight(static_cast<size_t>(n_tiles) * per_tile, 0.f);
+  // Greedy tiling in canonical order: a tile takes runs until it is full or
+  // one more run would exceed the parent-slot cap.  With P = 1 there are no
+  // runs, but one (empty) tile still carries the order-0 row.
+  std::vector<std::vector<int>> tiles;
+  {
+    std::vector<int> cur;
+    std::unordered_map<uint32_t, int> keys;
+    for (int ri = 0; ri < static_cast<int>(runs.size()); ++ri) {
+      const bool new_key = keys.find(runs[ri].parent_key) == keys.end();
+      if (static_cast<int>(cur.size()) == per_tile ||
+          (new_key && static_cast<int>(keys.size()) == max_slots)) {
+        tiles.push_back(cur);
+        cur.clear();
+        keys.clear();
+      }
+      keys.emplace(runs[ri].parent_key, 0);
+      cur.push_back(ri);
+    }
+    if (!cur.empty() || tiles.empty()) tiles.push_back(cur);
+  }
+  const int n_tiles = static_cast<int>(tiles.size());
+  const size_t nblk = static_cast<size_t>(n_tiles) * sata::kWaves * rb;
+  std::vector<uint32_t> kside(nblk * 16, 0);
+  std::vector<uint32_t> qside(nblk * 4, 0);
+  std::vector<uint32_t> rowinfo(nblk * 16, 0);
+  std::vector<uint32_t> parents(static_cast<size_t>(n_tiles) * max_slots, 0);
+  std::vector<float> pweight(static_cast<size_t>(n_tiles) * max_slots, 0.f);
+  std::vector<float> kscale(static_cast<size_t>(n_tiles) * max_slots, 0.f);
   std::vector<int32_t> nslot(n_tiles, 0);
   for (int t = 0; t < n_tiles; ++t) {
     std::unordered_map<uint32_t, int> slot_of;
     for (int u = 0; u < per_tile; ++u) {
-      const size_t ri = static_cast<size_t>(t) * per_tile + u;
       const int w = u / (4 * rb);
       const int bl = (u / 4) % rb;
       const int g = u % 4;
       const size_t blk = (static_cast<size_t>(t) * sata::kWaves + w) * rb + bl;
-      if (ri >= runs.size()) {
+      if (u >= static_cast<int>(tiles[t].size())) {
         // Empty run: masked children reading the zero row, parent slot 0.
         for (int j = 0; j < 4; ++j) kside[blk * 16 + 4 * g + j] = static_cast<uint32_t>(xk_zero) << 16;
         qside[blk * 4 + g] = 0;
         continue;
       }
-      const Run& run = runs[ri];
+      const Run& run = runs[tiles[t][u]];
       auto it = slot_of.find(run.parent_key);
       int slot;
       if (it == slot_of.end()) {
         slot = static_cast<int>(slot_of.size());
         slot_of.emplace(run.parent_key, slot);
-        parents[static_cast<size_t>(t) * per_tile + slot] =
-            (run.parent_key & 0xffffu) | (((run.parent_key >> 24) & 3u) << 16);
-        pweight[static_cast<size_t>(t) * per_tile + slot] = run.parent_weight;
+        const size_t si = static_cast<size_t>(t) * max_slots + slot;
+        parents[si] = (run.parent_key & 0xffffu) | (((run.parent_key >> 24) & 3u) << 16);
+        pweight[si] = run.parent_weight;
+        kscale[si] = run.kscale;
       } else {
         slot = it->second;
       }
       qside[blk * 4 + g] = static_cast<uint32_t>(slot) | (static_cast<uint32_t>(run.c0) << 16);
       for (int j = 0; j < 4; ++j) {
-        const int code = run.cnt[j];
+        const int code = run.code[j];
         const uint32_t pko = static_cast<uint32_t>(slot * kstr);
         const uint32_t xko = code == 0 ? static_cast<uint32_t>(xk_zero)
                                        : static_cast<uint32_t>(((code - 1) * b->d + run.c0 + j) * kstr);
         kside[blk * 16 + 4 * g + j] = pko | (xko << 16);
         if (run.row[j] >= 0)
           rowinfo[blk * 16 + 4 * g + j] =
-              static_cast<uint32_t>(run.row[j] + 1) | (static_cast<uint32_t>(code) << 28);
+              static_cast<uint32_t>(run.row[j] + 1) | (static_cast<uint32_t>(run.cnt[j]) << 28);
       }
     }
     // Every tile has at least one parent slot so empty runs read finite features.
     nslot[t] = std::max(1, static_cast<int32_t>(slot_of.size()));
   }
   lay->n_tiles = n_tiles;
+  if (!upload_tables) return SATA_OK;
   int st;
   if ((st = upload(b, kside, &lay->kside)) != SATA_OK) return st;
   if ((st = upload(b, qside, &lay->qside)) != SATA_OK) return st;
   if ((st = upload(b, rowinfo, &lay->rowinfo)) != SATA_OK) return st;
   if ((st = upload(b, parents, &lay->parents)) != SATA_OK) return st;
   if ((st = upload(b, pweight, &lay->pweight)) != SATA_OK) return st;
+  if ((st = upload(b, kscale, &lay->kscale)) != SATA_OK) return st;
   if ((st = upload(b, nslot, &lay->nslot)) != SATA_OK) return st;
   return SATA_OK;
 }
@@ -231,19 +290,39 @@ int check_device(const sata_basis* b) {
   return dev == b->device ? SATA_OK : SATA_ERR_INVALID_ARG;
 }
 
-// Tokens per prefill window and the workspace it needs.  The window bounds
-// the per-tile readout records kept in the workspace (at most kPrefillWsCap).
+// Tokens per prefill window and the workspace it needs (records of one
+// window; the window is bounded so that they fit kPrefillWsCap).
 constexpr size_t kPrefillWsCap = size_t(16) << 30;
 
-void prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype, int64_t* nw, size_t* bytes) {
+struct PrefillPlan {
+  int64_t nw = 0;         // tokens per window
+  int64_t nwp = 0;        // nw rounded up to 64
+  size_t rec_bytes = 0;   // per-tile records
+  size_t intra_bytes = 0;
+  size_t carry_bytes = 0;
+  size_t total = 0;
+};
+
+PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) {
+  const bool bf16 = dtype == SATA_BF16;
   const int nt = b->lay[dtype].n_tiles;
-  const int64_t per_token = BH * (nt + 1) * sata::padded_dv(b->d) * 4;
-  int64_t w = static_cast<int64_t>(kPrefillWsCap / static_cast<size_t>(per_token));
-  w = std::max<int64_t>(sata::kChunk, (w / sata::kChunk) * sata::kChunk);
-  const int64_t nround = (n + sata::kChunk - 1) / sata::kChunk * sata::kChunk;
-  w = std::min(w, std::max<int64_t>(nround, sata::kChunk));
-  *nw = w;
-  *bytes = static_cast<size_t>(per_token) * static_cast<size_t>(w);
+  const int dvp = sata::padded_dv(b->d);
+  const int L = sata::prefill_chunk(bf16);
+  const size_t rec_elt = sata::prefill_bf16_records(b->d, bf16) ? 2 : 4;
+  // bytes per token of window (records + intra) and per chunk (carry)
+  const size_t per_token = static_cast<size_t>(BH) * dvp * (nt * rec_elt + 4);
+  int64_t w = static_cast<int64_t>(kPrefillWsCap / per_token);
+  w = std::max<int64_t>(64, (w / 64) * 64);
+  const int64_t nround = std::max<int64_t>(64, (n + 63) / 64 * 64);
+  PrefillPlan pl;
+  pl.nw = std::min(w, nround);
+  pl.nwp = (pl.nw + 63) / 64 * 64;
+  pl.rec_bytes = static_cast<size_t>(BH) * nt * dvp * pl.nwp * rec_elt;
+  pl.intra_bytes = static_cast<size_t>(BH) * dvp * pl.nwp * 4;
+  pl.carry_bytes = static_cast<size_t>(BH) * ((pl.nwp + L - 1) / L) * dvp * 4;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  pl.total = up(pl.rec_bytes) + up(pl.intra_bytes) + up(pl.carry_bytes);
+  return pl;
 }
 
 int decode_tiles(const sata_basis* b) {
@@ -292,6 +371,12 @@ static int build_basis_impl(int d_k, int P, double c, bool upload_tables, sata_b
   }
   b->D = total;
   if (!upload_tables) {
+    int st = build_layout(b, rank, false, false, &b->lay[0]);
+    if (st == SATA_OK) st = build_layout(b, rank, true, false, &b->lay[1]);
+    if (st != SATA_OK) {
+      release(b);
+      return st;
+    }
     *out = b;
     return SATA_OK;
   }
@@ -302,8 +387,8 @@ static int build_basis_impl(int d_k, int P, double c, bool upload_tables, sata_b
   }
   int st = upload(b, b->packed, &b->d_rows);
   if (st == SATA_OK) st = upload(b, b->weight, &b->d_weight);
-  if (st == SATA_OK) st = build_layout(b, rank, false, &b->lay[0]);
-  if (st == SATA_OK) st = build_layout(b, rank, true, &b->lay[1]);
+  if (st == SATA_OK) st = build_layout(b, rank, false, true, &b->lay[0]);
+  if (st == SATA_OK) st = build_layout(b, rank, true, true, &b->lay[1]);
   if (st != SATA_OK) {
     release(b);
     return st;
@@ -378,9 +463,7 @@ int sata_prefill_workspace(const sata_basis* b, int B, int H, int n, int d_v, in
   if (!b || !bytes || B < 1 || H < 1 || n < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
-  int64_t nw = 0;
-  prefill_plan(b, static_cast<int64_t>(B) * H, n, dtype, &nw, bytes);
-  if (n == 0) *bytes = 0;
+  *bytes = n == 0 ? 0 : prefill_plan(b, static_cast<int64_t>(B) * H, n, dtype).total;
   return SATA_OK;
 }
 
@@ -397,28 +480,30 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
     return SATA_ERR_INVALID_ARG;
   const int64_t BH = static_cast<int64_t>(B) * H;
   if (BH > 65535) return SATA_ERR_UNSUPPORTED;  // grid y limit
-  int64_t nw = 0;
-  size_t need = 0;
-  prefill_plan(b, BH, n, dtype, &nw, &need);
-  if (need > 0 && (!ws || ws_bytes < need)) return SATA_ERR_WORKSPACE;
+  const PrefillPlan pl = prefill_plan(b, BH, n, dtype);
+  if (!ws || ws_bytes < pl.total) return SATA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
   if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SATA_BF16;
   const PrefillLayout& lay = b->lay[dtype];
   const int64_t stride = sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D);
-  for (int64_t t0 = 0; t0 < n; t0 += nw) {
-    const int w = static_cast<int>(std::min<int64_t>(nw, n - t0));
-    sata::IntraArgs ia{q, k, v, static_cast<float*>(ws), n, t0, w, lay.n_tiles, b->P,
-                       static_cast<float>(1.0 / b->c)};
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* base = static_cast<char*>(ws);
+  sata::PrefillWs pw{base, reinterpret_cast<float*>(base + up(pl.rec_bytes)),
+                     reinterpret_cast<float*>(base + up(pl.rec_bytes) + up(pl.intra_bytes)),
+                     static_cast<int>(pl.nwp)};
+  const float inv_c = static_cast<float>(1.0 / b->c);
+  for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
+    const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
+    sata::IntraArgs ia{q, k, v, pw, n, t0, w, b->P, inv_c};
     if (sata::launch_prefill_intra(b->d, bf16, static_cast<int>(BH), ia, s) != hipSuccess)
       return SATA_ERR_HIP;
-    sata::ScanArgs sa{q, k, v, state, stride, static_cast<float*>(ws), lay, n, t0, w,
-                      static_cast<int>(b->D), static_cast<float>(1.0 / b->c)};
+    sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c};
     if (sata::launch_prefill_scan(b->d, bf16, static_cast<int>(BH), sa, s) != hipSuccess)
       return SATA_ERR_HIP;
-    sata::ReduceArgs ra{static_cast<const float*>(ws), out, n, t0, w, lay.n_tiles + 1};
-    if (sata::launch_prefill_reduce(b->d, static_cast<int>(BH), ra, s) != hipSuccess)
+    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles};
+    if (sata::launch_prefill_reduce(b->d, bf16, static_cast<int>(BH), ra, s) != hipSuccess)
       return SATA_ERR_HIP;
   }
   return SATA_OK;

@@ -9,43 +9,62 @@
 
 namespace sata {
 
-// Waves per prefill workgroup and tokens per prefill chunk.
+// Waves per prefill workgroup.
 constexpr int kWaves = 4;
-constexpr int kChunk = 32;
 
 // Rows of one decode tile and threads of every decode / reduce block.
-constexpr int kDecodeRows = 1024;
+constexpr int kDecodeRows = 512;
 constexpr int kThreads = 256;
 
+// Tokens per prefill chunk: 64 for bf16 inputs (the readout operand of the
+// state is refreshed once per chunk, so longer chunks amortise it), 32 for
+// fp32 inputs (fp32 cross-wave buffers would not fit LDS at 64).
+constexpr int prefill_chunk(bool bf16) { return bf16 ? 64 : 32; }
+
 // Row blocks of 16 rows per wave held on chip by the prefill scan, per
-// (head dim, input dtype).  Sized so that the fp32 state tile plus the readout
-// accumulators fit the 512 registers a lane owns at one wave per SIMD.
+// (head dim, input dtype): the fp32 state tile (rb * column blocks * 4
+// registers) plus the readout accumulators must fit the 256 accumulator
+// registers of a lane at one wave per SIMD.
 constexpr int prefill_rb(int d, bool bf16) {
-  return d == 64 ? (bf16 ? 12 : 8) : d == 32 ? 8 : d == 16 ? (bf16 ? 8 : 4) : (bf16 ? 2 : 1);
+  return d == 64 ? 8 : d == 32 ? 8 : d == 16 ? (bf16 ? 8 : 4) : (bf16 ? 2 : 1);
 }
+
+// Runs of four rows per tile and the cap on distinct parent multisets per
+// tile (the per-chunk parent-feature tables are sized by it).
+constexpr int prefill_runs_per_tile(int d, bool bf16) { return 4 * prefill_rb(d, bf16) * kWaves; }
+constexpr int prefill_slots(int d, bool bf16) {
+  return prefill_runs_per_tile(d, bf16) < 80 ? prefill_runs_per_tile(d, bf16) : 80;
+}
+
+// LDS row stride (floats) of the key / parent-feature tables.
+constexpr int prefill_kstride(bool bf16) { return prefill_chunk(bf16) + 4; }
+
+// Readout records are bf16 for bf16 inputs at d >= 32 (the per-tile partial
+// sums there are small next to the order-0 and intra-chunk terms, which stay
+// fp32), fp32 otherwise.
+constexpr bool prefill_bf16_records(int d, bool bf16) { return bf16 && d >= 32; }
 
 // Floats between consecutive heads' states: the state size rounded up to a
 // multiple of 64 floats, so every head's S rows start 256-byte aligned.
 constexpr int64_t state_stride(int64_t state_floats) { return (state_floats + 63) & ~int64_t(63); }
 
-// LDS row strides of the prefill scan (floats): key / parent-feature tables.
-constexpr int kKStride = kChunk + 4;
-
-// Padded widths of the per-token readout records written to the workspace.
+// Padded widths of the per-token readout records (value columns + den).
 constexpr int padded_dv(int dv) { return (dv + 1 + 3) & ~3; }
 // Column blocks of 16 (value columns plus the z column).
 constexpr int col_blocks(int dv) { return (dv + 1 + 15) / 16; }
 
 // One internal tile layout of the prefill scan (device arrays).
-//   kside[tile][wave][rb][16]: LDS dword offsets used by lane row j of a row
-//       block to build its key features: low 16 bits = parent row in the
-//       parent-feature table, high 16 bits = child row in the scaled key table.
+//   kside[tile][wave][rb][16]: LDS offsets (floats) used by lane row j of a
+//       row block to build its key features: low 16 bits = parent row of the
+//       parent-feature table, high 16 bits = child row of the key table.
 //   qside[tile][wave][rb][4]: parent slot (low 16 bits) and first child index
 //       (high 16 bits) of the run held by lane group g.
 //   rowinfo[tile][wave][rb][16]: (canonical row + 1) | (count << 28), 0 = pad.
-//   parents[tile][slot]: i1 | i2 << 8 | order << 16 of each distinct parent,
-//   pweight[tile][slot]: 1 / prod(count!) of that parent.
-//   nslot[tile]: number of distinct parents of the tile.
+//   parents[tile][slot]: i1 | i2 << 8 | order << 16 of each parent slot;
+//   pweight[tile][slot]: 1 / prod(count!) of that parent (query side);
+//   kscale[tile][slot]: factor of the key-side parent feature (1, or 1/3 for
+//       the slot that feeds the (i, i, i) rows).
+//   nslot[tile]: number of parent slots of the tile.
 struct PrefillLayout {
   int rb = 0;
   int n_tiles = 0;
@@ -54,7 +73,19 @@ struct PrefillLayout {
   uint32_t* rowinfo = nullptr;
   uint32_t* parents = nullptr;
   float* pweight = nullptr;
+  float* kscale = nullptr;
   int32_t* nslot = nullptr;
+};
+
+// Prefill workspace of one window of nw tokens (nwp = nw rounded up to 64):
+//   rec:   [BH][n_tiles][DVP][nwp]  per-tile readout records (bf16 or fp32)
+//   intra: [BH][DVP][nwp]           intra-chunk records (fp32)
+//   carry: [BH][nchunk][DVP]        order-0 prefix at each chunk start (fp32)
+struct PrefillWs {
+  void* rec;
+  float* intra;
+  float* carry;
+  int nwp;
 };
 
 struct ScanArgs {
@@ -63,7 +94,7 @@ struct ScanArgs {
   const void* v;
   float* state;          // [BH][stride]
   int64_t stride;        // floats between consecutive heads' states
-  float* part;           // [BH][n_tiles + 1][nw][DVP]
+  PrefillWs ws;
   PrefillLayout lay;
   int64_t n_total;       // tokens per head in q/k/v/out
   int64_t t0;            // first token of this window
@@ -76,22 +107,21 @@ struct IntraArgs {
   const void* q;
   const void* k;
   const void* v;
-  float* part;           // slot n_tiles of [BH][n_tiles + 1][nw][DVP]
+  PrefillWs ws;
   int64_t n_total;
   int64_t t0;
   int nw;
-  int n_tiles;
   int P;
   float inv_c;
 };
 
 struct ReduceArgs {
-  const float* part;
+  PrefillWs ws;
   float* out;            // [BH][n_total][dv]
   int64_t n_total;
   int64_t t0;
   int nw;
-  int nslots;            // n_tiles + 1
+  int n_tiles;
 };
 
 struct DecodeArgs {
@@ -113,7 +143,7 @@ struct DecodeArgs {
 // the launch error.
 hipError_t launch_prefill_scan(int d, bool bf16, int BH, const ScanArgs& a, hipStream_t s);
 hipError_t launch_prefill_intra(int d, bool bf16, int BH, const IntraArgs& a, hipStream_t s);
-hipError_t launch_prefill_reduce(int d, int BH, const ReduceArgs& a, hipStream_t s);
+hipError_t launch_prefill_reduce(int d, bool bf16, int BH, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_decode(int d, bool bf16, const DecodeArgs& a, hipStream_t s);
 
 }  // namespace sata

@@ -1,12 +1,13 @@
 // Chunked causal prefill of SATA on gfx950 (CDNA4).
 //
-// The sequence is cut into chunks of kChunk tokens.  For a query i in chunk t
+// The sequence is cut into chunks of L tokens.  For a query i in chunk t
 //   num_i = sum_{j <= i, j in t} T_P(x_ij) v_j            (intra-chunk, exact polynomial)
-//         + sum_m w_m phi_m(q_i) S_m(<t)                  (inter-chunk, through the state)
-// and likewise for den with v replaced by 1.  The state S(<t) holds every
-// key before chunk t [SATA page, section "Engineering of constant compute
-// cost": the fixed-size state accumulates phi(k) v over the processed
-// tokens, one scan per Taylor order].
+//         + sum_{j before t} v_j                          (order 0, carried exactly)
+//         + sum_{m of order >= 1} w_m phi_m(q_i) S_m(<t)  (inter-chunk, through the state)
+// and likewise for den with v replaced by 1.  S(<t) holds every key before
+// chunk t [SATA page, section "Engineering of constant compute cost": the
+// fixed-size state accumulates phi(k) v over the processed tokens, one scan
+// per Taylor order].
 //
 // Kernels:
 //   prefill_scan   grid = (row tiles) x (heads).  A workgroup owns a tile of
@@ -16,11 +17,11 @@
 //                  (each row = parent feature x one more coordinate, the
 //                  nested i1 <= ... <= ip structure of the index matrices),
 //                  reads out  phi_q(Q_t) S  and updates  S += phi_k(K_t)^T [V_t 1]
-//                  on MFMA (bf16 operands for bf16 inputs, fp32 otherwise).
-//                  The order-0 row (the running sum of v and the token count)
-//                  is carried exactly in fp32 by tile 0.
+//                  on MFMA (bf16 operands for bf16 inputs, fp32 otherwise),
+//                  and writes one readout record per token.  Tile 0 also
+//                  records the exact order-0 prefix of every chunk.
 //   prefill_intra  grid = (chunks) x (heads): the intra-chunk part, fp32.
-//   prefill_reduce sums the per-tile readout records in a fixed order and divides.
+//   prefill_reduce sums the records in a fixed order and divides.
 //
 // Internal row order.  The rows of a tile are grouped in runs of four
 // children (P, c0..c0+3) of one parent multiset P (c0 a multiple of 4,
@@ -28,7 +29,14 @@
 // m = P + {c} is kept divided by cnt_c(m), the multiplicity of c in m; the
 // query features then factor as [w(P) prod_{i in P} q_i/c] * q_c/c, with w(P)
 // = 1/prod(count!) of the parent, and the key features as
-// [prod_{i in P} k_i] * k_c/cnt_c(m).
+// [prod_{i in P} k_i] * k_c/cnt_c(m) (the 1/3 of the (i, i, i) rows sits on a
+// parent slot of its own).
+//
+// One chunk takes three barrier-separated phases:
+//   A  cross-wave sum of the previous chunk's readout (writes its records)
+//      and staging of this chunk from registers prefetched a chunk earlier;
+//   B  parent features of the tile's parent slots (+ the order-0 carry);
+//   C  readout into the LDS reduction buffer, then the state update.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -39,11 +47,10 @@ namespace sata {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Two floats rounded to bf16 (nearest even) and packed in one register.  The
 // empty asm pins the conversion at this point of the program, so the
@@ -55,6 +62,9 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   return r;
 }
 
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // 16-byte LDS load at an offset the caller guarantees to be a multiple of 4 floats.
 __device__ __forceinline__ float4 lds4(const float* base, int off) {
   return *reinterpret_cast<const float4*>(__builtin_assume_aligned(base + off, 16));
@@ -64,6 +74,8 @@ __device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i
 __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
 // One thread's share of a chunk of q, k or v: EPT consecutive elements of one
 // token, fetched with 16-byte (or narrower) vector loads.
@@ -94,44 +106,50 @@ struct ChunkRegs {
   }
 };
 
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
-
-template <int DK, bool BF16, int RB>
-struct ScanShape {
+template <int DK, bool BF16>
+struct Cfg {
   static constexpr int DV = DK;
-  static constexpr int L = kChunk;
-  static constexpr int NB = col_blocks(DV);     // 16-wide column blocks incl. z
+  static constexpr int L = prefill_chunk(BF16);
+  static constexpr int RB = prefill_rb(DK, BF16);
+  static constexpr int NB = col_blocks(DV);        // 16-wide column blocks incl. z
   static constexpr int NC = NB * 16;
   static constexpr int DVP = padded_dv(DV);
-  static constexpr int NSLOT = 4 * RB * kWaves;  // bound on distinct parents per tile
-  static constexpr int KSTR = kKStride;          // xk / pk row stride (floats)
-  static constexpr int QSTR = L + 1;             // pq row stride
-  static constexpr int XQSTR = DK + 4;           // xq row stride
-  static constexpr int RSTR = NC + 4;            // readout reduction row stride
-  static constexpr int VSTR = L + 8;             // bf16 V' row stride (elements)
-  static constexpr int XK_ZERO = 3 * DK * KSTR;  // dword offset of the zero row
-  static constexpr int NKS = (RB + 1) / 2;       // bf16 readout K-slices (2 blocks each)
+  static constexpr int NSLOT = prefill_slots(DK, BF16);
+  static constexpr int KSTR = prefill_kstride(BF16); // xk / pk row stride (floats)
+  static constexpr int QSTR = L + 1;                 // pq row stride
+  static constexpr int XQSTR = DK + 4;               // xq row stride
+  static constexpr bool RECB = prefill_bf16_records(DK, BF16);
+  static constexpr int RSTR = RECB ? L + 8 : L + 4;  // reduction row stride (elements)
+  static constexpr int VSTR = L + 8;                 // bf16 V' row stride (elements)
+  static constexpr int XK_ZERO = 2 * DK * KSTR;      // offset of the zero row
+  static constexpr int NKS = (RB + 1) / 2;           // bf16 readout K-slices (2 blocks each)
+  static constexpr int MB = L / 16;                  // 16-token blocks per chunk
+  static constexpr int EPT = L * DK / (kWaves * 64); // staged elements per thread and tensor
+  static constexpr int TPG = L / (RECB ? 8 : 4);     // token groups of the cross-wave sum
+  using IT = typename std::conditional<BF16, uint16_t, float>::type;
+  using RedT = typename std::conditional<RECB, uint16_t, float>::type;
 };
 
-template <int DK, bool BF16, int RB>
+template <int DK, bool BF16>
 __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
-  using Sh = ScanShape<DK, BF16, RB>;
-  constexpr int DV = Sh::DV, L = Sh::L, NB = Sh::NB, NC = Sh::NC, DVP = Sh::DVP;
-  constexpr int NSLOT = Sh::NSLOT, KSTR = Sh::KSTR, QSTR = Sh::QSTR, XQSTR = Sh::XQSTR;
-  constexpr int RSTR = Sh::RSTR, VSTR = Sh::VSTR, XK_ZERO = Sh::XK_ZERO;
-  using IT = typename std::conditional<BF16, uint16_t, float>::type;
+  using C = Cfg<DK, BF16>;
+  constexpr int DV = C::DV, L = C::L, RB = C::RB, NB = C::NB, NC = C::NC, DVP = C::DVP;
+  constexpr int NSLOT = C::NSLOT, KSTR = C::KSTR, QSTR = C::QSTR, XQSTR = C::XQSTR;
+  constexpr int RSTR = C::RSTR, VSTR = C::VSTR, XK_ZERO = C::XK_ZERO, MB = C::MB, EPT = C::EPT;
+  using IT = typename C::IT;
+  using RedT = typename C::RedT;
 
-  __shared__ __attribute__((aligned(16))) float xk[(3 * DK + 1) * KSTR];
+  __shared__ __attribute__((aligned(16))) float xk[(2 * DK + 1) * KSTR];
   __shared__ __attribute__((aligned(16))) float pk[NSLOT * KSTR];
   __shared__ __attribute__((aligned(16))) float pq[NSLOT * QSTR];
   __shared__ __attribute__((aligned(16))) float xq[L * XQSTR];
-  __shared__ __attribute__((aligned(16))) float red[kWaves * L * RSTR];
+  __shared__ __attribute__((aligned(16))) RedT red[kWaves * (DV + 1) * RSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vt[BF16 ? NC * VSTR : 8];
   __shared__ __attribute__((aligned(16))) float vv[BF16 ? 4 : L * NC];
   __shared__ float carry[NC];
   __shared__ uint32_t spar[NSLOT];
-  __shared__ float spw[NSLOT];
+  __shared__ float spwq[NSLOT];
+  __shared__ float spwk[NSLOT];
 
   const int tile = blockIdx.x;
   const int head = blockIdx.y;
@@ -153,7 +171,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   const int nslot = a.lay.nslot[tile];
   for (int s = tid; s < nslot; s += kWaves * 64) {
     spar[s] = a.lay.parents[tile * NSLOT + s];
-    spw[s] = a.lay.pweight[tile * NSLOT + s];
+    spwq[s] = a.lay.pweight[tile * NSLOT + s];
+    spwk[s] = a.lay.kscale[tile * NSLOT + s];
   }
   for (int i = tid; i < KSTR; i += kWaves * 64) xk[XK_ZERO + i] = 0.f;
   if constexpr (BF16) {
@@ -196,18 +215,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     // tile is never held in VGPRs at once.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(S[b][nb]));
-    __builtin_amdgcn_sched_barrier(0);  // one row block of loads in flight at a time
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // bf16 copy of the state used as the readout operand; refreshed right
-  // after every update so the fp32 tile never has to leave the accumulators.
-  uint32_t Sb[BF16 ? RB : 1][BF16 ? NB : 1][2];
+  // bf16 copy of the state used as the readout operand, grouped per readout
+  // K-slice (two row blocks): refreshed right after every update.
+  u32x4 Sb[BF16 ? C::NKS : 1][BF16 ? NB : 1];
   if constexpr (BF16) {
 #pragma unroll
-    for (int b = 0; b < RB; ++b)
+    for (int kk = 0; kk < C::NKS; ++kk)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        Sb[b][nb][0] = pack_bf16(S[b][nb][0], S[b][nb][1]);
-        Sb[b][nb][1] = pack_bf16(S[b][nb][2], S[b][nb][3]);
+        Sb[kk][nb][0] = pack_bf16(S[2 * kk][nb][0], S[2 * kk][nb][1]);
+        Sb[kk][nb][1] = pack_bf16(S[2 * kk][nb][2], S[2 * kk][nb][3]);
+        Sb[kk][nb][2] = 2 * kk + 1 < RB ? pack_bf16(S[2 * kk + 1 < RB ? 2 * kk + 1 : 0][nb][0],
+                                                    S[2 * kk + 1 < RB ? 2 * kk + 1 : 0][nb][1]) : 0u;
+        Sb[kk][nb][3] = 2 * kk + 1 < RB ? pack_bf16(S[2 * kk + 1 < RB ? 2 * kk + 1 : 0][nb][2],
+                                                    S[2 * kk + 1 < RB ? 2 * kk + 1 : 0][nb][3]) : 0u;
       }
   }
   if (tile == 0 && tid < NC) carry[tid] = tid < DV ? st[tid] : (tid == DV ? st[zoff] : 0.f);
@@ -215,13 +238,47 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   const IT* qh = static_cast<const IT*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
   const IT* kh = static_cast<const IT*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
   const IT* vh = static_cast<const IT*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
-  float* parth = a.part + static_cast<int64_t>(head) * (n_tiles + 1) * a.nw * DVP +
-                 static_cast<int64_t>(tile) * a.nw * DVP;
+  const int nwp = a.ws.nwp;
+  RedT* rech = static_cast<RedT*>(a.ws.rec) +
+               (static_cast<int64_t>(head) * n_tiles + tile) * DVP * static_cast<int64_t>(nwp);
+  const int nch = (a.nw + L - 1) / L;
+  float* carryh = a.ws.carry + static_cast<int64_t>(head) * ((nwp + L - 1) / L) * DVP;
 
-  // Each thread stages EPT consecutive elements of one token per tensor.
-  constexpr int EPT = L * DK / (kWaves * 64);
-  const int st_t = (tid * EPT) / DK;
-  const int st_i = (tid * EPT) % DK;
+  // Cross-wave sum of one chunk's readout (LDS red) into its records.
+  auto red_sum = [&](int ch) {
+    for (int e = tid; e < (DV + 1) * C::TPG; e += kWaves * 64) {
+      const int c = e / C::TPG;
+      const int tg = e % C::TPG;
+      if constexpr (C::RECB) {
+        float sum[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum[j] = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 8 * tg]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sum[2 * j] += bf16_lo(x[j]);
+            sum[2 * j + 1] += bf16_hi(x[j]);
+          }
+        }
+        const u32x4 o = {pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3]), pack_bf16(sum[4], sum[5]),
+                         pack_bf16(sum[6], sum[7])};
+        *reinterpret_cast<u32x4*>(&rech[static_cast<int64_t>(c) * nwp + ch * L + 8 * tg]) = o;
+      } else {
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww)
+          sum += *reinterpret_cast<const f32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 4 * tg]);
+        *reinterpret_cast<f32x4*>(&rech[static_cast<int64_t>(c) * nwp + ch * L + 4 * tg]) = sum;
+      }
+    }
+  };
+
+  // Each thread stages EPT consecutive elements of one token per tensor;
+  // consecutive lanes take consecutive tokens (conflict-free transposed writes).
+  const int st_t = tid % L;
+  const int st_i = (tid / L) * EPT;
   ChunkRegs<IT, EPT> rq, rk, rv;
   {
     const bool ok = st_t < min(L, a.nw);
@@ -230,7 +287,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     rv.load(vh + (a.t0 + st_t) * DV + st_i, ok);
   }
 
-  const int nch = (a.nw + L - 1) / L;
   for (int ch = 0; ch < nch; ++ch) {
     const int64_t tb = a.t0 + static_cast<int64_t>(ch) * L;
     const int nvalid = min(L, a.nw - ch * L);
@@ -238,18 +294,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     // recomputed each chunk (a few integer ops) instead of held live.
 #pragma unroll
     for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(ks[b]), "+v"(qs[b]));
-    __syncthreads();  // previous chunk is done with every LDS buffer
 
-    // Stage the chunk from the registers prefetched during the previous
-    // chunk: xq[t][i] = q/c, xk[code][i][t] = k/code, V' columns.
+    // ---- phase A: previous chunk's records, then stage this chunk --------
+    if (ch > 0) red_sum(ch - 1);
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      float4 q4;
+      q4.x = to_f32(rq.raw(e)) * a.inv_c;
+      q4.y = to_f32(rq.raw(e + 1 < EPT ? e + 1 : e)) * a.inv_c;
+      q4.z = to_f32(rq.raw(e + 2 < EPT ? e + 2 : e)) * a.inv_c;
+      q4.w = to_f32(rq.raw(e + 3 < EPT ? e + 3 : e)) * a.inv_c;
+      if constexpr (EPT >= 4) {
+        *reinterpret_cast<float4*>(__builtin_assume_aligned(&xq[st_t * XQSTR + st_i + e], 16)) = q4;
+      } else {
+        xq[st_t * XQSTR + st_i + e] = q4.x;
+        if (EPT > 1) xq[st_t * XQSTR + st_i + e + 1] = q4.y;
+      }
+    }
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const float qv = to_f32(rq.raw(e)) * a.inv_c;
       const float kv = to_f32(rk.raw(e));
-      xq[st_t * XQSTR + st_i + e] = qv;
       xk[(st_i + e) * KSTR + st_t] = kv;
       xk[(DK + st_i + e) * KSTR + st_t] = kv * 0.5f;
-      xk[(2 * DK + st_i + e) * KSTR + st_t] = kv * (1.f / 3.f);
       if constexpr (BF16)
         vt[(st_i + e) * VSTR + st_t] = rv.raw(e);
       else
@@ -265,7 +331,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     }
     __syncthreads();
 
-    // Parent features of the tile's distinct parents (order <= 2).
+    // ---- phase B: parent features (order <= 2) and the order-0 carry -----
     for (int e = tid; e < nslot * L; e += kWaves * 64) {
       const int s = e / L;
       const int t = e % L;
@@ -273,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
       const int np = (pw >> 16) & 3;
       const int i1 = pw & 255;
       const int i2 = (pw >> 8) & 255;
-      float fk = 1.f, fq = spw[s];
+      float fk = spwk[s], fq = spwq[s];
       if (np >= 1) {
         fk *= xk[i1 * KSTR + t];
         fq *= xq[t * XQSTR + i1];
@@ -285,100 +351,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
       pk[s * KSTR + t] = fk;
       pq[s * QSTR + t] = fq;
     }
-    __syncthreads();
-
-    // Readout against the state before this chunk: acc[mb] = phi_q(Q) S.
-    f32x4 acc[L / 16][NB];
-#pragma unroll
-    for (int mb = 0; mb < L / 16; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if constexpr (BF16) {
-#pragma unroll
-      for (int kk = 0; kk < Sh::NKS; ++kk) {
-        const int b0 = 2 * kk;
-        const int b1 = (2 * kk + 1 < RB) ? 2 * kk + 1 : 2 * kk;
-        const bool has1 = 2 * kk + 1 < RB;
-        // Query features of both token blocks for this K-slice (8 rows per lane).
-        bf16x8 A[L / 16];
-        const int slot0 = qs[b0] & 0xffff;
-        const int c00 = qs[b0] >> 16;
-        const int slot1 = qs[b1] & 0xffff;
-        const int c01 = qs[b1] >> 16;
-#pragma unroll
-        for (int mb = 0; mb < L / 16; ++mb) {
-          const int t = mb * 16 + lr;
-          const float p0 = pq[slot0 * QSTR + t];
-          const float4 x0 = lds4(xq, t * XQSTR + c00);
-          float p1 = 0.f;
-          float4 x1 = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (has1) {
-            p1 = pq[slot1 * QSTR + t];
-            x1 = lds4(xq, t * XQSTR + c01);
-          }
-          A[mb][0] = static_cast<__bf16>(p0 * x0.x);
-          A[mb][1] = static_cast<__bf16>(p0 * x0.y);
-          A[mb][2] = static_cast<__bf16>(p0 * x0.z);
-          A[mb][3] = static_cast<__bf16>(p0 * x0.w);
-          A[mb][4] = static_cast<__bf16>(p1 * x1.x);
-          A[mb][5] = static_cast<__bf16>(p1 * x1.y);
-          A[mb][6] = static_cast<__bf16>(p1 * x1.z);
-          A[mb][7] = static_cast<__bf16>(p1 * x1.w);
-        }
-        // State rows of the K-slice as the bf16 B operand, one column block at a time.
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const u32x4 bw = {Sb[b0][nb][0], Sb[b0][nb][1], has1 ? Sb[b1][nb][0] : 0u,
-                            has1 ? Sb[b1][nb][1] : 0u};
-          const bf16x8 Bop = __builtin_bit_cast(bf16x8, bw);
-#pragma unroll
-          for (int mb = 0; mb < L / 16; ++mb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], Bop, acc[mb][nb], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const int slot = qs[b] & 0xffff;
-        const int c0 = qs[b] >> 16;
-#pragma unroll
-        for (int mb = 0; mb < L / 16; ++mb) {
-          const int t = mb * 16 + lr;
-          const float p = pq[slot * QSTR + t];
-          const float4 x = lds4(xq, t * XQSTR + c0);
-          const float av[4] = {p * x.x, p * x.y, p * x.z, p * x.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], S[b][nb][r], acc[mb][nb], 0, 0, 0);
-        }
-      }
-    }
-
-    // Sum the waves' readouts (fixed order) and write this tile's records.
-#pragma unroll
-    for (int mb = 0; mb < L / 16; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          red[(w * L + mb * 16 + 4 * g + r) * RSTR + nb * 16 + lr] = acc[mb][nb][r];
-    __syncthreads();
-    for (int e = tid; e < nvalid * (DV + 1); e += kWaves * 64) {
-      const int t = e / (DV + 1);
-      const int c = e % (DV + 1);
-      float sum = red[t * RSTR + c];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) sum += red[(ww * L + t) * RSTR + c];
-      if (tile == 0) sum += carry[c];
-      parth[static_cast<int64_t>(ch * L + t) * DVP + c] = sum;
-    }
     if (tile == 0) {
-      __syncthreads();  // carry was read above
+      // Order-0 prefix at this chunk's start, then add the chunk (exact fp32).
       if (tid < DV) {
+        carryh[static_cast<int64_t>(ch) * DVP + tid] = carry[tid];
         float s = 0.f;
         for (int t = 0; t < nvalid; ++t) {
           if constexpr (BF16)
@@ -388,65 +364,154 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         }
         carry[tid] += s;
       } else if (tid == DV) {
+        carryh[static_cast<int64_t>(ch) * DVP + DV] = carry[DV];
         carry[DV] += static_cast<float>(nvalid);
       }
     }
+    __syncthreads();
 
-    // State update: S += phi_k(K)^T [V 1] for every row block.  Software
-    // pipelined per row block (LDS loads of block b+1 in flight while block b
-    // runs on MFMA) with scheduling fences, so only a couple of blocks'
-    // temporaries are live.
-    if constexpr (BF16) {
-      bf16x8 Bv[NB];
+    // ---- phase C: readout against the state before this chunk -----------
+    // (two 16-token blocks at a time), written to the reduction buffer.
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        Bv[nb] = *reinterpret_cast<const bf16x8*>(&vt[(nb * 16 + lr) * VSTR + 8 * g]);
-      float4 cp0, cp1, cx0, cx1;
-      {
-        const int pko = ks[0] & 0xffff;
-        const int xko = ks[0] >> 16;
-        cp0 = lds4(pk, pko + 8 * g);
-        cp1 = lds4(pk, pko + 8 * g + 4);
-        cx0 = lds4(xk, xko + 8 * g);
-        cx1 = lds4(xk, xko + 8 * g + 4);
-      }
+    for (int half = 0; half < MB / 2; ++half) {
+      f32x4 acc[2][NB];
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        float4 np0, np1, nx0, nx1;
-        if (b + 1 < RB) {
-          const int pko = ks[b + 1 < RB ? b + 1 : b] & 0xffff;
-          const int xko = ks[b + 1 < RB ? b + 1 : b] >> 16;
-          np0 = lds4(pk, pko + 8 * g);
-          np1 = lds4(pk, pko + 8 * g + 4);
-          nx0 = lds4(xk, xko + 8 * g);
-          nx1 = lds4(xk, xko + 8 * g + 4);
-        }
-        const u32x4 aw = {pack_bf16(cp0.x * cx0.x, cp0.y * cx0.y), pack_bf16(cp0.z * cx0.z, cp0.w * cx0.w),
-                          pack_bf16(cp1.x * cx1.x, cp1.y * cx1.y), pack_bf16(cp1.z * cx1.z, cp1.w * cx1.w)};
-        const bf16x8 A = __builtin_bit_cast(bf16x8, aw);
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv[nb], S[b][nb], 0, 0, 0);
-        if (b > 0) {
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) {
+#pragma unroll
+        for (int kk = 0; kk < C::NKS; ++kk) {
+          const int b0 = 2 * kk;
+          const int b1 = (2 * kk + 1 < RB) ? 2 * kk + 1 : 2 * kk;
+          const bool has1 = 2 * kk + 1 < RB;
+          const int slot0 = qs[b0] & 0xffff;
+          const int c00 = qs[b0] >> 16;
+          const int slot1 = qs[b1] & 0xffff;
+          const int c01 = qs[b1] >> 16;
+          bf16x8 A[2];
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const int t = (2 * half + mb) * 16 + lr;
+            const float p0 = pq[slot0 * QSTR + t];
+            const float4 x0 = lds4(xq, t * XQSTR + c00);
+            float p1 = 0.f;
+            float4 x1 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (has1) {
+              p1 = pq[slot1 * QSTR + t];
+              x1 = lds4(xq, t * XQSTR + c01);
+            }
+            const u32x4 aw = {pack_bf16(p0 * x0.x, p0 * x0.y), pack_bf16(p0 * x0.z, p0 * x0.w),
+                              pack_bf16(p1 * x1.x, p1 * x1.y), pack_bf16(p1 * x1.z, p1 * x1.w)};
+            A[mb] = __builtin_bit_cast(bf16x8, aw);
+          }
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            const int bp = b > 0 ? b - 1 : 0;
-            Sb[bp][nb][0] = pack_bf16(S[bp][nb][0], S[bp][nb][1]);
-            Sb[bp][nb][1] = pack_bf16(S[bp][nb][2], S[bp][nb][3]);
+            const bf16x8 Bop = __builtin_bit_cast(bf16x8, Sb[kk][nb]);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], Bop, acc[mb][nb], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const int slot = qs[b] & 0xffff;
+          const int c0 = qs[b] >> 16;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const int t = (2 * half + mb) * 16 + lr;
+            const float p = pq[slot * QSTR + t];
+            const float4 x = lds4(xq, t * XQSTR + c0);
+            const float av[4] = {p * x.x, p * x.y, p * x.z, p * x.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], S[b][nb][r], acc[mb][nb], 0, 0, 0);
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < RB) {
-          cp0 = np0;
-          cp1 = np1;
-          cx0 = nx0;
-          cx1 = nx1;
+      }
+      // C layout: lane holds column nb*16 + lr of tokens 4g..4g+3 -> one
+      // 4-token vector store per (block, column block).
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = nb * 16 + lr;
+          if (col <= DV) {
+            RedT* dst = &red[(w * (DV + 1) + col) * RSTR + (2 * half + mb) * 16 + 4 * g];
+            if constexpr (C::RECB) {
+              const u32x2 o = {pack_bf16(acc[mb][nb][0], acc[mb][nb][1]), pack_bf16(acc[mb][nb][2], acc[mb][nb][3])};
+              *reinterpret_cast<u32x2*>(__builtin_assume_aligned(dst, 8)) = o;
+            } else {
+              *reinterpret_cast<f32x4*>(__builtin_assume_aligned(dst, 16)) = acc[mb][nb];
+            }
+          }
+        }
+    }
+
+    // ---- phase C: state update S += phi_k(K)^T [V 1] ----------------------
+    if constexpr (BF16) {
+#pragma unroll
+      for (int kst = 0; kst < L / 32; ++kst) {
+        bf16x8 Bv[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          Bv[nb] = *reinterpret_cast<const bf16x8*>(
+              __builtin_assume_aligned(&vt[(nb * 16 + lr) * VSTR + 32 * kst + 8 * g], 16));
+        // Software pipelined per row block: the LDS loads of block b+1 are in
+        // flight while block b runs on MFMA; fences bound the live registers.
+        float4 cp0, cp1, cx0, cx1;
+        {
+          const int pko = (ks[0] & 0xffff) + 32 * kst + 8 * g;
+          const int xko = (ks[0] >> 16) + 32 * kst + 8 * g;
+          cp0 = lds4(pk, pko);
+          cp1 = lds4(pk, pko + 4);
+          cx0 = lds4(xk, xko);
+          cx1 = lds4(xk, xko + 4);
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          float4 np0, np1, nx0, nx1;
+          if (b + 1 < RB) {
+            const int bn = b + 1 < RB ? b + 1 : b;
+            const int pko = (ks[bn] & 0xffff) + 32 * kst + 8 * g;
+            const int xko = (ks[bn] >> 16) + 32 * kst + 8 * g;
+            np0 = lds4(pk, pko);
+            np1 = lds4(pk, pko + 4);
+            nx0 = lds4(xk, xko);
+            nx1 = lds4(xk, xko + 4);
+          }
+          const u32x4 aw = {pack_bf16(cp0.x * cx0.x, cp0.y * cx0.y), pack_bf16(cp0.z * cx0.z, cp0.w * cx0.w),
+                            pack_bf16(cp1.x * cx1.x, cp1.y * cx1.y), pack_bf16(cp1.z * cx1.z, cp1.w * cx1.w)};
+          const bf16x8 A = __builtin_bit_cast(bf16x8, aw);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv[nb], S[b][nb], 0, 0, 0);
+          // After the last K-step, repack the previous block for the next readout.
+          if (kst == L / 32 - 1 && b > 0) {
+            const int bp = b > 0 ? b - 1 : 0;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              Sb[bp / 2][nb][2 * (bp % 2)] = pack_bf16(S[bp][nb][0], S[bp][nb][1]);
+              Sb[bp / 2][nb][2 * (bp % 2) + 1] = pack_bf16(S[bp][nb][2], S[bp][nb][3]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (b + 1 < RB) {
+            cp0 = np0;
+            cp1 = np1;
+            cx0 = nx0;
+            cx1 = nx1;
+          }
         }
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        Sb[RB - 1][nb][0] = pack_bf16(S[RB - 1][nb][0], S[RB - 1][nb][1]);
-        Sb[RB - 1][nb][1] = pack_bf16(S[RB - 1][nb][2], S[RB - 1][nb][3]);
+        Sb[(RB - 1) / 2][nb][2 * ((RB - 1) % 2)] = pack_bf16(S[RB - 1][nb][0], S[RB - 1][nb][1]);
+        Sb[(RB - 1) / 2][nb][2 * ((RB - 1) % 2) + 1] = pack_bf16(S[RB - 1][nb][2], S[RB - 1][nb][3]);
       }
     } else {
 #pragma unroll
@@ -466,7 +531,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         }
       }
     }
+    __syncthreads();
   }
+  if (nch > 0) red_sum(nch - 1);
 
   // Write the state tile back in canonical layout.  The row table pointer is
   // laundered so the addresses are recomputed here instead of being kept live
@@ -494,19 +561,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   if (tile == 0) {
-    __syncthreads();
     if (tid < DV) st[tid] = carry[tid];
     else if (tid == DV) st[zoff] = carry[DV];
   }
 }
 
 // Intra-chunk part: for each token i of a chunk, sum over the chunk's tokens
-// j <= i of T_P(q_i.k_j/c) (v_j, 1), in fp32 with Horner's rule.
-template <int DK, typename IT>
+// j <= i of T_P(q_i.k_j/c) (v_j, 1), in fp32 with Horner's rule.  Thread
+// (token i, column group) -> record columns [DVP][nwp] written coalesced.
+template <int DK, bool BF16>
 __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
-  constexpr int DV = DK, L = kChunk, DVP = padded_dv(DV);
-  constexpr int TPT = 256 / L;                 // threads per token
-  constexpr int CPT = (DV + TPT - 1) / TPT;    // columns per thread
+  using IT = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int DV = DK, L = prefill_chunk(BF16);
+  constexpr int NG = 256 / L;                  // column groups
+  constexpr int CPG = (DV + NG - 1) / NG;      // columns per group
   __shared__ float sq[L][DK + 1];
   __shared__ float sk[L][DK + 1];
   __shared__ float sv[L][DV + 1];
@@ -528,13 +596,13 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
     sv[t][c] = t < nvalid ? load_in(vh, (tb + t) * DV + c) : 0.f;
   }
   __syncthreads();
-  const int i = tid / TPT;
-  const int sub = tid % TPT;
+  const int i = tid % L;
+  const int grp = tid / L;
   if (i >= nvalid) return;
-  float rcp[4] = {0.f, 1.f, 0.5f, 1.f / 3.f};
-  float num[CPT];
+  const float rcp[4] = {0.f, 1.f, 0.5f, 1.f / 3.f};
+  float num[CPG];
 #pragma unroll
-  for (int cc = 0; cc < CPT; ++cc) num[cc] = 0.f;
+  for (int cc = 0; cc < CPG; ++cc) num[cc] = 0.f;
   float den = 0.f;
   for (int j = 0; j <= i; ++j) {
     float x = 0.f;
@@ -544,104 +612,111 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
     for (int p = a.P - 1; p >= 1; --p) wgt = fmaf(wgt, x * rcp[p], 1.f);
     den += wgt;
 #pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) {
-      const int c = sub + TPT * cc;
+    for (int cc = 0; cc < CPG; ++cc) {
+      const int c = grp * CPG + cc;
       if (c < DV) num[cc] = fmaf(wgt, sv[j][c], num[cc]);
     }
   }
-  float* rec = a.part + ((static_cast<int64_t>(head) * (a.n_tiles + 1) + a.n_tiles) * a.nw +
-                         static_cast<int64_t>(ch) * L + i) * DVP;
+  constexpr int DVP = padded_dv(DV);
+  float* rec = a.ws.intra + static_cast<int64_t>(head) * DVP * a.ws.nwp + static_cast<int64_t>(ch) * L + i;
 #pragma unroll
-  for (int cc = 0; cc < CPT; ++cc) {
-    const int c = sub + TPT * cc;
-    if (c < DV) rec[c] = num[cc];
+  for (int cc = 0; cc < CPG; ++cc) {
+    const int c = grp * CPG + cc;
+    if (c < DV) rec[static_cast<int64_t>(c) * a.ws.nwp] = num[cc];
   }
-  if (sub == 0) rec[DV] = den;
+  if (grp == 0) rec[static_cast<int64_t>(DV) * a.ws.nwp] = den;
 }
 
-// out = (sum over records of num) / (sum over records of den), fixed order.
-template <int DV>
+// out = (tile records + intra record + order-0 carry) for num / for den,
+// summed in a fixed order.  Block = (64 tokens, head).
+template <int DK, bool BF16>
 __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
-  constexpr int DVP = padded_dv(DV);
+  constexpr int DV = DK, DVP = padded_dv(DV), L = prefill_chunk(BF16);
+  constexpr bool RECB = prefill_bf16_records(DK, BF16);
   constexpr int TB = 64;
-  __shared__ __attribute__((aligned(16))) float acc[TB * DVP];
+  __shared__ float acc[(DV + 1) * (TB + 1)];
   const int head = blockIdx.y;
   const int t0 = blockIdx.x * TB;
-  const int ntok = min(TB, a.nw - t0);
   const int tid = threadIdx.x;
-  const int n4 = ntok * DVP / 4;
-  const float4* base = reinterpret_cast<const float4*>(a.part) +
-                       (static_cast<int64_t>(head) * a.nslots * a.nw + t0) * (DVP / 4);
-  const int64_t sstride = static_cast<int64_t>(a.nw) * (DVP / 4);
-  for (int e = tid; e < n4; e += 256) {
-    float4 s = base[e];
-    for (int sl = 1; sl < a.nslots; ++sl) {
-      const float4 x = base[sl * sstride + e];
-      s.x += x.x;
-      s.y += x.y;
-      s.z += x.z;
-      s.w += x.w;
+  const int nwp = a.ws.nwp;
+  const int64_t slab = static_cast<int64_t>(DVP) * nwp;
+  const float* intra = a.ws.intra + head * slab;
+  const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + L - 1) / L) * DVP;
+  for (int e = tid; e < (DV + 1) * (TB / 4); e += 256) {
+    const int c = e / (TB / 4);
+    const int t = 4 * (e % (TB / 4));
+    const int64_t off = static_cast<int64_t>(c) * nwp + t0 + t;
+    f32x4 s = *reinterpret_cast<const f32x4*>(&intra[off]);
+    if constexpr (RECB) {
+      const uint16_t* rec = static_cast<const uint16_t*>(a.ws.rec) + static_cast<int64_t>(head) * a.n_tiles * slab;
+      for (int tl = 0; tl < a.n_tiles; ++tl) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(&rec[tl * slab + off]);
+        s[0] += bf16_lo(x[0]);
+        s[1] += bf16_hi(x[0]);
+        s[2] += bf16_lo(x[1]);
+        s[3] += bf16_hi(x[1]);
+      }
+    } else {
+      const float* rec = static_cast<const float*>(a.ws.rec) + static_cast<int64_t>(head) * a.n_tiles * slab;
+      for (int tl = 0; tl < a.n_tiles; ++tl) s += *reinterpret_cast<const f32x4*>(&rec[tl * slab + off]);
     }
-    reinterpret_cast<float4*>(acc)[e] = s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] += carry[((t0 + t + j) / L) * DVP + c];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[c * (TB + 1) + t + j] = s[j];
   }
   __syncthreads();
+  const int ntok = min(TB, a.nw - t0);
   float* out = a.out + (static_cast<int64_t>(head) * a.n_total + a.t0 + t0) * DV;
   for (int e = tid; e < ntok * DV; e += 256) {
     const int t = e / DV, c = e % DV;
-    out[static_cast<int64_t>(t) * DV + c] = acc[t * DVP + c] / acc[t * DVP + DV];
+    out[static_cast<int64_t>(t) * DV + c] = acc[c * (TB + 1) + t] / acc[DV * (TB + 1) + t];
   }
 }
 
 template <int D, bool BF16>
 hipError_t launch_scan_t(int BH, const ScanArgs& a, hipStream_t s) {
-  constexpr int RB = prefill_rb(D, BF16);
   dim3 grid(a.lay.n_tiles, BH);
-  prefill_scan<D, BF16, RB><<<grid, kWaves * 64, 0, s>>>(a);
+  prefill_scan<D, BF16><<<grid, kWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_intra_t(bool bf16, int BH, const IntraArgs& a, hipStream_t s) {
-  dim3 grid((a.nw + kChunk - 1) / kChunk, BH);
-  if (bf16)
-    prefill_intra<D, uint16_t><<<grid, 256, 0, s>>>(a);
-  else
-    prefill_intra<D, float><<<grid, 256, 0, s>>>(a);
+template <int D, bool BF16>
+hipError_t launch_intra_t(int BH, const IntraArgs& a, hipStream_t s) {
+  constexpr int L = prefill_chunk(BF16);
+  dim3 grid((a.nw + L - 1) / L, BH);
+  prefill_intra<D, BF16><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
+
+template <int D, bool BF16>
+hipError_t launch_reduce_t(int BH, const ReduceArgs& a, hipStream_t s) {
+  dim3 grid((a.nw + 63) / 64, BH);
+  prefill_reduce<D, BF16><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+#define SATA_DISPATCH(fn, d, bf16, ...)                                   \
+  switch (d) {                                                            \
+    case 8: return bf16 ? fn<8, true>(__VA_ARGS__) : fn<8, false>(__VA_ARGS__);     \
+    case 16: return bf16 ? fn<16, true>(__VA_ARGS__) : fn<16, false>(__VA_ARGS__);  \
+    case 32: return bf16 ? fn<32, true>(__VA_ARGS__) : fn<32, false>(__VA_ARGS__);  \
+    case 64: return bf16 ? fn<64, true>(__VA_ARGS__) : fn<64, false>(__VA_ARGS__);  \
+    default: return hipErrorInvalidValue;                                 \
+  }
 
 }  // namespace
 
 hipError_t launch_prefill_scan(int d, bool bf16, int BH, const ScanArgs& a, hipStream_t s) {
-  switch (d) {
-    case 8: return bf16 ? launch_scan_t<8, true>(BH, a, s) : launch_scan_t<8, false>(BH, a, s);
-    case 16: return bf16 ? launch_scan_t<16, true>(BH, a, s) : launch_scan_t<16, false>(BH, a, s);
-    case 32: return bf16 ? launch_scan_t<32, true>(BH, a, s) : launch_scan_t<32, false>(BH, a, s);
-    case 64: return bf16 ? launch_scan_t<64, true>(BH, a, s) : launch_scan_t<64, false>(BH, a, s);
-    default: return hipErrorInvalidValue;
-  }
+  SATA_DISPATCH(launch_scan_t, d, bf16, BH, a, s)
 }
 
 hipError_t launch_prefill_intra(int d, bool bf16, int BH, const IntraArgs& a, hipStream_t s) {
-  switch (d) {
-    case 8: return launch_intra_t<8>(bf16, BH, a, s);
-    case 16: return launch_intra_t<16>(bf16, BH, a, s);
-    case 32: return launch_intra_t<32>(bf16, BH, a, s);
-    case 64: return launch_intra_t<64>(bf16, BH, a, s);
-    default: return hipErrorInvalidValue;
-  }
+  SATA_DISPATCH(launch_intra_t, d, bf16, BH, a, s)
 }
 
-hipError_t launch_prefill_reduce(int d, int BH, const ReduceArgs& a, hipStream_t s) {
-  dim3 grid((a.nw + 63) / 64, BH);
-  switch (d) {
-    case 8: prefill_reduce<8><<<grid, 256, 0, s>>>(a); break;
-    case 16: prefill_reduce<16><<<grid, 256, 0, s>>>(a); break;
-    case 32: prefill_reduce<32><<<grid, 256, 0, s>>>(a); break;
-    case 64: prefill_reduce<64><<<grid, 256, 0, s>>>(a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+hipError_t launch_prefill_reduce(int d, bool bf16, int BH, const ReduceArgs& a, hipStream_t s) {
+  SATA_DISPATCH(launch_reduce_t, d, bf16, BH, a, s)
 }
 
 }  // namespace sata
