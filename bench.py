@@ -27,6 +27,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
 METRIC = "causal SATA tokens/sec/head (prefill, decode) + % of HBM/MFMA roofline"
+# HBM bytes moved by one decode_update_readout launch of this workload, from the
+# FETCH_SIZE / WRITE_SIZE counters scaled by a 1 GiB copy
+# (profiles/decode_update_readout_c4_hbm_traffic.txt).  Re-measure after any
+# change to the decode kernel.
+DECODE_TRAFFIC_BYTES = 6.4497e9
 
 
 def parse():
@@ -37,6 +42,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB), the "
+                         "reference for scaling hardware byte counters")
     return ap.parse_args()
 
 
@@ -101,6 +109,13 @@ def main():
     pws = sa.workspace(sa.prefill_workspace_bytes(basis, w.B, w.H, w.n, w.d_v, sa.SATA_BF16), dev)
     dws = sa.workspace(sa.decode_workspace_bytes(basis, S, w.d_v, sa.SATA_BF16), dev)
     stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev_p = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev_d = [torch.cuda.Event(enable_timing=True) for _ in range(dsteps + 1)]
@@ -183,7 +198,9 @@ def main():
                    "hbm_gbs": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "kernel": "decode_update_readout", "achieved": dec_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": DECODE_TRAFFIC_BYTES if dsteps else None,
+                     "traffic_unit": "bytes per launch (HBM, counter-measured)",
+                     "algorithmic_bytes": dec_bytes},
         "check": {"decode_row_normwise_err": max(errs)},
     }
     if not args.no_cpu_baseline:

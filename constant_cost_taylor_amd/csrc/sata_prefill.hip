@@ -88,21 +88,19 @@ struct ChunkRegs {
     unsigned char b[kVec];
   };
   Piece p[kLoads];
+  bool ok;
+  // The load is unconditional (src must be a valid address): a select on
+  // the loaded value would make the wave wait for it here, turning the
+  // prefetch into a synchronous load.  Invalid tokens are zeroed at use.
   __device__ __forceinline__ void load(const IT* src, bool valid) {
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      if (valid) {
-        p[j] = reinterpret_cast<const Piece*>(src)[j];
-      } else {
-#pragma unroll
-        for (int x = 0; x < kVec; ++x) p[j].b[x] = 0;
-      }
-    }
+    for (int j = 0; j < kLoads; ++j) p[j] = reinterpret_cast<const Piece*>(src)[j];
+    ok = valid;
   }
   __device__ __forceinline__ IT raw(int e) const {
     IT v;
     __builtin_memcpy(&v, reinterpret_cast<const unsigned char*>(p) + e * sizeof(IT), sizeof(IT));
-    return v;
+    return ok ? v : IT(0);
   }
 };
 
@@ -281,10 +279,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   const int st_i = (tid / L) * EPT;
   ChunkRegs<IT, EPT> rq, rk, rv;
   {
+    // Tokens past the window read the window's first token (always valid).
     const bool ok = st_t < min(L, a.nw);
-    rq.load(qh + (a.t0 + st_t) * DK + st_i, ok);
-    rk.load(kh + (a.t0 + st_t) * DK + st_i, ok);
-    rv.load(vh + (a.t0 + st_t) * DV + st_i, ok);
+    const int64_t tn = a.t0 + (ok ? st_t : 0);
+    rq.load(qh + tn * DK + st_i, ok);
+    rk.load(kh + tn * DK + st_i, ok);
+    rv.load(vh + tn * DV + st_i, ok);
   }
 
   for (int ch = 0; ch < nch; ++ch) {
@@ -323,8 +323,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     }
     // Prefetch the next chunk; the loads stay in flight through this chunk.
     if (ch + 1 < nch) {
-      const int64_t tn = tb + L + st_t;
       const bool ok = st_t < min(L, a.nw - (ch + 1) * L);
+      const int64_t tn = tb + L + (ok ? st_t : 0);
       rq.load(qh + tn * DK + st_i, ok);
       rk.load(kh + tn * DK + st_i, ok);
       rv.load(vh + tn * DV + st_i, ok);
@@ -375,46 +375,73 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
 #pragma unroll
     for (int half = 0; half < MB / 2; ++half) {
       f32x4 acc[2][NB];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (BF16) {
-#pragma unroll
-        for (int kk = 0; kk < C::NKS; ++kk) {
+        // Per K-slice operand data: parent feature and 4 child coordinates of
+        // the lane group's run in both row blocks, for both token blocks.
+        struct QData {
+          float p[2][2];
+          float4 x[2][2];
+        };
+        auto load_q = [&](int kk, QData& dq) {
           const int b0 = 2 * kk;
           const int b1 = (2 * kk + 1 < RB) ? 2 * kk + 1 : 2 * kk;
-          const bool has1 = 2 * kk + 1 < RB;
-          const int slot0 = qs[b0] & 0xffff;
-          const int c00 = qs[b0] >> 16;
-          const int slot1 = qs[b1] & 0xffff;
-          const int c01 = qs[b1] >> 16;
-          bf16x8 A[2];
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) {
             const int t = (2 * half + mb) * 16 + lr;
-            const float p0 = pq[slot0 * QSTR + t];
-            const float4 x0 = lds4(xq, t * XQSTR + c00);
-            float p1 = 0.f;
-            float4 x1 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (has1) {
-              p1 = pq[slot1 * QSTR + t];
-              x1 = lds4(xq, t * XQSTR + c01);
+            dq.p[mb][0] = pq[(qs[b0] & 0xffff) * QSTR + t];
+            dq.x[mb][0] = lds4(xq, t * XQSTR + (qs[b0] >> 16));
+            if (2 * kk + 1 < RB) {
+              dq.p[mb][1] = pq[(qs[b1] & 0xffff) * QSTR + t];
+              dq.x[mb][1] = lds4(xq, t * XQSTR + (qs[b1] >> 16));
+            } else {
+              dq.p[mb][1] = 0.f;
+              dq.x[mb][1] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
+          }
+        };
+        auto build_q = [&](const QData& dq, bf16x8 (&A)[2]) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const float p0 = dq.p[mb][0], p1 = dq.p[mb][1];
+            const float4 x0 = dq.x[mb][0], x1 = dq.x[mb][1];
             const u32x4 aw = {pack_bf16(p0 * x0.x, p0 * x0.y), pack_bf16(p0 * x0.z, p0 * x0.w),
                               pack_bf16(p1 * x1.x, p1 * x1.y), pack_bf16(p1 * x1.z, p1 * x1.w)};
             A[mb] = __builtin_bit_cast(bf16x8, aw);
           }
+        };
+        QData dq0, dq1;
+        bf16x8 Acur[2], Anext[2];
+        load_q(0, dq0);
+        build_q(dq0, Acur);
+        if (C::NKS > 1) load_q(C::NKS > 1 ? 1 : 0, dq0);
+        if (C::NKS > 2) load_q(C::NKS > 2 ? 2 : 0, dq1);
+#pragma unroll
+        for (int kk = 0; kk < C::NKS; ++kk) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const bf16x8 Bop = __builtin_bit_cast(bf16x8, Sb[kk][nb]);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], Bop, acc[mb][nb], 0, 0, 0);
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  Acur[mb], Bop, kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb], 0, 0, 0);
           }
+          // Operands of the next K-slice are built in the shadow of these MFMAs.
+          if (kk + 1 < C::NKS) build_q(dq0, Anext);
+          if (kk + 3 < C::NKS) load_q(kk + 3 < C::NKS ? kk + 3 : 0, dq0);
           __builtin_amdgcn_sched_barrier(0);
+          if (kk + 1 < C::NKS) {
+            Acur[0] = Anext[0];
+            Acur[1] = Anext[1];
+            const QData tq = dq0;
+            dq0 = dq1;
+            dq1 = tq;
+          }
         }
       } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
           const int slot = qs[b] & 0xffff;
@@ -454,58 +481,71 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
 
     // ---- phase C: state update S += phi_k(K)^T [V 1] ----------------------
     if constexpr (BF16) {
-#pragma unroll
-      for (int kst = 0; kst < L / 32; ++kst) {
-        bf16x8 Bv[NB];
+      // Steps s = (K-step, row block).  At step s the MFMAs of s run while the
+      // operand of s+1 is built (VALU) and the LDS data of s+3 is fetched; the
+      // previous block's new state is repacked for the next readout after the
+      // last K-step.  Fences keep every group's temporaries bounded.
+      constexpr int NST = (L / 32) * RB;
+      struct KData {
+        float4 p0, p1, x0, x1;
+      };
+      auto load_k = [&](int st_, KData& dk) {
+        const int kst = st_ / RB, b = st_ % RB;
+        const int pko = (ks[b] & 0xffff) + 32 * kst + 8 * g;
+        const int xko = (ks[b] >> 16) + 32 * kst + 8 * g;
+        dk.p0 = lds4(pk, pko);
+        dk.p1 = lds4(pk, pko + 4);
+        dk.x0 = lds4(xk, xko);
+        dk.x1 = lds4(xk, xko + 4);
+      };
+      auto build_k = [&](const KData& dk) {
+        const u32x4 aw = {pack_bf16(dk.p0.x * dk.x0.x, dk.p0.y * dk.x0.y),
+                          pack_bf16(dk.p0.z * dk.x0.z, dk.p0.w * dk.x0.w),
+                          pack_bf16(dk.p1.x * dk.x1.x, dk.p1.y * dk.x1.y),
+                          pack_bf16(dk.p1.z * dk.x1.z, dk.p1.w * dk.x1.w)};
+        return __builtin_bit_cast(bf16x8, aw);
+      };
+      auto load_v = [&](int kst, bf16x8 (&Bv)[NB]) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           Bv[nb] = *reinterpret_cast<const bf16x8*>(
               __builtin_assume_aligned(&vt[(nb * 16 + lr) * VSTR + 32 * kst + 8 * g], 16));
-        // Software pipelined per row block: the LDS loads of block b+1 are in
-        // flight while block b runs on MFMA; fences bound the live registers.
-        float4 cp0, cp1, cx0, cx1;
-        {
-          const int pko = (ks[0] & 0xffff) + 32 * kst + 8 * g;
-          const int xko = (ks[0] >> 16) + 32 * kst + 8 * g;
-          cp0 = lds4(pk, pko);
-          cp1 = lds4(pk, pko + 4);
-          cx0 = lds4(xk, xko);
-          cx1 = lds4(xk, xko + 4);
+      };
+      bf16x8 Bv[NB], Bvn[NB];
+      load_v(0, Bv);
+      KData d0, d1;
+      load_k(0, d0);
+      bf16x8 Acur = build_k(d0);
+      if (NST > 1) load_k(NST > 1 ? 1 : 0, d0);
+      if (NST > 2) load_k(NST > 2 ? 2 : 0, d1);
+#pragma unroll
+      for (int st_ = 0; st_ < NST; ++st_) {
+        const int kst = st_ / RB, b = st_ % RB;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur, Bv[nb], S[b][nb], 0, 0, 0);
+        bf16x8 Anext = Acur;
+        if (st_ + 1 < NST) Anext = build_k(d0);
+        if (st_ + 3 < NST) load_k(st_ + 3 < NST ? st_ + 3 : 0, d0);
+        if (b == RB - 2 && kst + 1 < L / 32) load_v(kst + 1 < L / 32 ? kst + 1 : 0, Bvn);
+        if (kst == L / 32 - 1 && b > 0) {
+          const int bp = b > 0 ? b - 1 : 0;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            Sb[bp / 2][nb][2 * (bp % 2)] = pack_bf16(S[bp][nb][0], S[bp][nb][1]);
+            Sb[bp / 2][nb][2 * (bp % 2) + 1] = pack_bf16(S[bp][nb][2], S[bp][nb][3]);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        Acur = Anext;
+        {
+          const KData t2 = d0;
+          d0 = d1;
+          d1 = t2;
+        }
+        if (b == RB - 1 && kst + 1 < L / 32) {
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          float4 np0, np1, nx0, nx1;
-          if (b + 1 < RB) {
-            const int bn = b + 1 < RB ? b + 1 : b;
-            const int pko = (ks[bn] & 0xffff) + 32 * kst + 8 * g;
-            const int xko = (ks[bn] >> 16) + 32 * kst + 8 * g;
-            np0 = lds4(pk, pko);
-            np1 = lds4(pk, pko + 4);
-            nx0 = lds4(xk, xko);
-            nx1 = lds4(xk, xko + 4);
-          }
-          const u32x4 aw = {pack_bf16(cp0.x * cx0.x, cp0.y * cx0.y), pack_bf16(cp0.z * cx0.z, cp0.w * cx0.w),
-                            pack_bf16(cp1.x * cx1.x, cp1.y * cx1.y), pack_bf16(cp1.z * cx1.z, cp1.w * cx1.w)};
-          const bf16x8 A = __builtin_bit_cast(bf16x8, aw);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv[nb], S[b][nb], 0, 0, 0);
-          // After the last K-step, repack the previous block for the next readout.
-          if (kst == L / 32 - 1 && b > 0) {
-            const int bp = b > 0 ? b - 1 : 0;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              Sb[bp / 2][nb][2 * (bp % 2)] = pack_bf16(S[bp][nb][0], S[bp][nb][1]);
-              Sb[bp / 2][nb][2 * (bp % 2) + 1] = pack_bf16(S[bp][nb][2], S[bp][nb][3]);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          if (b + 1 < RB) {
-            cp0 = np0;
-            cp1 = np1;
-            cx0 = nx0;
-            cx1 = nx1;
-          }
+          for (int nb = 0; nb < NB; ++nb) Bv[nb] = Bvn[nb];
         }
       }
 #pragma unroll
