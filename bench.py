@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--flatness", action="store_true",
+                    help="instead of the step: prefill cost per token of the long-context workload "
+                         "(16 heads, d_k=d_v=32, P=4, bf16) at n = 2^16, 2^18, 2^20")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB), the "
                          "reference for scaling hardware byte counters")
@@ -81,12 +84,67 @@ def cpu_baseline(w, q, k, v, qs, ks, vs, budget_s):
                       f"({rows} head-tokens, float64 numpy, {el:.1f} s)"}
 
 
+def flatness(args):
+    """Prefill time per token at growing context: the state is fixed-size, so
+    the per-token cost should not grow with n.  Inputs: seeded unit-norm
+    Gaussian q, k and Gaussian v generated on the device (same distribution as
+    the seeded host generators, which would take minutes at 2^20 tokens)."""
+    import torch
+    import constant_cost_taylor_amd as sa
+    import workloads as W
+    w = W.WORKLOADS["c5_long"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    basis = sa.build_basis(w.d_k, w.P, w.c)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 * w.cfg)
+    rows = []
+    for lg in (16, 18, 20):
+        n = 1 << lg
+        shape = (w.B, w.H, n, w.d_k)
+        q = torch.randn(shape, generator=g, device=dev)
+        q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        k = torch.randn(shape, generator=g, device=dev)
+        k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        v = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+        state = sa.new_state(basis, w.B * w.H, dev)
+        ws = sa.workspace(sa.prefill_workspace_bytes(basis, w.B, w.H, n, w.d_v, sa.SATA_BF16), dev)
+        stream = torch.cuda.current_stream(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ms = []
+        for it in range(args.warmup + args.steps):
+            state.zero_()
+            ev[0].record(stream)
+            sa.prefill(basis, q, k, v, state=state, out=out, ws=ws)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                ms.append(ev[0].elapsed_time(ev[1]))
+        t = float(np.median(ms))
+        tok = w.B * w.H * n
+        rows.append({"n": n, "ms": t, "ns_per_head_token": 1e6 * t / tok,
+                     "head_tokens_per_s": tok / (t * 1e-3), "finite": bool(torch.isfinite(out).all())})
+        print(f"flatness n=2^{lg}: {t:.2f} ms", file=sys.stderr, flush=True)
+        del q, k, v, out, state, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "prefill per-token cost vs context length", "unit": "ns/head-token",
+                      "config": {"workload": f"long-context prefill: batch {w.B} x {w.H} heads, "
+                                             f"d_k=d_v={w.d_k}, P={w.P}, bf16 inputs, f32 state"},
+                      "steps": args.steps, "warmup": args.warmup, "points": rows,
+                      "ratio_2e20_over_2e16": rows[-1]["ns_per_head_token"] / rows[0]["ns_per_head_token"]}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (heads are independent; the multi-GPU "
               "sharding is a design note only). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.flatness:
+        flatness(args)
+        return
     import torch
     import constant_cost_taylor_amd as sa
     import workloads as W

@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <unordered_map>
@@ -291,8 +292,19 @@ int check_device(const sata_basis* b) {
 }
 
 // Tokens per prefill window and the workspace it needs (records of one
-// window; the window is bounded so that they fit kPrefillWsCap).
-constexpr size_t kPrefillWsCap = size_t(16) << 30;
+// window; the window is bounded so that they fit the workspace cap: 16 GiB,
+// or the byte count in the environment variable SATA_PREFILL_WS_CAP, read at
+// every call, so the workspace query and the prefill call must see the same
+// value).
+size_t prefill_ws_cap() {
+  const char* e = std::getenv("SATA_PREFILL_WS_CAP");
+  if (e && *e) {
+    char* end = nullptr;
+    const unsigned long long v = std::strtoull(e, &end, 10);
+    if (end && *end == 0 && v > 0) return static_cast<size_t>(v);
+  }
+  return size_t(16) << 30;
+}
 
 struct PrefillPlan {
   int64_t nw = 0;         // tokens per window
@@ -311,7 +323,7 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
   const size_t rec_elt = sata::prefill_bf16_records(b->d, bf16) ? 2 : 4;
   // bytes per token of window (records + intra) and per chunk (carry)
   const size_t per_token = static_cast<size_t>(BH) * dvp * (nt * rec_elt + 4);
-  int64_t w = static_cast<int64_t>(kPrefillWsCap / per_token);
+  int64_t w = static_cast<int64_t>(prefill_ws_cap() / per_token);
   w = std::max<int64_t>(64, (w / 64) * 64);
   const int64_t nround = std::max<int64_t>(64, (n + 63) / 64 * 64);
   PrefillPlan pl;

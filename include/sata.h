@@ -101,7 +101,11 @@ int64_t sata_state_floats(const sata_basis* basis, int d_v);
  * Returns -1 on an invalid argument. */
 int64_t sata_state_stride(const sata_basis* basis, int d_v);
 
-/* Device workspace in bytes that sata_prefill needs for these sizes. */
+/* Device workspace in bytes that sata_prefill needs for these sizes.  Long
+ * sequences are processed in windows whose per-token records fit a cap of
+ * 16 GiB; the environment variable SATA_PREFILL_WS_CAP (bytes, read at every
+ * call: keep it unchanged between this query and the prefill) lowers or
+ * raises it, trading workspace for one state reload per window. */
 int sata_prefill_workspace(const sata_basis* basis, int B, int H, int n, int d_v, int dtype,
                            size_t* bytes);
 

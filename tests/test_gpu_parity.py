@@ -203,6 +203,47 @@ def test_prefill_then_decode(d, P, dtype):
         assert O.row_normwise_error(got[h], ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d,P,dtype,n", [(64, 4, W.BF16, 700), (16, 4, W.F32, 530)])
+def test_prefill_many_windows(d, P, dtype, n, monkeypatch):
+    """A small workspace cap splits the sequence into many windows (the state
+    is written back and reloaded between them); results are unchanged."""
+    b = SA.build_basis(d, P, 1.0)
+    q, k, v = W.make_qkv(1, 2, n, d, d, dtype, 15000 + d)
+    code = SA.SATA_BF16 if dtype == W.BF16 else SA.SATA_F32
+    full = SA.prefill_workspace_bytes(b, 1, 2, n, d, code)
+    monkeypatch.setenv("SATA_PREFILL_WS_CAP", str(max(1, full // 6)))
+    small = SA.prefill_workspace_bytes(b, 1, 2, n, d, code)
+    note(f"many windows d={d} {dtype} n={n} ws {full} -> {small}")
+    assert small < full
+    out, _ = run_prefill(b, q, k, v, dtype)
+    got = out.cpu().numpy()
+    for h in range(2):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
+        assert O.row_normwise_error(got[0, h], ref) <= TOL[dtype], h
+
+
+def test_misaligned_and_host_only_rejected():
+    note("misaligned pointers / host-only handle on the GPU")
+    b = SA.build_basis(16, 4, 1.0)
+    x = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    st = SA.new_state(b, 1)
+    ws = SA.workspace(1 << 20)
+    L = SA.lib()
+    p = x.data_ptr()
+    # q not 16-byte aligned
+    assert L.sata_prefill(b.handle, 1, 1, 8, 16, SA.SATA_BF16, p + 2, p, p, out.data_ptr(), st.data_ptr(),
+                          ws.data_ptr(), ws.numel(), None) == SA.SATA_ERR_INVALID_ARG
+    # decode: out not 16-byte aligned
+    assert L.sata_decode_step(b.handle, 1, 16, SA.SATA_BF16, p, p, p, out.data_ptr() + 4, st.data_ptr(),
+                              ws.data_ptr(), ws.numel(), None) == SA.SATA_ERR_INVALID_ARG
+    hb = SA.build_basis(16, 4, 1.0, host_only=True)
+    assert L.sata_decode_step(hb.handle, 1, 16, SA.SATA_BF16, p, p, p, out.data_ptr(), st.data_ptr(),
+                              ws.data_ptr(), ws.numel(), None) == SA.SATA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert float(st.abs().sum()) == 0.0 and float(out.abs().sum()) == 0.0
+
+
 def test_prefill_deterministic():
     note("prefill run-twice bitwise")
     d, P, dtype = 32, 4, W.BF16
