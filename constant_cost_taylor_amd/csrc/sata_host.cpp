@@ -319,19 +319,20 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
   const bool bf16 = dtype == SATA_BF16;
   const int nt = b->lay[dtype].n_tiles;
   const int dvp = sata::padded_dv(b->d);
-  const int L = sata::prefill_chunk(bf16);
+  const int T = sata::prefill_window(bf16);
   const size_t rec_elt = sata::prefill_bf16_records(b->d, bf16) ? 2 : 4;
   // bytes per token of window (records + intra) and per chunk (carry)
   const size_t per_token = static_cast<size_t>(BH) * dvp * (nt * rec_elt + 4);
   int64_t w = static_cast<int64_t>(prefill_ws_cap() / per_token);
-  w = std::max<int64_t>(64, (w / 64) * 64);
+  // windows start on readout-window boundaries
+  w = std::max<int64_t>(T, (w / T) * T);
   const int64_t nround = std::max<int64_t>(64, (n + 63) / 64 * 64);
   PrefillPlan pl;
   pl.nw = std::min(w, nround);
   pl.nwp = (pl.nw + 63) / 64 * 64;
   pl.rec_bytes = static_cast<size_t>(BH) * nt * dvp * pl.nwp * rec_elt;
   pl.intra_bytes = static_cast<size_t>(BH) * dvp * pl.nwp * 4;
-  pl.carry_bytes = static_cast<size_t>(BH) * ((pl.nwp + L - 1) / L) * dvp * 4;
+  pl.carry_bytes = static_cast<size_t>(BH) * ((pl.nwp + T - 1) / T) * dvp * 4;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   pl.total = up(pl.rec_bytes) + up(pl.intra_bytes) + up(pl.carry_bytes);
   return pl;

@@ -21,6 +21,13 @@ constexpr int kThreads = 256;
 // fp32 inputs (fp32 cross-wave buffers would not fit LDS at 64).
 constexpr int prefill_chunk(bool bf16) { return bf16 ? 64 : 32; }
 
+// Tokens per readout window: the readout of every chunk in a window uses the
+// state as it stood at the window's start (for bf16 inputs, whose readout
+// operand is a bf16 copy of the state refreshed once per window), and the
+// keys of the window before the query are summed exactly by the intra-window
+// kernel.  fp32 inputs read the live state, so their window is one chunk.
+constexpr int prefill_window(bool bf16) { return bf16 ? 256 : prefill_chunk(bf16); }
+
 // Row blocks of 16 rows per wave held on chip by the prefill scan, per
 // (head dim, input dtype): the fp32 state tile (rb * column blocks * 4
 // registers) plus the readout accumulators must fit the 256 accumulator
@@ -79,8 +86,8 @@ struct PrefillLayout {
 
 // Prefill workspace of one window of nw tokens (nwp = nw rounded up to 64):
 //   rec:   [BH][n_tiles][DVP][nwp]  per-tile readout records (bf16 or fp32)
-//   intra: [BH][DVP][nwp]           intra-chunk records (fp32)
-//   carry: [BH][nchunk][DVP]        order-0 prefix at each chunk start (fp32)
+//   intra: [BH][DVP][nwp]           intra-window records (fp32)
+//   carry: [BH][nrwin][DVP]         order-0 prefix at each readout window start (fp32)
 struct PrefillWs {
   void* rec;
   float* intra;

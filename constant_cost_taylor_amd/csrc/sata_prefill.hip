@@ -108,6 +108,8 @@ template <int DK, bool BF16>
 struct Cfg {
   static constexpr int DV = DK;
   static constexpr int L = prefill_chunk(BF16);
+  static constexpr int T = prefill_window(BF16);     // readout window (tokens)
+  static constexpr int SC = T / L;                   // chunks per readout window
   static constexpr int RB = prefill_rb(DK, BF16);
   static constexpr int NB = col_blocks(DV);        // 16-wide column blocks incl. z
   static constexpr int NC = NB * 16;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   RedT* rech = static_cast<RedT*>(a.ws.rec) +
                (static_cast<int64_t>(head) * n_tiles + tile) * DVP * static_cast<int64_t>(nwp);
   const int nch = (a.nw + L - 1) / L;
-  float* carryh = a.ws.carry + static_cast<int64_t>(head) * ((nwp + L - 1) / L) * DVP;
+  float* carryh = a.ws.carry + static_cast<int64_t>(head) * ((nwp + C::T - 1) / C::T) * DVP;
 
   // Cross-wave sum of one chunk's readout (LDS red) into its records.
   auto red_sum = [&](int ch) {
@@ -287,7 +289,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     rv.load(vh + tn * DV + st_i, ok);
   }
 
-  for (int ch = 0; ch < nch; ++ch) {
+  // Outer loop over readout windows, inner loop over their chunks: the bf16
+  // readout operand is loop-invariant inside a window and refreshed after it.
+  for (int ch0 = 0; ch0 < nch; ch0 += C::SC) {
+  const int ch_end = min(nch, ch0 + C::SC);
+  for (int ch = ch0; ch < ch_end; ++ch) {
     const int64_t tb = a.t0 + static_cast<int64_t>(ch) * L;
     const int nvalid = min(L, a.nw - ch * L);
     // Launder the run metadata so the LDS addresses derived from it are
@@ -352,9 +358,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
       pq[s * QSTR + t] = fq;
     }
     if (tile == 0) {
-      // Order-0 prefix at this chunk's start, then add the chunk (exact fp32).
+      // Order-0 prefix at each readout window's start, then add the chunk
+      // (exact fp32).
+      const bool wstart = ch % C::SC == 0;
       if (tid < DV) {
-        carryh[static_cast<int64_t>(ch) * DVP + tid] = carry[tid];
+        if (wstart) carryh[static_cast<int64_t>(ch / C::SC) * DVP + tid] = carry[tid];
         float s = 0.f;
         for (int t = 0; t < nvalid; ++t) {
           if constexpr (BF16)
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         }
         carry[tid] += s;
       } else if (tid == DV) {
-        carryh[static_cast<int64_t>(ch) * DVP + DV] = carry[DV];
+        if (wstart) carryh[static_cast<int64_t>(ch / C::SC) * DVP + DV] = carry[DV];
         carry[DV] += static_cast<float>(nvalid);
       }
     }
@@ -482,9 +490,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     // ---- phase C: state update S += phi_k(K)^T [V 1] ----------------------
     if constexpr (BF16) {
       // Steps s = (K-step, row block).  At step s the MFMAs of s run while the
-      // operand of s+1 is built (VALU) and the LDS data of s+3 is fetched; the
-      // previous block's new state is repacked for the next readout after the
-      // last K-step.  Fences keep every group's temporaries bounded.
+      // operand of s+1 is built (VALU) and the LDS data of s+3 is fetched.
+      // Fences keep every group's temporaries bounded.
       constexpr int NST = (L / 32) * RB;
       struct KData {
         float4 p0, p1, x0, x1;
@@ -528,14 +535,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         if (st_ + 1 < NST) Anext = build_k(d0);
         if (st_ + 3 < NST) load_k(st_ + 3 < NST ? st_ + 3 : 0, d0);
         if (b == RB - 2 && kst + 1 < L / 32) load_v(kst + 1 < L / 32 ? kst + 1 : 0, Bvn);
-        if (kst == L / 32 - 1 && b > 0) {
-          const int bp = b > 0 ? b - 1 : 0;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            Sb[bp / 2][nb][2 * (bp % 2)] = pack_bf16(S[bp][nb][0], S[bp][nb][1]);
-            Sb[bp / 2][nb][2 * (bp % 2) + 1] = pack_bf16(S[bp][nb][2], S[bp][nb][3]);
-          }
-        }
         __builtin_amdgcn_sched_barrier(0);
         Acur = Anext;
         {
@@ -547,11 +546,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) Bv[nb] = Bvn[nb];
         }
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        Sb[(RB - 1) / 2][nb][2 * ((RB - 1) % 2)] = pack_bf16(S[RB - 1][nb][0], S[RB - 1][nb][1]);
-        Sb[(RB - 1) / 2][nb][2 * ((RB - 1) % 2) + 1] = pack_bf16(S[RB - 1][nb][2], S[RB - 1][nb][3]);
       }
     } else {
 #pragma unroll
@@ -572,6 +566,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
       }
     }
     __syncthreads();
+  }
+  if constexpr (BF16) {
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        Sb[b / 2][nb][2 * (b % 2)] = pack_bf16(S[b][nb][0], S[b][nb][1]);
+        Sb[b / 2][nb][2 * (b % 2) + 1] = pack_bf16(S[b][nb][2], S[b][nb][3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   }
   if (nch > 0) red_sum(nch - 1);
 
@@ -606,59 +612,73 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   }
 }
 
-// Intra-chunk part: for each token i of a chunk, sum over the chunk's tokens
-// j <= i of T_P(q_i.k_j/c) (v_j, 1), in fp32 with Horner's rule.  Thread
-// (token i, column group) -> record columns [DVP][nwp] written coalesced.
+// Intra-window part: for each token i of a readout window of T tokens, the
+// sum over the window's keys j <= i of T_P(q_i.k_j/c) (v_j, 1), in fp32 with
+// Horner's rule.  Block = (window, head); thread (token i, column group);
+// keys are staged through LDS in tiles of KT tokens and read as broadcasts.
+// Writes record columns [DVP][nwp] (coalesced over tokens).
 template <int DK, bool BF16>
 __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
   using IT = typename std::conditional<BF16, uint16_t, float>::type;
-  constexpr int DV = DK, L = prefill_chunk(BF16);
-  constexpr int NG = 256 / L;                  // column groups
-  constexpr int CPG = (DV + NG - 1) / NG;      // columns per group
-  __shared__ float sq[L][DK + 1];
-  __shared__ float sk[L][DK + 1];
-  __shared__ float sv[L][DV + 1];
-  const int ch = blockIdx.x;
+  constexpr int DV = DK, T = prefill_window(BF16);
+  constexpr int KT = T < 64 ? T : 64;         // keys per LDS tile
+  constexpr int NG = 256 / T;                 // column groups
+  constexpr int CPG = (DV + NG - 1) / NG;     // columns per group
+  __shared__ __attribute__((aligned(16))) float sk[KT][DK];
+  __shared__ __attribute__((aligned(16))) float sv[KT][DV];
+  const int win = blockIdx.x;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
-  const int64_t tb = a.t0 + static_cast<int64_t>(ch) * L;
-  const int nvalid = min(L, a.nw - ch * L);
+  const int64_t tb = a.t0 + static_cast<int64_t>(win) * T;
+  const int nvalid = min(T, a.nw - win * T);
   const IT* qh = static_cast<const IT*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
   const IT* kh = static_cast<const IT*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
   const IT* vh = static_cast<const IT*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
-  for (int e = tid; e < L * DK; e += 256) {
-    const int t = e / DK, i = e % DK;
-    sq[t][i] = t < nvalid ? load_in(qh, (tb + t) * DK + i) * a.inv_c : 0.f;
-    sk[t][i] = t < nvalid ? load_in(kh, (tb + t) * DK + i) : 0.f;
-  }
-  for (int e = tid; e < L * DV; e += 256) {
-    const int t = e / DV, c = e % DV;
-    sv[t][c] = t < nvalid ? load_in(vh, (tb + t) * DV + c) : 0.f;
-  }
-  __syncthreads();
-  const int i = tid % L;
-  const int grp = tid / L;
-  if (i >= nvalid) return;
+  const int i = tid % T;
+  const int grp = tid / T;
+  float qi[DK];
+#pragma unroll
+  for (int d = 0; d < DK; ++d) qi[d] = i < nvalid ? load_in(qh, (tb + i) * DK + d) * a.inv_c : 0.f;
   const float rcp[4] = {0.f, 1.f, 0.5f, 1.f / 3.f};
   float num[CPG];
 #pragma unroll
   for (int cc = 0; cc < CPG; ++cc) num[cc] = 0.f;
   float den = 0.f;
-  for (int j = 0; j <= i; ++j) {
-    float x = 0.f;
+  const int ntile = (nvalid + KT - 1) / KT;
+  for (int jt = 0; jt < ntile; ++jt) {
+    __syncthreads();
+    for (int e = tid; e < KT * DK; e += 256) {
+      const int t = e / DK, d = e % DK;
+      const bool ok = jt * KT + t < nvalid;
+      sk[t][d] = ok ? load_in(kh, (tb + jt * KT + t) * DK + d) : 0.f;
+      sv[t][d] = ok ? load_in(vh, (tb + jt * KT + t) * DV + d) : 0.f;
+    }
+    __syncthreads();
+    const int jend = min(KT, i - jt * KT + 1);   // keys j <= i of this tile
+    if (i >= nvalid) continue;
+    for (int j = 0; j < jend; ++j) {
+      float x = 0.f;
 #pragma unroll
-    for (int d = 0; d < DK; ++d) x = fmaf(sq[i][d], sk[j][d], x);
-    float wgt = 1.f;
-    for (int p = a.P - 1; p >= 1; --p) wgt = fmaf(wgt, x * rcp[p], 1.f);
-    den += wgt;
+      for (int d = 0; d < DK; d += 4) {
+        const float4 kk = *reinterpret_cast<const float4*>(&sk[j][d]);
+        x = fmaf(qi[d], kk.x, x);
+        x = fmaf(qi[d + 1], kk.y, x);
+        x = fmaf(qi[d + 2], kk.z, x);
+        x = fmaf(qi[d + 3], kk.w, x);
+      }
+      float wgt = 1.f;
+      for (int p = a.P - 1; p >= 1; --p) wgt = fmaf(wgt, x * rcp[p], 1.f);
+      den += wgt;
 #pragma unroll
-    for (int cc = 0; cc < CPG; ++cc) {
-      const int c = grp * CPG + cc;
-      if (c < DV) num[cc] = fmaf(wgt, sv[j][c], num[cc]);
+      for (int cc = 0; cc < CPG; ++cc) {
+        const int c = grp * CPG + cc;
+        if (c < DV) num[cc] = fmaf(wgt, sv[j][c], num[cc]);
+      }
     }
   }
+  if (i >= nvalid) return;
   constexpr int DVP = padded_dv(DV);
-  float* rec = a.ws.intra + static_cast<int64_t>(head) * DVP * a.ws.nwp + static_cast<int64_t>(ch) * L + i;
+  float* rec = a.ws.intra + static_cast<int64_t>(head) * DVP * a.ws.nwp + static_cast<int64_t>(win) * T + i;
 #pragma unroll
   for (int cc = 0; cc < CPG; ++cc) {
     const int c = grp * CPG + cc;
@@ -667,11 +687,158 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
   if (grp == 0) rec[static_cast<int64_t>(DV) * a.ws.nwp] = den;
 }
 
+// Intra-window part on MFMA, for bf16 inputs.  Block = (readout window of T
+// tokens, head); wave w owns the queries [64w, 64w + 64) of the window.  For
+// every 32-key slice up to its last query:
+//   X^T = K_s Q_w^T                       (bf16 MFMA, fp32 accumulate)
+//   W'  = T_P(X / c) - 1 by Horner's rule in fp32, zero for keys after the query
+//   O^T += V'^T_s M + V'^T_s W'           (M = the 0/1 causal mask)
+// V' = [v, 1, 0...]: its ones row gives the denominator.  The order-0 term
+// goes through the exact 0/1 mask, so only the small higher-order weights W'
+// are rounded to bf16.
+template <int DK>
+__global__ __launch_bounds__(256) void prefill_intra_mfma(IntraArgs a) {
+  constexpr int DV = DK, T = prefill_window(true);
+  constexpr int KP = DK < 32 ? 32 : DK;        // head dim padded to the MFMA K
+  constexpr int KSTEPS = KP / 32;
+  constexpr int KSTR = KP + 8;                 // bf16 per staged key row
+  constexpr int NB = col_blocks(DV), NC = NB * 16;
+  constexpr int VSTR = T + 8;                  // bf16 per staged V' row
+  constexpr int DVP = padded_dv(DV);
+  static_assert(T == 256 && DK % 8 == 0, "window of four 64-query waves");
+  __shared__ __attribute__((aligned(16))) uint16_t ks_[T * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[NC * VSTR];
+  const int win = blockIdx.x;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int lr = l & 15;
+  const int g = l >> 4;
+  const int64_t tb = a.t0 + static_cast<int64_t>(win) * T;
+  const int nvalid = min(T, a.nw - win * T);
+  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
+  const uint16_t* kh = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
+  const uint16_t* vh = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
+
+  // Stage K row-major (zero-padded to KP, zero past the window) and V'^T.
+  for (int e = tid; e < T * (KP / 8); e += 256) {
+    const int t = e / (KP / 8);
+    const int c8 = (e % (KP / 8)) * 8;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (t < nvalid && c8 < DK) val = *reinterpret_cast<const u32x4*>(kh + (tb + t) * DK + c8);
+    *reinterpret_cast<u32x4*>(&ks_[t * KSTR + c8]) = val;
+  }
+  for (int e = tid; e < T * (DV / 8); e += 256) {
+    const int t = e % T;
+    const int c8 = (e / T) * 8;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (t < nvalid) val = *reinterpret_cast<const u32x4*>(vh + (tb + t) * DV + c8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      vt[(c8 + j) * VSTR + t] = static_cast<uint16_t>((j & 1) ? (val[j / 2] >> 16) : (val[j / 2] & 0xffffu));
+  }
+  for (int e = tid; e < (NC - DV) * T; e += 256) {
+    const int c = DV + e / T;
+    const int t = e % T;
+    vt[c * VSTR + t] = (c == DV && t < nvalid) ? static_cast<uint16_t>(0x3f80) : static_cast<uint16_t>(0);
+  }
+
+  // Query operands (B of X^T): lane holds query 16 qb + lr, dims 32 kst + 8 g ...
+  bf16x8 qop[4][KSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int kst = 0; kst < KSTEPS; ++kst) {
+      const int qi = 64 * w + 16 * qb + lr;
+      const int d0 = 32 * kst + 8 * g;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (qi < nvalid && d0 < DK) val = *reinterpret_cast<const u32x4*>(qh + (tb + qi) * DK + d0);
+      qop[qb][kst] = __builtin_bit_cast(bf16x8, val);
+    }
+  __syncthreads();
+
+  f32x4 O[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) O[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float rcp[4] = {0.f, 1.f, 0.5f, 1.f / 3.f};
+  const int nslice = min(2 * w + 2, (nvalid + 31) / 32);
+  for (int sl = 0; sl < nslice; ++sl) {
+    f32x4 X[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) X[kk][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kst = 0; kst < KSTEPS; ++kst)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&ks_[(32 * sl + 16 * kk + lr) * KSTR + 32 * kst + 8 * g]);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+          X[kk][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qop[qb][kst], X[kk][qb], 0, 0, 0);
+      }
+    // Weights in B layout: lane holds query 16 qb + lr and keys
+    // 32 sl + 16 (j / 4) + 4 g + j % 4 for j = 0..7.
+    bf16x8 Bm[4], Bw[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int qi = 64 * w + 16 * qb + lr;
+      float wv[8], mv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = 32 * sl + 16 * (j / 4) + 4 * g + (j % 4);
+        const float x = X[j / 4][qb][j % 4] * a.inv_c;
+        float h = 0.f;
+        for (int p = a.P - 1; p >= 1; --p) h = x * rcp[p] * (1.f + h);
+        const bool ok = key <= qi;
+        wv[j] = ok ? h : 0.f;
+        mv[j] = ok ? 1.f : 0.f;
+      }
+      const u32x4 ww = {pack_bf16(wv[0], wv[1]), pack_bf16(wv[2], wv[3]), pack_bf16(wv[4], wv[5]),
+                        pack_bf16(wv[6], wv[7])};
+      const u32x4 mm = {pack_bf16(mv[0], mv[1]), pack_bf16(mv[2], mv[3]), pack_bf16(mv[4], mv[5]),
+                        pack_bf16(mv[6], mv[7])};
+      Bw[qb] = __builtin_bit_cast(bf16x8, ww);
+      Bm[qb] = __builtin_bit_cast(bf16x8, mm);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint16_t* vr = &vt[(16 * nb + lr) * VSTR + 32 * sl + 4 * g];
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(__builtin_assume_aligned(vr, 8));
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(__builtin_assume_aligned(vr + 16, 8));
+      const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+      const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bm[qb], O[nb][qb], 0, 0, 0);
+        O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bw[qb], O[nb][qb], 0, 0, 0);
+      }
+    }
+  }
+  // O^T in C layout: lane holds query 16 qb + lr, value columns 16 nb + 4 g + r.
+  float* rec = a.ws.intra + static_cast<int64_t>(head) * DVP * a.ws.nwp + static_cast<int64_t>(win) * T;
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const int qi = 64 * w + 16 * qb + lr;
+    if (qi >= nvalid) continue;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int col = 16 * nb + 4 * g + r;
+        if (col <= DV) rec[static_cast<int64_t>(col) * a.ws.nwp + qi] = O[nb][qb][r];
+      }
+  }
+}
+
 // out = (tile records + intra record + order-0 carry) for num / for den,
 // summed in a fixed order.  Block = (64 tokens, head).
 template <int DK, bool BF16>
 __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
-  constexpr int DV = DK, DVP = padded_dv(DV), L = prefill_chunk(BF16);
+  constexpr int DV = DK, DVP = padded_dv(DV), T = prefill_window(BF16);
   constexpr bool RECB = prefill_bf16_records(DK, BF16);
   constexpr int TB = 64;
   __shared__ float acc[(DV + 1) * (TB + 1)];
@@ -681,7 +848,7 @@ __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
   const int nwp = a.ws.nwp;
   const int64_t slab = static_cast<int64_t>(DVP) * nwp;
   const float* intra = a.ws.intra + head * slab;
-  const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + L - 1) / L) * DVP;
+  const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + T - 1) / T) * DVP;
   for (int e = tid; e < (DV + 1) * (TB / 4); e += 256) {
     const int c = e / (TB / 4);
     const int t = 4 * (e % (TB / 4));
@@ -701,7 +868,7 @@ __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
       for (int tl = 0; tl < a.n_tiles; ++tl) s += *reinterpret_cast<const f32x4*>(&rec[tl * slab + off]);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] += carry[((t0 + t + j) / L) * DVP + c];
+    for (int j = 0; j < 4; ++j) s[j] += carry[((t0 + t + j) / T) * DVP + c];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[c * (TB + 1) + t + j] = s[j];
   }
@@ -723,9 +890,12 @@ hipError_t launch_scan_t(int BH, const ScanArgs& a, hipStream_t s) {
 
 template <int D, bool BF16>
 hipError_t launch_intra_t(int BH, const IntraArgs& a, hipStream_t s) {
-  constexpr int L = prefill_chunk(BF16);
-  dim3 grid((a.nw + L - 1) / L, BH);
-  prefill_intra<D, BF16><<<grid, 256, 0, s>>>(a);
+  constexpr int T = prefill_window(BF16);
+  dim3 grid((a.nw + T - 1) / T, BH);
+  if constexpr (BF16)
+    prefill_intra_mfma<D><<<grid, 256, 0, s>>>(a);
+  else
+    prefill_intra<D, BF16><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
