@@ -178,6 +178,16 @@ std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32
   return runs;
 }
 
+// Tile layouts.  Two encodings:
+//  * float32 inputs: parent slots for every parent; key side reads a parent
+//    table and a separate key table; the query side reads a per-slot table
+//    and the scan keeps rows divided by the multiplicity of their last index.
+//  * bfloat16 inputs: one key-side table (key rows, halved key rows, a zero
+//    row, a ones row, then slots for order-2 parents only, which carry the
+//    parent's 1/prod(count!) and the 1/3 of the (i, i, i) rows); the query
+//    side is the plain monomial prod(q/c), built from two query coordinates
+//    (index d = the constant 1) and the run's four children; the scan keeps
+//    row m divided by prod(count!) of m.
 int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& rank, bool bf16,
                  bool upload_tables, PrefillLayout* lay) {
   const int rb = sata::prefill_rb(b->d, bf16);
@@ -185,8 +195,12 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
   const int max_slots = sata::prefill_slots(b->d, bf16);
   const int kstr = sata::prefill_kstride(bf16);
   const int xk_zero = 2 * b->d * kstr;
+  const bool v2 = bf16;
+  const int row_zero = 2 * b->d, row_ones = 2 * b->d + 1, row_slot = 2 * b->d + 2;
   lay->rb = rb;
   const std::vector<Run> runs = build_runs(*b, rank);
+  auto parent_order = [](uint32_t key) { return static_cast<int>((key >> 24) & 0x7f); };
+  auto needs_slot = [&](const Run& r) { return !v2 || parent_order(r.parent_key) >= 2; };
   // Greedy tiling in canonical order: a tile takes runs until it is full or
   // one more run would exceed the parent-slot cap.  With P = 1 there are no
   // runs, but one (empty) tile still carries the order-0 row.
@@ -195,14 +209,14 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
     std::vector<int> cur;
     std::unordered_map<uint32_t, int> keys;
     for (int ri = 0; ri < static_cast<int>(runs.size()); ++ri) {
-      const bool new_key = keys.find(runs[ri].parent_key) == keys.end();
+      const bool new_key = needs_slot(runs[ri]) && keys.find(runs[ri].parent_key) == keys.end();
       if (static_cast<int>(cur.size()) == per_tile ||
           (new_key && static_cast<int>(keys.size()) == max_slots)) {
         tiles.push_back(cur);
         cur.clear();
         keys.clear();
       }
-      keys.emplace(runs[ri].parent_key, 0);
+      if (needs_slot(runs[ri])) keys.emplace(runs[ri].parent_key, 0);
       cur.push_back(ri);
     }
     if (!cur.empty() || tiles.empty()) tiles.push_back(cur);
@@ -224,12 +238,54 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
       const int g = u % 4;
       const size_t blk = (static_cast<size_t>(t) * sata::kWaves + w) * rb + bl;
       if (u >= static_cast<int>(tiles[t].size())) {
-        // Empty run: masked children reading the zero row, parent slot 0.
-        for (int j = 0; j < 4; ++j) kside[blk * 16 + 4 * g + j] = static_cast<uint32_t>(xk_zero) << 16;
-        qside[blk * 4 + g] = 0;
+        // Empty run: masked children reading the zero row (parent slot 0, or
+        // the ones row / the constant query coordinate).
+        for (int j = 0; j < 4; ++j)
+          kside[blk * 16 + 4 * g + j] =
+              v2 ? static_cast<uint32_t>(row_ones * kstr) | (static_cast<uint32_t>(row_zero * kstr) << 16)
+                 : static_cast<uint32_t>(xk_zero) << 16;
+        qside[blk * 4 + g] = v2 ? static_cast<uint32_t>(b->d) | (static_cast<uint32_t>(b->d) << 8) : 0u;
         continue;
       }
       const Run& run = runs[tiles[t][u]];
+      if (v2) {
+        const int pp = parent_order(run.parent_key);
+        const int i1 = pp >= 1 ? static_cast<int>(run.parent_key & 0xffu) : b->d;
+        const int i2 = pp >= 2 ? static_cast<int>((run.parent_key >> 8) & 0xffu) : b->d;
+        int prow;
+        if (pp == 0) {
+          prow = row_ones;
+        } else if (pp == 1) {
+          prow = i1;
+        } else {
+          auto it = slot_of.find(run.parent_key);
+          int slot;
+          if (it == slot_of.end()) {
+            slot = static_cast<int>(slot_of.size());
+            slot_of.emplace(run.parent_key, slot);
+            const size_t si = static_cast<size_t>(t) * max_slots + slot;
+            parents[si] = static_cast<uint32_t>(i1) | (static_cast<uint32_t>(i2) << 8);
+            kscale[si] = run.kscale * run.parent_weight;
+          } else {
+            slot = it->second;
+          }
+          prow = row_slot + slot;
+        }
+        qside[blk * 4 + g] = static_cast<uint32_t>(i1) | (static_cast<uint32_t>(i2) << 8) |
+                             (static_cast<uint32_t>(run.c0) << 16);
+        const double cf = 1.0 / static_cast<double>(run.parent_weight);   // prod(count!) of the parent
+        for (int j = 0; j < 4; ++j) {
+          const int code = run.code[j];
+          const int xrow = code == 0 ? row_zero : (code - 1) * b->d + run.c0 + j;
+          kside[blk * 16 + 4 * g + j] =
+              static_cast<uint32_t>(prow * kstr) | (static_cast<uint32_t>(xrow * kstr) << 16);
+          if (run.row[j] >= 0) {
+            const uint32_t fac = static_cast<uint32_t>(std::lround(cf * run.cnt[j]));
+            rowinfo[blk * 16 + 4 * g + j] = static_cast<uint32_t>(run.row[j] + 1) | (fac << 28);
+          }
+        }
+        continue;
+      }
       auto it = slot_of.find(run.parent_key);
       int slot;
       if (it == slot_of.end()) {
@@ -254,8 +310,9 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
               static_cast<uint32_t>(run.row[j] + 1) | (static_cast<uint32_t>(run.cnt[j]) << 28);
       }
     }
-    // Every tile has at least one parent slot so empty runs read finite features.
-    nslot[t] = std::max(1, static_cast<int32_t>(slot_of.size()));
+    // Every tile has at least one parent slot so empty runs read finite
+    // features (the bfloat16 encoding needs none).
+    nslot[t] = v2 ? static_cast<int32_t>(slot_of.size()) : std::max(1, static_cast<int32_t>(slot_of.size()));
   }
   lay->n_tiles = n_tiles;
   if (!upload_tables) return SATA_OK;

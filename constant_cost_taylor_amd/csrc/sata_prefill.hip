@@ -687,6 +687,423 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
   if (grp == 0) rec[static_cast<int64_t>(DV) * a.ws.nwp] = den;
 }
 
+// Scan for bf16 inputs.  Same chunk pipeline as the fp32 scan, with a leaner
+// per-chunk body:
+//  * one LDS key table kt = [k rows | k/2 rows | zero row | ones row | parent
+//    slots]; only order-2 parents need a slot (filled 8 tokens per item),
+//    order 0 and 1 parents read the ones row or a key row directly;
+//  * the query side is the plain monomial prod(q/c), built in registers from
+//    two staged query coordinates (index d = the constant 1) and the run's
+//    four children; the parent weights live on the key side, and the state is
+//    kept divided by prod(count!) of each row inside the scan;
+//  * the cross-wave readout sum goes through an fp32 LDS buffer;
+//  * masking of tokens past the window happens only in a partial chunk.
+template <int DK>
+struct CfgB {
+  static constexpr int DV = DK;
+  static constexpr int L = prefill_chunk(true);
+  static constexpr int T = prefill_window(true);
+  static constexpr int SC = T / L;
+  static constexpr int RB = prefill_rb(DK, true);
+  static constexpr int NB = col_blocks(DV);
+  static constexpr int NC = NB * 16;
+  static constexpr int DVP = padded_dv(DV);
+  static constexpr int NSLOT = prefill_slots(DK, true);
+  static constexpr int KSTR = prefill_kstride(true);
+  static constexpr int XQSTR = DK + 4;
+  static constexpr int RSTR = L + 4;
+  static constexpr int VSTR = L + 8;
+  static constexpr int ROW_ZERO = 2 * DK, ROW_ONES = 2 * DK + 1, ROW_SLOT = 2 * DK + 2;
+  static constexpr int KT_ROWS = ROW_SLOT + NSLOT;
+  static constexpr int NKS = RB / 2;
+  static constexpr int MB = L / 16;
+  static constexpr int EPT = L * DK / (kWaves * 64);
+  static constexpr bool RECB = prefill_bf16_records(DK, true);
+  static_assert(RB % 2 == 0, "readout K-slices pair row blocks");
+};
+
+template <int DK>
+__global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) {
+  using C = CfgB<DK>;
+  constexpr int DV = C::DV, L = C::L, RB = C::RB, NB = C::NB, NC = C::NC, DVP = C::DVP;
+  constexpr int NSLOT = C::NSLOT, KSTR = C::KSTR, XQSTR = C::XQSTR, RSTR = C::RSTR, VSTR = C::VSTR;
+  constexpr int EPT = C::EPT;
+
+  __shared__ __attribute__((aligned(16))) float kt[C::KT_ROWS * KSTR];
+  __shared__ __attribute__((aligned(16))) float xq[L * XQSTR];
+  __shared__ __attribute__((aligned(16))) float red[kWaves * (DV + 1) * RSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[NC * VSTR];
+  __shared__ float carry[NC];
+  __shared__ uint32_t spar[NSLOT];
+  __shared__ float spsc[NSLOT];
+
+  const int tile = blockIdx.x;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int lr = l & 15;
+  const int g = l >> 4;
+  const int n_tiles = a.lay.n_tiles;
+  const int lay_base = (tile * kWaves + w) * RB;
+
+  // Per-lane run metadata: key side (parent row | child row, as kt offsets),
+  // query side (parent coordinates i1 | i2 << 8 | first child << 16).
+  uint32_t ks[RB], qs[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    ks[b] = a.lay.kside[(lay_base + b) * 16 + lr];
+    qs[b] = a.lay.qside[(lay_base + b) * 4 + g];
+  }
+  const int nslot = a.lay.nslot[tile];
+  for (int s = tid; s < nslot; s += kWaves * 64) {
+    spar[s] = a.lay.parents[tile * NSLOT + s];
+    spsc[s] = a.lay.kscale[tile * NSLOT + s];
+  }
+  for (int i = tid; i < KSTR; i += kWaves * 64) {
+    kt[C::ROW_ZERO * KSTR + i] = 0.f;
+    kt[C::ROW_ONES * KSTR + i] = 1.f;
+  }
+  for (int t = tid; t < L; t += kWaves * 64) {
+    xq[t * XQSTR + DK] = 1.f;
+    xq[t * XQSTR + DK + 1] = 0.f;
+    xq[t * XQSTR + DK + 2] = 0.f;
+    xq[t * XQSTR + DK + 3] = 0.f;
+  }
+  for (int e = tid; e < (NC - DV) * VSTR; e += kWaves * 64) {
+    const int c = DV + e / VSTR;
+    vt[c * VSTR + e % VSTR] = (c == DV) ? static_cast<uint16_t>(0x3f80) : static_cast<uint16_t>(0);
+  }
+
+  // State tile into the accumulators (C layout: lane holds column nb*16 + lr
+  // of rows 4g + r), divided by prod(count!) of each row.
+  float* st = a.state + static_cast<int64_t>(head) * a.stride;
+  const int64_t zoff = static_cast<int64_t>(a.D) * DV;
+  f32x4 S[RB][NB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t info = a.lay.rowinfo[(lay_base + b) * 16 + 4 * g + r];
+      const int64_t m = info ? static_cast<int64_t>(info & 0x0fffffffu) - 1 : 0;
+      const float inv_fac = info ? 1.f / static_cast<float>(info >> 28) : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = nb * 16 + lr;
+        float val = 0.f;
+        if (col < DV) val = st[m * DV + col];
+        else if (col == DV) val = st[zoff + m];
+        S[b][nb][r] = val * inv_fac;
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(S[b][nb]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // bf16 copy of the state (readout operand), per K-slice of two row blocks.
+  u32x4 Sb[C::NKS][NB];
+  auto refresh = [&]() {
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        Sb[b / 2][nb][2 * (b % 2)] = pack_bf16(S[b][nb][0], S[b][nb][1]);
+        Sb[b / 2][nb][2 * (b % 2) + 1] = pack_bf16(S[b][nb][2], S[b][nb][3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  refresh();
+  if (tile == 0 && tid < NC) carry[tid] = tid < DV ? st[tid] : (tid == DV ? st[zoff] : 0.f);
+
+  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
+  const uint16_t* kh = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
+  const uint16_t* vh = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
+  const int nwp = a.ws.nwp;
+  using RedT = typename std::conditional<C::RECB, uint16_t, float>::type;
+  RedT* rech = static_cast<RedT*>(a.ws.rec) +
+               (static_cast<int64_t>(head) * n_tiles + tile) * DVP * static_cast<int64_t>(nwp);
+  const int nch = (a.nw + L - 1) / L;
+  float* carryh = a.ws.carry + static_cast<int64_t>(head) * ((nwp + C::T - 1) / C::T) * DVP;
+
+  // Cross-wave sum of one chunk's readout (fp32 LDS) into its records.
+  auto red_sum = [&](int ch) {
+    for (int e = tid; e < (DV + 1) * (L / 4); e += kWaves * 64) {
+      const int c = e / (L / 4);
+      const int tg = e % (L / 4);
+      f32x4 sum = *reinterpret_cast<const f32x4*>(&red[c * RSTR + 4 * tg]);
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww)
+        sum += *reinterpret_cast<const f32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 4 * tg]);
+      const int64_t off = static_cast<int64_t>(c) * nwp + ch * L + 4 * tg;
+      if constexpr (C::RECB) {
+        const u32x2 o = {pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
+        *reinterpret_cast<u32x2*>(&rech[off]) = o;
+      } else {
+        *reinterpret_cast<f32x4*>(&rech[off]) = sum;
+      }
+    }
+  };
+
+  // Staging: each thread holds EPT consecutive elements of one token per
+  // tensor; consecutive lanes take consecutive tokens.
+  const int st_t = tid % L;
+  const int st_i = (tid / L) * EPT;
+  ChunkRegs<uint16_t, EPT> rq, rk, rv;
+  {
+    const bool ok = st_t < min(L, a.nw);
+    const int64_t tn = a.t0 + (ok ? st_t : 0);
+    rq.load(qh + tn * DK + st_i, true);
+    rk.load(kh + tn * DK + st_i, true);
+    rv.load(vh + tn * DV + st_i, true);
+  }
+
+  for (int ch0 = 0; ch0 < nch; ch0 += C::SC) {
+    const int ch_end = min(nch, ch0 + C::SC);
+    for (int ch = ch0; ch < ch_end; ++ch) {
+      const int64_t tb = a.t0 + static_cast<int64_t>(ch) * L;
+      const int nvalid = min(L, a.nw - ch * L);
+#pragma unroll
+      for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(ks[b]), "+v"(qs[b]));
+
+      // ---- phase A: previous chunk's records, then stage this chunk ------
+      if (ch > 0) red_sum(ch - 1);
+      if constexpr (EPT >= 4) {
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+          float4 q4;
+          q4.x = to_f32(rq.raw(e)) * a.inv_c;
+          q4.y = to_f32(rq.raw(e + 1)) * a.inv_c;
+          q4.z = to_f32(rq.raw(e + 2)) * a.inv_c;
+          q4.w = to_f32(rq.raw(e + 3)) * a.inv_c;
+          *reinterpret_cast<float4*>(__builtin_assume_aligned(&xq[st_t * XQSTR + st_i + e], 16)) = q4;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) xq[st_t * XQSTR + st_i + e] = to_f32(rq.raw(e)) * a.inv_c;
+      }
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const float kv = to_f32(rk.raw(e));
+        kt[(st_i + e) * KSTR + st_t] = kv;
+        kt[(DK + st_i + e) * KSTR + st_t] = kv * 0.5f;
+        vt[(st_i + e) * VSTR + st_t] = rv.raw(e);
+      }
+      if (nvalid < L && st_t >= nvalid) {
+        // Tokens past the window: zero keys and values (queries stay finite).
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          kt[(st_i + e) * KSTR + st_t] = 0.f;
+          kt[(DK + st_i + e) * KSTR + st_t] = 0.f;
+          vt[(st_i + e) * VSTR + st_t] = 0;
+        }
+      }
+      if (ch + 1 < nch) {
+        const bool ok = st_t < min(L, a.nw - (ch + 1) * L);
+        const int64_t tn = tb + L + (ok ? st_t : 0);
+        rq.load(qh + tn * DK + st_i, true);
+        rk.load(kh + tn * DK + st_i, true);
+        rv.load(vh + tn * DV + st_i, true);
+      }
+      __syncthreads();
+
+      // ---- phase B: order-2 parent key features, 8 tokens per item -------
+      for (int e = tid; e < nslot * (L / 8); e += kWaves * 64) {
+        const int s = e / (L / 8);
+        const int t8 = (e % (L / 8)) * 8;
+        const uint32_t pw = spar[s];
+        const int i1 = pw & 255;
+        const int i2 = (pw >> 8) & 255;
+        const float sc = spsc[s];
+        const float4 a0 = lds4(kt, i1 * KSTR + t8), a1 = lds4(kt, i1 * KSTR + t8 + 4);
+        const float4 b0 = lds4(kt, i2 * KSTR + t8), b1 = lds4(kt, i2 * KSTR + t8 + 4);
+        float* dst = &kt[(C::ROW_SLOT + s) * KSTR + t8];
+        *reinterpret_cast<float4*>(__builtin_assume_aligned(dst, 16)) =
+            make_float4(sc * a0.x * b0.x, sc * a0.y * b0.y, sc * a0.z * b0.z, sc * a0.w * b0.w);
+        *reinterpret_cast<float4*>(__builtin_assume_aligned(dst + 4, 16)) =
+            make_float4(sc * a1.x * b1.x, sc * a1.y * b1.y, sc * a1.z * b1.z, sc * a1.w * b1.w);
+      }
+      if (tile == 0) {
+        // Order-0 prefix at each readout window's start, then add the chunk
+        // (exact fp32).
+        const bool wstart = ch % C::SC == 0;
+        if (tid < DV) {
+          if (wstart) carryh[static_cast<int64_t>(ch / C::SC) * DVP + tid] = carry[tid];
+          float sv = 0.f;
+          for (int t = 0; t < nvalid; ++t) sv += __uint_as_float(static_cast<uint32_t>(vt[tid * VSTR + t]) << 16);
+          carry[tid] += sv;
+        } else if (tid == DV) {
+          if (wstart) carryh[static_cast<int64_t>(ch / C::SC) * DVP + DV] = carry[DV];
+          carry[DV] += static_cast<float>(nvalid);
+        }
+      }
+      __syncthreads();
+
+      // ---- phase C: readout against the state at the window start --------
+      // (two 16-token blocks at a time) into the fp32 reduction buffer.
+#pragma unroll
+      for (int half = 0; half < C::MB / 2; ++half) {
+        f32x4 acc[2][NB];
+        struct QData {
+          float p1[2][2], p2[2][2];
+          float4 x[2][2];
+        };
+        auto load_q = [&](int kk, QData& dq) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const int t = (2 * half + mb) * 16 + lr;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t q = qs[2 * kk + h];
+              dq.p1[mb][h] = xq[t * XQSTR + (q & 255)];
+              dq.p2[mb][h] = xq[t * XQSTR + ((q >> 8) & 255)];
+              dq.x[mb][h] = lds4(xq, t * XQSTR + (q >> 16));
+            }
+          }
+        };
+        auto build_q = [&](const QData& dq, bf16x8 (&A)[2]) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const float p0 = dq.p1[mb][0] * dq.p2[mb][0];
+            const float p1 = dq.p1[mb][1] * dq.p2[mb][1];
+            const float4 x0 = dq.x[mb][0], x1 = dq.x[mb][1];
+            const u32x4 aw = {pack_bf16(p0 * x0.x, p0 * x0.y), pack_bf16(p0 * x0.z, p0 * x0.w),
+                              pack_bf16(p1 * x1.x, p1 * x1.y), pack_bf16(p1 * x1.z, p1 * x1.w)};
+            A[mb] = __builtin_bit_cast(bf16x8, aw);
+          }
+        };
+        QData dq0, dq1;
+        bf16x8 Acur[2], Anext[2];
+        load_q(0, dq0);
+        build_q(dq0, Acur);
+        if (C::NKS > 1) load_q(C::NKS > 1 ? 1 : 0, dq0);
+        if (C::NKS > 2) load_q(C::NKS > 2 ? 2 : 0, dq1);
+#pragma unroll
+        for (int kk = 0; kk < C::NKS; ++kk) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const bf16x8 Bop = __builtin_bit_cast(bf16x8, Sb[kk][nb]);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  Acur[mb], Bop, kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb], 0, 0, 0);
+          }
+          if (kk + 1 < C::NKS) build_q(dq0, Anext);
+          if (kk + 3 < C::NKS) load_q(kk + 3 < C::NKS ? kk + 3 : 0, dq0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (kk + 1 < C::NKS) {
+            Acur[0] = Anext[0];
+            Acur[1] = Anext[1];
+            const QData tq = dq0;
+            dq0 = dq1;
+            dq1 = tq;
+          }
+        }
+        // C layout: lane holds column nb*16 + lr of tokens 4g..4g+3.
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int col = nb * 16 + lr;
+            if (col <= DV)
+              *reinterpret_cast<f32x4*>(__builtin_assume_aligned(
+                  &red[(w * (DV + 1) + col) * RSTR + (2 * half + mb) * 16 + 4 * g], 16)) = acc[mb][nb];
+          }
+      }
+
+      // ---- phase C: state update S += phi_k(K)^T [V 1] --------------------
+      {
+        constexpr int NST = (L / 32) * RB;
+        struct KData {
+          float4 p0, p1, x0, x1;
+        };
+        auto load_k = [&](int st_, KData& dk) {
+          const int kst = st_ / RB, b = st_ % RB;
+          const int pko = (ks[b] & 0xffff) + 32 * kst + 8 * g;
+          const int xko = (ks[b] >> 16) + 32 * kst + 8 * g;
+          dk.p0 = lds4(kt, pko);
+          dk.p1 = lds4(kt, pko + 4);
+          dk.x0 = lds4(kt, xko);
+          dk.x1 = lds4(kt, xko + 4);
+        };
+        auto build_k = [&](const KData& dk) {
+          const u32x4 aw = {pack_bf16(dk.p0.x * dk.x0.x, dk.p0.y * dk.x0.y),
+                            pack_bf16(dk.p0.z * dk.x0.z, dk.p0.w * dk.x0.w),
+                            pack_bf16(dk.p1.x * dk.x1.x, dk.p1.y * dk.x1.y),
+                            pack_bf16(dk.p1.z * dk.x1.z, dk.p1.w * dk.x1.w)};
+          return __builtin_bit_cast(bf16x8, aw);
+        };
+        auto load_v = [&](int kst, bf16x8 (&Bv)[NB]) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            Bv[nb] = *reinterpret_cast<const bf16x8*>(
+                __builtin_assume_aligned(&vt[(nb * 16 + lr) * VSTR + 32 * kst + 8 * g], 16));
+        };
+        bf16x8 Bv[NB], Bvn[NB];
+        load_v(0, Bv);
+        KData d0, d1;
+        load_k(0, d0);
+        bf16x8 Acur = build_k(d0);
+        if (NST > 1) load_k(NST > 1 ? 1 : 0, d0);
+        if (NST > 2) load_k(NST > 2 ? 2 : 0, d1);
+#pragma unroll
+        for (int st_ = 0; st_ < NST; ++st_) {
+          const int kst = st_ / RB, b = st_ % RB;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur, Bv[nb], S[b][nb], 0, 0, 0);
+          bf16x8 Anext = Acur;
+          if (st_ + 1 < NST) Anext = build_k(d0);
+          if (st_ + 3 < NST) load_k(st_ + 3 < NST ? st_ + 3 : 0, d0);
+          if (b == RB - 2 && kst + 1 < L / 32) load_v(kst + 1 < L / 32 ? kst + 1 : 0, Bvn);
+          __builtin_amdgcn_sched_barrier(0);
+          Acur = Anext;
+          {
+            const KData t2 = d0;
+            d0 = d1;
+            d1 = t2;
+          }
+          if (b == RB - 1 && kst + 1 < L / 32) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) Bv[nb] = Bvn[nb];
+          }
+        }
+      }
+      __syncthreads();
+    }
+    refresh();
+  }
+  if (nch > 0) red_sum(nch - 1);
+
+  // State tile back in canonical layout (times prod(count!) of each row).
+  const uint32_t* rowinfo = a.lay.rowinfo;
+  float* stw = st;
+  asm volatile("" : "+s"(rowinfo), "+s"(stw));
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t info = rowinfo[(lay_base + b) * 16 + 4 * g + r];
+      if (info) {
+        const int64_t m = static_cast<int64_t>(info & 0x0fffffffu) - 1;
+        const float fac = static_cast<float>(info >> 28);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = nb * 16 + lr;
+          const float val = S[b][nb][r] * fac;
+          if (col < DV) stw[m * DV + col] = val;
+          else if (col == DV) stw[zoff + m] = val;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (tile == 0) {
+    if (tid < DV) st[tid] = carry[tid];
+    else if (tid == DV) st[zoff] = carry[DV];
+  }
+}
+
 // Intra-window part on MFMA, for bf16 inputs.  Block = (readout window of T
 // tokens, head); wave w owns the queries [64w, 64w + 64) of the window.  For
 // every 32-key slice up to its last query:
@@ -884,7 +1301,10 @@ __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
 template <int D, bool BF16>
 hipError_t launch_scan_t(int BH, const ScanArgs& a, hipStream_t s) {
   dim3 grid(a.lay.n_tiles, BH);
-  prefill_scan<D, BF16><<<grid, kWaves * 64, 0, s>>>(a);
+  if constexpr (BF16)
+    prefill_scan_bf16<D><<<grid, kWaves * 64, 0, s>>>(a);
+  else
+    prefill_scan<D, BF16><<<grid, kWaves * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
