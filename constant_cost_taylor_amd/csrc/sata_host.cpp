@@ -222,7 +222,8 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
     if (!cur.empty() || tiles.empty()) tiles.push_back(cur);
   }
   const int n_tiles = static_cast<int>(tiles.size());
-  const size_t nblk = static_cast<size_t>(n_tiles) * sata::kWaves * rb;
+  const int nw = sata::prefill_waves(bf16);
+  const size_t nblk = static_cast<size_t>(n_tiles) * nw * rb;
   std::vector<uint32_t> kside(nblk * 16, 0);
   std::vector<uint32_t> qside(nblk * 4, 0);
   std::vector<uint32_t> rowinfo(nblk * 16, 0);
@@ -236,7 +237,7 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
       const int w = u / (4 * rb);
       const int bl = (u / 4) % rb;
       const int g = u % 4;
-      const size_t blk = (static_cast<size_t>(t) * sata::kWaves + w) * rb + bl;
+      const size_t blk = (static_cast<size_t>(t) * nw + w) * rb + bl;
       if (u >= static_cast<int>(tiles[t].size())) {
         // Empty run: masked children reading the zero row (parent slot 0, or
         // the ones row / the constant query coordinate).

@@ -9,8 +9,13 @@
 
 namespace sata {
 
-// Waves per prefill workgroup.
+// Waves per prefill workgroup of the fp32 scan (and of the intra-window and
+// reduce kernels).
 constexpr int kWaves = 4;
+
+// Waves per prefill scan workgroup: the bf16 scan runs two waves per SIMD so
+// one wave's LDS traffic and operand building overlap the other's MFMAs.
+constexpr int prefill_waves(bool bf16) { return bf16 ? 8 : kWaves; }
 
 // Rows of one decode tile and threads of every decode / reduce block.
 constexpr int kDecodeRows = 512;
@@ -29,16 +34,17 @@ constexpr int prefill_chunk(bool bf16) { return bf16 ? 64 : 32; }
 constexpr int prefill_window(bool bf16) { return bf16 ? 256 : prefill_chunk(bf16); }
 
 // Row blocks of 16 rows per wave held on chip by the prefill scan, per
-// (head dim, input dtype): the fp32 state tile (rb * column blocks * 4
-// registers) plus the readout accumulators must fit the 256 accumulator
-// registers of a lane at one wave per SIMD.
+// (head dim, input dtype).  fp32 (one wave per SIMD): the state tile
+// (rb * column blocks * 4 registers) plus the readout accumulators fit the
+// 256 accumulator registers of a lane.  bf16 (two waves per SIMD): state,
+// its bf16 copy and the working set fit 256 registers per lane.
 constexpr int prefill_rb(int d, bool bf16) {
-  return d == 64 ? 8 : d == 32 ? 8 : d == 16 ? (bf16 ? 8 : 4) : (bf16 ? 2 : 1);
+  return bf16 ? (d >= 16 ? 4 : 2) : (d >= 32 ? 8 : d == 16 ? 4 : 1);
 }
 
 // Runs of four rows per tile and the cap on distinct parent multisets per
 // tile (the per-chunk parent-feature tables are sized by it).
-constexpr int prefill_runs_per_tile(int d, bool bf16) { return 4 * prefill_rb(d, bf16) * kWaves; }
+constexpr int prefill_runs_per_tile(int d, bool bf16) { return 4 * prefill_rb(d, bf16) * prefill_waves(bf16); }
 constexpr int prefill_slots(int d, bool bf16) {
   return prefill_runs_per_tile(d, bf16) < 80 ? prefill_runs_per_tile(d, bf16) : 80;
 }

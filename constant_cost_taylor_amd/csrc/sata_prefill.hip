@@ -704,6 +704,7 @@ struct CfgB {
   static constexpr int L = prefill_chunk(true);
   static constexpr int T = prefill_window(true);
   static constexpr int SC = T / L;
+  static constexpr int NW = prefill_waves(true);
   static constexpr int RB = prefill_rb(DK, true);
   static constexpr int NB = col_blocks(DV);
   static constexpr int NC = NB * 16;
@@ -711,27 +712,28 @@ struct CfgB {
   static constexpr int NSLOT = prefill_slots(DK, true);
   static constexpr int KSTR = prefill_kstride(true);
   static constexpr int XQSTR = DK + 4;
-  static constexpr int RSTR = L + 4;
+  static constexpr int RSTR = L + 8;           // bf16 per reduction row
   static constexpr int VSTR = L + 8;
   static constexpr int ROW_ZERO = 2 * DK, ROW_ONES = 2 * DK + 1, ROW_SLOT = 2 * DK + 2;
   static constexpr int KT_ROWS = ROW_SLOT + NSLOT;
   static constexpr int NKS = RB / 2;
   static constexpr int MB = L / 16;
-  static constexpr int EPT = L * DK / (kWaves * 64);
+  static constexpr int EPT = L * DK / (NW * 64);
   static constexpr bool RECB = prefill_bf16_records(DK, true);
   static_assert(RB % 2 == 0, "readout K-slices pair row blocks");
 };
 
 template <int DK>
-__global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) {
+__global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_bf16(ScanArgs a) {
   using C = CfgB<DK>;
+  constexpr int NW = C::NW;
   constexpr int DV = C::DV, L = C::L, RB = C::RB, NB = C::NB, NC = C::NC, DVP = C::DVP;
   constexpr int NSLOT = C::NSLOT, KSTR = C::KSTR, XQSTR = C::XQSTR, RSTR = C::RSTR, VSTR = C::VSTR;
   constexpr int EPT = C::EPT;
 
   __shared__ __attribute__((aligned(16))) float kt[C::KT_ROWS * KSTR];
   __shared__ __attribute__((aligned(16))) float xq[L * XQSTR];
-  __shared__ __attribute__((aligned(16))) float red[kWaves * (DV + 1) * RSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t red[NW * (DV + 1) * RSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vt[NC * VSTR];
   __shared__ float carry[NC];
   __shared__ uint32_t spar[NSLOT];
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) 
   const int lr = l & 15;
   const int g = l >> 4;
   const int n_tiles = a.lay.n_tiles;
-  const int lay_base = (tile * kWaves + w) * RB;
+  const int lay_base = (tile * NW + w) * RB;
 
   // Per-lane run metadata: key side (parent row | child row, as kt offsets),
   // query side (parent coordinates i1 | i2 << 8 | first child << 16).
@@ -756,21 +758,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) 
     qs[b] = a.lay.qside[(lay_base + b) * 4 + g];
   }
   const int nslot = a.lay.nslot[tile];
-  for (int s = tid; s < nslot; s += kWaves * 64) {
+  for (int s = tid; s < nslot; s += NW * 64) {
     spar[s] = a.lay.parents[tile * NSLOT + s];
     spsc[s] = a.lay.kscale[tile * NSLOT + s];
   }
-  for (int i = tid; i < KSTR; i += kWaves * 64) {
+  for (int i = tid; i < KSTR; i += NW * 64) {
     kt[C::ROW_ZERO * KSTR + i] = 0.f;
     kt[C::ROW_ONES * KSTR + i] = 1.f;
   }
-  for (int t = tid; t < L; t += kWaves * 64) {
+  for (int t = tid; t < L; t += NW * 64) {
     xq[t * XQSTR + DK] = 1.f;
     xq[t * XQSTR + DK + 1] = 0.f;
     xq[t * XQSTR + DK + 2] = 0.f;
     xq[t * XQSTR + DK + 3] = 0.f;
   }
-  for (int e = tid; e < (NC - DV) * VSTR; e += kWaves * 64) {
+  for (int e = tid; e < (NC - DV) * VSTR; e += NW * 64) {
     const int c = DV + e / VSTR;
     vt[c * VSTR + e % VSTR] = (c == DV) ? static_cast<uint16_t>(0x3f80) : static_cast<uint16_t>(0);
   }
@@ -796,8 +798,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) 
         S[b][nb][r] = val * inv_fac;
       }
     }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(S[b][nb]));
     __builtin_amdgcn_sched_barrier(0);
   }
   // bf16 copy of the state (readout operand), per K-slice of two row blocks.
@@ -826,21 +826,32 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) 
   const int nch = (a.nw + L - 1) / L;
   float* carryh = a.ws.carry + static_cast<int64_t>(head) * ((nwp + C::T - 1) / C::T) * DVP;
 
-  // Cross-wave sum of one chunk's readout (fp32 LDS) into its records.
+  // Cross-wave sum of one chunk's readout (bf16 partials in LDS, summed in
+  // fp32 in a fixed order) into its records, 8 tokens per item.
   auto red_sum = [&](int ch) {
-    for (int e = tid; e < (DV + 1) * (L / 4); e += kWaves * 64) {
-      const int c = e / (L / 4);
-      const int tg = e % (L / 4);
-      f32x4 sum = *reinterpret_cast<const f32x4*>(&red[c * RSTR + 4 * tg]);
+    for (int e = tid; e < (DV + 1) * (L / 8); e += NW * 64) {
+      const int c = e / (L / 8);
+      const int tg = e % (L / 8);
+      float sum[8];
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww)
-        sum += *reinterpret_cast<const f32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 4 * tg]);
-      const int64_t off = static_cast<int64_t>(c) * nwp + ch * L + 4 * tg;
+      for (int j = 0; j < 8; ++j) sum[j] = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 8 * tg]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sum[2 * j] += bf16_lo(x[j]);
+          sum[2 * j + 1] += bf16_hi(x[j]);
+        }
+      }
+      const int64_t off = static_cast<int64_t>(c) * nwp + ch * L + 8 * tg;
       if constexpr (C::RECB) {
-        const u32x2 o = {pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
-        *reinterpret_cast<u32x2*>(&rech[off]) = o;
+        const u32x4 o = {pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3]), pack_bf16(sum[4], sum[5]),
+                         pack_bf16(sum[6], sum[7])};
+        *reinterpret_cast<u32x4*>(&rech[off]) = o;
       } else {
-        *reinterpret_cast<f32x4*>(&rech[off]) = sum;
+        *reinterpret_cast<f32x4*>(&rech[off]) = f32x4{sum[0], sum[1], sum[2], sum[3]};
+        *reinterpret_cast<f32x4*>(&rech[off + 4]) = f32x4{sum[4], sum[5], sum[6], sum[7]};
       }
     }
   };
@@ -908,7 +919,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) 
       __syncthreads();
 
       // ---- phase B: order-2 parent key features, 8 tokens per item -------
-      for (int e = tid; e < nslot * (L / 8); e += kWaves * 64) {
+      for (int e = tid; e < nslot * (L / 8); e += NW * 64) {
         const int s = e / (L / 8);
         const int t8 = (e % (L / 8)) * 8;
         const uint32_t pw = spar[s];
@@ -940,75 +951,63 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) 
       __syncthreads();
 
       // ---- phase C: readout against the state at the window start --------
-      // (two 16-token blocks at a time) into the fp32 reduction buffer.
-#pragma unroll
-      for (int half = 0; half < C::MB / 2; ++half) {
-        f32x4 acc[2][NB];
+      // (one 16-token block at a time) into the bf16 reduction buffer.
+      {
         struct QData {
-          float p1[2][2], p2[2][2];
-          float4 x[2][2];
+          float p1[2], p2[2];
+          float4 x[2];
         };
-        auto load_q = [&](int kk, QData& dq) {
+        // step s = (token block mb, K-slice kk): the two row blocks 2kk, 2kk+1
+        auto load_q = [&](int s_, QData& dq) {
+          const int mb = s_ / C::NKS, kk = s_ % C::NKS;
+          const int t = mb * 16 + lr;
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const int t = (2 * half + mb) * 16 + lr;
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t q = qs[2 * kk + h];
+            dq.p1[h] = xq[t * XQSTR + (q & 255)];
+            dq.p2[h] = xq[t * XQSTR + ((q >> 8) & 255)];
+            dq.x[h] = lds4(xq, t * XQSTR + (q >> 16));
+          }
+        };
+        auto build_q = [&](const QData& dq) {
+          const float p0 = dq.p1[0] * dq.p2[0];
+          const float p1 = dq.p1[1] * dq.p2[1];
+          const float4 x0 = dq.x[0], x1 = dq.x[1];
+          const u32x4 aw = {pack_bf16(p0 * x0.x, p0 * x0.y), pack_bf16(p0 * x0.z, p0 * x0.w),
+                            pack_bf16(p1 * x1.x, p1 * x1.y), pack_bf16(p1 * x1.z, p1 * x1.w)};
+          return __builtin_bit_cast(bf16x8, aw);
+        };
+        constexpr int NQS = C::MB * C::NKS;
+        QData dq;
+        load_q(0, dq);
+        bf16x8 Acur = build_q(dq);
+        if (NQS > 1) load_q(NQS > 1 ? 1 : 0, dq);
+        f32x4 acc[NB];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const uint32_t q = qs[2 * kk + h];
-              dq.p1[mb][h] = xq[t * XQSTR + (q & 255)];
-              dq.p2[mb][h] = xq[t * XQSTR + ((q >> 8) & 255)];
-              dq.x[mb][h] = lds4(xq, t * XQSTR + (q >> 16));
+        for (int s_ = 0; s_ < NQS; ++s_) {
+          const int mb = s_ / C::NKS, kk = s_ % C::NKS;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                Acur, __builtin_bit_cast(bf16x8, Sb[kk][nb]), kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb], 0, 0, 0);
+          bf16x8 Anext = Acur;
+          if (s_ + 1 < NQS) Anext = build_q(dq);
+          if (s_ + 2 < NQS) load_q(s_ + 2 < NQS ? s_ + 2 : 0, dq);
+          if (kk == C::NKS - 1) {
+            // C layout: lane holds column nb*16 + lr of tokens 4g..4g+3.
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              const int col = nb * 16 + lr;
+              if (col <= DV) {
+                const u32x2 o = {pack_bf16(acc[nb][0], acc[nb][1]), pack_bf16(acc[nb][2], acc[nb][3])};
+                *reinterpret_cast<u32x2*>(__builtin_assume_aligned(
+                    &red[(w * (DV + 1) + col) * RSTR + mb * 16 + 4 * g], 8)) = o;
+              }
             }
           }
-        };
-        auto build_q = [&](const QData& dq, bf16x8 (&A)[2]) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const float p0 = dq.p1[mb][0] * dq.p2[mb][0];
-            const float p1 = dq.p1[mb][1] * dq.p2[mb][1];
-            const float4 x0 = dq.x[mb][0], x1 = dq.x[mb][1];
-            const u32x4 aw = {pack_bf16(p0 * x0.x, p0 * x0.y), pack_bf16(p0 * x0.z, p0 * x0.w),
-                              pack_bf16(p1 * x1.x, p1 * x1.y), pack_bf16(p1 * x1.z, p1 * x1.w)};
-            A[mb] = __builtin_bit_cast(bf16x8, aw);
-          }
-        };
-        QData dq0, dq1;
-        bf16x8 Acur[2], Anext[2];
-        load_q(0, dq0);
-        build_q(dq0, Acur);
-        if (C::NKS > 1) load_q(C::NKS > 1 ? 1 : 0, dq0);
-        if (C::NKS > 2) load_q(C::NKS > 2 ? 2 : 0, dq1);
-#pragma unroll
-        for (int kk = 0; kk < C::NKS; ++kk) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const bf16x8 Bop = __builtin_bit_cast(bf16x8, Sb[kk][nb]);
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  Acur[mb], Bop, kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb], 0, 0, 0);
-          }
-          if (kk + 1 < C::NKS) build_q(dq0, Anext);
-          if (kk + 3 < C::NKS) load_q(kk + 3 < C::NKS ? kk + 3 : 0, dq0);
           __builtin_amdgcn_sched_barrier(0);
-          if (kk + 1 < C::NKS) {
-            Acur[0] = Anext[0];
-            Acur[1] = Anext[1];
-            const QData tq = dq0;
-            dq0 = dq1;
-            dq1 = tq;
-          }
+          Acur = Anext;
         }
-        // C layout: lane holds column nb*16 + lr of tokens 4g..4g+3.
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const int col = nb * 16 + lr;
-            if (col <= DV)
-              *reinterpret_cast<f32x4*>(__builtin_assume_aligned(
-                  &red[(w * (DV + 1) + col) * RSTR + (2 * half + mb) * 16 + 4 * g], 16)) = acc[mb][nb];
-          }
       }
 
       // ---- phase C: state update S += phi_k(K)^T [V 1] --------------------
@@ -1039,34 +1038,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan_bf16(ScanArgs a) 
             Bv[nb] = *reinterpret_cast<const bf16x8*>(
                 __builtin_assume_aligned(&vt[(nb * 16 + lr) * VSTR + 32 * kst + 8 * g], 16));
         };
-        bf16x8 Bv[NB], Bvn[NB];
-        load_v(0, Bv);
-        KData d0, d1;
-        load_k(0, d0);
-        bf16x8 Acur = build_k(d0);
-        if (NST > 1) load_k(NST > 1 ? 1 : 0, d0);
-        if (NST > 2) load_k(NST > 2 ? 2 : 0, d1);
+        bf16x8 Bv[NB];
+        KData dk;
+        load_k(0, dk);
+        bf16x8 Acur = build_k(dk);
+        if (NST > 1) load_k(NST > 1 ? 1 : 0, dk);
 #pragma unroll
         for (int st_ = 0; st_ < NST; ++st_) {
           const int kst = st_ / RB, b = st_ % RB;
+          if (b == 0) load_v(kst, Bv);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
             S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur, Bv[nb], S[b][nb], 0, 0, 0);
           bf16x8 Anext = Acur;
-          if (st_ + 1 < NST) Anext = build_k(d0);
-          if (st_ + 3 < NST) load_k(st_ + 3 < NST ? st_ + 3 : 0, d0);
-          if (b == RB - 2 && kst + 1 < L / 32) load_v(kst + 1 < L / 32 ? kst + 1 : 0, Bvn);
+          if (st_ + 1 < NST) Anext = build_k(dk);
+          if (st_ + 2 < NST) load_k(st_ + 2 < NST ? st_ + 2 : 0, dk);
           __builtin_amdgcn_sched_barrier(0);
           Acur = Anext;
-          {
-            const KData t2 = d0;
-            d0 = d1;
-            d1 = t2;
-          }
-          if (b == RB - 1 && kst + 1 < L / 32) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) Bv[nb] = Bvn[nb];
-          }
         }
       }
       __syncthreads();
@@ -1302,7 +1290,7 @@ template <int D, bool BF16>
 hipError_t launch_scan_t(int BH, const ScanArgs& a, hipStream_t s) {
   dim3 grid(a.lay.n_tiles, BH);
   if constexpr (BF16)
-    prefill_scan_bf16<D><<<grid, kWaves * 64, 0, s>>>(a);
+    prefill_scan_bf16<D><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
   else
     prefill_scan<D, BF16><<<grid, kWaves * 64, 0, s>>>(a);
   return hipGetLastError();
