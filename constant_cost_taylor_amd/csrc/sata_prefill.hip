@@ -827,9 +827,28 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_bf16
   float* carryh = a.ws.carry + static_cast<int64_t>(head) * ((nwp + C::T - 1) / C::T) * DVP;
 
   // Cross-wave sum of one chunk's readout (bf16 partials in LDS, summed in
-  // fp32 in a fixed order) into its records, 8 tokens per item.
+  // fp32 in a fixed order) into its records: value columns 8 tokens per item
+  // (one item per thread at d = 64), the z column one token per item.  The
+  // bf16 halves are accumulated with dot2 against (1, 0) / (0, 1).
   auto red_sum = [&](int ch) {
-    for (int e = tid; e < (DV + 1) * (L / 8); e += NW * 64) {
+    // Selectors as explicit bf16 pairs in registers (no reliance on how an
+    // inline constant is read for packed bf16 operands).
+    uint32_t lo_bits = 0x00003f80u, hi_bits = 0x3f800000u;
+    asm volatile("" : "+v"(lo_bits), "+v"(hi_bits));
+    const bf16x2 sel_lo = __builtin_bit_cast(bf16x2, lo_bits);
+    const bf16x2 sel_hi = __builtin_bit_cast(bf16x2, hi_bits);
+    if ((tid & 7) == 0 && (tid >> 3) < L) {
+      const int t = tid >> 3;
+      float sz = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) sz += __uint_as_float(static_cast<uint32_t>(red[(ww * (DV + 1) + DV) * RSTR + t]) << 16);
+      const int64_t off = static_cast<int64_t>(DV) * nwp + ch * L + t;
+      if constexpr (C::RECB)
+        rech[off] = static_cast<uint16_t>(pack_bf16(sz, 0.f) & 0xffffu);
+      else
+        rech[off] = sz;
+    }
+    for (int e = tid; e < DV * (L / 8); e += NW * 64) {
       const int c = e / (L / 8);
       const int tg = e % (L / 8);
       float sum[8];
@@ -840,8 +859,10 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_bf16
         const u32x4 x = *reinterpret_cast<const u32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 8 * tg]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          sum[2 * j] += bf16_lo(x[j]);
-          sum[2 * j + 1] += bf16_hi(x[j]);
+          const uint32_t xj = x[j];   // scalar copy: bit_cast of a vector element is miscompiled
+          const bf16x2 xx = __builtin_bit_cast(bf16x2, xj);
+          sum[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(xx, sel_lo, sum[2 * j], false);
+          sum[2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(xx, sel_hi, sum[2 * j + 1], false);
         }
       }
       const int64_t off = static_cast<int64_t>(c) * nwp + ch * L + 8 * tg;
@@ -877,8 +898,9 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_bf16
 #pragma unroll
       for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(ks[b]), "+v"(qs[b]));
 
-      // ---- phase A: previous chunk's records, then stage this chunk ------
-      if (ch > 0) red_sum(ch - 1);
+      // ---- phase A: stage this chunk, then the previous chunk's records ---
+      // (staging first: its wait for the prefetched loads must not also wait
+      // for the record stores)
       if constexpr (EPT >= 4) {
 #pragma unroll
         for (int e = 0; e < EPT; e += 4) {
@@ -909,6 +931,7 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_bf16
           vt[(st_i + e) * VSTR + st_t] = 0;
         }
       }
+      if (ch > 0) red_sum(ch - 1);
       if (ch + 1 < nch) {
         const bool ok = st_t < min(L, a.nw - (ch + 1) * L);
         const int64_t tn = tb + L + (ok ? st_t : 0);
