@@ -29,7 +29,7 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
 METRIC = "causal SATA tokens/sec/head (prefill, decode) + % of HBM/MFMA roofline"
 # HBM bytes moved by one decode_update_readout launch of this workload, from the
 # FETCH_SIZE / WRITE_SIZE counters scaled by a 1 GiB copy
-# (profiles/decode_update_readout_c4_hbm_traffic.txt).  Re-measure after any
+# (profiles/decode_update_readout_256x4096_d64_hbm_traffic.txt).  Re-measure after any
 # change to the decode kernel.
 DECODE_TRAFFIC_BYTES = 6.4497e9
 
@@ -92,12 +92,12 @@ def flatness(args):
     import torch
     import constant_cost_taylor_amd as sa
     import workloads as W
-    w = W.WORKLOADS["c5_long"]
+    w = W.WORKLOADS["long_d32_n1m"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     basis = sa.build_basis(w.d_k, w.P, w.c)
     g = torch.Generator(device=dev)
-    g.manual_seed(1000 * w.cfg)
+    g.manual_seed(1000 * w.seed)
     rows = []
     for lg in (16, 18, 20):
         n = 1 << lg
@@ -150,7 +150,7 @@ def main():
     import workloads as W
     from oracle import sata_oracle as O
 
-    w = W.WORKLOADS["c4_decode"]
+    w = W.WORKLOADS["decode_256x4096_d64"]
     S = w.B * w.H
     dsteps = args.decode_steps
     q, k, v = W.workload_inputs(w)

@@ -105,7 +105,7 @@ def test_decode_steps_from_empty_state(d, P, dtype, steps):
 
 CASES = [
     # name, B, H, n, d, P, c, dtype
-    ("c1_full", 1, 1, 256, 8, 3, 1.0, W.F32),
+    ("tiny_full", 1, 1, 256, 8, 3, 1.0, W.F32),
     ("d8_P1", 1, 2, 100, 8, 1, 1.0, W.F32),
     ("d8_P2_c2", 2, 1, 77, 8, 2, 2.0, W.F32),
     ("d16_ragged", 1, 3, 1000, 16, 4, 1.0, W.F32),
@@ -272,8 +272,8 @@ def test_workspace_too_small_changes_nothing():
 # The study's workloads at full size (sampled rows where the oracle is O(n) per row)
 # ----------------------------------------------------------------------------
 
-def test_workload_c2_full():
-    w = W.WORKLOADS["c2_d16"]
+def test_workload_d16_n4096_full():
+    w = W.WORKLOADS["d16_n4096"]
     note(f"workload {w.name} B={w.B} H={w.H} n={w.n}")
     q, k, v = W.workload_inputs(w)
     b = SA.build_basis(w.d_k, w.P, w.c)
@@ -289,8 +289,8 @@ def test_workload_c2_full():
             assert O.row_normwise_error(g, ref) <= TOL[w.dtype], (bb, h)
 
 
-def test_workload_c3_sampled():
-    w = W.WORKLOADS["c3_d64"]
+def test_workload_d64_n16384_sampled():
+    w = W.WORKLOADS["d64_n16384"]
     note(f"workload {w.name} B={w.B} H={w.H} n={w.n}")
     q, k, v = W.workload_inputs(w)
     b = SA.build_basis(w.d_k, w.P, w.c)
@@ -302,10 +302,10 @@ def test_workload_c3_sampled():
         assert O.row_normwise_error(got[0, h][rows], ref) <= TOL[w.dtype], h
 
 
-def test_workload_c4_decode():
+def test_workload_decode_256x4096_d64():
     """256 resident states: 4096-token prefill, then decode steps; every
     decode output and sampled prefill rows of 8 states are checked."""
-    w = W.WORKLOADS["c4_decode"]
+    w = W.WORKLOADS["decode_256x4096_d64"]
     steps = 16
     note(f"workload {w.name} states={w.B * w.H} n={w.n} steps={steps}")
     q, k, v = W.workload_inputs(w)
@@ -335,8 +335,8 @@ def test_workload_c4_decode():
         assert O.row_normwise_error(got_d[:, s], ref) <= TOL[w.dtype], ("decode", s)
 
 
-def test_workload_c5_sampled():
-    w = W.WORKLOADS["c5_long"]
+def test_workload_long_d32_n1m_sampled():
+    w = W.WORKLOADS["long_d32_n1m"]
     note(f"workload {w.name} H={w.H} n={w.n}")
     rows = W.sampled_rows(w.n)
     b = SA.build_basis(w.d_k, w.P, w.c)

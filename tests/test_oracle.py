@@ -296,7 +296,7 @@ def test_softmax_stable_matches_naive():
 
 
 def test_truncation_error_bound_and_decrease():
-    w = W.WORKLOADS["c1_tiny"]
+    w = W.WORKLOADS["tiny_d8_n256"]
     q, k, v = (a[0, 0].astype(np.float64) for a in W.workload_inputs(w))
     sm = O.exact_softmax(q, k, v)
     errs = []
@@ -345,7 +345,7 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_inputs_recipe():
-    w = W.WORKLOADS["c1_tiny"]
+    w = W.WORKLOADS["tiny_d8_n256"]
     q, k, v = W.workload_inputs(w)
     assert q.shape == (1, 1, 256, 8) and v.shape == (1, 1, 256, 8)
     np.testing.assert_allclose(np.linalg.norm(q.astype(np.float64), axis=-1), 1.0, rtol=1e-6)

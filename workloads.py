@@ -6,7 +6,7 @@ workload's dtype and names the workload shapes.  The HIP path and the CPU
 oracle both consume exactly the arrays produced here.
 
 Recipe (the same for every workload):
-  * ``numpy.random.Generator(PCG64(seed))`` with seed = 1000*cfg + {q: 1, k: 2, v: 3};
+  * ``numpy.random.Generator(PCG64(s))`` with s = 1000 * (workload seed) + {q: 1, k: 2, v: 3};
     draws are taken in C order over ``[B, H, n, d]``.
   * q and k rows are i.i.d. N(0, 1) in float64, scaled to unit L2 norm;
     v is i.i.d. N(0, 1).
@@ -27,7 +27,7 @@ BF16 = "bf16"
 class Workload:
     """One named workload: shapes, order count P, logit scale c and input dtype."""
     name: str
-    cfg: int          # seed family (1..5)
+    seed: int         # seed family (1..5): seeds derive from 1000 * seed
     B: int
     H: int
     n: int
@@ -42,12 +42,12 @@ class Workload:
 # 4x8 heads n=4096 d=16 P=4 fp32, 1x4 heads n=16384 d=64 P=4 bf16, the decode
 # workload with 256 resident d=64 states, and 16 heads of d=32 at n=2^20).
 WORKLOADS = {
-    "c1_tiny": Workload("c1_tiny", 1, 1, 1, 256, 8, 8, 3, 1.0, F32),
-    "c2_d16": Workload("c2_d16", 2, 4, 8, 4096, 16, 16, 4, 1.0, F32),
-    "c3_d64": Workload("c3_d64", 3, 1, 4, 16384, 64, 64, 4, 1.0, BF16),
+    "tiny_d8_n256": Workload("tiny_d8_n256", 1, 1, 1, 256, 8, 8, 3, 1.0, F32),
+    "d16_n4096": Workload("d16_n4096", 2, 4, 8, 4096, 16, 16, 4, 1.0, F32),
+    "d64_n16384": Workload("d64_n16384", 3, 1, 4, 16384, 64, 64, 4, 1.0, BF16),
     # decode: 8 x 32 = 256 states, 4096-token prefill then 1024 single-token steps
-    "c4_decode": Workload("c4_decode", 4, 8, 32, 4096, 64, 64, 4, 1.0, BF16),
-    "c5_long": Workload("c5_long", 5, 1, 16, 1 << 20, 32, 32, 4, 1.0, BF16),
+    "decode_256x4096_d64": Workload("decode_256x4096_d64", 4, 8, 32, 4096, 64, 64, 4, 1.0, BF16),
+    "long_d32_n1m": Workload("long_d32_n1m", 5, 1, 16, 1 << 20, 32, 32, 4, 1.0, BF16),
 }
 DECODE_STEPS = 1024
 
@@ -102,20 +102,20 @@ def make_qkv(B: int, H: int, n: int, d_k: int, d_v: int, dtype: str, seed_base: 
 def workload_inputs(w: Workload, n: int | None = None):
     """Inputs of a workload (optionally a shorter prefix length n, same seeds)."""
     nn = w.n if n is None else n
-    return make_qkv(w.B, w.H, nn, w.d_k, w.d_v, w.dtype, 1000 * w.cfg)
+    return make_qkv(w.B, w.H, nn, w.d_k, w.d_v, w.dtype, 1000 * w.seed)
 
 
 def head_inputs(w: Workload, h: int, n: int | None = None):
     """Per-head inputs for the long-context workload (seed + 10*h), shape [n, d]."""
     nn = w.n if n is None else n
-    q, k, v = make_qkv(1, 1, nn, w.d_k, w.d_v, w.dtype, 1000 * w.cfg + 10 * h)
+    q, k, v = make_qkv(1, 1, nn, w.d_k, w.d_v, w.dtype, 1000 * w.seed + 10 * h)
     return q[0, 0], k[0, 0], v[0, 0]
 
 
 def decode_inputs(w: Workload, steps: int = DECODE_STEPS):
     """Per-step decode inputs [steps, S, d] with S = B*H states (seed + 100)."""
     S = w.B * w.H
-    q, k, v = make_qkv(1, steps, S, w.d_k, w.d_v, w.dtype, 1000 * w.cfg + 100)
+    q, k, v = make_qkv(1, steps, S, w.d_k, w.d_v, w.dtype, 1000 * w.seed + 100)
     return q[0], k[0], v[0]
 
 
