@@ -139,33 +139,55 @@ __global__ __launch_bounds__(kThreads) void decode_update_readout(DecodeArgs a) 
   }
 }
 
-// One block per state: groups of DVP threads sum interleaved tiles, then the
-// groups are combined in a fixed order and num / den is written.
+// One block per state: groups of DVP/4 threads sum interleaved tiles with
+// float4 loads (four loads in flight per thread), then the groups are combined
+// in a fixed order and num / den is written.
 template <int DV>
 __global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
   constexpr int DVP = padded_dv(DV);
-  constexpr int G = kThreads / DVP;
-  __shared__ float red[G * DVP];
+  constexpr int Q = DVP / 4;            // float4 columns per tile record
+  constexpr int G = kThreads / Q;       // tile groups
+  __shared__ float4 red[G * Q];
+  __shared__ float tot[DVP];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
-  const int grp = tid / DVP;
-  const int c = tid % DVP;
-  const float* part = a.part + static_cast<int64_t>(s) * a.n_tiles * DVP;
+  const int grp = tid / Q;
+  const int c = tid % Q;
+  const float4* part = reinterpret_cast<const float4*>(a.part + static_cast<int64_t>(s) * a.n_tiles * DVP);
   if (grp < G) {
-    float acc = 0.f;
-    for (int t = grp; t < a.n_tiles; t += G) acc += part[static_cast<int64_t>(t) * DVP + c];
-    red[grp * DVP + c] = acc;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int t = grp;
+    for (; t + 3 * G < a.n_tiles; t += 4 * G) {
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = part[static_cast<int64_t>(t + u * G) * Q + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc.x += x[u].x;
+        acc.y += x[u].y;
+        acc.z += x[u].z;
+        acc.w += x[u].w;
+      }
+    }
+    for (; t < a.n_tiles; t += G) {
+      const float4 x = part[static_cast<int64_t>(t) * Q + c];
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    red[grp * Q + c] = acc;
   }
   __syncthreads();
-  if (tid < DV) {
-    float num = 0.f, den = 0.f;
+  if (tid < DVP) {
+    const float* redf = reinterpret_cast<const float*>(red);
+    float sum = 0.f;
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      num += red[gg * DVP + tid];
-      den += red[gg * DVP + DV];
-    }
-    a.out[static_cast<int64_t>(s) * DV + tid] = num / den;
+    for (int gg = 0; gg < G; ++gg) sum += redf[gg * DVP + tid];
+    tot[tid] = sum;
   }
+  __syncthreads();
+  if (tid < DV) a.out[static_cast<int64_t>(s) * DV + tid] = tot[tid] / tot[DV];
 }
 
 template <int D>
