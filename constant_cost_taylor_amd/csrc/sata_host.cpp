@@ -370,6 +370,7 @@ struct PrefillPlan {
   size_t rec_bytes = 0;   // per-tile records
   size_t intra_bytes = 0;
   size_t carry_bytes = 0;
+  size_t amax_bytes = 0;
   size_t total = 0;
 };
 
@@ -391,8 +392,9 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
   pl.rec_bytes = static_cast<size_t>(BH) * nt * dvp * pl.nwp * rec_elt;
   pl.intra_bytes = static_cast<size_t>(BH) * dvp * pl.nwp * 4;
   pl.carry_bytes = static_cast<size_t>(BH) * ((pl.nwp + T - 1) / T) * dvp * 4;
+  pl.amax_bytes = bf16 ? static_cast<size_t>(BH) * sata::kAmaxSplit * 4 * 4 : 0;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  pl.total = up(pl.rec_bytes) + up(pl.intra_bytes) + up(pl.carry_bytes);
+  pl.total = up(pl.rec_bytes) + up(pl.intra_bytes) + up(pl.carry_bytes) + up(pl.amax_bytes);
   return pl;
 }
 
@@ -561,9 +563,10 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
   const int64_t stride = sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   char* base = static_cast<char*>(ws);
-  sata::PrefillWs pw{base, reinterpret_cast<float*>(base + up(pl.rec_bytes)),
-                     reinterpret_cast<float*>(base + up(pl.rec_bytes) + up(pl.intra_bytes)),
-                     static_cast<int>(pl.nwp)};
+  const size_t off_intra = up(pl.rec_bytes), off_carry = off_intra + up(pl.intra_bytes);
+  const size_t off_amax = off_carry + up(pl.carry_bytes);
+  sata::PrefillWs pw{base, reinterpret_cast<float*>(base + off_intra), reinterpret_cast<float*>(base + off_carry),
+                     pl.amax_bytes ? reinterpret_cast<float*>(base + off_amax) : nullptr, static_cast<int>(pl.nwp)};
   const float inv_c = static_cast<float>(1.0 / b->c);
   for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
     const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
@@ -573,7 +576,7 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
     sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c};
     if (sata::launch_prefill_scan(b->d, bf16, static_cast<int>(BH), sa, s) != hipSuccess)
       return SATA_ERR_HIP;
-    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles};
+    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c};
     if (sata::launch_prefill_reduce(b->d, bf16, static_cast<int>(BH), ra, s) != hipSuccess)
       return SATA_ERR_HIP;
   }

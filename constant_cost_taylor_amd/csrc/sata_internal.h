@@ -90,14 +90,19 @@ struct PrefillLayout {
   int32_t* nslot = nullptr;
 };
 
+// Token slices of the max-abs pre-pass of the bf16 prefill (per head).
+constexpr int kAmaxSplit = 32;
+
 // Prefill workspace of one window of nw tokens (nwp = nw rounded up to 64):
 //   rec:   [BH][n_tiles][DVP][nwp]  per-tile readout records (bf16 or fp32)
 //   intra: [BH][DVP][nwp]           intra-window records (fp32)
 //   carry: [BH][nrwin][DVP]         order-0 prefix at each readout window start (fp32)
+//   amax:  [BH][kAmaxSplit][4]      max |q|, |k|, |v| per token slice (bf16 inputs)
 struct PrefillWs {
   void* rec;
   float* intra;
   float* carry;
+  float* amax;
   int nwp;
 };
 
@@ -135,6 +140,7 @@ struct ReduceArgs {
   int64_t t0;
   int nw;
   int n_tiles;
+  float inv_c;           // 1 / c (selects the bf16 scan's operand type)
 };
 
 struct DecodeArgs {

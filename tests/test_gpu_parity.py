@@ -244,6 +244,53 @@ def test_misaligned_and_host_only_rejected():
     assert float(st.abs().sum()) == 0.0 and float(out.abs().sum()) == 0.0
 
 
+def _rows_bf16(x):
+    return W.round_bf16(np.asarray(x, dtype=np.float64)).astype(np.float32)
+
+
+@pytest.mark.parametrize("d", [32, 64])
+def test_prefill_bf16_scaled_inputs(d):
+    """bf16 inputs far from unit scale (v x 3000, k x 1/64, q x 64: the logits
+    are unchanged) exercise the per-head power-of-two operand scaling."""
+    note(f"scaled bf16 inputs d={d}")
+    n = 600
+    q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 16000 + d)
+    q, k, v = _rows_bf16(q * 64.0), _rows_bf16(k / 64.0), _rows_bf16(v * 3000.0)
+    b = SA.build_basis(d, 4, 1.0)
+    out, st = run_prefill(b, q, k, v, W.BF16)
+    got = out.cpu().numpy()
+    for h in range(2):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], 4, 1.0)
+        assert O.row_normwise_error(got[0, h], ref) <= TOL[W.BF16], h
+    # the state written back is the canonical one
+    basis = O.enumerate_basis(d, 4)
+    D = b.total_rows
+    S, z = O.direct_state(f64(k[0, 1]), f64(v[0, 1]), basis)
+    gS = st.cpu().numpy()[1, :D * d].reshape(D, d)
+    assert np.max(np.abs(gS - S)) <= TOL[W.BF16] * np.max(np.abs(S))
+
+
+@pytest.mark.parametrize("d", [32, 64])
+def test_prefill_bf16_large_query_coordinates(d):
+    """A query coordinate far larger than the keys' scale (first coordinate of
+    q = 12, first coordinate of k ~ 1e-3) with moderate logits: outside the
+    range of the f16 operand path, so the bf16 operand path runs."""
+    note(f"large query coordinates d={d}")
+    n = 500
+    q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 17000 + d)
+    q = q.copy()
+    k = k.copy()
+    q[..., 0] = 12.0
+    k[..., 0] *= 1e-2
+    q, k, v = _rows_bf16(q), _rows_bf16(k), _rows_bf16(v)
+    b = SA.build_basis(d, 4, 1.0)
+    out, _ = run_prefill(b, q, k, v, W.BF16)
+    got = out.cpu().numpy()
+    for h in range(2):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], 4, 1.0)
+        assert O.row_normwise_error(got[0, h], ref) <= TOL[W.BF16], h
+
+
 def test_prefill_deterministic():
     note("prefill run-twice bitwise")
     d, P, dtype = 32, 4, W.BF16
