@@ -1177,6 +1177,11 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
       }
       __syncthreads();
 
+      // ---- phase C: readout and update, in opposite orders on the two waves
+      // that share a SIMD (waves w and w + NW/2), so one wave's LDS- and
+      // VALU-heavy readout overlaps the other's MFMA-heavy update.  Both read
+      // only this chunk's tables and the window-start readout operand.
+      auto readout = [&]() {
       // ---- phase C: readout against the state at the window start --------
       // (one 16-token block at a time) into the bf16 reduction buffer.
       {
@@ -1248,7 +1253,8 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
           Acur = Anext;
         }
       }
-
+      };
+      auto update = [&]() {
       // ---- phase C: state update S += phi_k(K)^T [V 1] --------------------
       {
         constexpr int NST = (L / 32) * RB;
@@ -1303,6 +1309,14 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
           __builtin_amdgcn_sched_barrier(0);
           Acur = Anext;
         }
+      }
+      };
+      if (w < NW / 2) {
+        readout();
+        update();
+      } else {
+        update();
+        readout();
       }
       __syncthreads();
     }
