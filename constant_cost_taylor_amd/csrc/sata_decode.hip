@@ -13,7 +13,10 @@
 // with the row weight), then streams its slice of S as float4 rows (d_v/4
 // threads per row), fusing the rank-1 update with the readout partial sums,
 // then streams z.  Per-tile partial sums go to the workspace and a second
-// kernel reduces them in a fixed order and divides.
+// kernel reduces them in a fixed order and divides.  The state is touched once
+// per step and is far larger than the caches, so its loads and stores carry
+// the non-temporal hint (measured: about 7 % more read-modify-write bandwidth
+// than plain loads and stores on gfx950).
 #include <hip/hip_runtime.h>
 
 #include "sata_internal.h"
@@ -26,7 +29,10 @@ __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
 
-__device__ __forceinline__ float4 fma4(float s, float4 v, float4 acc) {
+// Four floats as a clang vector (the non-temporal builtins take vector types).
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4v fma4(float s, f4v v, f4v acc) {
   acc.x = fmaf(s, v.x, acc.x);
   acc.y = fmaf(s, v.y, acc.y);
   acc.z = fmaf(s, v.z, acc.z);
@@ -83,28 +89,28 @@ __global__ __launch_bounds__(kThreads) void decode_update_readout(DecodeArgs a) 
   __syncthreads();
 
   float* st = a.state + static_cast<int64_t>(s) * a.stride;
-  float4* S4 = reinterpret_cast<float4*>(st + static_cast<int64_t>(r0) * DV);
+  f4v* S4 = reinterpret_cast<f4v*>(st + static_cast<int64_t>(r0) * DV);
   const int c4 = tid % TPR;
   const int rs = tid / TPR;
-  const float4 vv = make_float4(xv[4 * c4], xv[4 * c4 + 1], xv[4 * c4 + 2], xv[4 * c4 + 3]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const f4v vv = {xv[4 * c4], xv[4 * c4 + 1], xv[4 * c4 + 2], xv[4 * c4 + 3]};
+  f4v acc = {0.f, 0.f, 0.f, 0.f};
 
   int r = rs;
   for (; r + (U - 1) * RPP < nrows; r += U * RPP) {
-    float4 x[U];
+    f4v x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = S4[static_cast<int64_t>(r + u * RPP) * TPR + c4];
+    for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(&S4[static_cast<int64_t>(r + u * RPP) * TPR + c4]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       x[u] = fma4(fk[r + u * RPP], vv, x[u]);
-      S4[static_cast<int64_t>(r + u * RPP) * TPR + c4] = x[u];
+      __builtin_nontemporal_store(x[u], &S4[static_cast<int64_t>(r + u * RPP) * TPR + c4]);
       acc = fma4(fq[r + u * RPP], x[u], acc);
     }
   }
   for (; r < nrows; r += RPP) {
-    float4 x = S4[static_cast<int64_t>(r) * TPR + c4];
+    f4v x = __builtin_nontemporal_load(&S4[static_cast<int64_t>(r) * TPR + c4]);
     x = fma4(fk[r], vv, x);
-    S4[static_cast<int64_t>(r) * TPR + c4] = x;
+    __builtin_nontemporal_store(x, &S4[static_cast<int64_t>(r) * TPR + c4]);
     acc = fma4(fq[r], x, acc);
   }
 
@@ -112,8 +118,8 @@ __global__ __launch_bounds__(kThreads) void decode_update_readout(DecodeArgs a) 
   float* z = st + static_cast<int64_t>(a.D) * DV + r0;
   float dacc = 0.f;
   for (int rr = tid; rr < nrows; rr += kThreads) {
-    const float zz = z[rr] + fk[rr];
-    z[rr] = zz;
+    const float zz = __builtin_nontemporal_load(&z[rr]) + fk[rr];
+    __builtin_nontemporal_store(zz, &z[rr]);
     dacc = fmaf(fq[rr], zz, dacc);
   }
 
