@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsata.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["sata_host.cpp", "sata_decode.hip", "sata_prefill.hip"]
+SOURCES = ["sata_host.cpp", "sata_decode.hip", "sata_prefill.hip", "sata_prefill_b16.hip"]
 
 # Packed fp32 instructions are disabled for every HIP compile.
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -101,10 +101,12 @@ struct Run {
 };
 
 // Runs of four children (P, c0..c0+3) over every parent of order 0..P-2, in
-// canonical row order.  A child whose index already occurs twice in the
-// parent (the (i, i, i) rows) gets a run of its own, fed by a parent slot
-// whose key feature carries the 1/3, so only the k and k/2 tables are needed.
-std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32_t, int64_t>& rank) {
+// canonical row order.  With split_iii, a child whose index already occurs
+// twice in the parent (the (i, i, i) rows) gets a run of its own, fed by a
+// parent slot whose key feature carries the 1/3, so only the k and k/2 tables
+// are needed (float32 encoding); otherwise it stays in its parent's run.
+std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32_t, int64_t>& rank,
+                            bool split_iii) {
   std::vector<Run> runs;
   for (int p = 1; p < b.P; ++p) {
     const int pp = p - 1;
@@ -143,7 +145,7 @@ std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32
           if (c < lo) continue;
           int cnt = 0;
           const int64_t row = child_row(c, &cnt);
-          if (cnt > 2) continue;   // handled by its own run below
+          if (cnt > 2 && split_iii) continue;   // handled by its own run below
           run.row[j] = row;
           run.code[j] = cnt;
           run.cnt[j] = cnt;
@@ -153,7 +155,7 @@ std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32
       }
       // The child equal to a twice-repeated last index: k^3/3 = (k^2/3) * k.
       int cnt = 0;
-      if (pp >= 2) {
+      if (pp >= 2 && split_iii) {
         const int64_t row = child_row(lo, &cnt);
         if (cnt > 2) {
           Run run;
@@ -182,12 +184,11 @@ std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32
 //  * float32 inputs: parent slots for every parent; key side reads a parent
 //    table and a separate key table; the query side reads a per-slot table
 //    and the scan keeps rows divided by the multiplicity of their last index.
-//  * bfloat16 inputs: one key-side table (key rows, halved key rows, a zero
-//    row, a ones row, then slots for order-2 parents only, which carry the
-//    parent's 1/prod(count!) and the 1/3 of the (i, i, i) rows); the query
-//    side is the plain monomial prod(q/c), built from two query coordinates
-//    (index d = the constant 1) and the run's four children; the scan keeps
-//    row m divided by prod(count!) of m.
+//  * bfloat16 inputs: one key table (d key rows, a zero row, a ones row, then
+//    one slot row per order-2 parent of the tile); key and query features
+//    are plain monomials (the query side from two coordinates, index d = the
+//    constant 1, and the run's four children) and the row weights w_m are
+//    applied to the state when the scan rounds it to its readout operand.
 int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& rank, bool bf16,
                  bool upload_tables, PrefillLayout* lay) {
   const int rb = sata::prefill_rb(b->d, bf16);
@@ -196,9 +197,9 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
   const int kstr = sata::prefill_kstride(bf16);
   const int xk_zero = 2 * b->d * kstr;
   const bool v2 = bf16;
-  const int row_zero = 2 * b->d, row_ones = 2 * b->d + 1, row_slot = 2 * b->d + 2;
+  const int row_zero = b->d, row_ones = b->d + 1, row_slot = b->d + 2;
   lay->rb = rb;
-  const std::vector<Run> runs = build_runs(*b, rank);
+  const std::vector<Run> runs = build_runs(*b, rank, !bf16);
   auto parent_order = [](uint32_t key) { return static_cast<int>((key >> 24) & 0x7f); };
   auto needs_slot = [&](const Run& r) { return !v2 || parent_order(r.parent_key) >= 2; };
   // Greedy tiling in canonical order: a tile takes runs until it is full or
@@ -230,6 +231,7 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
   std::vector<uint32_t> parents(static_cast<size_t>(n_tiles) * max_slots, 0);
   std::vector<float> pweight(static_cast<size_t>(n_tiles) * max_slots, 0.f);
   std::vector<float> kscale(static_cast<size_t>(n_tiles) * max_slots, 0.f);
+  std::vector<float> rweight(v2 ? nblk * 16 : 0, 0.f);
   std::vector<int32_t> nslot(n_tiles, 0);
   for (int t = 0; t < n_tiles; ++t) {
     std::unordered_map<uint32_t, int> slot_of;
@@ -243,7 +245,7 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
         // the ones row / the constant query coordinate).
         for (int j = 0; j < 4; ++j)
           kside[blk * 16 + 4 * g + j] =
-              v2 ? static_cast<uint32_t>(row_ones * kstr) | (static_cast<uint32_t>(row_zero * kstr) << 16)
+              v2 ? static_cast<uint32_t>(row_ones) | (static_cast<uint32_t>(row_zero) << 16)
                  : static_cast<uint32_t>(xk_zero) << 16;
         qside[blk * 4 + g] = v2 ? static_cast<uint32_t>(b->d) | (static_cast<uint32_t>(b->d) << 8) : 0u;
         continue;
@@ -266,7 +268,6 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
             slot_of.emplace(run.parent_key, slot);
             const size_t si = static_cast<size_t>(t) * max_slots + slot;
             parents[si] = static_cast<uint32_t>(i1) | (static_cast<uint32_t>(i2) << 8);
-            kscale[si] = run.kscale * run.parent_weight;
           } else {
             slot = it->second;
           }
@@ -274,15 +275,12 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
         }
         qside[blk * 4 + g] = static_cast<uint32_t>(i1) | (static_cast<uint32_t>(i2) << 8) |
                              (static_cast<uint32_t>(run.c0) << 16);
-        const double cf = 1.0 / static_cast<double>(run.parent_weight);   // prod(count!) of the parent
         for (int j = 0; j < 4; ++j) {
-          const int code = run.code[j];
-          const int xrow = code == 0 ? row_zero : (code - 1) * b->d + run.c0 + j;
-          kside[blk * 16 + 4 * g + j] =
-              static_cast<uint32_t>(prow * kstr) | (static_cast<uint32_t>(xrow * kstr) << 16);
+          const int xrow = run.row[j] >= 0 ? run.c0 + j : row_zero;
+          kside[blk * 16 + 4 * g + j] = static_cast<uint32_t>(prow) | (static_cast<uint32_t>(xrow) << 16);
           if (run.row[j] >= 0) {
-            const uint32_t fac = static_cast<uint32_t>(std::lround(cf * run.cnt[j]));
-            rowinfo[blk * 16 + 4 * g + j] = static_cast<uint32_t>(run.row[j] + 1) | (fac << 28);
+            rowinfo[blk * 16 + 4 * g + j] = static_cast<uint32_t>(run.row[j] + 1);
+            rweight[blk * 16 + 4 * g + j] = b->weight[run.row[j]];
           }
         }
         continue;
@@ -324,6 +322,7 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
   if ((st = upload(b, parents, &lay->parents)) != SATA_OK) return st;
   if ((st = upload(b, pweight, &lay->pweight)) != SATA_OK) return st;
   if ((st = upload(b, kscale, &lay->kscale)) != SATA_OK) return st;
+  if ((st = upload(b, rweight, &lay->rweight)) != SATA_OK) return st;
   if ((st = upload(b, nslot, &lay->nslot)) != SATA_OK) return st;
   return SATA_OK;
 }
@@ -368,20 +367,26 @@ struct PrefillPlan {
   int64_t nw = 0;         // tokens per window
   int64_t nwp = 0;        // nw rounded up to 64
   size_t rec_bytes = 0;   // per-tile records
+  size_t recz_bytes = 0;  // per-tile den records (bfloat16 inputs)
   size_t intra_bytes = 0;
   size_t carry_bytes = 0;
   size_t amax_bytes = 0;
+  size_t stg_bytes = 0;   // staged 16-bit tables (bfloat16 inputs)
+  size_t vsum_bytes = 0;  // per-chunk sums of v (bfloat16 inputs)
   size_t total = 0;
 };
 
 PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) {
   const bool bf16 = dtype == SATA_BF16;
   const int nt = b->lay[dtype].n_tiles;
-  const int dvp = sata::padded_dv(b->d);
+  const int d = b->d;
+  const int dvp = sata::padded_dv(d);
   const int T = sata::prefill_window(bf16);
-  const size_t rec_elt = sata::prefill_bf16_records(b->d, bf16) ? 2 : 4;
-  // bytes per token of window (records + intra) and per chunk (carry)
-  const size_t per_token = static_cast<size_t>(BH) * dvp * (nt * rec_elt + 4);
+  const size_t rec_elt = sata::prefill_bf16_records(d, bf16) ? 2 : 4;
+  // bytes per token of window: records, intra, staged tables, chunk sums
+  const size_t per_token =
+      bf16 ? static_cast<size_t>(BH) * (nt * (d * rec_elt + 4) + dvp * 4 + 8 * d + dvp)
+           : static_cast<size_t>(BH) * dvp * (nt * rec_elt + 4);
   int64_t w = static_cast<int64_t>(prefill_ws_cap() / per_token);
   // windows start on readout-window boundaries
   w = std::max<int64_t>(T, (w / T) * T);
@@ -389,12 +394,16 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
   PrefillPlan pl;
   pl.nw = std::min(w, nround);
   pl.nwp = (pl.nw + 63) / 64 * 64;
-  pl.rec_bytes = static_cast<size_t>(BH) * nt * dvp * pl.nwp * rec_elt;
+  pl.rec_bytes = static_cast<size_t>(BH) * nt * (bf16 ? d : dvp) * pl.nwp * rec_elt;
+  pl.recz_bytes = bf16 ? static_cast<size_t>(BH) * nt * pl.nwp * 4 : 0;
   pl.intra_bytes = static_cast<size_t>(BH) * dvp * pl.nwp * 4;
   pl.carry_bytes = static_cast<size_t>(BH) * ((pl.nwp + T - 1) / T) * dvp * 4;
   pl.amax_bytes = bf16 ? static_cast<size_t>(BH) * sata::kAmaxSplit * 4 * 4 : 0;
+  pl.stg_bytes = bf16 ? static_cast<size_t>(BH) * pl.nwp * 4 * d * 2 : 0;
+  pl.vsum_bytes = bf16 ? static_cast<size_t>(BH) * (pl.nwp / 64) * dvp * 4 : 0;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  pl.total = up(pl.rec_bytes) + up(pl.intra_bytes) + up(pl.carry_bytes) + up(pl.amax_bytes);
+  pl.total = up(pl.rec_bytes) + up(pl.recz_bytes) + up(pl.intra_bytes) + up(pl.carry_bytes) +
+             up(pl.amax_bytes) + up(pl.stg_bytes) + up(pl.vsum_bytes);
   return pl;
 }
 
@@ -563,22 +572,41 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
   const int64_t stride = sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   char* base = static_cast<char*>(ws);
-  const size_t off_intra = up(pl.rec_bytes), off_carry = off_intra + up(pl.intra_bytes);
-  const size_t off_amax = off_carry + up(pl.carry_bytes);
-  sata::PrefillWs pw{base, reinterpret_cast<float*>(base + off_intra), reinterpret_cast<float*>(base + off_carry),
-                     pl.amax_bytes ? reinterpret_cast<float*>(base + off_amax) : nullptr, static_cast<int>(pl.nwp)};
+  size_t off = 0;
+  auto carve = [&](size_t bytes) -> char* {
+    if (bytes == 0) return nullptr;
+    char* p = base + off;
+    off += up(bytes);
+    return p;
+  };
+  sata::PrefillWs pw{};
+  pw.rec = carve(pl.rec_bytes);
+  pw.intra = reinterpret_cast<float*>(carve(pl.intra_bytes));
+  pw.carry = reinterpret_cast<float*>(carve(pl.carry_bytes));
+  pw.amax = reinterpret_cast<float*>(carve(pl.amax_bytes));
+  pw.nwp = static_cast<int>(pl.nwp);
+  pw.recz = reinterpret_cast<float*>(carve(pl.recz_bytes));
+  pw.stg = reinterpret_cast<uint16_t*>(carve(pl.stg_bytes));
+  pw.vsum = reinterpret_cast<float*>(carve(pl.vsum_bytes));
   const float inv_c = static_cast<float>(1.0 / b->c);
   for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
     const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
     sata::IntraArgs ia{q, k, v, pw, n, t0, w, b->P, inv_c};
-    if (sata::launch_prefill_intra(b->d, bf16, static_cast<int>(BH), ia, s) != hipSuccess)
-      return SATA_ERR_HIP;
     sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c};
-    if (sata::launch_prefill_scan(b->d, bf16, static_cast<int>(BH), sa, s) != hipSuccess)
-      return SATA_ERR_HIP;
     sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c};
-    if (sata::launch_prefill_reduce(b->d, bf16, static_cast<int>(BH), ra, s) != hipSuccess)
-      return SATA_ERR_HIP;
+    if (bf16) {
+      if (sata::launch_prefill_b16(b->d, static_cast<int>(BH), sa, s) != hipSuccess) return SATA_ERR_HIP;
+      if (sata::launch_prefill_intra(b->d, true, static_cast<int>(BH), ia, s) != hipSuccess)
+        return SATA_ERR_HIP;
+      if (sata::launch_reduce_b16(b->d, static_cast<int>(BH), ra, s) != hipSuccess) return SATA_ERR_HIP;
+    } else {
+      if (sata::launch_prefill_intra(b->d, false, static_cast<int>(BH), ia, s) != hipSuccess)
+        return SATA_ERR_HIP;
+      if (sata::launch_prefill_scan(b->d, false, static_cast<int>(BH), sa, s) != hipSuccess)
+        return SATA_ERR_HIP;
+      if (sata::launch_prefill_reduce(b->d, false, static_cast<int>(BH), ra, s) != hipSuccess)
+        return SATA_ERR_HIP;
+    }
   }
   return SATA_OK;
 }

@@ -66,7 +66,8 @@ constexpr int padded_dv(int dv) { return (dv + 1 + 3) & ~3; }
 // Column blocks of 16 (value columns plus the z column).
 constexpr int col_blocks(int dv) { return (dv + 1 + 15) / 16; }
 
-// One internal tile layout of the prefill scan (device arrays).
+// One internal tile layout of the prefill scan (device arrays).  Two
+// encodings.  float32 inputs:
 //   kside[tile][wave][rb][16]: LDS offsets (floats) used by lane row j of a
 //       row block to build its key features: low 16 bits = parent row of the
 //       parent-feature table, high 16 bits = child row of the key table.
@@ -77,7 +78,15 @@ constexpr int col_blocks(int dv) { return (dv + 1 + 15) / 16; }
 //   pweight[tile][slot]: 1 / prod(count!) of that parent (query side);
 //   kscale[tile][slot]: factor of the key-side parent feature (1, or 1/3 for
 //       the slot that feeds the (i, i, i) rows).
-//   nslot[tile]: number of parent slots of the tile.
+// bfloat16 inputs (key table rows: d key rows, a zero row, a ones row, then
+// one row per order-2 parent slot):
+//   kside: key-table row of the parent feature (low 16 bits) and of the
+//       child coordinate (high 16 bits) of lane row j;
+//   qside: i1 | i2 << 8 | c0 << 16 of the run of lane group g (index d = the
+//       constant 1);
+//   rowinfo: canonical row + 1, 0 = pad;  rweight: w_m of the row, 0 = pad;
+//   parents[tile][slot]: i1 | i2 << 8 of each order-2 parent slot.
+// Both: nslot[tile] = number of parent slots of the tile.
 struct PrefillLayout {
   int rb = 0;
   int n_tiles = 0;
@@ -87,23 +96,36 @@ struct PrefillLayout {
   uint32_t* parents = nullptr;
   float* pweight = nullptr;
   float* kscale = nullptr;
+  float* rweight = nullptr;
   int32_t* nslot = nullptr;
 };
 
 // Token slices of the max-abs pre-pass of the bf16 prefill (per head).
 constexpr int kAmaxSplit = 32;
 
-// Prefill workspace of one window of nw tokens (nwp = nw rounded up to 64):
-//   rec:   [BH][n_tiles][DVP][nwp]  per-tile readout records (bf16 or fp32)
-//   intra: [BH][DVP][nwp]           intra-window records (fp32)
+// Prefill workspace of one window of nw tokens (nwp = nw rounded up to 64).
+// float32 inputs:
+//   rec:   [BH][n_tiles][DVP][nwp]  per-tile readout records (fp32)
+//   intra: [BH][DVP][nwp]           intra-chunk records (fp32)
+//   carry: [BH][nchunks][DVP]       order-0 prefix at each chunk start (fp32)
+// bfloat16 inputs:
+//   rec:   [BH][n_tiles][nwp][DV]   per-tile readout records of the value
+//                                   columns (bf16 at d >= 32, else fp32)
+//   recz:  [BH][n_tiles][nwp]       per-tile den records (fp32)
+//   intra: [BH][nwp][DVP]           intra-window records (fp32)
 //   carry: [BH][nrwin][DVP]         order-0 prefix at each readout window start (fp32)
-//   amax:  [BH][kAmaxSplit][4]      max |q|, |k|, |v| per token slice (bf16 inputs)
+//   amax:  [BH][kAmaxSplit][4]      max |q|, |k|, |v| per token slice
+//   stg:   [BH][nwp/64][4][DK][64]  staged 16-bit tables of each 64-token chunk
+//   vsum:  [BH][nwp/64][DVP]        sum of v per chunk (fp32), token count at DV
 struct PrefillWs {
   void* rec;
   float* intra;
   float* carry;
   float* amax;
   int nwp;
+  float* recz;
+  uint16_t* stg;
+  float* vsum;
 };
 
 struct ScanArgs {
@@ -164,5 +186,9 @@ hipError_t launch_prefill_scan(int d, bool bf16, int BH, const ScanArgs& a, hipS
 hipError_t launch_prefill_intra(int d, bool bf16, int BH, const IntraArgs& a, hipStream_t s);
 hipError_t launch_prefill_reduce(int d, bool bf16, int BH, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_decode(int d, bool bf16, const DecodeArgs& a, hipStream_t s);
+// bfloat16 inputs: max-abs pre-pass, staging, order-0 carry and the scan of
+// one call window; then the reduce (after the intra-window kernel).
+hipError_t launch_prefill_b16(int d, int BH, const ScanArgs& a, hipStream_t s);
+hipError_t launch_reduce_b16(int d, int BH, const ReduceArgs& a, hipStream_t s);
 
 }  // namespace sata

@@ -698,663 +698,6 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
   if (grp == 0) rec[static_cast<int64_t>(DV) * a.ws.nwp] = den;
 }
 
-// Scans for bf16 inputs: one kernel body, two operand types.
-//
-//  * f16 operands (the fast path): q, k, v enter the MFMAs as f16 after exact
-//    power-of-two scaling per head and window, k' = k 2^-ek, q' = (q/c) 2^ek,
-//    v' = v 2^-ev, with ek, ev from the maxima of |k| and |v| (zero when those
-//    are already in comfortable ranges; then |k'| < 2, every key feature is
-//    below 8 in magnitude and |v'| < 2^15).  Products of two f16 values are
-//    formed with packed f16 multiplies.  Taken when max|q'| <= 2, which
-//    bounds every query feature; otherwise the bf16 path runs.  The
-//    readout operand is the state times a per-wave power of two chosen at
-//    each refresh to keep it inside the f16 range; the query side carries the
-//    inverse factor.  Records of value columns carry the factor 2^-ev, which
-//    the reduce kernel removes.
-//  * bf16 operands (fallback): products in fp32, rounded to bf16.
-//
-// Shared structure: the same chunk pipeline as the fp32 scan, with
-//  * one LDS key table kt = [k rows | k/2 rows | zero row | ones row | parent
-//    slots]; only order-2 parents need a slot (filled 8 tokens per item),
-//    order 0 and 1 parents read the ones row or a key row directly;
-//  * the query side is the plain monomial prod(q/c): the parent weights live
-//    on the key side, and the state is kept divided by prod(count!) of each
-//    row inside the scan (f16: also by the scale factors of its order);
-//  * the cross-wave readout sum goes through a bf16 LDS buffer, summed in
-//    fp32 with dot2;
-//  * masking of tokens past the window happens only in a partial chunk.
-
-// Per-head scale exponents of the f16 path from the window's max-abs values.
-struct HalfScales {
-  bool safe;
-  int ek;
-  int ev;
-};
-
-__device__ __forceinline__ HalfScales half_scales(const float* amax, float inv_c) {
-  float mq = 0.f, mk = 0.f, mv = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < kAmaxSplit; ++s) {
-    mq = fmaxf(mq, amax[4 * s]);
-    mk = fmaxf(mk, amax[4 * s + 1]);
-    mv = fmaxf(mv, amax[4 * s + 2]);
-  }
-  // Scale only outside comfortable ranges (|k| in [1/16, 2), |v| in
-  // [2^-8, 2^15)): mk = m 2^e with m in [0.5, 1) gives the exponent e.
-  HalfScales h;
-  h.ek = 0;
-  h.ev = 0;
-  int e = 0;
-  if (mk > 0.f) {
-    (void)frexpf(mk, &e);
-    if (e > 1 || e < -3) h.ek = e;
-  }
-  if (mv > 0.f) {
-    (void)frexpf(mv, &e);
-    if (e > 15) h.ev = e - 15;
-    else if (e < -7) h.ev = e;
-  }
-  const float qmax = ldexpf(mq * inv_c, h.ek);
-  h.safe = isfinite(mq) && isfinite(mk) && isfinite(mv) && qmax <= 2.f && h.ek > -40 && h.ek < 40 &&
-           h.ev > -40 && h.ev < 40;
-  return h;
-}
-
-// Max |x| of q, k, v over a slice of a window's tokens, per head.  Grid =
-// (kAmaxSplit slices, heads); the absolute values are compared as bf16 bit
-// patterns (monotone for non-NaN values), eight per 16-byte load.
-template <int DK>
-__global__ __launch_bounds__(256) void prefill_amax(ScanArgs a) {
-  const int sp = blockIdx.x;
-  const int head = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int64_t per = (a.nw + kAmaxSplit - 1) / kAmaxSplit;
-  const int64_t t_begin = static_cast<int64_t>(sp) * per;
-  const int64_t t_end = min(static_cast<int64_t>(a.nw), t_begin + per);
-  __shared__ uint32_t wmax[3][4];
-  uint32_t m[3] = {0u, 0u, 0u};
-  if (t_begin < t_end) {
-    const int64_t e0 = (a.t0 + t_begin) * DK, e1 = (a.t0 + t_end) * DK;   // DK % 8 == 0
-    const void* src[3] = {a.q, a.k, a.v};
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      const uint16_t* p = static_cast<const uint16_t*>(src[x]) + static_cast<int64_t>(head) * a.n_total * DK;
-      uint32_t acc = 0u;
-      for (int64_t e = e0 + 8 * tid; e < e1; e += 8 * 256) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p + e);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w2 = v[j] & 0x7fff7fffu;
-          acc = max(acc, max(w2 & 0xffffu, w2 >> 16));
-        }
-      }
-      m[x] = acc;
-    }
-  }
-#pragma unroll
-  for (int x = 0; x < 3; ++x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m[x] = max(m[x], static_cast<uint32_t>(__shfl_xor(static_cast<int>(m[x]), o)));
-    if ((tid & 63) == 0) wmax[x][tid >> 6] = m[x];
-  }
-  __syncthreads();
-  if (tid < 3) {
-    const uint32_t r = max(max(wmax[tid][0], wmax[tid][1]), max(wmax[tid][2], wmax[tid][3]));
-    a.ws.amax[(static_cast<int64_t>(head) * kAmaxSplit + sp) * 4 + tid] = __uint_as_float(r << 16);
-  }
-}
-
-template <int DK, bool H16>
-struct CfgB {
-  static constexpr int DV = DK;
-  static constexpr int L = prefill_chunk(true);
-  static constexpr int T = prefill_window(true);
-  static constexpr int SC = T / L;
-  static constexpr int NW = prefill_waves(true);
-  static constexpr int RB = prefill_rb(DK, true);
-  static constexpr int NB = col_blocks(DV);
-  static constexpr int NC = NB * 16;
-  static constexpr int DVP = padded_dv(DV);
-  static constexpr int NSLOT = prefill_slots(DK, true);
-  static constexpr int KSTR_HOST = prefill_kstride(true);   // row stride of the host kt offsets
-  static constexpr int KSTR = H16 ? L + 8 : KSTR_HOST;      // kt row stride (elements)
-  static constexpr int XQSTR = H16 ? DK + 8 : DK + 4;
-  static constexpr int RSTR = L + 8;                        // bf16 per reduction row
-  static constexpr int VSTR = L + 8;
-  static constexpr int ROW_ZERO = 2 * DK, ROW_ONES = 2 * DK + 1, ROW_SLOT = 2 * DK + 2;
-  static constexpr int KT_ROWS = ROW_SLOT + NSLOT;
-  static constexpr int NKS = RB / 2;
-  static constexpr int MB = L / 16;
-  static constexpr int EPT = L * DK / (NW * 64);
-  static constexpr bool RECB = prefill_bf16_records(DK, true);
-  using TT = typename std::conditional<H16, _Float16, float>::type;     // table element
-  using OP8 = typename std::conditional<H16, f16x8, bf16x8>::type;      // MFMA operand
-  static_assert(RB % 2 == 0, "readout K-slices pair row blocks");
-  static_assert((KSTR * sizeof(TT)) % 16 == 0 && (XQSTR * sizeof(TT)) % 16 == 0, "16-byte aligned table rows");
-};
-
-template <bool H16>
-__device__ __forceinline__ f32x4 mfma16(typename CfgB<8, H16>::OP8 a, typename CfgB<8, H16>::OP8 b, f32x4 c) {
-  if constexpr (H16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-template <int DK, bool H16>
-__global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(ScanArgs a) {
-  using C = CfgB<DK, H16>;
-  using TT = typename C::TT;
-  using OP8 = typename C::OP8;
-  constexpr int NW = C::NW;
-  constexpr int DV = C::DV, L = C::L, RB = C::RB, NB = C::NB, NC = C::NC, DVP = C::DVP;
-  constexpr int NSLOT = C::NSLOT, KSTR = C::KSTR, XQSTR = C::XQSTR, RSTR = C::RSTR, VSTR = C::VSTR;
-  constexpr int EPT = C::EPT;
-
-  const int tile = blockIdx.x;
-  const int head = blockIdx.y;
-  const HalfScales hs = half_scales(a.ws.amax + static_cast<int64_t>(head) * kAmaxSplit * 4, a.inv_c);
-  if (hs.safe != H16) return;   // the other operand type handles this head
-
-  __shared__ __attribute__((aligned(16))) TT kt[C::KT_ROWS * KSTR];
-  __shared__ __attribute__((aligned(16))) TT xq[L * XQSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t red[NW * (DV + 1) * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[NC * VSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vraw[H16 ? DV * VSTR : 8];   // bf16 v (order-0 carry)
-  __shared__ float carry[NC];
-  __shared__ uint32_t spar[NSLOT];
-  __shared__ float spsc[NSLOT];
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int l = tid & 63;
-  const int lr = l & 15;
-  const int g = l >> 4;
-  const int n_tiles = a.lay.n_tiles;
-  const int lay_base = (tile * NW + w) * RB;
-  // f16: k' = k 2^-ek, q' = (q/c) 2^ek, v' = v 2^-ev.
-  const float kmul = H16 ? ldexpf(1.f, -hs.ek) : 1.f;
-  const float qmul = H16 ? ldexpf(a.inv_c, hs.ek) : a.inv_c;
-  const float vmul = H16 ? ldexpf(1.f, -hs.ev) : 1.f;
-
-  // Per-lane run metadata: key side (parent row | child row, as kt offsets),
-  // query side (parent coordinates i1 | i2 << 8 | first child << 16; index d
-  // is the constant 1).
-  uint32_t ks[RB], qs[RB];
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    ks[b] = a.lay.kside[(lay_base + b) * 16 + lr];
-    qs[b] = a.lay.qside[(lay_base + b) * 4 + g];
-    if constexpr (H16) {
-      const uint32_t pr = (ks[b] & 0xffffu) / C::KSTR_HOST, xr = (ks[b] >> 16) / C::KSTR_HOST;
-      ks[b] = pr * KSTR | ((xr * KSTR) << 16);
-    }
-  }
-  const int nslot = a.lay.nslot[tile];
-  for (int s = tid; s < nslot; s += NW * 64) {
-    spar[s] = a.lay.parents[tile * NSLOT + s];
-    spsc[s] = a.lay.kscale[tile * NSLOT + s];
-  }
-  for (int i = tid; i < KSTR; i += NW * 64) {
-    kt[C::ROW_ZERO * KSTR + i] = static_cast<TT>(0.f);
-    kt[C::ROW_ONES * KSTR + i] = static_cast<TT>(1.f);
-  }
-  for (int t = tid; t < L; t += NW * 64) {
-    xq[t * XQSTR + DK] = static_cast<TT>(1.f);
-    for (int j = DK + 1; j < XQSTR; ++j) xq[t * XQSTR + j] = static_cast<TT>(0.f);
-  }
-  const uint16_t one16 = H16 ? static_cast<uint16_t>(0x3c00) : static_cast<uint16_t>(0x3f80);
-  for (int e = tid; e < (NC - DV) * VSTR; e += NW * 64) {
-    const int c = DV + e / VSTR;
-    vt[c * VSTR + e % VSTR] = (c == DV) ? one16 : static_cast<uint16_t>(0);
-  }
-
-  // Row order of a canonical row (f16 scale exponent of its state).
-  const int64_t off2 = 1 + DK, off3 = 1 + DK + static_cast<int64_t>(DK) * (DK + 1) / 2;
-  auto row_exp = [&](int64_t m, bool value_col) {
-    const int p = m >= off3 ? 3 : m >= off2 ? 2 : m >= 1 ? 1 : 0;
-    return p * hs.ek + (value_col ? hs.ev : 0);
-  };
-
-  // State tile into the accumulators (C layout: lane holds column nb*16 + lr
-  // of rows 4g + r), divided by prod(count!) of each row (f16: and scaled).
-  float* st = a.state + static_cast<int64_t>(head) * a.stride;
-  const int64_t zoff = static_cast<int64_t>(a.D) * DV;
-  f32x4 S[RB][NB];
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t info = a.lay.rowinfo[(lay_base + b) * 16 + 4 * g + r];
-      const int64_t m = info ? static_cast<int64_t>(info & 0x0fffffffu) - 1 : 0;
-      const float inv_fac = info ? 1.f / static_cast<float>(info >> 28) : 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int col = nb * 16 + lr;
-        float val = 0.f;
-        if (col < DV) val = st[m * DV + col];
-        else if (col == DV) val = st[zoff + m];
-        val *= inv_fac;
-        if constexpr (H16) val = ldexpf(val, -row_exp(m, col < DV));
-        S[b][nb][r] = val;
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // 16-bit copy of the state (readout operand), per K-slice of two row blocks.
-  // f16: scaled by 2^-ew (per wave, per refresh); qsc = 2^ew rides on the
-  // query side.
-  u32x4 Sb[C::NKS][NB];
-  float qsc = 1.f;
-  auto refresh = [&]() {
-    float sc = 1.f;
-    if constexpr (H16) {
-      float mx = 0.f;
-#pragma unroll
-      for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(S[b][nb][r]));
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      int e = 0;
-      if (mx > 0.f) (void)frexpf(mx, &e);
-      const int ew = __builtin_amdgcn_readfirstlane(min(15, max(0, e - 14)));   // wave-uniform
-      sc = ldexpf(1.f, -ew);
-      qsc = ldexpf(1.f, ew);
-    }
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (H16) {
-          const f32x4 x = S[b][nb] * sc;
-          Sb[b / 2][nb][2 * (b % 2)] = pack_f16(x[0], x[1]);
-          Sb[b / 2][nb][2 * (b % 2) + 1] = pack_f16(x[2], x[3]);
-        } else {
-          Sb[b / 2][nb][2 * (b % 2)] = pack_bf16(S[b][nb][0], S[b][nb][1]);
-          Sb[b / 2][nb][2 * (b % 2) + 1] = pack_bf16(S[b][nb][2], S[b][nb][3]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  refresh();
-  if (tile == 0 && tid < NC) carry[tid] = tid < DV ? st[tid] : (tid == DV ? st[zoff] : 0.f);
-
-  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
-  const uint16_t* kh = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
-  const uint16_t* vh = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
-  const int nwp = a.ws.nwp;
-  using RedT = typename std::conditional<C::RECB, uint16_t, float>::type;
-  RedT* rech = static_cast<RedT*>(a.ws.rec) +
-               (static_cast<int64_t>(head) * n_tiles + tile) * DVP * static_cast<int64_t>(nwp);
-  const int nch = (a.nw + L - 1) / L;
-  float* carryh = a.ws.carry + static_cast<int64_t>(head) * ((nwp + C::T - 1) / C::T) * DVP;
-
-  // Cross-wave sum of one chunk's readout (bf16 partials in LDS, summed in
-  // fp32 in a fixed order) into its records: value columns 8 tokens per item
-  // (one item per thread at d = 64), the z column one token per item.  The
-  // bf16 halves are accumulated with dot2 against (1, 0) / (0, 1).
-  auto red_sum = [&](int ch) {
-    // Selectors as explicit bf16 pairs in registers (no reliance on how an
-    // inline constant is read for packed bf16 operands).
-    uint32_t lo_bits = 0x00003f80u, hi_bits = 0x3f800000u;
-    asm volatile("" : "+v"(lo_bits), "+v"(hi_bits));
-    const bf16x2 sel_lo = __builtin_bit_cast(bf16x2, lo_bits);
-    const bf16x2 sel_hi = __builtin_bit_cast(bf16x2, hi_bits);
-    if ((tid & 7) == 0 && (tid >> 3) < L) {
-      const int t = tid >> 3;
-      float sz = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) sz += __uint_as_float(static_cast<uint32_t>(red[(ww * (DV + 1) + DV) * RSTR + t]) << 16);
-      const int64_t off = static_cast<int64_t>(DV) * nwp + ch * L + t;
-      if constexpr (C::RECB)
-        rech[off] = static_cast<uint16_t>(pack_bf16(sz, 0.f) & 0xffffu);
-      else
-        rech[off] = sz;
-    }
-    for (int e = tid; e < DV * (L / 8); e += NW * 64) {
-      const int c = e / (L / 8);
-      const int tg = e % (L / 8);
-      float sum[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sum[j] = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 8 * tg]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t xj = x[j];   // scalar copy: bit_cast of a vector element is miscompiled
-          const bf16x2 xx = __builtin_bit_cast(bf16x2, xj);
-          sum[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(xx, sel_lo, sum[2 * j], false);
-          sum[2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(xx, sel_hi, sum[2 * j + 1], false);
-        }
-      }
-      const int64_t off = static_cast<int64_t>(c) * nwp + ch * L + 8 * tg;
-      if constexpr (C::RECB) {
-        const u32x4 o = {pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3]), pack_bf16(sum[4], sum[5]),
-                         pack_bf16(sum[6], sum[7])};
-        *reinterpret_cast<u32x4*>(&rech[off]) = o;
-      } else {
-        *reinterpret_cast<f32x4*>(&rech[off]) = f32x4{sum[0], sum[1], sum[2], sum[3]};
-        *reinterpret_cast<f32x4*>(&rech[off + 4]) = f32x4{sum[4], sum[5], sum[6], sum[7]};
-      }
-    }
-  };
-
-  // Staging: each thread holds EPT consecutive elements of one token per
-  // tensor; consecutive lanes take consecutive tokens.
-  const int st_t = tid % L;
-  const int st_i = (tid / L) * EPT;
-  ChunkRegs<uint16_t, EPT> rq, rk, rv;
-  {
-    const bool ok = st_t < min(L, a.nw);
-    const int64_t tn = a.t0 + (ok ? st_t : 0);
-    rq.load(qh + tn * DK + st_i, true);
-    rk.load(kh + tn * DK + st_i, true);
-    rv.load(vh + tn * DV + st_i, true);
-  }
-
-  for (int ch0 = 0; ch0 < nch; ch0 += C::SC) {
-    const int ch_end = min(nch, ch0 + C::SC);
-    for (int ch = ch0; ch < ch_end; ++ch) {
-      const int64_t tb = a.t0 + static_cast<int64_t>(ch) * L;
-      const int nvalid = min(L, a.nw - ch * L);
-#pragma unroll
-      for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(ks[b]), "+v"(qs[b]));
-
-      // ---- phase A: stage this chunk, then the previous chunk's records ---
-      // (staging first: its wait for the prefetched loads must not also wait
-      // for the record stores)
-      if constexpr (H16) {
-        if constexpr (EPT >= 2) {
-#pragma unroll
-          for (int e = 0; e < EPT; e += 2) {
-            const uint32_t q2 = pack_f16(to_f32(rq.raw(e)) * qmul, to_f32(rq.raw(e + 1)) * qmul);
-            *reinterpret_cast<uint32_t*>(&xq[st_t * XQSTR + st_i + e]) = q2;
-          }
-        } else {
-          xq[st_t * XQSTR + st_i] = static_cast<_Float16>(to_f32(rq.raw(0)) * qmul);
-        }
-        auto stage_kv = [&]() {
-#pragma unroll
-          for (int e = 0; e < EPT; ++e) {
-            const float kv = to_f32(rk.raw(e)) * kmul;
-            const _Float16 kh16 = static_cast<_Float16>(kv);
-            kt[(st_i + e) * KSTR + st_t] = kh16;
-            kt[(DK + st_i + e) * KSTR + st_t] = kh16 * static_cast<_Float16>(0.5f);
-            const float vv = to_f32(rv.raw(e)) * vmul;
-            vt[(st_i + e) * VSTR + st_t] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(vv));
-          }
-        };
-        stage_kv();
-        if (tile == 0) {
-#pragma unroll
-          for (int e = 0; e < EPT; ++e) vraw[(st_i + e) * VSTR + st_t] = rv.raw(e);
-        }
-      } else {
-        if constexpr (EPT >= 4) {
-#pragma unroll
-          for (int e = 0; e < EPT; e += 4) {
-            float4 q4;
-            q4.x = to_f32(rq.raw(e)) * qmul;
-            q4.y = to_f32(rq.raw(e + 1)) * qmul;
-            q4.z = to_f32(rq.raw(e + 2)) * qmul;
-            q4.w = to_f32(rq.raw(e + 3)) * qmul;
-            *reinterpret_cast<float4*>(__builtin_assume_aligned(&xq[st_t * XQSTR + st_i + e], 16)) = q4;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < EPT; ++e) xq[st_t * XQSTR + st_i + e] = to_f32(rq.raw(e)) * qmul;
-        }
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          const float kv = to_f32(rk.raw(e));
-          kt[(st_i + e) * KSTR + st_t] = kv;
-          kt[(DK + st_i + e) * KSTR + st_t] = kv * 0.5f;
-          vt[(st_i + e) * VSTR + st_t] = rv.raw(e);
-        }
-      }
-      if (nvalid < L && st_t >= nvalid) {
-        // Tokens past the window: zero keys and values (queries stay finite).
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          kt[(st_i + e) * KSTR + st_t] = static_cast<TT>(0.f);
-          kt[(DK + st_i + e) * KSTR + st_t] = static_cast<TT>(0.f);
-          vt[(st_i + e) * VSTR + st_t] = 0;
-          if constexpr (H16)
-            if (tile == 0) vraw[(st_i + e) * VSTR + st_t] = 0;
-        }
-      }
-      if (ch > 0) red_sum(ch - 1);
-      if (ch + 1 < nch) {
-        const bool ok = st_t < min(L, a.nw - (ch + 1) * L);
-        const int64_t tn = tb + L + (ok ? st_t : 0);
-        rq.load(qh + tn * DK + st_i, true);
-        rk.load(kh + tn * DK + st_i, true);
-        rv.load(vh + tn * DV + st_i, true);
-      }
-      __syncthreads();
-
-      // ---- phase B: order-2 parent features, 8 tokens per item ------------
-      for (int e = tid; e < nslot * (L / 8); e += NW * 64) {
-        const int s = e / (L / 8);
-        const int t8 = (e % (L / 8)) * 8;
-        const uint32_t pw = spar[s];
-        const int i1 = pw & 255;
-        const int i2 = (pw >> 8) & 255;
-        const float sc = spsc[s];
-        if constexpr (H16) {
-          const f16x8 x1 = *reinterpret_cast<const f16x8*>(&kt[i1 * KSTR + t8]);
-          const f16x8 x2 = *reinterpret_cast<const f16x8*>(&kt[i2 * KSTR + t8]);
-          *reinterpret_cast<f16x8*>(&kt[(C::ROW_SLOT + s) * KSTR + t8]) = (x1 * x2) * static_cast<_Float16>(sc);
-        } else {
-          const float4 a0 = lds4(kt, i1 * KSTR + t8), a1 = lds4(kt, i1 * KSTR + t8 + 4);
-          const float4 b0 = lds4(kt, i2 * KSTR + t8), b1 = lds4(kt, i2 * KSTR + t8 + 4);
-          float* dst = &kt[(C::ROW_SLOT + s) * KSTR + t8];
-          *reinterpret_cast<float4*>(__builtin_assume_aligned(dst, 16)) =
-              make_float4(sc * a0.x * b0.x, sc * a0.y * b0.y, sc * a0.z * b0.z, sc * a0.w * b0.w);
-          *reinterpret_cast<float4*>(__builtin_assume_aligned(dst + 4, 16)) =
-              make_float4(sc * a1.x * b1.x, sc * a1.y * b1.y, sc * a1.z * b1.z, sc * a1.w * b1.w);
-        }
-      }
-      if (tile == 0) {
-        // Order-0 prefix at each readout window's start, then add the chunk
-        // (exact fp32, from the bf16 values).
-        const uint16_t* vsrc = H16 ? vraw : vt;
-        const bool wstart = ch % C::SC == 0;
-        if (tid < DV) {
-          if (wstart) carryh[static_cast<int64_t>(ch / C::SC) * DVP + tid] = carry[tid];
-          float sv = 0.f;
-          for (int t = 0; t < nvalid; ++t) sv += __uint_as_float(static_cast<uint32_t>(vsrc[tid * VSTR + t]) << 16);
-          carry[tid] += sv;
-        } else if (tid == DV) {
-          if (wstart) carryh[static_cast<int64_t>(ch / C::SC) * DVP + DV] = carry[DV];
-          carry[DV] += static_cast<float>(nvalid);
-        }
-      }
-      __syncthreads();
-
-      // ---- phase C: readout and update, in opposite orders on the two waves
-      // that share a SIMD (waves w and w + NW/2), so one wave's LDS- and
-      // VALU-heavy readout overlaps the other's MFMA-heavy update.  Both read
-      // only this chunk's tables and the window-start readout operand.
-      auto readout = [&]() {
-      // ---- phase C: readout against the state at the window start --------
-      // (one 16-token block at a time) into the bf16 reduction buffer.
-      {
-        struct QData {
-          TT p1[2], p2[2];
-          typename std::conditional<H16, f16x4, float4>::type x[2];
-        };
-        // step s = (token block mb, K-slice kk): the two row blocks 2kk, 2kk+1
-        auto load_q = [&](int s_, QData& dq) {
-          const int mb = s_ / C::NKS, kk = s_ % C::NKS;
-          const int t = mb * 16 + lr;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t q = qs[2 * kk + h];
-            dq.p1[h] = xq[t * XQSTR + (q & 255)];
-            dq.p2[h] = xq[t * XQSTR + ((q >> 8) & 255)];
-            if constexpr (H16)
-              dq.x[h] = *reinterpret_cast<const f16x4*>(&xq[t * XQSTR + ((q >> 16) & 255)]);
-            else
-              dq.x[h] = lds4(xq, t * XQSTR + ((q >> 16) & 255));
-          }
-        };
-        auto build_q = [&](const QData& dq) {
-          if constexpr (H16) {
-            const f16x2 pa = {dq.p1[0], dq.p1[1]}, pb = {dq.p2[0], dq.p2[1]};
-            const f16x2 pp = pa * pb * static_cast<_Float16>(qsc);
-            const _Float16 p0 = pp[0], p1 = pp[1];
-            const f16x4 a0 = dq.x[0] * p0, a1 = dq.x[1] * p1;
-            const f16x8 r = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            return r;
-          } else {
-            const float p0 = dq.p1[0] * dq.p2[0];
-            const float p1 = dq.p1[1] * dq.p2[1];
-            const float4 x0 = dq.x[0], x1 = dq.x[1];
-            const u32x4 aw = {pack_bf16(p0 * x0.x, p0 * x0.y), pack_bf16(p0 * x0.z, p0 * x0.w),
-                              pack_bf16(p1 * x1.x, p1 * x1.y), pack_bf16(p1 * x1.z, p1 * x1.w)};
-            return __builtin_bit_cast(bf16x8, aw);
-          }
-        };
-        constexpr int NQS = C::MB * C::NKS;
-        QData dq;
-        load_q(0, dq);
-        OP8 Acur = build_q(dq);
-        if (NQS > 1) load_q(NQS > 1 ? 1 : 0, dq);
-        f32x4 acc[NB];
-#pragma unroll
-        for (int s_ = 0; s_ < NQS; ++s_) {
-          const int mb = s_ / C::NKS, kk = s_ % C::NKS;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[nb] = mfma16<H16>(Acur, __builtin_bit_cast(OP8, Sb[kk][nb]),
-                                  kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb]);
-          OP8 Anext = Acur;
-          if (s_ + 1 < NQS) Anext = build_q(dq);
-          if (s_ + 2 < NQS) load_q(s_ + 2 < NQS ? s_ + 2 : 0, dq);
-          if (kk == C::NKS - 1) {
-            // C layout: lane holds column nb*16 + lr of tokens 4g..4g+3.
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              const int col = nb * 16 + lr;
-              if (col <= DV) {
-                const u32x2 o = {pack_bf16(acc[nb][0], acc[nb][1]), pack_bf16(acc[nb][2], acc[nb][3])};
-                *reinterpret_cast<u32x2*>(__builtin_assume_aligned(
-                    &red[(w * (DV + 1) + col) * RSTR + mb * 16 + 4 * g], 8)) = o;
-              }
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          Acur = Anext;
-        }
-      }
-      };
-      auto update = [&]() {
-      // ---- phase C: state update S += phi_k(K)^T [V 1] --------------------
-      {
-        constexpr int NST = (L / 32) * RB;
-        struct KData {
-          typename std::conditional<H16, f16x8, float4>::type p0, p1, x0, x1;   // f16: p0, x0 only
-        };
-        auto load_k = [&](int st_, KData& dk) {
-          const int kst = st_ / RB, b = st_ % RB;
-          const int pko = (ks[b] & 0xffff) + 32 * kst + 8 * g;
-          const int xko = (ks[b] >> 16) + 32 * kst + 8 * g;
-          if constexpr (H16) {
-            dk.p0 = *reinterpret_cast<const f16x8*>(&kt[pko]);
-            dk.x0 = *reinterpret_cast<const f16x8*>(&kt[xko]);
-          } else {
-            dk.p0 = lds4(kt, pko);
-            dk.p1 = lds4(kt, pko + 4);
-            dk.x0 = lds4(kt, xko);
-            dk.x1 = lds4(kt, xko + 4);
-          }
-        };
-        auto build_k = [&](const KData& dk) {
-          if constexpr (H16) {
-            return dk.p0 * dk.x0;
-          } else {
-            const u32x4 aw = {pack_bf16(dk.p0.x * dk.x0.x, dk.p0.y * dk.x0.y),
-                              pack_bf16(dk.p0.z * dk.x0.z, dk.p0.w * dk.x0.w),
-                              pack_bf16(dk.p1.x * dk.x1.x, dk.p1.y * dk.x1.y),
-                              pack_bf16(dk.p1.z * dk.x1.z, dk.p1.w * dk.x1.w)};
-            return __builtin_bit_cast(bf16x8, aw);
-          }
-        };
-        auto load_v = [&](int kst, OP8 (&Bv)[NB]) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            Bv[nb] = *reinterpret_cast<const OP8*>(
-                __builtin_assume_aligned(&vt[(nb * 16 + lr) * VSTR + 32 * kst + 8 * g], 16));
-        };
-        OP8 Bv[NB];
-        KData dk;
-        load_k(0, dk);
-        OP8 Acur = build_k(dk);
-        if (NST > 1) load_k(NST > 1 ? 1 : 0, dk);
-#pragma unroll
-        for (int st_ = 0; st_ < NST; ++st_) {
-          const int kst = st_ / RB, b = st_ % RB;
-          if (b == 0) load_v(kst, Bv);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) S[b][nb] = mfma16<H16>(Acur, Bv[nb], S[b][nb]);
-          OP8 Anext = Acur;
-          if (st_ + 1 < NST) Anext = build_k(dk);
-          if (st_ + 2 < NST) load_k(st_ + 2 < NST ? st_ + 2 : 0, dk);
-          __builtin_amdgcn_sched_barrier(0);
-          Acur = Anext;
-        }
-      }
-      };
-      if (w < NW / 2) {
-        readout();
-        update();
-      } else {
-        update();
-        readout();
-      }
-      __syncthreads();
-    }
-    refresh();
-  }
-  if (nch > 0) red_sum(nch - 1);
-
-  // State tile back in canonical layout (times prod(count!) of each row; f16:
-  // and unscaled).
-  const uint32_t* rowinfo = a.lay.rowinfo;
-  float* stw = st;
-  asm volatile("" : "+s"(rowinfo), "+s"(stw));
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t info = rowinfo[(lay_base + b) * 16 + 4 * g + r];
-      if (info) {
-        const int64_t m = static_cast<int64_t>(info & 0x0fffffffu) - 1;
-        const float fac = static_cast<float>(info >> 28);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = nb * 16 + lr;
-          float val = S[b][nb][r] * fac;
-          if constexpr (H16) val = ldexpf(val, row_exp(m, col < DV));
-          if (col < DV) stw[m * DV + col] = val;
-          else if (col == DV) stw[zoff + m] = val;
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (tile == 0) {
-    if (tid < DV) st[tid] = carry[tid];
-    else if (tid == DV) st[zoff] = carry[DV];
-  }
-}
-
 // Intra-window part on MFMA, for bf16 inputs.  Block = (readout window of T
 // tokens, head); wave w owns the queries [64w, 64w + 64) of the window.  For
 // every 32-key slice up to its last query:
@@ -1486,19 +829,18 @@ __global__ __launch_bounds__(256) void prefill_intra_mfma(IntraArgs a) {
       }
     }
   }
-  // O^T in C layout: lane holds query 16 qb + lr, value columns 16 nb + 4 g + r.
-  float* rec = a.ws.intra + static_cast<int64_t>(head) * DVP * a.ws.nwp + static_cast<int64_t>(win) * T;
+  // O^T in C layout: lane holds query 16 qb + lr, value columns 16 nb + 4 g + r;
+  // records are token-major, DVP columns a token.
+  float* rec = a.ws.intra + (static_cast<int64_t>(head) * a.ws.nwp + static_cast<int64_t>(win) * T) * DVP;
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
     const int qi = 64 * w + 16 * qb + lr;
     if (qi >= nvalid) continue;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = 16 * nb + 4 * g + r;
-        if (col <= DV) rec[static_cast<int64_t>(col) * a.ws.nwp + qi] = O[nb][qb][r];
-      }
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = 16 * nb + 4 * g;
+      if (col + 4 <= DVP) *reinterpret_cast<f32x4*>(&rec[static_cast<int64_t>(qi) * DVP + col]) = O[nb][qb];
+    }
   }
 }
 
@@ -1506,6 +848,7 @@ __global__ __launch_bounds__(256) void prefill_intra_mfma(IntraArgs a) {
 // summed in a fixed order.  Block = (64 tokens, head).
 template <int DK, bool BF16>
 __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
+  static_assert(!BF16, "bfloat16 inputs use prefill_reduce_b16");
   constexpr int DV = DK, DVP = padded_dv(DV), T = prefill_window(BF16);
   constexpr bool RECB = prefill_bf16_records(DK, BF16);
   constexpr int TB = 64;
@@ -1517,13 +860,7 @@ __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
   const int64_t slab = static_cast<int64_t>(DVP) * nwp;
   const float* intra = a.ws.intra + head * slab;
   const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + T - 1) / T) * DVP;
-  // bf16 inputs scanned with f16 operands carry 2^-ev in their value-column
-  // records.
-  float rscale = 1.f;
-  if constexpr (BF16) {
-    const HalfScales hs = half_scales(a.ws.amax + static_cast<int64_t>(head) * kAmaxSplit * 4, a.inv_c);
-    if (hs.safe) rscale = ldexpf(1.f, hs.ev);
-  }
+  const float rscale = 1.f;
   for (int e = tid; e < (DV + 1) * (TB / 4); e += 256) {
     const int c = e / (TB / 4);
     const int t = 4 * (e % (TB / 4));
@@ -1562,21 +899,13 @@ __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
 
 template <int D, bool BF16>
 hipError_t launch_scan_t(int BH, const ScanArgs& a, hipStream_t s) {
-  dim3 grid(a.lay.n_tiles, BH);
   if constexpr (BF16) {
-    // Max-abs pre-pass, then both operand types: each head is scanned by the
-    // one its scales select; the other returns at once.
-    prefill_amax<D><<<dim3(kAmaxSplit, BH), 256, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    prefill_scan_b16<D, true><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    prefill_scan_b16<D, false><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
+    return hipErrorInvalidValue;   // bfloat16 inputs: launch_prefill_b16
   } else {
+    dim3 grid(a.lay.n_tiles, BH);
     prefill_scan<D, BF16><<<grid, kWaves * 64, 0, s>>>(a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 template <int D, bool BF16>
@@ -1592,9 +921,13 @@ hipError_t launch_intra_t(int BH, const IntraArgs& a, hipStream_t s) {
 
 template <int D, bool BF16>
 hipError_t launch_reduce_t(int BH, const ReduceArgs& a, hipStream_t s) {
-  dim3 grid((a.nw + 63) / 64, BH);
-  prefill_reduce<D, BF16><<<grid, 256, 0, s>>>(a);
-  return hipGetLastError();
+  if constexpr (BF16) {
+    return hipErrorInvalidValue;   // bfloat16 inputs: launch_reduce_b16
+  } else {
+    dim3 grid((a.nw + 63) / 64, BH);
+    prefill_reduce<D, BF16><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
 }
 
 #define SATA_DISPATCH(fn, d, bf16, ...)                                   \

@@ -1,0 +1,953 @@
+// Chunked causal prefill of SATA for bfloat16 inputs on gfx950 (CDNA4).
+//
+// Same split of the output as the float32 path [SATA page, section
+// "Engineering of constant compute cost": a fixed-size state of
+// phi(k) v^T sums, read out per token through the weighted feature map]:
+//   num_i = (intra-window part, exact polynomial)      prefill_intra_mfma
+//         + (order 0 before the window, exact sums)    prefill_carry
+//         + sum_{m of order >= 1} w_m phi_m(q_i) S_m   prefill_scan_b16
+// over readout windows of 256 tokens, and likewise for den with v -> 1.
+//
+// Kernels of one call window (launch order):
+//   prefill_amax     max |q|, |k|, |v| per head (32 token slices).
+//   prefill_stage    per (64-token chunk, head): q, k, v converted once into
+//                    the scan's 16-bit tables (f16 after exact power-of-two
+//                    scaling, or bf16 as is) in four layouts: keys and values
+//                    index-major, queries index-major and token-major; plus
+//                    exact fp32 sums of v per chunk.
+//   prefill_carry    order-0 prefix at each readout-window start, and the
+//                    order-0 row of the state.
+//   prefill_scan_b16 grid = (row tiles) x (heads), 8 waves.  Per chunk the
+//                    staged tables arrive in LDS by DMA (global_load_lds,
+//                    double-buffered, one chunk ahead); the state slice of the
+//                    tile stays in registers.  Two barrier-separated segments
+//                    per chunk, each with MFMA work:
+//                      1  readout  phi_q(Q) Sb  into the cross-wave buffer
+//                      2  cross-wave sum into the tile's records, key
+//                         features of the next chunk's order-2 parents, and
+//                         the update  S += phi_k(K)^T [V 1].
+//   prefill_reduce_b16  out = (intra + records + carry) / den per token.
+//
+// Feature map.  Rows of a tile come in runs of four children (P, c..c+3) of
+// one parent multiset P (the nested i1 <= ... <= ip index structure); a
+// child's feature is the parent's times one coordinate.  Features are plain
+// monomials prod k_i and prod q_i: the weights w_m = 1 / (prod count! c^p)
+// multiply the state when it is rounded to the 16-bit readout operand Sb
+// (once per readout window), so the state itself is the canonical S (times
+// exact powers of two on the f16 path).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "sata_internal.h"
+
+namespace sata {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kL = 64;   // tokens per chunk
+
+// Two floats rounded (nearest even) to bf16 / f16 and packed in one register.
+// The empty asm pins the conversion here so the fp32 inputs die early.
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  bf16x2 v = {static_cast<__bf16>(x), static_cast<__bf16>(y)};
+  uint32_t r = __builtin_bit_cast(uint32_t, v);
+  asm volatile("" : "+v"(r));
+  return r;
+}
+__device__ __forceinline__ uint32_t pack_f16(float x, float y) {
+  f16x2 v = {static_cast<_Float16>(x), static_cast<_Float16>(y)};
+  uint32_t r = __builtin_bit_cast(uint32_t, v);
+  asm volatile("" : "+v"(r));
+  return r;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its global stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// 16 bytes a lane from global memory straight into LDS (lane l writes bytes
+// [16 l, 16 l + 16) after the wave-uniform LDS address).
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+}
+// The same after this wave's LDS DMA (global_load_lds) has landed.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  lds_barrier();
+}
+
+// Per-head scale exponents of the f16 operand path, from the window's
+// max-abs values: k' = k 2^-ek, q' = q 2^ek, v' = v 2^-ev (exact), with ek,
+// ev zero unless |k| is outside [1/16, 2) or |v| outside [2^-8, 2^15).  Then
+// |k'| < 2, and the path is taken when also max |q'| <= 2: every feature (a
+// product of at most three coordinates) is below 8 in magnitude and every
+// value below 2^15, far inside the f16 range.  Otherwise the head runs with
+// bf16 operands.
+struct HalfScales {
+  bool safe;
+  int ek;
+  int ev;
+};
+
+__device__ __forceinline__ HalfScales half_scales(const float* amax) {
+  float mq = 0.f, mk = 0.f, mv = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < kAmaxSplit; ++s) {
+    mq = fmaxf(mq, amax[4 * s]);
+    mk = fmaxf(mk, amax[4 * s + 1]);
+    mv = fmaxf(mv, amax[4 * s + 2]);
+  }
+  HalfScales h;
+  h.ek = 0;
+  h.ev = 0;
+  int e = 0;
+  if (mk > 0.f) {
+    (void)frexpf(mk, &e);   // mk = m 2^e, m in [0.5, 1)
+    if (e > 1 || e < -3) h.ek = e;
+  }
+  if (mv > 0.f) {
+    (void)frexpf(mv, &e);
+    if (e > 15) h.ev = e - 15;
+    else if (e < -7) h.ev = e;
+  }
+  const float qmax = ldexpf(mq, h.ek);
+  h.safe = isfinite(mq) && isfinite(mk) && isfinite(mv) && qmax <= 2.f && h.ek > -40 && h.ek < 40 &&
+           h.ev > -40 && h.ev < 40;
+  return h;
+}
+
+__device__ __forceinline__ const HalfScales head_scales(const PrefillWs& ws, int head) {
+  return half_scales(ws.amax + static_cast<int64_t>(head) * kAmaxSplit * 4);
+}
+
+// ---------------------------------------------------------------------------
+// Max |x| of q, k, v over a slice of the window's tokens, per head.  Grid =
+// (kAmaxSplit slices, heads); absolute values compared as bf16 bit patterns
+// (monotone for non-NaN values; a NaN pattern exceeds every finite one and
+// makes the head take the bf16 path), eight per 16-byte load.
+template <int DK>
+__global__ __launch_bounds__(256) void prefill_amax(ScanArgs a) {
+  const int sp = blockIdx.x;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t per = (a.nw + kAmaxSplit - 1) / kAmaxSplit;
+  const int64_t t_begin = static_cast<int64_t>(sp) * per;
+  const int64_t t_end = min(static_cast<int64_t>(a.nw), t_begin + per);
+  __shared__ uint32_t wmax[3][4];
+  uint32_t m[3] = {0u, 0u, 0u};
+  if (t_begin < t_end) {
+    const int64_t e0 = (a.t0 + t_begin) * DK, e1 = (a.t0 + t_end) * DK;   // DK % 8 == 0
+    const void* src[3] = {a.q, a.k, a.v};
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      const uint16_t* p = static_cast<const uint16_t*>(src[x]) + static_cast<int64_t>(head) * a.n_total * DK;
+      uint32_t acc = 0u;
+      for (int64_t e = e0 + 8 * tid; e < e1; e += 8 * 256) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w2 = v[j] & 0x7fff7fffu;
+          acc = max(acc, max(w2 & 0xffffu, w2 >> 16));
+        }
+      }
+      m[x] = acc;
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m[x] = max(m[x], static_cast<uint32_t>(__shfl_xor(static_cast<int>(m[x]), o)));
+    if ((tid & 63) == 0) wmax[x][tid >> 6] = m[x];
+  }
+  __syncthreads();
+  if (tid < 3) {
+    const uint32_t r = max(max(wmax[tid][0], wmax[tid][1]), max(wmax[tid][2], wmax[tid][3]));
+    a.ws.amax[(static_cast<int64_t>(head) * kAmaxSplit + sp) * 4 + tid] = __uint_as_float(r << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Staging pre-pass.  Block = (64-token chunk, head).  Writes the chunk's four
+// 16-bit tables (each DK x 128 bytes, tokens past the window zero):
+//   KT[i][t] = k'_t[i]   VT[c][t] = v'_t[c]   QT[i][t] = q'_t[i]   QN[t][i] = q'_t[i]
+// and vsum[c] = sum_t v_t[c] (fp32, from the bf16 values), vsum[DV] = tokens.
+template <int DK>
+__global__ __launch_bounds__(256) void prefill_stage(ScanArgs a) {
+  constexpr int DV = DK, L = kL, NU = DK / 8, DVP = padded_dv(DV);
+  constexpr int TS = L + 8;   // LDS row stride of the transposes (16-bit elements)
+  __shared__ __attribute__((aligned(16))) uint16_t tr[3][DK * TS];
+  __shared__ float vraw[L][DV + 1];
+  const int ch = blockIdx.x;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const HalfScales hs = head_scales(a.ws, head);
+  const int nvalid = min(L, a.nw - ch * L);
+  const int64_t tok0 = a.t0 + static_cast<int64_t>(ch) * L;
+  const int nchp = a.ws.nwp / L;
+  float mul[3] = {1.f, 1.f, 1.f};   // k, v, q
+  if (hs.safe) {
+    mul[0] = ldexpf(1.f, -hs.ek);
+    mul[1] = ldexpf(1.f, -hs.ev);
+    mul[2] = ldexpf(1.f, hs.ek);
+  }
+  uint16_t* rec = a.ws.stg + (static_cast<int64_t>(head) * nchp + ch) * (4 * DK * L);
+  const uint16_t* src[3] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                            static_cast<const uint16_t*>(a.q)};
+  for (int e = tid; e < 3 * L * NU; e += 256) {
+    const int x = e / (L * NU);
+    const int r = e % (L * NU);
+    const int t = r / NU, u = r % NU;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (t < nvalid)
+      raw = *reinterpret_cast<const u32x4*>(src[x] + (static_cast<int64_t>(head) * a.n_total + tok0 + t) * DK + 8 * u);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t wj = raw[j];
+      const float lo = bf16_lo(wj), hi = bf16_hi(wj);
+      if (x == 1) {
+        vraw[t][8 * u + 2 * j] = lo;
+        vraw[t][8 * u + 2 * j + 1] = hi;
+      }
+      o[j] = hs.safe ? pack_f16(lo * mul[x], hi * mul[x]) : wj;
+      tr[x][(8 * u + 2 * j) * TS + t] = static_cast<uint16_t>(o[j] & 0xffffu);
+      tr[x][(8 * u + 2 * j + 1) * TS + t] = static_cast<uint16_t>(o[j] >> 16);
+    }
+    if (x == 2) *reinterpret_cast<u32x4*>(rec + 3 * DK * L + t * DK + 8 * u) = o;
+  }
+  __syncthreads();
+  for (int e = tid; e < 3 * DK * 8; e += 256) {
+    const int x = e / (DK * 8);
+    const int i = (e / 8) % DK, u = e % 8;
+    *reinterpret_cast<u32x4*>(rec + x * DK * L + i * L + 8 * u) =
+        *reinterpret_cast<const u32x4*>(&tr[x][i * TS + 8 * u]);
+  }
+  if (tid <= DV) {
+    float s = 0.f;
+    if (tid < DV) {
+      for (int t = 0; t < nvalid; ++t) s += vraw[t][tid];
+    } else {
+      s = static_cast<float>(nvalid);
+    }
+    a.ws.vsum[(static_cast<int64_t>(head) * nchp + ch) * DVP + tid] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Order-0 carry.  Block = head; thread c <= DV runs over the window's chunks
+// in order: carry[r][c] = (order-0 row of the state) + (sum of v[c], or the
+// token count for c = DV, over the chunks before readout window r).  The
+// order-0 row of the state ends as the sum over the whole window.
+template <int DK>
+__global__ __launch_bounds__(128) void prefill_carry(ScanArgs a) {
+  constexpr int DV = DK, DVP = padded_dv(DV), L = kL, SC = prefill_window(true) / kL;
+  const int head = blockIdx.x;
+  const int c = threadIdx.x;
+  if (c > DV) return;
+  float* st = a.state + static_cast<int64_t>(head) * a.stride;
+  const int64_t zoff = static_cast<int64_t>(a.D) * DV;
+  float acc = c < DV ? st[c] : st[zoff];
+  const int nch = (a.nw + L - 1) / L;
+  const int nchp = a.ws.nwp / L;
+  const float* vs = a.ws.vsum + static_cast<int64_t>(head) * nchp * DVP + c;
+  float* carry = a.ws.carry + static_cast<int64_t>(head) * ((a.ws.nwp + SC * L - 1) / (SC * L)) * DVP + c;
+  for (int ch = 0; ch < nch; ++ch) {
+    if (ch % SC == 0) carry[(ch / SC) * DVP] = acc;
+    acc += vs[static_cast<int64_t>(ch) * DVP];
+  }
+  if (c < DV) st[c] = acc;
+  else st[zoff] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// The scan.
+template <int DK>
+struct CfgS {
+  static constexpr int DV = DK;
+  static constexpr int L = kL;
+  static constexpr int T = prefill_window(true);
+  static constexpr int SC = T / L;                 // chunks per readout window
+  static constexpr int NW = prefill_waves(true);
+  static constexpr int RB = prefill_rb(DK, true);  // 16-row blocks per wave
+  static constexpr int NKS = RB / 2;               // readout K-slices (two blocks each)
+  static constexpr int NB = col_blocks(DV);        // 16-column blocks incl. den
+  static constexpr int NSLOT = prefill_slots(DK, true);
+  static constexpr int NU = DK / 8;                // 16-byte units per QN / red row
+  static constexpr int ROW_ZERO = DK, ROW_ONES = DK + 1, ROW_SLOT = DK + 2;
+  static constexpr int KT_ROWS = ROW_SLOT + NSLOT;
+  // LDS carve-up (bytes); tables of 64-token rows are 128 bytes a row.
+  static constexpr int KT_B = KT_ROWS * 128;
+  static constexpr int VT_B = DV * 128;
+  static constexpr int QT_B = (DK + 1) * 128;
+  static constexpr int QN_B = L * 2 * DK;
+  static constexpr int RED_B = NW * L * 2 * DV;
+  static constexpr int DEN_B = NW * L * 4;
+  static constexpr int WL_B = NW * RB * 16 * 4;
+  static constexpr int O_KT = 0;
+  static constexpr int O_VT = O_KT + 2 * KT_B;
+  static constexpr int O_QT = O_VT + 2 * VT_B;
+  static constexpr int O_QN = O_QT + 2 * QT_B;
+  static constexpr int O_RED = O_QN + 2 * QN_B;
+  static constexpr int O_DEN = O_RED + RED_B;
+  static constexpr int O_WL = O_DEN + DEN_B;
+  static constexpr int O_MAX = O_WL + WL_B;
+  static constexpr int LDS_B = O_MAX + 16 * NW;
+  // DMA: 4 tables of DK/8 blocks of 1 KB per chunk.
+  static constexpr int NBLK = 4 * NU;
+  static constexpr int NDMA = (NBLK + NW - 1) / NW;
+  // Where the den column sits in the readout output (C layout of a block).
+  static constexpr int NB_DEN = DV / 16, G_DEN = (DV % 16) / 4, R_DEN = DV % 4;
+  static_assert(LDS_B <= 160 * 1024, "LDS budget");
+  static_assert(RB % 2 == 0, "readout K-slices pair row blocks");
+};
+
+// Swizzles (16-byte units).  A 64-token row of KT / VT / QT / slots keeps its
+// eight 8-token units in the order u ^ ((row >> 1) & 7); a QN row (one
+// token) keeps its DK/8 units in the order u ^ (((t >> 2) ^ (t >> 5)) & (DK/8 - 1)).
+__device__ __forceinline__ int swz_row(int row) { return (row >> 1) & 7; }
+template <int NU>
+__device__ __forceinline__ int swz_tok(int t) { return ((t >> 2) ^ (t >> 5)) & (NU - 1); }
+
+template <bool H16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Elementwise product of two packed 16-bit 8-vectors (one MFMA operand).
+// f16: packed f16 multiplies; bf16: exact fp32 products rounded once.
+template <bool H16>
+__device__ __forceinline__ u32x4 mul8(u32x4 x, u32x4 y) {
+  if constexpr (H16) {
+    return __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, x) * __builtin_bit_cast(f16x8, y));
+  } else {
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t xj = x[j], yj = y[j];
+      r[j] = pack_bf16(bf16_lo(xj) * bf16_lo(yj), bf16_hi(xj) * bf16_hi(yj));
+    }
+    return r;
+  }
+}
+
+template <int DK, bool H16>
+__global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(ScanArgs a) {
+  using C = CfgS<DK>;
+  constexpr int DV = C::DV, L = C::L, NW = C::NW, RB = C::RB, NKS = C::NKS, NB = C::NB, NU = C::NU;
+  constexpr int NSLOT = C::NSLOT;
+
+  const int tile = blockIdx.x;
+  const int head = blockIdx.y;
+  const HalfScales hs = head_scales(a.ws, head);
+  if (hs.safe != H16) return;   // the other operand type scans this head
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_B];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int lr = l & 15;
+  const int g = l >> 4;
+  const int lay_base = (tile * NW + w) * RB;
+  const int nch = (a.nw + L - 1) / L;
+  const int nchp = a.ws.nwp / L;
+
+  // ---- constant rows, row weights -----------------------------------------
+  const uint32_t one2 = H16 ? 0x3c003c00u : 0x3f803f80u;
+  for (int e = tid; e < 6 * 32; e += NW * 64) {
+    const int r = e / 32, j = e % 32;   // KT zero (x2), KT ones (x2), QT ones (x2)
+    int off;
+    uint32_t val;
+    if (r < 2) {
+      off = C::O_KT + r * C::KT_B + C::ROW_ZERO * 128;
+      val = 0u;
+    } else if (r < 4) {
+      off = C::O_KT + (r - 2) * C::KT_B + C::ROW_ONES * 128;
+      val = one2;
+    } else {
+      off = C::O_QT + (r - 4) * C::QT_B + DK * 128;
+      val = one2;
+    }
+    *reinterpret_cast<uint32_t*>(lds + off + 4 * j) = val;
+  }
+  float* wl = reinterpret_cast<float*>(lds + C::O_WL);
+  for (int e = tid; e < NW * RB * 16; e += NW * 64)
+    wl[e] = a.lay.rweight[static_cast<int64_t>(tile) * NW * RB * 16 + e];
+
+  // ---- per-lane layout constants --------------------------------------------
+  // Update: KT byte offsets of the parent and child rows of lane row lr in
+  // block b, for the 8-token unit g of the first 32 tokens (the second 32
+  // tokens: offset ^ 64).
+  uint32_t okp[RB], okc[RB];
+  // Readout: QT byte offsets of the two parent coordinates of the run of
+  // lane group g in block b at tokens 4 lr .. 4 lr + 3, and the QN byte
+  // offset of its four children for token block 0 (token block mb: ^ 2 DK mb).
+  uint32_t oq1[RB], oq2[RB], oqc[RB];
+  {
+    const int sq = (lr ^ (lr >> 3)) & (NU - 1);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const uint32_t ks = a.lay.kside[(lay_base + b) * 16 + lr];
+      const int pr = ks & 0xffff, cr = ks >> 16;
+      okp[b] = pr * 128 + 16 * (g ^ swz_row(pr));
+      okc[b] = cr * 128 + 16 * (g ^ swz_row(cr));
+      const uint32_t qs = a.lay.qside[(lay_base + b) * 4 + g];
+      const int i1 = qs & 255, i2 = (qs >> 8) & 255, c0 = (qs >> 16) & 255;
+      oq1[b] = i1 * 128 + 16 * ((lr >> 1) ^ swz_row(i1)) + 8 * (lr & 1);
+      oq2[b] = i2 * 128 + 16 * ((lr >> 1) ^ swz_row(i2)) + 8 * (lr & 1);
+      oqc[b] = (4 * lr * 2 * DK + 16 * ((c0 >> 3) ^ sq) + 8 * ((c0 >> 2) & 1)) ^ (2 * DK * (lr & 1));
+    }
+  }
+  // Update, values: VT byte offset of row lr (column block 0), unit g; the
+  // rows of block nb are 2048 nb bytes further.
+  const uint32_t ovt = (DV >= 16 ? lr : (lr & (DV - 1))) * 128 + 16 * (g ^ swz_row(lr));
+  // Parent slots: up to two items (slot, 8-token unit) per thread.
+  const int nslot = a.lay.nslot[tile];
+  uint32_t so12[2], sod[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + i * NW * 64;
+    sod[i] = 0xffffffffu;
+    so12[i] = 0u;
+    if (e < nslot * 8) {
+      const int s = e >> 3, u = e & 7;
+      const uint32_t par = a.lay.parents[tile * NSLOT + s];
+      const int i1 = par & 255, i2 = (par >> 8) & 255, R = C::ROW_SLOT + s;
+      so12[i] = static_cast<uint32_t>(i1 * 128 + 16 * (u ^ swz_row(i1))) |
+                (static_cast<uint32_t>(i2 * 128 + 16 * (u ^ swz_row(i2))) << 16);
+      sod[i] = R * 128 + 16 * (u ^ swz_row(R));
+    }
+  }
+  // DMA: this wave's blocks of a chunk record: global byte offset per lane,
+  // LDS destination per block (buffer 0; buffer 1 adds the table size).
+  uint32_t gofs[C::NDMA];
+  int ldst[C::NDMA], lstep[C::NDMA];
+#pragma unroll
+  for (int i = 0; i < C::NDMA; ++i) {
+    const int beta = w + NW * i;
+    gofs[i] = 0u;
+    ldst[i] = -1;
+    lstep[i] = 0;
+    if (beta < C::NBLK) {
+      const int tau = beta / NU, bb = beta % NU;
+      const int p = 64 * bb + l;   // 16-byte unit of the table
+      if (tau < 3) {
+        const int row = p >> 3, q = p & 7;
+        gofs[i] = tau * DK * 128 + (row * 8 + (q ^ swz_row(row))) * 16;
+      } else {
+        const int t = p / NU, q = p % NU;
+        gofs[i] = 3 * DK * 128 + (t * NU + (q ^ swz_tok<NU>(t))) * 16;
+      }
+      const int base = tau == 0 ? C::O_KT : tau == 1 ? C::O_VT : tau == 2 ? C::O_QT : C::O_QN;
+      lstep[i] = tau == 0 ? C::KT_B : tau == 1 ? C::VT_B : tau == 2 ? C::QT_B : C::QN_B;
+      ldst[i] = base + 1024 * bb;
+    }
+  }
+  const unsigned char* stg = reinterpret_cast<const unsigned char*>(a.ws.stg) +
+                             static_cast<int64_t>(head) * nchp * (8 * DK * L);
+  auto dma = [&](int ch, int X) {
+    const unsigned char* src = stg + static_cast<int64_t>(ch) * (8 * DK * L);
+#pragma unroll
+    for (int i = 0; i < C::NDMA; ++i)
+      if (ldst[i] >= 0)
+        dma16(src + gofs[i], lds + __builtin_amdgcn_readfirstlane(ldst[i] + X * lstep[i]));
+  };
+
+  // ---- state tile into registers (C layout: lane holds column 16 nb + lr of
+  // rows 4 g + r of block b); f16 path: times 2^-(p ek + ev) for a value
+  // column of an order-p row, 2^-(p ek) for den.
+  float* st = a.state + static_cast<int64_t>(head) * a.stride;
+  const int64_t zoff = static_cast<int64_t>(a.D) * DV;
+  const int64_t off2 = 1 + DK, off3 = 1 + DK + static_cast<int64_t>(DK) * (DK + 1) / 2;
+  auto row_exp = [&](int64_t m, bool value_col) {
+    const int p = m >= off3 ? 3 : m >= off2 ? 2 : m >= 1 ? 1 : 0;
+    return p * hs.ek + (value_col ? hs.ev : 0);
+  };
+  f32x4 S[RB][NB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t info = a.lay.rowinfo[(lay_base + b) * 16 + 4 * g + r];
+      const int64_t m = info ? static_cast<int64_t>(info) - 1 : 0;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = nb * 16 + lr;
+        float val = 0.f;
+        if (info) {
+          if (col < DV) val = st[m * DV + col];
+          else if (col == DV) val = st[zoff + m];
+          if constexpr (H16) val = ldexpf(val, -row_exp(m, col < DV));
+        }
+        S[b][nb][r] = val;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- readout operand: Sb = S w 2^-ew, one ew per tile and readout window
+  // (f16: max |S| max(w) 2^-ew in [2^13, 2^14); bf16: ew = 0).  Two steps around a
+  // barrier: each wave posts its max |S|, then every wave derives ew from
+  // the tile's max and rounds its slice.
+  u32x4 Sb[NKS][NB];
+  int ew = 0;
+  float* wmx = reinterpret_cast<float*>(lds + C::O_MAX);
+  // Largest row weight of the lane's rows: max |S| times it bounds max |S w|.
+  float wlmax = 0.f;
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wlmax = fmaxf(wlmax, fabsf(a.lay.rweight[(lay_base + b) * 16 + 4 * g + r]));
+  auto post_max = [&]() {
+    if constexpr (H16) {
+      float mx = 0.f;
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(S[b][nb][r]));
+      mx *= wlmax;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if (l == 0) wmx[w] = mx;
+    }
+  };
+  auto refresh = [&]() {
+    float sc = 1.f;
+    if constexpr (H16) {
+      float mx = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, wmx[ww]);
+      int e = 0;
+      if (mx > 0.f) (void)frexpf(mx, &e);
+      ew = __builtin_amdgcn_readfirstlane(mx > 0.f ? e - 14 : 0);
+      sc = ldexpf(1.f, -ew);
+    }
+    const float* wb = wl + (w * RB) * 16 + 4 * g;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const f32x4 wr = *reinterpret_cast<const f32x4*>(wb + 16 * b) * sc;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const f32x4 x = S[b][nb] * wr;
+        if constexpr (H16) {
+          Sb[b / 2][nb][2 * (b % 2)] = pack_f16(x[0], x[1]);
+          Sb[b / 2][nb][2 * (b % 2) + 1] = pack_f16(x[2], x[3]);
+        } else {
+          Sb[b / 2][nb][2 * (b % 2)] = pack_bf16(x[0], x[1]);
+          Sb[b / 2][nb][2 * (b % 2) + 1] = pack_bf16(x[2], x[3]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- records ---------------------------------------------------------------
+  using RedT = typename std::conditional<prefill_bf16_records(DK, true), uint16_t, float>::type;
+  const int nwp = a.ws.nwp;
+  RedT* rech = static_cast<RedT*>(a.ws.rec) + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * nwp * DV;
+  float* reczh = a.ws.recz + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * nwp;
+  const uint16_t* red = reinterpret_cast<const uint16_t*>(lds + C::O_RED);
+  const float* den = reinterpret_cast<const float*>(lds + C::O_DEN);
+
+  // Cross-wave sum of chunk ch's readout (bf16 partials in LDS; value units
+  // of 8 columns summed in fp32 with dot2, den in fp32), times 2^ew, into the
+  // records.  Red row rho = lr + 16 mb holds token 4 lr + (mb ^ (lr & 1)).
+  auto red_sum = [&](int ch) {
+    uint32_t lo_bits = 0x00003f80u, hi_bits = 0x3f800000u;
+    asm volatile("" : "+v"(lo_bits), "+v"(hi_bits));
+    const bf16x2 sel_lo = __builtin_bit_cast(bf16x2, lo_bits);
+    const bf16x2 sel_hi = __builtin_bit_cast(bf16x2, hi_bits);
+    const float sc = ldexpf(1.f, ew);
+    for (int e = tid; e < L * NU; e += NW * 64) {
+      const int rho = e / NU, u = e % NU;
+      const int t = 4 * (rho & 15) + ((rho >> 4) ^ (rho & 1));
+      const int off = rho * DV + 8 * (u ^ swz_row(rho) % NU);
+      float sum[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum[j] = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&red[ww * L * DV + off]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t xj = x[j];   // scalar copy: bit_cast of a vector element is miscompiled
+          const bf16x2 xx = __builtin_bit_cast(bf16x2, xj);
+          sum[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(xx, sel_lo, sum[2 * j], false);
+          sum[2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(xx, sel_hi, sum[2 * j + 1], false);
+        }
+      }
+      const int64_t ro = (static_cast<int64_t>(ch) * L + t) * DV + 8 * u;
+      if constexpr (std::is_same<RedT, uint16_t>::value) {
+        const u32x4 o = {pack_bf16(sum[0] * sc, sum[1] * sc), pack_bf16(sum[2] * sc, sum[3] * sc),
+                         pack_bf16(sum[4] * sc, sum[5] * sc), pack_bf16(sum[6] * sc, sum[7] * sc)};
+        *reinterpret_cast<u32x4*>(&rech[ro]) = o;
+      } else {
+        *reinterpret_cast<f32x4*>(&rech[ro]) = f32x4{sum[0], sum[1], sum[2], sum[3]} * sc;
+        *reinterpret_cast<f32x4*>(&rech[ro + 4]) = f32x4{sum[4], sum[5], sum[6], sum[7]} * sc;
+      }
+    }
+    // den: the last wave, one token per lane.
+    if (tid >= (NW - 1) * 64) {
+      const int t = l;
+      float sz = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) sz += den[ww * L + t];
+      reczh[static_cast<int64_t>(ch) * L + t] = sz * sc;
+    }
+  };
+
+  // Parent features of the order-2 parent slots of a chunk (buffer X).
+  auto slots = [&](int X) {
+    unsigned char* kt = lds + C::O_KT + X * C::KT_B;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (sod[i] != 0xffffffffu) {
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(kt + (so12[i] & 0xffffu));
+        const u32x4 x2 = *reinterpret_cast<const u32x4*>(kt + (so12[i] >> 16));
+        *reinterpret_cast<u32x4*>(kt + sod[i]) = mul8<H16>(x1, x2);
+      }
+    }
+  };
+
+  // Readout of chunk X's queries against Sb into the cross-wave buffer.
+  // MFMA: A = Sb^T (16 value columns x 32 rows), B = phi_q^T (32 rows x 16
+  // tokens), so lane (lr, g) gets token slot lr, columns 16 nb + 4 g + r.
+  // Token slot lr of token block mb is token 4 lr + (mb ^ (lr & 1)).
+  auto readout = [&](int X) {
+    const unsigned char* qt = lds + C::O_QT + X * C::QT_B;
+    const unsigned char* qn = lds + C::O_QN + X * C::QN_B;
+    uint16_t* redw = reinterpret_cast<uint16_t*>(lds + C::O_RED) + w * L * DV;
+    // Parent products for the lane's four tokens, in token-block order.
+    u32x2 pp[RB];
+    float pf[RB][4];
+    const bool odd = lr & 1;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const u32x2 x1 = *reinterpret_cast<const u32x2*>(qt + oq1[b]);
+      const u32x2 x2 = *reinterpret_cast<const u32x2*>(qt + oq2[b]);
+      if constexpr (H16) {
+        const f16x4 p = __builtin_bit_cast(f16x4, x1) * __builtin_bit_cast(f16x4, x2);
+        u32x2 pw = __builtin_bit_cast(u32x2, p);
+        // odd lanes: swap the tokens of each pair (token order mb ^ 1)
+        if (odd) {
+          pw[0] = __builtin_amdgcn_alignbit(pw[0], pw[0], 16);
+          pw[1] = __builtin_amdgcn_alignbit(pw[1], pw[1], 16);
+        }
+        pp[b] = pw;
+      } else {
+        float v[4] = {bf16_lo(x1[0]) * bf16_lo(x2[0]), bf16_hi(x1[0]) * bf16_hi(x2[0]),
+                      bf16_lo(x1[1]) * bf16_lo(x2[1]), bf16_hi(x1[1]) * bf16_hi(x2[1])};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pf[b][j] = odd ? v[j ^ 1] : v[j];
+      }
+    }
+    float dn[4] = {0.f, 0.f, 0.f, 0.f};
+    auto load_c = [&](int mb, int kk, u32x2 (&c)[2]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        c[h] = *reinterpret_cast<const u32x2*>(qn + (oqc[2 * kk + h] ^ (2 * DK * mb)));
+    };
+    auto build = [&](int mb, int kk, const u32x2 (&c)[2]) {
+      u32x4 B;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = 2 * kk + h;
+        if constexpr (H16) {
+          const uint32_t pw = pp[b][mb >> 1];   // scalar copy: bit_cast of a vector element is miscompiled
+          const _Float16 p = __builtin_bit_cast(f16x2, pw)[mb & 1];
+          const f16x4 x = __builtin_bit_cast(f16x4, c[h]) * p;
+          const u32x2 xw = __builtin_bit_cast(u32x2, x);
+          B[2 * h] = xw[0];
+          B[2 * h + 1] = xw[1];
+        } else {
+          const float p = pf[b][mb];
+          B[2 * h] = pack_bf16(bf16_lo(c[h][0]) * p, bf16_hi(c[h][0]) * p);
+          B[2 * h + 1] = pack_bf16(bf16_lo(c[h][1]) * p, bf16_hi(c[h][1]) * p);
+        }
+      }
+      return B;
+    };
+    constexpr int NST = 4 * NKS;
+    u32x2 cc[2];
+    load_c(0, 0, cc);
+    u32x4 Bcur = build(0, 0, cc);
+    if (NST > 1) load_c(1 / NKS, 1 % NKS, cc);
+    f32x4 acc[NB];
+#pragma unroll
+    for (int s_ = 0; s_ < NST; ++s_) {
+      const int mb = s_ / NKS, kk = s_ % NKS;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = mfma16<H16>(Sb[kk][nb], Bcur, kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb]);
+      u32x4 Bnext = Bcur;
+      if (s_ + 1 < NST) Bnext = build((s_ + 1) / NKS, (s_ + 1) % NKS, cc);
+      if (s_ + 2 < NST) load_c((s_ + 2) / NKS, (s_ + 2) % NKS, cc);
+      if (kk == NKS - 1) {
+        const int rho = lr + 16 * mb;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          if (16 * nb < DV && (16 * nb + 16 <= DV || 4 * g < DV % 16)) {
+            const int cu = 2 * nb + (g >> 1);
+            const u32x2 o = {pack_bf16(acc[nb][0], acc[nb][1]), pack_bf16(acc[nb][2], acc[nb][3])};
+            *reinterpret_cast<u32x2*>(&redw[rho * DV + 8 * (cu ^ (swz_row(rho) % NU)) + 4 * (g & 1)]) = o;
+          }
+        }
+        dn[mb] = acc[C::NB_DEN][C::R_DEN];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      Bcur = Bnext;
+    }
+    if (g == C::G_DEN) {
+      // tokens 4 lr + j, j = mb ^ (lr & 1)
+      const f32x4 o = odd ? f32x4{dn[1], dn[0], dn[3], dn[2]} : f32x4{dn[0], dn[1], dn[2], dn[3]};
+      *reinterpret_cast<f32x4*>(lds + C::O_DEN + (w * L + 4 * lr) * 4) = o;
+    }
+  };
+
+  // State update of chunk X: S += phi_k(K)^T [V 1].  A = key features (16
+  // rows x 32 tokens) = parent row x child row; B = V' (32 tokens x 16
+  // columns), the den block a constant.
+  auto update = [&](int X) {
+    const unsigned char* kt = lds + C::O_KT + X * C::KT_B;
+    const unsigned char* vt = lds + C::O_VT + X * C::VT_B;
+    constexpr int NST = 2 * RB;
+    auto load_k = [&](int st_, u32x4 (&d)[2]) {
+      const int kst = st_ / RB, b = st_ % RB;
+      d[0] = *reinterpret_cast<const u32x4*>(kt + (okp[b] ^ (64 * kst)));
+      d[1] = *reinterpret_cast<const u32x4*>(kt + (okc[b] ^ (64 * kst)));
+    };
+    u32x4 Bv[NB];
+    auto load_v = [&](int kst) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 16 * nb + lr;
+        const uint32_t cst = col == DV ? one2 & 0xffffu : 0u;   // den column: ones
+        if (16 * nb >= DV) {
+          const uint32_t c2 = cst | (cst << 16);
+          Bv[nb] = u32x4{c2, c2, c2, c2};
+        } else {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(vt + ((ovt ^ (64 * kst)) + 2048 * nb));
+          if (16 * nb + 16 <= DV) {
+            Bv[nb] = x;
+          } else {
+            const uint32_t c2 = cst | (cst << 16);
+            Bv[nb] = col < DV ? x : u32x4{c2, c2, c2, c2};
+          }
+        }
+      }
+    };
+    u32x4 dk[2];
+    load_k(0, dk);
+    u32x4 Acur = mul8<H16>(dk[0], dk[1]);
+    if (NST > 1) load_k(1, dk);
+#pragma unroll
+    for (int st_ = 0; st_ < NST; ++st_) {
+      const int kst = st_ / RB, b = st_ % RB;
+      if (b == 0) load_v(kst);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) S[b][nb] = mfma16<H16>(Acur, Bv[nb], S[b][nb]);
+      u32x4 Anext = Acur;
+      if (st_ + 1 < NST) Anext = mul8<H16>(dk[0], dk[1]);
+      if (st_ + 2 < NST) load_k(st_ + 2, dk);
+      __builtin_amdgcn_sched_barrier(0);
+      Acur = Anext;
+    }
+  };
+
+  // ---- prologue: chunk 0 in buffer 0, its parent slots, the first Sb -------
+  if (nch > 0) dma(0, 0);
+  post_max();
+  dma_barrier();
+  slots(0);
+  refresh();
+  lds_barrier();
+
+  // ---- chunks -------------------------------------------------------------------
+  for (int ch = 0; ch < nch; ++ch) {
+    const int X = ch & 1;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(okp[b]), "+v"(okc[b]));
+    // segment 1: prefetch the next chunk, read out this one
+    if (ch + 1 < nch) dma(ch + 1, X ^ 1);
+    if (ch > 0 && ch % C::SC == 0) refresh();
+    readout(X);
+    dma_barrier();
+    // segment 2: records of this chunk, parent slots of the next, update
+    auto side = [&]() {
+      red_sum(ch);
+      if (ch + 1 < nch) slots(X ^ 1);
+    };
+    if (w < NW / 2) {
+      update(X);
+      side();
+    } else {
+      side();
+      update(X);
+    }
+    if (ch % C::SC == C::SC - 1 && ch + 1 < nch) post_max();
+    lds_barrier();
+  }
+
+  // ---- state tile back (f16 path: unscaled) --------------------------------------
+  const uint32_t* rowinfo = a.lay.rowinfo;
+  float* stw = st;
+  asm volatile("" : "+s"(rowinfo), "+s"(stw));
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t info = rowinfo[(lay_base + b) * 16 + 4 * g + r];
+      if (info) {
+        const int64_t m = static_cast<int64_t>(info) - 1;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = nb * 16 + lr;
+          float val = S[b][nb][r];
+          if constexpr (H16) val = ldexpf(val, row_exp(m, col < DV));
+          if (col < DV) stw[m * DV + col] = val;
+          else if (col == DV) stw[zoff + m] = val;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// out = (intra + sum over tiles of the records + carry) for num / for den,
+// summed in a fixed order.  Block = (64 tokens, head); value items of 8
+// columns, den per token first.
+template <int DK>
+__global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
+  constexpr int DV = DK, DVP = padded_dv(DV), T = prefill_window(true), NU = DV / 8, TB = 64;
+  using RedT = typename std::conditional<prefill_bf16_records(DK, true), uint16_t, float>::type;
+  __shared__ float dsh[TB];
+  const int head = blockIdx.y;
+  const int t0 = blockIdx.x * TB;
+  const int tid = threadIdx.x;
+  const int nwp = a.ws.nwp;
+  const int nt = a.n_tiles;
+  const int ntok = min(TB, a.nw - t0);
+  const HalfScales hs = head_scales(a.ws, head);
+  const float rscale = hs.safe ? ldexpf(1.f, hs.ev) : 1.f;   // value-column records carry 2^-ev
+  const float* intra = a.ws.intra + static_cast<int64_t>(head) * nwp * DVP;
+  const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + T - 1) / T) * DVP;
+  if (tid < TB) {
+    const int t = t0 + tid;
+    float s = 0.f;
+    if (tid < ntok) {
+      const float* rz = a.ws.recz + static_cast<int64_t>(head) * nt * nwp + t;
+      for (int tl = 0; tl < nt; ++tl) s += rz[static_cast<int64_t>(tl) * nwp];
+      s += intra[static_cast<int64_t>(t) * DVP + DV];
+      s += carry[(t / T) * DVP + DV];
+    }
+    dsh[tid] = s;
+  }
+  __syncthreads();
+  const RedT* rec = static_cast<const RedT*>(a.ws.rec) + static_cast<int64_t>(head) * nt * nwp * DV;
+  float* out = a.out + (static_cast<int64_t>(head) * a.n_total + a.t0) * DV;
+  for (int e = tid; e < ntok * NU; e += 256) {
+    const int tt = e / NU, u = e % NU;
+    const int t = t0 + tt;
+    float r[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = 0.f;
+    const RedT* rp = rec + static_cast<int64_t>(t) * DV + 8 * u;
+    for (int tl = 0; tl < nt; ++tl) {
+      if constexpr (std::is_same<RedT, uint16_t>::value) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(rp + static_cast<int64_t>(tl) * nwp * DV);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[2 * j] += bf16_lo(x[j]);
+          r[2 * j + 1] += bf16_hi(x[j]);
+        }
+      } else {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(rp + static_cast<int64_t>(tl) * nwp * DV);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(rp + static_cast<int64_t>(tl) * nwp * DV + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[j] += x0[j];
+          r[4 + j] += x1[j];
+        }
+      }
+    }
+    const float* ip = intra + static_cast<int64_t>(t) * DVP + 8 * u;
+    const float* cp = carry + (t / T) * DVP + 8 * u;
+    const float dinv = 1.f / dsh[tt];
+    f32x4 o0, o1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o0[j] = (ip[j] + r[j] * rscale + cp[j]) * dinv;
+      o1[j] = (ip[4 + j] + r[4 + j] * rscale + cp[4 + j]) * dinv;
+    }
+    *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(t) * DV + 8 * u) = o0;
+    *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(t) * DV + 8 * u + 4) = o1;
+  }
+}
+
+template <int D>
+hipError_t launch_b16_t(int BH, const ScanArgs& a, hipStream_t s) {
+  const int nch = (a.nw + kL - 1) / kL;
+  prefill_amax<D><<<dim3(kAmaxSplit, BH), 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prefill_stage<D><<<dim3(nch, BH), 256, 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prefill_carry<D><<<BH, 128, 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // Both operand types: each head is scanned by the one its scales select;
+  // the other returns at once.
+  const dim3 grid(a.lay.n_tiles, BH);
+  prefill_scan_b16<D, true><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prefill_scan_b16<D, false><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_reduce_b16_t(int BH, const ReduceArgs& a, hipStream_t s) {
+  prefill_reduce_b16<D><<<dim3((a.nw + 63) / 64, BH), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_b16(int d, int BH, const ScanArgs& a, hipStream_t s) {
+  switch (d) {
+    case 8: return launch_b16_t<8>(BH, a, s);
+    case 16: return launch_b16_t<16>(BH, a, s);
+    case 32: return launch_b16_t<32>(BH, a, s);
+    case 64: return launch_b16_t<64>(BH, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_reduce_b16(int d, int BH, const ReduceArgs& a, hipStream_t s) {
+  switch (d) {
+    case 8: return launch_reduce_b16_t<8>(BH, a, s);
+    case 16: return launch_reduce_b16_t<16>(BH, a, s);
+    case 32: return launch_reduce_b16_t<32>(BH, a, s);
+    case 64: return launch_reduce_b16_t<64>(BH, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sata
