@@ -79,6 +79,23 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+// Max over the wave (DPP: prefix maxima within rows of 16, then across rows;
+// lane 63 ends with the total).
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false);
+  return fmaxf(x, __int_as_float(y));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = dpp_max<0x111>(x);   // row_shr:1
+  x = dpp_max<0x112>(x);   // row_shr:2
+  x = dpp_max<0x114>(x);   // row_shr:4
+  x = dpp_max<0x118>(x);   // row_shr:8
+  x = dpp_max<0x142>(x);   // row_bcast:15
+  x = dpp_max<0x143>(x);   // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // 16 bytes a lane from global memory straight into LDS (lane l writes bytes
 // [16 l, 16 l + 16) after the wave-uniform LDS address).
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
@@ -394,24 +411,24 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
   // Update: KT byte offsets of the parent and child rows of lane row lr in
   // block b, for the 8-token unit g of the first 32 tokens (the second 32
   // tokens: offset ^ 64).
-  uint32_t okp[RB], okc[RB];
+  uint32_t okpc[RB];   // parent offset | child offset << 16
   // Readout: QT byte offsets of the two parent coordinates of the run of
   // lane group g in block b at tokens 4 lr .. 4 lr + 3, and the QN byte
-  // offset of its four children for token block 0 (token block mb: ^ 2 DK mb).
-  uint32_t oq1[RB], oq2[RB], oqc[RB];
+  // offset of its four children for token block 0 (token block mb: + 2 DK mb).
+  uint32_t oq12[RB], oqc[RB];   // oq12: first | second coordinate offset << 16
   {
     const int sq = (lr ^ (lr >> 3)) & (NU - 1);
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       const uint32_t ks = a.lay.kside[(lay_base + b) * 16 + lr];
       const int pr = ks & 0xffff, cr = ks >> 16;
-      okp[b] = pr * 128 + 16 * (g ^ swz_row(pr));
-      okc[b] = cr * 128 + 16 * (g ^ swz_row(cr));
+      okpc[b] = static_cast<uint32_t>(pr * 128 + 16 * (g ^ swz_row(pr))) |
+                (static_cast<uint32_t>(cr * 128 + 16 * (g ^ swz_row(cr))) << 16);
       const uint32_t qs = a.lay.qside[(lay_base + b) * 4 + g];
       const int i1 = qs & 255, i2 = (qs >> 8) & 255, c0 = (qs >> 16) & 255;
-      oq1[b] = i1 * 128 + 16 * ((lr >> 1) ^ swz_row(i1)) + 8 * (lr & 1);
-      oq2[b] = i2 * 128 + 16 * ((lr >> 1) ^ swz_row(i2)) + 8 * (lr & 1);
-      oqc[b] = (4 * lr * 2 * DK + 16 * ((c0 >> 3) ^ sq) + 8 * ((c0 >> 2) & 1)) ^ (2 * DK * (lr & 1));
+      oq12[b] = static_cast<uint32_t>(i1 * 128 + 16 * ((lr >> 1) ^ swz_row(i1)) + 8 * (lr & 1)) |
+                (static_cast<uint32_t>(i2 * 128 + 16 * ((lr >> 1) ^ swz_row(i2)) + 8 * (lr & 1)) << 16);
+      oqc[b] = 4 * lr * 2 * DK + 16 * ((c0 >> 3) ^ sq) + 8 * ((c0 >> 2) & 1);
     }
   }
   // Update, values: VT byte offset of row lr (column block 0), unit g; the
@@ -437,7 +454,7 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
   // DMA: this wave's blocks of a chunk record: global byte offset per lane,
   // LDS destination per block (buffer 0; buffer 1 adds the table size).
   uint32_t gofs[C::NDMA];
-  int ldst[C::NDMA], lstep[C::NDMA];
+  int ldst[C::NDMA], lstep[C::NDMA];   // wave-uniform
 #pragma unroll
   for (int i = 0; i < C::NDMA; ++i) {
     const int beta = w + NW * i;
@@ -455,18 +472,21 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
         gofs[i] = 3 * DK * 128 + (t * NU + (q ^ swz_tok<NU>(t))) * 16;
       }
       const int base = tau == 0 ? C::O_KT : tau == 1 ? C::O_VT : tau == 2 ? C::O_QT : C::O_QN;
-      lstep[i] = tau == 0 ? C::KT_B : tau == 1 ? C::VT_B : tau == 2 ? C::QT_B : C::QN_B;
-      ldst[i] = base + 1024 * bb;
+      lstep[i] = __builtin_amdgcn_readfirstlane(tau == 0 ? C::KT_B : tau == 1 ? C::VT_B : tau == 2 ? C::QT_B : C::QN_B);
+      ldst[i] = __builtin_amdgcn_readfirstlane(base + 1024 * bb);
     }
   }
   const unsigned char* stg = reinterpret_cast<const unsigned char*>(a.ws.stg) +
                              static_cast<int64_t>(head) * nchp * (8 * DK * L);
+  // Block i of this wave's share of chunk ch into buffer X.
+  auto dma_one = [&](int i, int ch, int X) {
+    if (ldst[i] >= 0)
+      dma16(stg + static_cast<int64_t>(ch) * (8 * DK * L) + gofs[i],
+            lds + __builtin_amdgcn_readfirstlane(ldst[i] + X * lstep[i]));
+  };
   auto dma = [&](int ch, int X) {
-    const unsigned char* src = stg + static_cast<int64_t>(ch) * (8 * DK * L);
 #pragma unroll
-    for (int i = 0; i < C::NDMA; ++i)
-      if (ldst[i] >= 0)
-        dma16(src + gofs[i], lds + __builtin_amdgcn_readfirstlane(ldst[i] + X * lstep[i]));
+    for (int i = 0; i < C::NDMA; ++i) dma_one(i, ch, X);
   };
 
   // ---- state tile into registers (C layout: lane holds column 16 nb + lr of
@@ -523,9 +543,7 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(S[b][nb][r]));
-      mx *= wlmax;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      mx = wave_max(mx * wlmax);
       if (l == 0) wmx[w] = mx;
     }
   };
@@ -566,51 +584,58 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
   float* reczh = a.ws.recz + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * nwp;
   const uint16_t* red = reinterpret_cast<const uint16_t*>(lds + C::O_RED);
   const float* den = reinterpret_cast<const float*>(lds + C::O_DEN);
+  // Two stacked 16 x 16 identities as an MFMA A operand: lane (lr, g) holds
+  // row lr, K = 8 g .. 8 g + 7; entry 1 where K % 16 == lr.
+  bf16x8 eye2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) eye2[j] = static_cast<__bf16>(8 * (g & 1) + j == lr ? 1.f : 0.f);
 
-  // Cross-wave sum of chunk ch's readout (bf16 partials in LDS; value units
-  // of 8 columns summed in fp32 with dot2, den in fp32), times 2^ew, into the
-  // records.  Red row rho = lr + 16 mb holds token 4 lr + (mb ^ (lr & 1)).
+  // Cross-wave sum of chunk ch's readout, times 2^ew, into the records.
+  // Value columns on MFMA: for a block of 16 tokens x 16 columns,
+  //   sum_w P_w^T = sum over wave pairs p of [I I] [P_2p; P_2p+1]^T,
+  // A = two stacked 16 x 16 identities, B = the bf16 partials of two waves
+  // (K = wave x column); D^T gives lane (lr, g) token slot lr, columns
+  // 4 g + r.  Red row rho = lr + 16 mb holds token 4 lr + mb.  den: fp32
+  // partials summed by the last wave, one token per lane.
+  constexpr int NCB = (DV + 15) / 16;        // 16-column blocks of values
+  constexpr int NITEM = 4 * NCB;             // (token block, column block)
+  constexpr int NIW = (NITEM + NW - 1) / NW; // items per wave
   auto red_sum = [&](int ch) {
-    uint32_t lo_bits = 0x00003f80u, hi_bits = 0x3f800000u;
-    asm volatile("" : "+v"(lo_bits), "+v"(hi_bits));
-    const bf16x2 sel_lo = __builtin_bit_cast(bf16x2, lo_bits);
-    const bf16x2 sel_hi = __builtin_bit_cast(bf16x2, hi_bits);
     const float sc = ldexpf(1.f, ew);
-    for (int e = tid; e < L * NU; e += NW * 64) {
-      const int rho = e / NU, u = e % NU;
-      const int t = 4 * (rho & 15) + ((rho >> 4) ^ (rho & 1));
-      const int off = rho * DV + 8 * (u ^ swz_row(rho) % NU);
-      float sum[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum[j] = 0.f;
+    for (int i = 0; i < NIW; ++i) {
+      const int item = w + NW * i;
+      if (item < NITEM) {
+        const int tb = item / NCB, cb = item % NCB;
+        const int rho = 16 * tb + lr;
+        const int unit = 2 * cb + (g & 1);
+        f32x4 D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(&red[ww * L * DV + off]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t xj = x[j];   // scalar copy: bit_cast of a vector element is miscompiled
-          const bf16x2 xx = __builtin_bit_cast(bf16x2, xj);
-          sum[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(xx, sel_lo, sum[2 * j], false);
-          sum[2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(xx, sel_hi, sum[2 * j + 1], false);
+        for (int pq = 0; pq < NW / 2; ++pq) {
+          const int ww = 2 * pq + (g >> 1);
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (DV >= 16 || (g & 1) == 0)
+            x = *reinterpret_cast<const u32x4*>(&red[ww * L * DV + rho * DV + 8 * (unit ^ (swz_row(rho) % NU))]);
+          D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eye2, __builtin_bit_cast(bf16x8, x), D, 0, 0, 0);
+        }
+        const int t = 4 * lr + tb;
+        const int col = 16 * cb + 4 * g;
+        if (col < DV) {
+          const int64_t ro = (static_cast<int64_t>(ch) * L + t) * DV + col;
+          if constexpr (std::is_same<RedT, uint16_t>::value) {
+            const u32x2 o = {pack_bf16(D[0] * sc, D[1] * sc), pack_bf16(D[2] * sc, D[3] * sc)};
+            *reinterpret_cast<u32x2*>(&rech[ro]) = o;
+          } else {
+            *reinterpret_cast<f32x4*>(&rech[ro]) = D * sc;
+          }
         }
       }
-      const int64_t ro = (static_cast<int64_t>(ch) * L + t) * DV + 8 * u;
-      if constexpr (std::is_same<RedT, uint16_t>::value) {
-        const u32x4 o = {pack_bf16(sum[0] * sc, sum[1] * sc), pack_bf16(sum[2] * sc, sum[3] * sc),
-                         pack_bf16(sum[4] * sc, sum[5] * sc), pack_bf16(sum[6] * sc, sum[7] * sc)};
-        *reinterpret_cast<u32x4*>(&rech[ro]) = o;
-      } else {
-        *reinterpret_cast<f32x4*>(&rech[ro]) = f32x4{sum[0], sum[1], sum[2], sum[3]} * sc;
-        *reinterpret_cast<f32x4*>(&rech[ro + 4]) = f32x4{sum[4], sum[5], sum[6], sum[7]} * sc;
-      }
     }
-    // den: the last wave, one token per lane.
     if (tid >= (NW - 1) * 64) {
-      const int t = l;
       float sz = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) sz += den[ww * L + t];
-      reczh[static_cast<int64_t>(ch) * L + t] = sz * sc;
+      for (int ww = 0; ww < NW; ++ww) sz += den[ww * L + l];
+      reczh[static_cast<int64_t>(ch) * L + l] = sz * sc;
     }
   };
 
@@ -630,40 +655,33 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
   // Readout of chunk X's queries against Sb into the cross-wave buffer.
   // MFMA: A = Sb^T (16 value columns x 32 rows), B = phi_q^T (32 rows x 16
   // tokens), so lane (lr, g) gets token slot lr, columns 16 nb + 4 g + r.
-  // Token slot lr of token block mb is token 4 lr + (mb ^ (lr & 1)).
-  auto readout = [&](int X) {
+  // Token slot lr of token block mb is token 4 lr + mb.
+  auto readout = [&](int X, auto&& hook) {
     const unsigned char* qt = lds + C::O_QT + X * C::QT_B;
     const unsigned char* qn = lds + C::O_QN + X * C::QN_B;
     uint16_t* redw = reinterpret_cast<uint16_t*>(lds + C::O_RED) + w * L * DV;
-    // Parent products for the lane's four tokens, in token-block order.
+    // Parent products for the lane's four tokens (token block mb = element mb).
     u32x2 pp[RB];
     float pf[RB][4];
-    const bool odd = lr & 1;
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      const u32x2 x1 = *reinterpret_cast<const u32x2*>(qt + oq1[b]);
-      const u32x2 x2 = *reinterpret_cast<const u32x2*>(qt + oq2[b]);
+      const u32x2 x1 = *reinterpret_cast<const u32x2*>(qt + (oq12[b] & 0xffffu));
+      const u32x2 x2 = *reinterpret_cast<const u32x2*>(qt + (oq12[b] >> 16));
       if constexpr (H16) {
         const f16x4 p = __builtin_bit_cast(f16x4, x1) * __builtin_bit_cast(f16x4, x2);
-        u32x2 pw = __builtin_bit_cast(u32x2, p);
-        // odd lanes: swap the tokens of each pair (token order mb ^ 1)
-        if (odd) {
-          pw[0] = __builtin_amdgcn_alignbit(pw[0], pw[0], 16);
-          pw[1] = __builtin_amdgcn_alignbit(pw[1], pw[1], 16);
-        }
-        pp[b] = pw;
+        pp[b] = __builtin_bit_cast(u32x2, p);
       } else {
         float v[4] = {bf16_lo(x1[0]) * bf16_lo(x2[0]), bf16_hi(x1[0]) * bf16_hi(x2[0]),
                       bf16_lo(x1[1]) * bf16_lo(x2[1]), bf16_hi(x1[1]) * bf16_hi(x2[1])};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pf[b][j] = odd ? v[j ^ 1] : v[j];
+        for (int j = 0; j < 4; ++j) pf[b][j] = v[j];
       }
     }
     float dn[4] = {0.f, 0.f, 0.f, 0.f};
     auto load_c = [&](int mb, int kk, u32x2 (&c)[2]) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        c[h] = *reinterpret_cast<const u32x2*>(qn + (oqc[2 * kk + h] ^ (2 * DK * mb)));
+        c[h] = *reinterpret_cast<const u32x2*>(qn + oqc[2 * kk + h] + 2 * DK * mb);
     };
     auto build = [&](int mb, int kk, const u32x2 (&c)[2]) {
       u32x4 B;
@@ -694,6 +712,7 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
 #pragma unroll
     for (int s_ = 0; s_ < NST; ++s_) {
       const int mb = s_ / NKS, kk = s_ % NKS;
+      hook(s_);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         acc[nb] = mfma16<H16>(Sb[kk][nb], Bcur, kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb]);
@@ -715,24 +734,21 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
       __builtin_amdgcn_sched_barrier(0);
       Bcur = Bnext;
     }
-    if (g == C::G_DEN) {
-      // tokens 4 lr + j, j = mb ^ (lr & 1)
-      const f32x4 o = odd ? f32x4{dn[1], dn[0], dn[3], dn[2]} : f32x4{dn[0], dn[1], dn[2], dn[3]};
-      *reinterpret_cast<f32x4*>(lds + C::O_DEN + (w * L + 4 * lr) * 4) = o;
-    }
+    if (g == C::G_DEN)   // tokens 4 lr + mb
+      *reinterpret_cast<f32x4*>(lds + C::O_DEN + (w * L + 4 * lr) * 4) = f32x4{dn[0], dn[1], dn[2], dn[3]};
   };
 
   // State update of chunk X: S += phi_k(K)^T [V 1].  A = key features (16
   // rows x 32 tokens) = parent row x child row; B = V' (32 tokens x 16
   // columns), the den block a constant.
-  auto update = [&](int X) {
+  auto update = [&](int X, auto&& hook) {
     const unsigned char* kt = lds + C::O_KT + X * C::KT_B;
     const unsigned char* vt = lds + C::O_VT + X * C::VT_B;
     constexpr int NST = 2 * RB;
     auto load_k = [&](int st_, u32x4 (&d)[2]) {
       const int kst = st_ / RB, b = st_ % RB;
-      d[0] = *reinterpret_cast<const u32x4*>(kt + (okp[b] ^ (64 * kst)));
-      d[1] = *reinterpret_cast<const u32x4*>(kt + (okc[b] ^ (64 * kst)));
+      d[0] = *reinterpret_cast<const u32x4*>(kt + ((okpc[b] & 0xffffu) ^ (64 * kst)));
+      d[1] = *reinterpret_cast<const u32x4*>(kt + ((okpc[b] >> 16) ^ (64 * kst)));
     };
     u32x4 Bv[NB];
     auto load_v = [&](int kst) {
@@ -761,6 +777,7 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
 #pragma unroll
     for (int st_ = 0; st_ < NST; ++st_) {
       const int kst = st_ / RB, b = st_ % RB;
+      hook(st_);
       if (b == 0) load_v(kst);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) S[b][nb] = mfma16<H16>(Acur, Bv[nb], S[b][nb]);
@@ -784,23 +801,27 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
   for (int ch = 0; ch < nch; ++ch) {
     const int X = ch & 1;
 #pragma unroll
-    for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(okp[b]), "+v"(okc[b]));
-    // segment 1: prefetch the next chunk, read out this one
-    if (ch + 1 < nch) dma(ch + 1, X ^ 1);
+    for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(okpc[b]));
+    // segment 1: read out this chunk; the next chunk's DMA goes out one
+    // block per readout step
     if (ch > 0 && ch % C::SC == 0) refresh();
-    readout(X);
+    readout(X, [&](int step) {
+      if (step < C::NDMA && ch + 1 < nch) dma_one(step, ch + 1, X ^ 1);
+    });
     dma_barrier();
-    // segment 2: records of this chunk, parent slots of the next, update
+    // segment 2: records of this chunk, parent slots of the next, update;
+    // the two waves sharing a SIMD take these in opposite orders
     auto side = [&]() {
       red_sum(ch);
       if (ch + 1 < nch) slots(X ^ 1);
     };
+    auto none = [&](int) {};
     if (w < NW / 2) {
-      update(X);
+      update(X, none);
       side();
     } else {
       side();
-      update(X);
+      update(X, none);
     }
     if (ch % C::SC == C::SC - 1 && ch + 1 < nch) post_max();
     lds_barrier();
