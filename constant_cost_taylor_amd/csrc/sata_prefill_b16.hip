@@ -364,18 +364,16 @@ __device__ __forceinline__ u32x4 mul8(u32x4 x, u32x4 y) {
   }
 }
 
+// One head-tile of the scan with one operand type (the kernel below picks it
+// per head).
 template <int DK, bool H16>
-__global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(ScanArgs a) {
+__device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& hs, unsigned char* lds) {
   using C = CfgS<DK>;
   constexpr int DV = C::DV, L = C::L, NW = C::NW, RB = C::RB, NKS = C::NKS, NB = C::NB, NU = C::NU;
   constexpr int NSLOT = C::NSLOT;
 
   const int tile = blockIdx.x;
   const int head = blockIdx.y;
-  const HalfScales hs = head_scales(a.ws, head);
-  if (hs.safe != H16) return;   // the other operand type scans this head
-
-  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_B];
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
@@ -852,6 +850,16 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
   }
 }
 
+template <int DK>
+__global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(ScanArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[CfgS<DK>::LDS_B];
+  const HalfScales hs = head_scales(a.ws, blockIdx.y);
+  if (hs.safe)
+    scan_tile<DK, true>(a, hs, lds);
+  else
+    scan_tile<DK, false>(a, hs, lds);
+}
+
 // ---------------------------------------------------------------------------
 // out = (intra + sum over tiles of the records + carry) for num / for den,
 // summed in a fixed order.  Block = (64 tokens, head); value items of 8
@@ -934,12 +942,8 @@ hipError_t launch_b16_t(int BH, const ScanArgs& a, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prefill_carry<D><<<BH, 128, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // Both operand types: each head is scanned by the one its scales select;
-  // the other returns at once.
   const dim3 grid(a.lay.n_tiles, BH);
-  prefill_scan_b16<D, true><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  prefill_scan_b16<D, false><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
+  prefill_scan_b16<D><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
