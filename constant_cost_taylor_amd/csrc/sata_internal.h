@@ -46,7 +46,8 @@ constexpr int prefill_rb(int d, bool bf16) {
 // tile (the per-chunk parent-feature tables are sized by it).
 constexpr int prefill_runs_per_tile(int d, bool bf16) { return 4 * prefill_rb(d, bf16) * prefill_waves(bf16); }
 constexpr int prefill_slots(int d, bool bf16) {
-  return prefill_runs_per_tile(d, bf16) < 80 ? prefill_runs_per_tile(d, bf16) : 80;
+  // bf16 scan: 64 slots x 8 token groups = one item per thread of its 512
+  return prefill_runs_per_tile(d, bf16) < (bf16 ? 64 : 80) ? prefill_runs_per_tile(d, bf16) : (bf16 ? 64 : 80);
 }
 
 // LDS row stride (floats) of the key / parent-feature tables.

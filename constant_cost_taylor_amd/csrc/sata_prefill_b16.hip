@@ -432,11 +432,12 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   // Update, values: VT byte offset of row lr (column block 0), unit g; the
   // rows of block nb are 2048 nb bytes further.
   const uint32_t ovt = (DV >= 16 ? lr : (lr & (DV - 1))) * 128 + 16 * (g ^ swz_row(lr));
-  // Parent slots: up to two items (slot, 8-token unit) per thread.
+  // Parent slots: items (slot, 8-token unit), at most one per thread.
+  constexpr int NSI = (NSLOT * 8 + NW * 64 - 1) / (NW * 64);
   const int nslot = a.lay.nslot[tile];
-  uint32_t so12[2], sod[2];
+  uint32_t so12[NSI], sod[NSI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NSI; ++i) {
     const int e = tid + i * NW * 64;
     sod[i] = 0xffffffffu;
     so12[i] = 0u;
@@ -641,7 +642,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   auto slots = [&](int X) {
     unsigned char* kt = lds + C::O_KT + X * C::KT_B;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NSI; ++i) {
       if (sod[i] != 0xffffffffu) {
         const u32x4 x1 = *reinterpret_cast<const u32x4*>(kt + (so12[i] & 0xffffu));
         const u32x4 x2 = *reinterpret_cast<const u32x4*>(kt + (so12[i] >> 16));
