@@ -338,6 +338,9 @@ struct CfgS {
 __device__ __forceinline__ int swz_row(int row) { return (row >> 1) & 7; }
 template <int NU>
 __device__ __forceinline__ int swz_tok(int t) { return ((t >> 2) ^ (t >> 5)) & (NU - 1); }
+// Cross-wave buffer row rho (d >= 32): 16-byte unit u at u ^ ((rho ^ (rho >> 3)) & (DV/8 - 1)).
+template <int NU>
+__device__ __forceinline__ int swz_red(int rho) { return (rho ^ (rho >> 3)) & (NU - 1); }
 
 template <bool H16>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -370,6 +373,9 @@ template <int DK, bool H16>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& hs, unsigned char* lds) {
   using C = CfgS<DK>;
   constexpr int DV = C::DV, L = C::L, NW = C::NW, RB = C::RB, NKS = C::NKS, NB = C::NB, NU = C::NU;
+  // d >= 32: a cross-wave buffer unit holds four columns of two adjacent
+  // column blocks (one 16-byte write per block pair)
+  constexpr bool PAIRED = DV >= 32;
   constexpr int NSLOT = C::NSLOT;
 
   const int tile = blockIdx.x;
@@ -412,8 +418,13 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   uint32_t okpc[RB];   // parent offset | child offset << 16
   // Readout: QT byte offsets of the two parent coordinates of the run of
   // lane group g in block b at tokens 4 lr .. 4 lr + 3, and the QN byte
-  // offset of its four children for token block 0 (token block mb: + 2 DK mb).
+  // offset of its four children for token block 0 (block mb: + 2 DK mb, odd
+  // blocks also - d4).
   uint32_t oq12[RB], oqc[RB];   // oq12: first | second coordinate offset << 16
+  // Token slot lr of token block mb is token 4 lr + (mb ^ (lr & 1)) (rows of
+  // both parities in every QN load); QN offsets of odd blocks are d4 lower.
+  const bool odd = lr & 1;
+  const uint32_t d4 = odd ? 2 * 2 * DK : 0;   // two token rows
   {
     const int sq = (lr ^ (lr >> 3)) & (NU - 1);
 #pragma unroll
@@ -426,7 +437,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       const int i1 = qs & 255, i2 = (qs >> 8) & 255, c0 = (qs >> 16) & 255;
       oq12[b] = static_cast<uint32_t>(i1 * 128 + 16 * ((lr >> 1) ^ swz_row(i1)) + 8 * (lr & 1)) |
                 (static_cast<uint32_t>(i2 * 128 + 16 * ((lr >> 1) ^ swz_row(i2)) + 8 * (lr & 1)) << 16);
-      oqc[b] = 4 * lr * 2 * DK + 16 * ((c0 >> 3) ^ sq) + 8 * ((c0 >> 2) & 1);
+      oqc[b] = (4 * lr + (odd ? 1 : 0)) * 2 * DK + 16 * ((c0 >> 3) ^ sq) + 8 * ((c0 >> 2) & 1);
     }
   }
   // Update, values: VT byte offset of row lr (column block 0), unit g; the
@@ -452,12 +463,13 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   }
   // DMA: this wave's blocks of a chunk record: global byte offset per lane,
   // LDS destination per block (buffer 0; buffer 1 adds the table size).
-  uint32_t gofs[C::NDMA];
+  uint32_t gofs[(C::NDMA + 1) / 2];       // two 16-bit offsets a register
   int ldst[C::NDMA], lstep[C::NDMA];   // wave-uniform
+#pragma unroll
+  for (int i = 0; i < (C::NDMA + 1) / 2; ++i) gofs[i] = 0u;
 #pragma unroll
   for (int i = 0; i < C::NDMA; ++i) {
     const int beta = w + NW * i;
-    gofs[i] = 0u;
     ldst[i] = -1;
     lstep[i] = 0;
     if (beta < C::NBLK) {
@@ -465,10 +477,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       const int p = 64 * bb + l;   // 16-byte unit of the table
       if (tau < 3) {
         const int row = p >> 3, q = p & 7;
-        gofs[i] = tau * DK * 128 + (row * 8 + (q ^ swz_row(row))) * 16;
+        gofs[i / 2] |= static_cast<uint32_t>(tau * DK * 128 + (row * 8 + (q ^ swz_row(row))) * 16) << (16 * (i & 1));
       } else {
         const int t = p / NU, q = p % NU;
-        gofs[i] = 3 * DK * 128 + (t * NU + (q ^ swz_tok<NU>(t))) * 16;
+        gofs[i / 2] |= static_cast<uint32_t>(3 * DK * 128 + (t * NU + (q ^ swz_tok<NU>(t))) * 16) << (16 * (i & 1));
       }
       const int base = tau == 0 ? C::O_KT : tau == 1 ? C::O_VT : tau == 2 ? C::O_QT : C::O_QN;
       lstep[i] = __builtin_amdgcn_readfirstlane(tau == 0 ? C::KT_B : tau == 1 ? C::VT_B : tau == 2 ? C::QT_B : C::QN_B);
@@ -480,7 +492,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   // Block i of this wave's share of chunk ch into buffer X.
   auto dma_one = [&](int i, int ch, int X) {
     if (ldst[i] >= 0)
-      dma16(stg + static_cast<int64_t>(ch) * (8 * DK * L) + gofs[i],
+      dma16(stg + static_cast<int64_t>(ch) * (8 * DK * L) + ((gofs[i / 2] >> (16 * (i & 1))) & 0xffffu),
             lds + __builtin_amdgcn_readfirstlane(ldst[i] + X * lstep[i]));
   };
   auto dma = [&](int ch, int X) {
@@ -584,23 +596,28 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   const uint16_t* red = reinterpret_cast<const uint16_t*>(lds + C::O_RED);
   const float* den = reinterpret_cast<const float*>(lds + C::O_DEN);
   // Two stacked 16 x 16 identities as an MFMA A operand: lane (lr, g) holds
-  // row lr, K = 8 g .. 8 g + 7; entry 1 where K % 16 == lr.
-  bf16x8 eye2;
+  // row lr, K = 8 g .. 8 g + 7; entry 1 where K % 16 == lr (built at use).
+  auto eye2 = [&]() {
+    bf16x8 e;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) eye2[j] = static_cast<__bf16>(8 * (g & 1) + j == lr ? 1.f : 0.f);
+    for (int j = 0; j < 8; ++j) e[j] = static_cast<__bf16>(8 * (g & 1) + j == lr ? 1.f : 0.f);
+    return e;
+  };
 
   // Cross-wave sum of chunk ch's readout, times 2^ew, into the records.
-  // Value columns on MFMA: for a block of 16 tokens x 16 columns,
+  // Value columns on MFMA: for a block of 16 tokens x 16 buffer positions,
   //   sum_w P_w^T = sum over wave pairs p of [I I] [P_2p; P_2p+1]^T,
   // A = two stacked 16 x 16 identities, B = the bf16 partials of two waves
-  // (K = wave x column); D^T gives lane (lr, g) token slot lr, columns
-  // 4 g + r.  Red row rho = lr + 16 mb holds token 4 lr + mb.  den: fp32
-  // partials summed by the last wave, one token per lane.
-  constexpr int NCB = (DV + 15) / 16;        // 16-column blocks of values
-  constexpr int NITEM = 4 * NCB;             // (token block, column block)
+  // (K = wave x position); D^T gives lane (lr, g) token slot lr, positions
+  // 4 g + r (four consecutive columns).  Red row rho = lr + 16 mb holds token
+  // 4 lr + (mb ^ (lr & 1)).  den: fp32 partials summed by the last wave, one
+  // token per lane.
+  constexpr int NCB = (DV + 15) / 16;        // 16-position blocks of a row
+  constexpr int NITEM = 4 * NCB;             // (token block, position block)
   constexpr int NIW = (NITEM + NW - 1) / NW; // items per wave
   auto red_sum = [&](int ch) {
     const float sc = ldexpf(1.f, ew);
+    const bf16x8 eye = eye2();
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       const int item = w + NW * i;
@@ -608,17 +625,19 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
         const int tb = item / NCB, cb = item % NCB;
         const int rho = 16 * tb + lr;
         const int unit = 2 * cb + (g & 1);
+        const int upos = PAIRED ? (unit ^ swz_red<NU>(rho)) : (unit ^ (swz_row(rho) % NU));
         f32x4 D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int pq = 0; pq < NW / 2; ++pq) {
           const int ww = 2 * pq + (g >> 1);
           u32x4 x = {0u, 0u, 0u, 0u};
           if (DV >= 16 || (g & 1) == 0)
-            x = *reinterpret_cast<const u32x4*>(&red[ww * L * DV + rho * DV + 8 * (unit ^ (swz_row(rho) % NU))]);
-          D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eye2, __builtin_bit_cast(bf16x8, x), D, 0, 0, 0);
+            x = *reinterpret_cast<const u32x4*>(&red[ww * L * DV + rho * DV + 8 * upos]);
+          D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eye, __builtin_bit_cast(bf16x8, x), D, 0, 0, 0);
         }
-        const int t = 4 * lr + tb;
-        const int col = 16 * cb + 4 * g;
+        const int t = 4 * lr + (tb ^ (lr & 1));
+        // positions 4 g .. 4 g + 3 of block cb = units 2 cb + (g >> 1), half g & 1
+        const int col = PAIRED ? 32 * (cb >> 1) + 16 * (g & 1) + 8 * (cb & 1) + 4 * (g >> 1) : 16 * cb + 4 * g;
         if (col < DV) {
           const int64_t ro = (static_cast<int64_t>(ch) * L + t) * DV + col;
           if constexpr (std::is_same<RedT, uint16_t>::value) {
@@ -654,33 +673,36 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   // Readout of chunk X's queries against Sb into the cross-wave buffer.
   // MFMA: A = Sb^T (16 value columns x 32 rows), B = phi_q^T (32 rows x 16
   // tokens), so lane (lr, g) gets token slot lr, columns 16 nb + 4 g + r.
-  // Token slot lr of token block mb is token 4 lr + mb.
+  // Token slot lr of token block mb is token 4 lr + (mb ^ (lr & 1)).
   auto readout = [&](int X, auto&& hook) {
     const unsigned char* qt = lds + C::O_QT + X * C::QT_B;
     const unsigned char* qn = lds + C::O_QN + X * C::QN_B;
     uint16_t* redw = reinterpret_cast<uint16_t*>(lds + C::O_RED) + w * L * DV;
-    // Parent products for the lane's four tokens (token block mb = element mb).
+    // Parent products for the lane's four tokens, in token-block order
+    // (element mb holds token 4 lr + (mb ^ (lr & 1))).
     u32x2 pp[RB];
     float pf[RB][4];
+    const uint32_t psel = odd ? 0x01000302u : 0x03020100u;   // byte select: swap the halves
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       const u32x2 x1 = *reinterpret_cast<const u32x2*>(qt + (oq12[b] & 0xffffu));
       const u32x2 x2 = *reinterpret_cast<const u32x2*>(qt + (oq12[b] >> 16));
       if constexpr (H16) {
         const f16x4 p = __builtin_bit_cast(f16x4, x1) * __builtin_bit_cast(f16x4, x2);
-        pp[b] = __builtin_bit_cast(u32x2, p);
+        const u32x2 pw = __builtin_bit_cast(u32x2, p);
+        pp[b] = u32x2{__builtin_amdgcn_perm(pw[0], pw[0], psel), __builtin_amdgcn_perm(pw[1], pw[1], psel)};
       } else {
         float v[4] = {bf16_lo(x1[0]) * bf16_lo(x2[0]), bf16_hi(x1[0]) * bf16_hi(x2[0]),
                       bf16_lo(x1[1]) * bf16_lo(x2[1]), bf16_hi(x1[1]) * bf16_hi(x2[1])};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pf[b][j] = v[j];
+        for (int j = 0; j < 4; ++j) pf[b][j] = odd ? v[j ^ 1] : v[j];
       }
     }
     float dn[4] = {0.f, 0.f, 0.f, 0.f};
     auto load_c = [&](int mb, int kk, u32x2 (&c)[2]) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        c[h] = *reinterpret_cast<const u32x2*>(qn + oqc[2 * kk + h] + 2 * DK * mb);
+        c[h] = *reinterpret_cast<const u32x2*>(qn + (oqc[2 * kk + h] - ((mb & 1) ? d4 : 0u)) + 2 * DK * mb);
     };
     auto build = [&](int mb, int kk, const u32x2 (&c)[2]) {
       u32x4 B;
@@ -720,12 +742,23 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       if (s_ + 2 < NST) load_c((s_ + 2) / NKS, (s_ + 2) % NKS, cc);
       if (kk == NKS - 1) {
         const int rho = lr + 16 * mb;
+        if constexpr (PAIRED) {
+          // unit 4 P + g = columns 32 P + 4 g .. +3 and 32 P + 16 + 4 g .. +3
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          if (16 * nb < DV && (16 * nb + 16 <= DV || 4 * g < DV % 16)) {
-            const int cu = 2 * nb + (g >> 1);
-            const u32x2 o = {pack_bf16(acc[nb][0], acc[nb][1]), pack_bf16(acc[nb][2], acc[nb][3])};
-            *reinterpret_cast<u32x2*>(&redw[rho * DV + 8 * (cu ^ (swz_row(rho) % NU)) + 4 * (g & 1)]) = o;
+          for (int P = 0; P < DV / 32; ++P) {
+            const u32x4 o = {pack_bf16(acc[2 * P][0], acc[2 * P][1]), pack_bf16(acc[2 * P][2], acc[2 * P][3]),
+                             pack_bf16(acc[2 * P + 1][0], acc[2 * P + 1][1]),
+                             pack_bf16(acc[2 * P + 1][2], acc[2 * P + 1][3])};
+            *reinterpret_cast<u32x4*>(&redw[rho * DV + 8 * ((4 * P + g) ^ swz_red<NU>(rho))]) = o;
+          }
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            if (16 * nb < DV && (16 * nb + 16 <= DV || 4 * g < DV % 16)) {
+              const int cu = 2 * nb + (g >> 1);
+              const u32x2 o = {pack_bf16(acc[nb][0], acc[nb][1]), pack_bf16(acc[nb][2], acc[nb][3])};
+              *reinterpret_cast<u32x2*>(&redw[rho * DV + 8 * (cu ^ (swz_row(rho) % NU)) + 4 * (g & 1)]) = o;
+            }
           }
         }
         dn[mb] = acc[C::NB_DEN][C::R_DEN];
@@ -733,8 +766,9 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       __builtin_amdgcn_sched_barrier(0);
       Bcur = Bnext;
     }
-    if (g == C::G_DEN)   // tokens 4 lr + mb
-      *reinterpret_cast<f32x4*>(lds + C::O_DEN + (w * L + 4 * lr) * 4) = f32x4{dn[0], dn[1], dn[2], dn[3]};
+    if (g == C::G_DEN)   // tokens 4 lr + j, j = mb ^ (lr & 1)
+      *reinterpret_cast<f32x4*>(lds + C::O_DEN + (w * L + 4 * lr) * 4) =
+          odd ? f32x4{dn[1], dn[0], dn[3], dn[2]} : f32x4{dn[0], dn[1], dn[2], dn[3]};
   };
 
   // State update of chunk X: S += phi_k(K)^T [V 1].  A = key features (16
