@@ -28,10 +28,10 @@ constexpr int prefill_chunk(bool bf16) { return bf16 ? 64 : 32; }
 
 // Tokens per readout window: the readout of every chunk in a window uses the
 // state as it stood at the window's start (for bf16 inputs, whose readout
-// operand is a bf16 copy of the state refreshed once per window), and the
+// operand is a 16-bit copy of the state refreshed once per window), and the
 // keys of the window before the query are summed exactly by the intra-window
 // kernel.  fp32 inputs read the live state, so their window is one chunk.
-constexpr int prefill_window(bool bf16) { return bf16 ? 256 : prefill_chunk(bf16); }
+constexpr int prefill_window(bool bf16) { return bf16 ? 512 : prefill_chunk(bf16); }
 
 // Row blocks of 16 rows per wave held on chip by the prefill scan, per
 // (head dim, input dtype).  fp32 (one wave per SIMD): the state tile

@@ -708,15 +708,16 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
 // goes through the exact 0/1 mask, so only the small higher-order weights W'
 // are rounded to bf16.
 template <int DK>
-__global__ __launch_bounds__(256) void prefill_intra_mfma(IntraArgs a) {
+__global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(IntraArgs a) {
   constexpr int DV = DK, T = prefill_window(true);
+  constexpr int NT = T;                        // threads: one 64-query wave per 64 tokens
   constexpr int KP = DK < 32 ? 32 : DK;        // head dim padded to the MFMA K
   constexpr int KSTEPS = KP / 32;
   constexpr int KSTR = KP + 8;                 // bf16 per staged key row
   constexpr int NB = col_blocks(DV), NC = NB * 16;
   constexpr int VSTR = T + 8;                  // bf16 per staged V' row
   constexpr int DVP = padded_dv(DV);
-  static_assert(T == 256 && DK % 8 == 0, "window of four 64-query waves");
+  static_assert(T % 64 == 0 && DK % 8 == 0, "window of 64-query waves");
   __shared__ __attribute__((aligned(16))) uint16_t ks_[T * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vt[NC * VSTR];
   const int win = blockIdx.x;
@@ -733,14 +734,14 @@ __global__ __launch_bounds__(256) void prefill_intra_mfma(IntraArgs a) {
   const uint16_t* vh = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
 
   // Stage K row-major (zero-padded to KP, zero past the window) and V'^T.
-  for (int e = tid; e < T * (KP / 8); e += 256) {
+  for (int e = tid; e < T * (KP / 8); e += NT) {
     const int t = e / (KP / 8);
     const int c8 = (e % (KP / 8)) * 8;
     u32x4 val = {0u, 0u, 0u, 0u};
     if (t < nvalid && c8 < DK) val = *reinterpret_cast<const u32x4*>(kh + (tb + t) * DK + c8);
     *reinterpret_cast<u32x4*>(&ks_[t * KSTR + c8]) = val;
   }
-  for (int e = tid; e < T * (DV / 8); e += 256) {
+  for (int e = tid; e < T * (DV / 8); e += NT) {
     const int t = e % T;
     const int c8 = (e / T) * 8;
     u32x4 val = {0u, 0u, 0u, 0u};
@@ -749,7 +750,7 @@ __global__ __launch_bounds__(256) void prefill_intra_mfma(IntraArgs a) {
     for (int j = 0; j < 8; ++j)
       vt[(c8 + j) * VSTR + t] = static_cast<uint16_t>((j & 1) ? (val[j / 2] >> 16) : (val[j / 2] & 0xffffu));
   }
-  for (int e = tid; e < (NC - DV) * T; e += 256) {
+  for (int e = tid; e < (NC - DV) * T; e += NT) {
     const int c = DV + e / T;
     const int t = e % T;
     vt[c * VSTR + t] = (c == DV && t < nvalid) ? static_cast<uint16_t>(0x3f80) : static_cast<uint16_t>(0);
@@ -913,7 +914,7 @@ hipError_t launch_intra_t(int BH, const IntraArgs& a, hipStream_t s) {
   constexpr int T = prefill_window(BF16);
   dim3 grid((a.nw + T - 1) / T, BH);
   if constexpr (BF16)
-    prefill_intra_mfma<D><<<grid, 256, 0, s>>>(a);
+    prefill_intra_mfma<D><<<grid, T, 0, s>>>(a);
   else
     prefill_intra<D, BF16><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
