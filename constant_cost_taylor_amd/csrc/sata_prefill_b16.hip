@@ -642,9 +642,9 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
           const int64_t ro = (static_cast<int64_t>(ch) * L + t) * DV + col;
           if constexpr (std::is_same<RedT, uint16_t>::value) {
             const u32x2 o = {pack_bf16(D[0] * sc, D[1] * sc), pack_bf16(D[2] * sc, D[3] * sc)};
-            *reinterpret_cast<u32x2*>(&rech[ro]) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(&rech[ro]));   // read once, later
           } else {
-            *reinterpret_cast<f32x4*>(&rech[ro]) = D * sc;
+            __builtin_nontemporal_store(D * sc, reinterpret_cast<f32x4*>(&rech[ro]));
           }
         }
       }
@@ -653,7 +653,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       float sz = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) sz += den[ww * L + l];
-      reczh[static_cast<int64_t>(ch) * L + l] = sz * sc;
+      __builtin_nontemporal_store(sz * sc, &reczh[static_cast<int64_t>(ch) * L + l]);
     }
   };
 
@@ -897,13 +897,15 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
 
 // ---------------------------------------------------------------------------
 // out = (intra + sum over tiles of the records + carry) for num / for den,
-// summed in a fixed order.  Block = (64 tokens, head); value items of 8
-// columns, den per token first.
+// summed in a fixed order.  Block = (64 tokens, head); den per token first
+// (four interleaved tile sums, combined in order), then value items of 8
+// columns.  Records are read once: non-temporal loads, four tiles in flight.
 template <int DK>
 __global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
   constexpr int DV = DK, DVP = padded_dv(DV), T = prefill_window(true), NU = DV / 8, TB = 64;
   using RedT = typename std::conditional<prefill_bf16_records(DK, true), uint16_t, float>::type;
   __shared__ float dsh[TB];
+  __shared__ float dpart[4][TB];
   const int head = blockIdx.y;
   const int t0 = blockIdx.x * TB;
   const int tid = threadIdx.x;
@@ -914,12 +916,20 @@ __global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
   const float rscale = hs.safe ? ldexpf(1.f, hs.ev) : 1.f;   // value-column records carry 2^-ev
   const float* intra = a.ws.intra + static_cast<int64_t>(head) * nwp * DVP;
   const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + T - 1) / T) * DVP;
+  {
+    const int tt = tid % TB, qq = tid / TB;   // 256 threads: 4 interleaved sums
+    float s = 0.f;
+    if (tt < ntok) {
+      const float* rz = a.ws.recz + static_cast<int64_t>(head) * nt * nwp + t0 + tt;
+      for (int tl = qq; tl < nt; tl += 4) s += __builtin_nontemporal_load(rz + static_cast<int64_t>(tl) * nwp);
+    }
+    dpart[qq][tt] = s;
+  }
+  __syncthreads();
   if (tid < TB) {
     const int t = t0 + tid;
-    float s = 0.f;
+    float s = ((dpart[0][tid] + dpart[1][tid]) + dpart[2][tid]) + dpart[3][tid];
     if (tid < ntok) {
-      const float* rz = a.ws.recz + static_cast<int64_t>(head) * nt * nwp + t;
-      for (int tl = 0; tl < nt; ++tl) s += rz[static_cast<int64_t>(tl) * nwp];
       s += intra[static_cast<int64_t>(t) * DVP + DV];
       s += carry[(t / T) * DVP + DV];
     }
@@ -935,24 +945,29 @@ __global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) r[j] = 0.f;
     const RedT* rp = rec + static_cast<int64_t>(t) * DV + 8 * u;
-    for (int tl = 0; tl < nt; ++tl) {
+    const int64_t tstride = static_cast<int64_t>(nwp) * DV;
+    auto add_tile = [&](int tl) {
       if constexpr (std::is_same<RedT, uint16_t>::value) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(rp + static_cast<int64_t>(tl) * nwp * DV);
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + tl * tstride));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          r[2 * j] += bf16_lo(x[j]);
-          r[2 * j + 1] += bf16_hi(x[j]);
+          const uint32_t xj = x[j];
+          r[2 * j] += bf16_lo(xj);
+          r[2 * j + 1] += bf16_hi(xj);
         }
       } else {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(rp + static_cast<int64_t>(tl) * nwp * DV);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(rp + static_cast<int64_t>(tl) * nwp * DV + 4);
+        const f32x4 x0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rp + tl * tstride));
+        const f32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rp + tl * tstride + 4));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           r[j] += x0[j];
           r[4 + j] += x1[j];
         }
       }
-    }
+    };
+    int tl = 0;
+#pragma unroll 4
+    for (; tl < nt; ++tl) add_tile(tl);
     const float* ip = intra + static_cast<int64_t>(t) * DVP + 8 * u;
     const float* cp = carry + (t / T) * DVP + 8 * u;
     const float dinv = 1.f / dsh[tt];
