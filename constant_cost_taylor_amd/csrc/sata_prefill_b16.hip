@@ -491,7 +491,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
                              static_cast<int64_t>(head) * nchp * (8 * DK * L);
   // Block i of this wave's share of chunk ch into buffer X.
   auto dma_one = [&](int i, int ch, int X) {
-    if (ldst[i] >= 0)
+    if (C::NBLK % NW == 0 || ldst[i] >= 0)
       dma16(stg + static_cast<int64_t>(ch) * (8 * DK * L) + ((gofs[i / 2] >> (16 * (i & 1))) & 0xffffu),
             lds + __builtin_amdgcn_readfirstlane(ldst[i] + X * lstep[i]));
   };
@@ -510,27 +510,48 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     const int p = m >= off3 ? 3 : m >= off2 ? 2 : m >= 1 ? 1 : 0;
     return p * hs.ek + (value_col ? hs.ev : 0);
   };
-  f32x4 S[RB][NB];
+  // Every row index first, then every load with no branch between them (a
+  // pad row or a column past den reads a valid word and is zeroed after), so
+  // the loads are all in flight at once; offsets are 32-bit (a head's state
+  // is below 2^32 bytes).
+  uint32_t info[RB][4];
+  float wr_lane[RB][4];
 #pragma unroll
-  for (int b = 0; b < RB; ++b) {
+  for (int b = 0; b < RB; ++b)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t info = a.lay.rowinfo[(lay_base + b) * 16 + 4 * g + r];
-      const int64_t m = info ? static_cast<int64_t>(info) - 1 : 0;
+      info[b][r] = a.lay.rowinfo[(lay_base + b) * 16 + 4 * g + r];
+      wr_lane[b][r] = a.lay.rweight[(lay_base + b) * 16 + 4 * g + r];
+    }
+  f32x4 S[RB][NB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t m = info[b][r] ? info[b][r] - 1 : 0u;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = nb * 16 + lr;
-        float val = 0.f;
-        if (info) {
-          if (col < DV) val = st[m * DV + col];
-          else if (col == DV) val = st[zoff + m];
-          if constexpr (H16) val = ldexpf(val, -row_exp(m, col < DV));
-        }
-        S[b][nb][r] = val;
+        const uint32_t off = col < DV ? m * DV + col : static_cast<uint32_t>(zoff) + m;
+        S[b][nb][r] = st[off];
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  // Chunk 0's tables go out behind the state loads (loads retire in order, so
+  // the wait for the state does not wait for these).
+  if (nch > 0) dma(0, 0);
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t m = info[b][r] ? info[b][r] - 1 : 0u;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = nb * 16 + lr;
+        float val = S[b][nb][r];
+        if constexpr (H16) val = ldexpf(val, -row_exp(m, col < DV));
+        S[b][nb][r] = (info[b][r] != 0u && col <= DV) ? val : 0.f;
+      }
+    }
 
   // ---- readout operand: Sb = S w 2^-ew, one ew per tile and readout window
   // (f16: max |S| max(w) 2^-ew in [2^13, 2^14); bf16: ew = 0).  Two steps around a
@@ -544,7 +565,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
 #pragma unroll
   for (int b = 0; b < RB; ++b)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wlmax = fmaxf(wlmax, fabsf(a.lay.rweight[(lay_base + b) * 16 + 4 * g + r]));
+    for (int r = 0; r < 4; ++r) wlmax = fmaxf(wlmax, fabsf(wr_lane[b][r]));
   auto post_max = [&]() {
     if constexpr (H16) {
       float mx = 0.f;
@@ -822,8 +843,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     }
   };
 
-  // ---- prologue: chunk 0 in buffer 0, its parent slots, the first Sb -------
-  if (nch > 0) dma(0, 0);
+  // ---- prologue: chunk 0's parent slots, the first Sb ---------------------------
   post_max();
   dma_barrier();
   slots(0);
@@ -838,8 +858,12 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     // segment 1: read out this chunk; the next chunk's DMA goes out one
     // block per readout step
     if (ch > 0 && ch % C::SC == 0) refresh();
+    // No branch around the DMA (a branch there splits the readout steps
+    // and undoes their software pipelining): the last chunk re-fetches
+    // itself into the idle buffer, which is never read again.
+    const int chn = ch + 1 < nch ? ch + 1 : ch;
     readout(X, [&](int step) {
-      if (step < C::NDMA && ch + 1 < nch) dma_one(step, ch + 1, X ^ 1);
+      if (step < C::NDMA) dma_one(step, chn, X ^ 1);
     });
     dma_barrier();
     // segment 2: records of this chunk, parent slots of the next, update;
@@ -861,27 +885,29 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   }
 
   // ---- state tile back (f16 path: unscaled) --------------------------------------
+  // Row indices again (the loop leaves no registers to keep them), all
+  // loaded before the first store.
   const uint32_t* rowinfo = a.lay.rowinfo;
   float* stw = st;
   asm volatile("" : "+s"(rowinfo), "+s"(stw));
+  uint32_t info2[RB][4];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) info2[b][r] = rowinfo[(lay_base + b) * 16 + 4 * g + r];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t info = rowinfo[(lay_base + b) * 16 + 4 * g + r];
-      if (info) {
-        const int64_t m = static_cast<int64_t>(info) - 1;
+      const uint32_t m = info2[b][r] - 1;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = nb * 16 + lr;
-          float val = S[b][nb][r];
-          if constexpr (H16) val = ldexpf(val, row_exp(m, col < DV));
-          if (col < DV) stw[m * DV + col] = val;
-          else if (col == DV) stw[zoff + m] = val;
-        }
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = nb * 16 + lr;
+        float val = S[b][nb][r];
+        if constexpr (H16) val = ldexpf(val, row_exp(m, col < DV));
+        if (info2[b][r] != 0u && col <= DV) stw[col < DV ? m * DV + col : static_cast<uint32_t>(zoff) + m] = val;
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
