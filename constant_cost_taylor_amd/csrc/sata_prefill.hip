@@ -205,22 +205,32 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   // last index.
   float* st = a.state + static_cast<int64_t>(head) * a.stride;
   const int64_t zoff = static_cast<int64_t>(a.D) * DV;
+  // Row indices first; within a block every load is unconditional (a pad
+  // row or a column past den reads a valid word and is zeroed), so a block's
+  // loads are in flight together.  32-bit offsets: a head's state is below
+  // 2^32 bytes.
+  uint32_t info[RB][4];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) info[b][r] = a.lay.rowinfo[(lay_base + b) * 16 + 4 * g + r];
   f32x4 S[RB][NB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t info = a.lay.rowinfo[(lay_base + b) * 16 + 4 * g + r];
-      const int64_t m = info ? static_cast<int64_t>(info & 0x0fffffffu) - 1 : 0;
-      const float inv_cnt = info ? 1.f / static_cast<float>(info >> 28) : 0.f;
+      const uint32_t m = info[b][r] ? (info[b][r] & 0x0fffffffu) - 1 : 0u;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = nb * 16 + lr;
-        float val = 0.f;
-        if (col < DV) val = st[m * DV + col];
-        else if (col == DV) val = st[zoff + m];
-        S[b][nb][r] = val * inv_cnt;
+        S[b][nb][r] = st[col < DV ? m * DV + col : static_cast<uint32_t>(zoff) + m];
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float inv_cnt = info[b][r] ? 1.f / static_cast<float>(info[b][r] >> 28) : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) S[b][nb][r] = (nb * 16 + lr <= DV) ? S[b][nb][r] * inv_cnt : 0.f;
     }
     // Move the block into accumulator registers right away, so the whole
     // tile is never held in VGPRs at once.
@@ -598,21 +608,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   const uint32_t* rowinfo = a.lay.rowinfo;
   float* stw = st;
   asm volatile("" : "+s"(rowinfo), "+s"(stw));
+  uint32_t info2[RB][4];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) info2[b][r] = rowinfo[(lay_base + b) * 16 + 4 * g + r];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t info = rowinfo[(lay_base + b) * 16 + 4 * g + r];
-      if (info) {
-        const int64_t m = static_cast<int64_t>(info & 0x0fffffffu) - 1;
-        const float cnt = static_cast<float>(info >> 28);
+      const uint32_t m = (info2[b][r] & 0x0fffffffu) - 1;
+      const float cnt = static_cast<float>(info2[b][r] >> 28);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = nb * 16 + lr;
-          const float val = S[b][nb][r] * cnt;
-          if (col < DV) stw[m * DV + col] = val;
-          else if (col == DV) stw[zoff + m] = val;
-        }
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = nb * 16 + lr;
+        if (info2[b][r] != 0u && col <= DV)
+          stw[col < DV ? m * DV + col : static_cast<uint32_t>(zoff) + m] = S[b][nb][r] * cnt;
       }
     }
     __builtin_amdgcn_sched_barrier(0);

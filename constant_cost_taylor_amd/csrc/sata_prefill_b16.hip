@@ -851,8 +851,11 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   lds_barrier();
 
   // ---- chunks -------------------------------------------------------------------
-  for (int ch = 0; ch < nch; ++ch) {
-    const int X = ch & 1;
+  // One chunk with its table buffer X as a compile-time constant (the loop
+  // below runs chunk pairs), so every buffer base folds into the immediate
+  // offset of the LDS instructions instead of costing address arithmetic.
+  auto chunk = [&](auto Xc, int ch) {
+    constexpr int X = decltype(Xc)::value;
 #pragma unroll
     for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(okpc[b]));
     // segment 1: read out this chunk; the next chunk's DMA goes out one
@@ -882,6 +885,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     }
     if (ch % C::SC == C::SC - 1 && ch + 1 < nch) post_max();
     lds_barrier();
+  };
+  for (int ch = 0; ch < nch; ch += 2) {
+    chunk(std::integral_constant<int, 0>{}, ch);
+    if (ch + 1 < nch) chunk(std::integral_constant<int, 1>{}, ch + 1);
   }
 
   // ---- state tile back (f16 path: unscaled) --------------------------------------
