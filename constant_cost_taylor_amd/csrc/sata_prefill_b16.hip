@@ -746,10 +746,12 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       return B;
     };
     constexpr int NST = 4 * NKS;
-    u32x2 cc[2];
-    load_c(0, 0, cc);
-    u32x4 Bcur = build(0, 0, cc);
-    if (NST > 1) load_c(1 / NKS, 1 % NKS, cc);
+    // child loads run two steps ahead of their use (a ring of two)
+    u32x2 cr[2][2];
+    load_c(0, 0, cr[0]);
+    u32x4 Bcur = build(0, 0, cr[0]);
+    if (NST > 1) load_c(1 / NKS, 1 % NKS, cr[1]);
+    if (NST > 2) load_c(2 / NKS, 2 % NKS, cr[0]);
     f32x4 acc[NB];
 #pragma unroll
     for (int s_ = 0; s_ < NST; ++s_) {
@@ -759,8 +761,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       for (int nb = 0; nb < NB; ++nb)
         acc[nb] = mfma16<H16>(Sb[kk][nb], Bcur, kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb]);
       u32x4 Bnext = Bcur;
-      if (s_ + 1 < NST) Bnext = build((s_ + 1) / NKS, (s_ + 1) % NKS, cc);
-      if (s_ + 2 < NST) load_c((s_ + 2) / NKS, (s_ + 2) % NKS, cc);
+      if (s_ + 1 < NST) Bnext = build((s_ + 1) / NKS, (s_ + 1) % NKS, cr[(s_ + 1) & 1]);
+      if (s_ + 3 < NST) load_c((s_ + 3) / NKS, (s_ + 3) % NKS, cr[(s_ + 1) & 1]);
       if (kk == NKS - 1) {
         const int rho = lr + 16 * mb;
         if constexpr (PAIRED) {
