@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 METRIC = "causal SATA tokens/sec/head (prefill, decode) + % of HBM/MFMA roofline"
 # HBM bytes moved by one decode_update_readout launch of this workload, from the
 # FETCH_SIZE / WRITE_SIZE counters scaled by a 1 GiB copy
@@ -45,6 +46,10 @@ def parse():
     ap.add_argument("--flatness", action="store_true",
                     help="instead of the step: prefill cost per token of the long-context workload "
                          "(16 heads, d_k=d_v=32, P=4, bf16) at n = 2^16, 2^18, 2^20")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the step: prefill throughput of the other workloads at their full "
+                         "sizes (d8 n256 fp32, d16 n4096 fp32, d64 n16384 bf16), each against the MFMA "
+                         "peak of its arithmetic")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB), the "
                          "reference for scaling hardware byte counters")
@@ -136,6 +141,55 @@ def flatness(args):
           flush=True)
 
 
+def configs(args):
+    """Prefill of the remaining workloads at their full sizes, from empty
+    states, inputs from the seeded generators (workloads.py)."""
+    import torch
+    import constant_cost_taylor_amd as sa
+    import workloads as W
+    from oracle import sata_oracle as O
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for name in ("tiny_d8_n256", "d16_n4096", "d64_n16384"):
+        w = W.WORKLOADS[name]
+        basis = sa.build_basis(w.d_k, w.P, w.c)
+        q, k, v = W.workload_inputs(w)
+        bf16 = w.dtype == W.BF16
+        tdt = torch.bfloat16 if bf16 else torch.float32
+        Q, K, V = (torch.from_numpy(np.ascontiguousarray(x)).to(tdt).to(dev) for x in (q, k, v))
+        out = torch.empty((w.B, w.H, w.n, w.d_v), dtype=torch.float32, device=dev)
+        state = sa.new_state(basis, w.B * w.H, dev)
+        ws = sa.workspace(sa.prefill_workspace_bytes(basis, w.B, w.H, w.n, w.d_v,
+                                                     sa.SATA_BF16 if bf16 else sa.SATA_F32), dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ms = []
+        for it in range(args.warmup + args.steps):
+            state.zero_()
+            ev[0].record(stream)
+            sa.prefill(basis, Q, K, V, state=state, out=out, ws=ws)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                ms.append(ev[0].elapsed_time(ev[1]))
+        t = float(np.median(ms))
+        tok = w.B * w.H * w.n
+        _, page_flops = O.cost_model(w.d_k, w.d_v, w.P)
+        tflops = tok * page_flops / (t * 1e-3) / 1e12
+        peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+        rows.append({"workload": f"{name}: batch {w.B} x {w.H} heads, n={w.n}, d_k=d_v={w.d_k}, P={w.P}, "
+                                 f"{'bf16' if bf16 else 'fp32'} inputs",
+                     "ms": t, "head_tokens_per_s": tok / (t * 1e-3), "page_tflops": tflops,
+                     "mfma_peak_tflops": peak, "mfma_frac": tflops / peak,
+                     "finite": bool(torch.isfinite(out).all())})
+        print(f"configs {name}: {t:.3f} ms", file=sys.stderr, flush=True)
+        del Q, K, V, out, state, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "prefill throughput per workload", "unit": "head-tokens/s",
+                      "steps": args.steps, "warmup": args.warmup, "points": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,6 +198,9 @@ def main():
         sys.exit(2)
     if args.flatness:
         flatness(args)
+        return
+    if args.configs:
+        configs(args)
         return
     import torch
     import constant_cost_taylor_amd as sa

@@ -115,6 +115,8 @@ CASES = [
     ("d16_bf16", 2, 2, 513, 16, 4, 1.0, W.BF16),
     ("d32_bf16", 1, 2, 777, 32, 4, 1.0, W.BF16),
     ("d64_bf16", 1, 2, 333, 64, 4, 1.0, W.BF16),
+    # 17 chunks in one call: two readout windows, an unpaired last chunk
+    ("d64_bf16_odd_chunks", 1, 1, 1050, 64, 4, 1.0, W.BF16),
     ("d64_bf16_P3", 1, 1, 200, 64, 3, 0.75, W.BF16),
     ("d8_bf16", 1, 1, 97, 8, 4, 1.0, W.BF16),
 ]
