@@ -1,4 +1,6 @@
-// Chunked causal prefill of SATA on gfx950 (CDNA4).
+// Chunked causal prefill of SATA on gfx950 (CDNA4) for float32 inputs, and
+// the intra-window kernel of the bfloat16 path (prefill_intra_mfma; the rest
+// of that path is in sata_prefill_b16.hip).
 //
 // The sequence is cut into chunks of L tokens.  For a query i in chunk t
 //   num_i = sum_{j <= i, j in t} T_P(x_ij) v_j            (intra-chunk, exact polynomial)
@@ -17,9 +19,8 @@
 //                  (each row = parent feature x one more coordinate, the
 //                  nested i1 <= ... <= ip structure of the index matrices),
 //                  reads out  phi_q(Q_t) S  and updates  S += phi_k(K_t)^T [V_t 1]
-//                  on MFMA (bf16 operands for bf16 inputs, fp32 otherwise),
-//                  and writes one readout record per token.  Tile 0 also
-//                  records the exact order-0 prefix of every chunk.
+//                  on fp32 MFMA, and writes one readout record per token.
+//                  Tile 0 also records the exact order-0 prefix of every chunk.
 //   prefill_intra  grid = (chunks) x (heads): the intra-chunk part, fp32.
 //   prefill_reduce sums the records in a fixed order and divides.
 //
@@ -51,9 +52,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Two floats rounded to bf16 (nearest even) and packed in one register.  The
 // empty asm pins the conversion at this point of the program, so the
@@ -64,17 +62,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   asm volatile("" : "+v"(r));
   return r;
 }
-
-// Two floats rounded to f16 (nearest even) and packed in one register.
-__device__ __forceinline__ uint32_t pack_f16(float x, float y) {
-  f16x2 v = {static_cast<_Float16>(x), static_cast<_Float16>(y)};
-  uint32_t r = __builtin_bit_cast(uint32_t, v);
-  asm volatile("" : "+v"(r));
-  return r;
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // 16-byte LDS load at an offset the caller guarantees to be a multiple of 4 floats.
 __device__ __forceinline__ float4 lds4(const float* base, int off) {
@@ -115,48 +102,42 @@ struct ChunkRegs {
   }
 };
 
-template <int DK, bool BF16>
+template <int DK>
 struct Cfg {
   static constexpr int DV = DK;
-  static constexpr int L = prefill_chunk(BF16);
-  static constexpr int T = prefill_window(BF16);     // readout window (tokens)
+  static constexpr int L = prefill_chunk(false);
+  static constexpr int T = prefill_window(false);    // readout window (tokens)
   static constexpr int SC = T / L;                   // chunks per readout window
-  static constexpr int RB = prefill_rb(DK, BF16);
+  static constexpr int RB = prefill_rb(DK, false);
   static constexpr int NB = col_blocks(DV);        // 16-wide column blocks incl. z
   static constexpr int NC = NB * 16;
   static constexpr int DVP = padded_dv(DV);
-  static constexpr int NSLOT = prefill_slots(DK, BF16);
-  static constexpr int KSTR = prefill_kstride(BF16); // xk / pk row stride (floats)
+  static constexpr int NSLOT = prefill_slots(DK, false);
+  static constexpr int KSTR = prefill_kstride(false); // xk / pk row stride (floats)
   static constexpr int QSTR = L + 1;                 // pq row stride
   static constexpr int XQSTR = DK + 4;               // xq row stride
-  static constexpr bool RECB = prefill_bf16_records(DK, BF16);
-  static constexpr int RSTR = RECB ? L + 8 : L + 4;  // reduction row stride (elements)
-  static constexpr int VSTR = L + 8;                 // bf16 V' row stride (elements)
+  static constexpr int RSTR = L + 4;                 // reduction row stride (floats)
   static constexpr int XK_ZERO = 2 * DK * KSTR;      // offset of the zero row
-  static constexpr int NKS = (RB + 1) / 2;           // bf16 readout K-slices (2 blocks each)
   static constexpr int MB = L / 16;                  // 16-token blocks per chunk
   static constexpr int EPT = L * DK / (kWaves * 64); // staged elements per thread and tensor
-  static constexpr int TPG = L / (RECB ? 8 : 4);     // token groups of the cross-wave sum
-  using IT = typename std::conditional<BF16, uint16_t, float>::type;
-  using RedT = typename std::conditional<RECB, uint16_t, float>::type;
+  static constexpr int TPG = L / 4;                  // token groups of the cross-wave sum
 };
 
-template <int DK, bool BF16>
+template <int DK>
 __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
-  using C = Cfg<DK, BF16>;
+  using C = Cfg<DK>;
   constexpr int DV = C::DV, L = C::L, RB = C::RB, NB = C::NB, NC = C::NC, DVP = C::DVP;
   constexpr int NSLOT = C::NSLOT, KSTR = C::KSTR, QSTR = C::QSTR, XQSTR = C::XQSTR;
-  constexpr int RSTR = C::RSTR, VSTR = C::VSTR, XK_ZERO = C::XK_ZERO, MB = C::MB, EPT = C::EPT;
-  using IT = typename C::IT;
-  using RedT = typename C::RedT;
+  constexpr int RSTR = C::RSTR, XK_ZERO = C::XK_ZERO, MB = C::MB, EPT = C::EPT;
+  using IT = float;
+  using RedT = float;
 
   __shared__ __attribute__((aligned(16))) float xk[(2 * DK + 1) * KSTR];
   __shared__ __attribute__((aligned(16))) float pk[NSLOT * KSTR];
   __shared__ __attribute__((aligned(16))) float pq[NSLOT * QSTR];
   __shared__ __attribute__((aligned(16))) float xq[L * XQSTR];
   __shared__ __attribute__((aligned(16))) RedT red[kWaves * (DV + 1) * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[BF16 ? NC * VSTR : 8];
-  __shared__ __attribute__((aligned(16))) float vv[BF16 ? 4 : L * NC];
+  __shared__ __attribute__((aligned(16))) float vv[L * NC];
   __shared__ float carry[NC];
   __shared__ uint32_t spar[NSLOT];
   __shared__ float spwq[NSLOT];
@@ -186,19 +167,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     spwk[s] = a.lay.kscale[tile * NSLOT + s];
   }
   for (int i = tid; i < KSTR; i += kWaves * 64) xk[XK_ZERO + i] = 0.f;
-  if constexpr (BF16) {
-    // Constant columns of V' = [v, 1, 0...]: the ones column feeds z.
-    for (int e = tid; e < (NC - DV) * VSTR; e += kWaves * 64) {
-      const int c = DV + e / VSTR;
-      vt[c * VSTR + e % VSTR] = (c == DV) ? static_cast<uint16_t>(0x3f80) : static_cast<uint16_t>(0);
-    }
-  } else {
-    for (int e = tid; e < L * (NC - DV); e += kWaves * 64) {
-      const int t = e / (NC - DV);
-      const int c = DV + e % (NC - DV);
-      vv[t * NC + c] = (c == DV) ? 1.f : 0.f;
-    }
+  for (int e = tid; e < L * (NC - DV); e += kWaves * 64) {
+    const int t = e / (NC - DV);
+    const int c = DV + e % (NC - DV);
+    vv[t * NC + c] = (c == DV) ? 1.f : 0.f;
   }
+
 
   // Load the state tile into the accumulators (C layout: lane holds column
   // nb*16 + lr of rows 4g + r), divided by the multiplicity of each row's
@@ -238,22 +212,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(S[b][nb]));
     __builtin_amdgcn_sched_barrier(0);
   }
-  // bf16 copy of the state used as the readout operand, grouped per readout
-  // K-slice (two row blocks): refreshed right after every update.
-  u32x4 Sb[BF16 ? C::NKS : 1][BF16 ? NB : 1];
-  if constexpr (BF16) {
-#pragma unroll
-    for (int kk = 0; kk < C::NKS; ++kk)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        Sb[kk][nb][0] = pack_bf16(S[2 * kk][nb][0], S[2 * kk][nb][1]);
-        Sb[kk][nb][1] = pack_bf16(S[2 * kk][nb][2], S[2 * kk][nb][3]);
-        Sb[kk][nb][2] = 2 * kk + 1 < RB ? pack_bf16(S[2 * kk + 1 < RB ? 2 * kk + 1 : 0][nb][0],
-                                                    S[2 * kk + 1 < RB ? 2 * kk + 1 : 0][nb][1]) : 0u;
-        Sb[kk][nb][3] = 2 * kk + 1 < RB ? pack_bf16(S[2 * kk + 1 < RB ? 2 * kk + 1 : 0][nb][2],
-                                                    S[2 * kk + 1 < RB ? 2 * kk + 1 : 0][nb][3]) : 0u;
-      }
-  }
   if (tile == 0 && tid < NC) carry[tid] = tid < DV ? st[tid] : (tid == DV ? st[zoff] : 0.f);
 
   const IT* qh = static_cast<const IT*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
@@ -270,29 +228,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     for (int e = tid; e < (DV + 1) * C::TPG; e += kWaves * 64) {
       const int c = e / C::TPG;
       const int tg = e % C::TPG;
-      if constexpr (C::RECB) {
-        float sum[8];
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sum[j] = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 8 * tg]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            sum[2 * j] += bf16_lo(x[j]);
-            sum[2 * j + 1] += bf16_hi(x[j]);
-          }
-        }
-        const u32x4 o = {pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3]), pack_bf16(sum[4], sum[5]),
-                         pack_bf16(sum[6], sum[7])};
-        *reinterpret_cast<u32x4*>(&rech[static_cast<int64_t>(c) * nwp + ch * L + 8 * tg]) = o;
-      } else {
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww)
-          sum += *reinterpret_cast<const f32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 4 * tg]);
-        *reinterpret_cast<f32x4*>(&rech[static_cast<int64_t>(c) * nwp + ch * L + 4 * tg]) = sum;
-      }
+      for (int ww = 0; ww < kWaves; ++ww)
+        sum += *reinterpret_cast<const f32x4*>(&red[(ww * (DV + 1) + c) * RSTR + 4 * tg]);
+      *reinterpret_cast<f32x4*>(&rech[static_cast<int64_t>(c) * nwp + ch * L + 4 * tg]) = sum;
     }
   };
 
@@ -310,8 +250,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     rv.load(vh + tn * DV + st_i, ok);
   }
 
-  // Outer loop over readout windows, inner loop over their chunks: the bf16
-  // readout operand is loop-invariant inside a window and refreshed after it.
+  // Chunks grouped by readout window (here a window is one chunk: the readout
+  // reads the live fp32 state).
   for (int ch0 = 0; ch0 < nch; ch0 += C::SC) {
   const int ch_end = min(nch, ch0 + C::SC);
   for (int ch = ch0; ch < ch_end; ++ch) {
@@ -343,10 +283,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
       const float kv = to_f32(rk.raw(e));
       xk[(st_i + e) * KSTR + st_t] = kv;
       xk[(DK + st_i + e) * KSTR + st_t] = kv * 0.5f;
-      if constexpr (BF16)
-        vt[(st_i + e) * VSTR + st_t] = rv.raw(e);
-      else
-        vv[st_t * NC + st_i + e] = rv.raw(e);
+      vv[st_t * NC + st_i + e] = rv.raw(e);
     }
     // Prefetch the next chunk; the loads stay in flight through this chunk.
     if (ch + 1 < nch) {
@@ -386,10 +323,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
         if (wstart) carryh[static_cast<int64_t>(ch / C::SC) * DVP + tid] = carry[tid];
         float s = 0.f;
         for (int t = 0; t < nvalid; ++t) {
-          if constexpr (BF16)
-            s += __uint_as_float(static_cast<uint32_t>(vt[tid * VSTR + t]) << 16);
-          else
-            s += vv[t * NC + tid];
+          s += vv[t * NC + tid];
         }
         carry[tid] += s;
       } else if (tid == DV) {
@@ -404,91 +338,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
 #pragma unroll
     for (int half = 0; half < MB / 2; ++half) {
       f32x4 acc[2][NB];
-      if constexpr (BF16) {
-        // Per K-slice operand data: parent feature and 4 child coordinates of
-        // the lane group's run in both row blocks, for both token blocks.
-        struct QData {
-          float p[2][2];
-          float4 x[2][2];
-        };
-        auto load_q = [&](int kk, QData& dq) {
-          const int b0 = 2 * kk;
-          const int b1 = (2 * kk + 1 < RB) ? 2 * kk + 1 : 2 * kk;
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const int t = (2 * half + mb) * 16 + lr;
-            dq.p[mb][0] = pq[(qs[b0] & 0xffff) * QSTR + t];
-            dq.x[mb][0] = lds4(xq, t * XQSTR + (qs[b0] >> 16));
-            if (2 * kk + 1 < RB) {
-              dq.p[mb][1] = pq[(qs[b1] & 0xffff) * QSTR + t];
-              dq.x[mb][1] = lds4(xq, t * XQSTR + (qs[b1] >> 16));
-            } else {
-              dq.p[mb][1] = 0.f;
-              dq.x[mb][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-          }
-        };
-        auto build_q = [&](const QData& dq, bf16x8 (&A)[2]) {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const float p0 = dq.p[mb][0], p1 = dq.p[mb][1];
-            const float4 x0 = dq.x[mb][0], x1 = dq.x[mb][1];
-            const u32x4 aw = {pack_bf16(p0 * x0.x, p0 * x0.y), pack_bf16(p0 * x0.z, p0 * x0.w),
-                              pack_bf16(p1 * x1.x, p1 * x1.y), pack_bf16(p1 * x1.z, p1 * x1.w)};
-            A[mb] = __builtin_bit_cast(bf16x8, aw);
-          }
-        };
-        QData dq0, dq1;
-        bf16x8 Acur[2], Anext[2];
-        load_q(0, dq0);
-        build_q(dq0, Acur);
-        if (C::NKS > 1) load_q(C::NKS > 1 ? 1 : 0, dq0);
-        if (C::NKS > 2) load_q(C::NKS > 2 ? 2 : 0, dq1);
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < C::NKS; ++kk) {
+      for (int b = 0; b < RB; ++b) {
+        const int slot = qs[b] & 0xffff;
+        const int c0 = qs[b] >> 16;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const bf16x8 Bop = __builtin_bit_cast(bf16x8, Sb[kk][nb]);
+        for (int mb = 0; mb < 2; ++mb) {
+          const int t = (2 * half + mb) * 16 + lr;
+          const float p = pq[slot * QSTR + t];
+          const float4 x = lds4(xq, t * XQSTR + c0);
+          const float av[4] = {p * x.x, p * x.y, p * x.z, p * x.w};
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  Acur[mb], Bop, kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb], 0, 0, 0);
-          }
-          // Operands of the next K-slice are built in the shadow of these MFMAs.
-          if (kk + 1 < C::NKS) build_q(dq0, Anext);
-          if (kk + 3 < C::NKS) load_q(kk + 3 < C::NKS ? kk + 3 : 0, dq0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (kk + 1 < C::NKS) {
-            Acur[0] = Anext[0];
-            Acur[1] = Anext[1];
-            const QData tq = dq0;
-            dq0 = dq1;
-            dq1 = tq;
-          }
-        }
-      } else {
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          const int slot = qs[b] & 0xffff;
-          const int c0 = qs[b] >> 16;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const int t = (2 * half + mb) * 16 + lr;
-            const float p = pq[slot * QSTR + t];
-            const float4 x = lds4(xq, t * XQSTR + c0);
-            const float av[4] = {p * x.x, p * x.y, p * x.z, p * x.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-              for (int nb = 0; nb < NB; ++nb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], S[b][nb][r], acc[mb][nb], 0, 0, 0);
-          }
+            for (int nb = 0; nb < NB; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], S[b][nb][r], acc[mb][nb], 0, 0, 0);
         }
       }
+    
       // C layout: lane holds column nb*16 + lr of tokens 4g..4g+3 -> one
       // 4-token vector store per (block, column block).
 #pragma unroll
@@ -498,106 +369,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
           const int col = nb * 16 + lr;
           if (col <= DV) {
             RedT* dst = &red[(w * (DV + 1) + col) * RSTR + (2 * half + mb) * 16 + 4 * g];
-            if constexpr (C::RECB) {
-              const u32x2 o = {pack_bf16(acc[mb][nb][0], acc[mb][nb][1]), pack_bf16(acc[mb][nb][2], acc[mb][nb][3])};
-              *reinterpret_cast<u32x2*>(__builtin_assume_aligned(dst, 8)) = o;
-            } else {
-              *reinterpret_cast<f32x4*>(__builtin_assume_aligned(dst, 16)) = acc[mb][nb];
-            }
+            *reinterpret_cast<f32x4*>(__builtin_assume_aligned(dst, 16)) = acc[mb][nb];
+          
           }
         }
     }
 
     // ---- phase C: state update S += phi_k(K)^T [V 1] ----------------------
-    if constexpr (BF16) {
-      // Steps s = (K-step, row block).  At step s the MFMAs of s run while the
-      // operand of s+1 is built (VALU) and the LDS data of s+3 is fetched.
-      // Fences keep every group's temporaries bounded.
-      constexpr int NST = (L / 32) * RB;
-      struct KData {
-        float4 p0, p1, x0, x1;
-      };
-      auto load_k = [&](int st_, KData& dk) {
-        const int kst = st_ / RB, b = st_ % RB;
-        const int pko = (ks[b] & 0xffff) + 32 * kst + 8 * g;
-        const int xko = (ks[b] >> 16) + 32 * kst + 8 * g;
-        dk.p0 = lds4(pk, pko);
-        dk.p1 = lds4(pk, pko + 4);
-        dk.x0 = lds4(xk, xko);
-        dk.x1 = lds4(xk, xko + 4);
-      };
-      auto build_k = [&](const KData& dk) {
-        const u32x4 aw = {pack_bf16(dk.p0.x * dk.x0.x, dk.p0.y * dk.x0.y),
-                          pack_bf16(dk.p0.z * dk.x0.z, dk.p0.w * dk.x0.w),
-                          pack_bf16(dk.p1.x * dk.x1.x, dk.p1.y * dk.x1.y),
-                          pack_bf16(dk.p1.z * dk.x1.z, dk.p1.w * dk.x1.w)};
-        return __builtin_bit_cast(bf16x8, aw);
-      };
-      auto load_v = [&](int kst, bf16x8 (&Bv)[NB]) {
+#pragma unroll
+    for (int kst = 0; kst < L / 4; ++kst) {
+      const int t = 4 * kst + g;
+      float bv[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bv[nb] = vv[t * NC + nb * 16 + lr];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int pko = ks[b] & 0xffff;
+        const int xko = ks[b] >> 16;
+        const float av = pk[pko + t] * xk[xko + t];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          Bv[nb] = *reinterpret_cast<const bf16x8*>(
-              __builtin_assume_aligned(&vt[(nb * 16 + lr) * VSTR + 32 * kst + 8 * g], 16));
-      };
-      bf16x8 Bv[NB], Bvn[NB];
-      load_v(0, Bv);
-      KData d0, d1;
-      load_k(0, d0);
-      bf16x8 Acur = build_k(d0);
-      if (NST > 1) load_k(NST > 1 ? 1 : 0, d0);
-      if (NST > 2) load_k(NST > 2 ? 2 : 0, d1);
-#pragma unroll
-      for (int st_ = 0; st_ < NST; ++st_) {
-        const int kst = st_ / RB, b = st_ % RB;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Acur, Bv[nb], S[b][nb], 0, 0, 0);
-        bf16x8 Anext = Acur;
-        if (st_ + 1 < NST) Anext = build_k(d0);
-        if (st_ + 3 < NST) load_k(st_ + 3 < NST ? st_ + 3 : 0, d0);
-        if (b == RB - 2 && kst + 1 < L / 32) load_v(kst + 1 < L / 32 ? kst + 1 : 0, Bvn);
-        __builtin_amdgcn_sched_barrier(0);
-        Acur = Anext;
-        {
-          const KData t2 = d0;
-          d0 = d1;
-          d1 = t2;
-        }
-        if (b == RB - 1 && kst + 1 < L / 32) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) Bv[nb] = Bvn[nb];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kst = 0; kst < L / 4; ++kst) {
-        const int t = 4 * kst + g;
-        float bv[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bv[nb] = vv[t * NC + nb * 16 + lr];
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          const int pko = ks[b] & 0xffff;
-          const int xko = ks[b] >> 16;
-          const float av = pk[pko + t] * xk[xko + t];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[nb], S[b][nb], 0, 0, 0);
-        }
+          S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[nb], S[b][nb], 0, 0, 0);
       }
     }
+  
     __syncthreads();
-  }
-  if constexpr (BF16) {
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        Sb[b / 2][nb][2 * (b % 2)] = pack_bf16(S[b][nb][0], S[b][nb][1]);
-        Sb[b / 2][nb][2 * (b % 2) + 1] = pack_bf16(S[b][nb][2], S[b][nb][3]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
   }
   }
   if (nch > 0) red_sum(nch - 1);
@@ -639,10 +435,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
 // Horner's rule.  Block = (window, head); thread (token i, column group);
 // keys are staged through LDS in tiles of KT tokens and read as broadcasts.
 // Writes record columns [DVP][nwp] (coalesced over tokens).
-template <int DK, bool BF16>
+template <int DK>
 __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
-  using IT = typename std::conditional<BF16, uint16_t, float>::type;
-  constexpr int DV = DK, T = prefill_window(BF16);
+  using IT = float;
+  constexpr int DV = DK, T = prefill_window(false);
   constexpr int KT = T < 64 ? T : 64;         // keys per LDS tile
   constexpr int NG = 256 / T;                 // column groups
   constexpr int CPG = (DV + NG - 1) / NG;     // columns per group
@@ -858,11 +654,9 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
 
 // out = (tile records + intra record + order-0 carry) for num / for den,
 // summed in a fixed order.  Block = (64 tokens, head).
-template <int DK, bool BF16>
+template <int DK>
 __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
-  static_assert(!BF16, "bfloat16 inputs use prefill_reduce_b16");
-  constexpr int DV = DK, DVP = padded_dv(DV), T = prefill_window(BF16);
-  constexpr bool RECB = prefill_bf16_records(DK, BF16);
+  constexpr int DV = DK, DVP = padded_dv(DV), T = prefill_window(false);
   constexpr int TB = 64;
   __shared__ float acc[(DV + 1) * (TB + 1)];
   const int head = blockIdx.y;
@@ -872,29 +666,16 @@ __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
   const int64_t slab = static_cast<int64_t>(DVP) * nwp;
   const float* intra = a.ws.intra + head * slab;
   const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + T - 1) / T) * DVP;
-  const float rscale = 1.f;
+  const float* rec = static_cast<const float*>(a.ws.rec) + static_cast<int64_t>(head) * a.n_tiles * slab;
   for (int e = tid; e < (DV + 1) * (TB / 4); e += 256) {
     const int c = e / (TB / 4);
     const int t = 4 * (e % (TB / 4));
     const int64_t off = static_cast<int64_t>(c) * nwp + t0 + t;
     f32x4 r = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (RECB) {
-      const uint16_t* rec = static_cast<const uint16_t*>(a.ws.rec) + static_cast<int64_t>(head) * a.n_tiles * slab;
-      for (int tl = 0; tl < a.n_tiles; ++tl) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(&rec[tl * slab + off]);
-        r[0] += bf16_lo(x[0]);
-        r[1] += bf16_hi(x[0]);
-        r[2] += bf16_lo(x[1]);
-        r[3] += bf16_hi(x[1]);
-      }
-    } else {
-      const float* rec = static_cast<const float*>(a.ws.rec) + static_cast<int64_t>(head) * a.n_tiles * slab;
-      for (int tl = 0; tl < a.n_tiles; ++tl) r += *reinterpret_cast<const f32x4*>(&rec[tl * slab + off]);
-    }
-    const float cs = c < DV ? rscale : 1.f;
+    for (int tl = 0; tl < a.n_tiles; ++tl) r += *reinterpret_cast<const f32x4*>(&rec[tl * slab + off]);
     f32x4 s = *reinterpret_cast<const f32x4*>(&intra[off]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] += r[j] * cs;
+    for (int j = 0; j < 4; ++j) s[j] += r[j];
 #pragma unroll
     for (int j = 0; j < 4; ++j) s[j] += carry[((t0 + t + j) / T) * DVP + c];
 #pragma unroll
@@ -909,37 +690,33 @@ __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
   }
 }
 
+// The scan and reduce here take float32 inputs; bfloat16 inputs have their
+// own scan and reduce (launch_prefill_b16, launch_reduce_b16).
 template <int D, bool BF16>
 hipError_t launch_scan_t(int BH, const ScanArgs& a, hipStream_t s) {
-  if constexpr (BF16) {
-    return hipErrorInvalidValue;   // bfloat16 inputs: launch_prefill_b16
-  } else {
-    dim3 grid(a.lay.n_tiles, BH);
-    prefill_scan<D, BF16><<<grid, kWaves * 64, 0, s>>>(a);
-    return hipGetLastError();
-  }
+  if (BF16) return hipErrorInvalidValue;
+  dim3 grid(a.lay.n_tiles, BH);
+  prefill_scan<D><<<grid, kWaves * 64, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_intra_t(int BH, const IntraArgs& a, hipStream_t s) {
   constexpr int T = prefill_window(BF16);
   dim3 grid((a.nw + T - 1) / T, BH);
-  if constexpr (BF16)
+  if (BF16)
     prefill_intra_mfma<D><<<grid, T, 0, s>>>(a);
   else
-    prefill_intra<D, BF16><<<grid, 256, 0, s>>>(a);
+    prefill_intra<D><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_reduce_t(int BH, const ReduceArgs& a, hipStream_t s) {
-  if constexpr (BF16) {
-    return hipErrorInvalidValue;   // bfloat16 inputs: launch_reduce_b16
-  } else {
-    dim3 grid((a.nw + 63) / 64, BH);
-    prefill_reduce<D, BF16><<<grid, 256, 0, s>>>(a);
-    return hipGetLastError();
-  }
+  if (BF16) return hipErrorInvalidValue;
+  dim3 grid((a.nw + 63) / 64, BH);
+  prefill_reduce<D><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 #define SATA_DISPATCH(fn, d, bf16, ...)                                   \

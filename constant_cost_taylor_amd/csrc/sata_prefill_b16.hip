@@ -6,7 +6,7 @@
 //   num_i = (intra-window part, exact polynomial)      prefill_intra_mfma
 //         + (order 0 before the window, exact sums)    prefill_carry
 //         + sum_{m of order >= 1} w_m phi_m(q_i) S_m   prefill_scan_b16
-// over readout windows of 256 tokens, and likewise for den with v -> 1.
+// over readout windows of 512 tokens, and likewise for den with v -> 1.
 //
 // Kernels of one call window (launch order):
 //   prefill_amax     max |q|, |k|, |v| per head (32 token slices).
@@ -19,9 +19,10 @@
 //                    order-0 row of the state.
 //   prefill_scan_b16 grid = (row tiles) x (heads), 8 waves.  Per chunk the
 //                    staged tables arrive in LDS by DMA (global_load_lds,
-//                    double-buffered, one chunk ahead); the state slice of the
-//                    tile stays in registers.  Two barrier-separated segments
-//                    per chunk, each with MFMA work:
+//                    double-buffered, one chunk ahead; the loop runs chunk
+//                    pairs so each buffer's offsets are constants); the state
+//                    slice of the tile stays in registers.  Two
+//                    barrier-separated segments per chunk, each with MFMA work:
 //                      1  readout  phi_q(Q) Sb  into the cross-wave buffer
 //                      2  cross-wave sum into the tile's records, key
 //                         features of the next chunk's order-2 parents, and
