@@ -506,8 +506,10 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
 }
 
 // Intra-window part on MFMA, for bf16 inputs.  Block = (readout window of T
-// tokens, head); wave w owns the queries [64w, 64w + 64) of the window.  For
-// every 32-key slice up to its last query:
+// tokens, head); each wave owns 64 queries of the window, the groups paired
+// so that the two waves sharing a SIMD (w and w + 4 of 8) take one early and
+// one late group (equal causal work per SIMD).  For every 32-key slice up to
+// the wave's last query:
 //   X^T = K_s Q_w^T                       (bf16 MFMA, fp32 accumulate)
 //   W'  = T_P(X / c) - 1 by Horner's rule in fp32, zero for keys after the query
 //   O^T += V'^T_s M + V'^T_s W'           (M = the 0/1 causal mask)
@@ -541,21 +543,39 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
   const uint16_t* vh = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
 
   // Stage K row-major (zero-padded to KP, zero past the window) and V'^T.
-  for (int e = tid; e < T * (KP / 8); e += NT) {
-    const int t = e / (KP / 8);
-    const int c8 = (e % (KP / 8)) * 8;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (t < nvalid && c8 < DK) val = *reinterpret_cast<const u32x4*>(kh + (tb + t) * DK + c8);
-    *reinterpret_cast<u32x4*>(&ks_[t * KSTR + c8]) = val;
+  // Every load first, from a valid address (the window's first token for
+  // items outside it, zeroed after), so they are in flight together.
+  constexpr int KI = T * (KP / 8) / NT, VI = T * (DV / 8) / NT;
+  static_assert(KI * NT == T * (KP / 8) && VI * NT == T * (DV / 8), "staging items per thread");
+  u32x4 kv[KI], vv[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int e = tid + i * NT;
+    const int t = e / (KP / 8), c8 = (e % (KP / 8)) * 8;
+    const bool ok = t < nvalid && c8 < DK;
+    kv[i] = *reinterpret_cast<const u32x4*>(kh + (tb + (ok ? t : 0)) * DK + (ok ? c8 : 0));
+    if (!ok) kv[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  for (int e = tid; e < T * (DV / 8); e += NT) {
-    const int t = e % T;
-    const int c8 = (e / T) * 8;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (t < nvalid) val = *reinterpret_cast<const u32x4*>(vh + (tb + t) * DV + c8);
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int e = tid + i * NT;
+    const int t = e % T, c8 = (e / T) * 8;
+    const bool ok = t < nvalid;
+    vv[i] = *reinterpret_cast<const u32x4*>(vh + (tb + (ok ? t : 0)) * DV + c8);
+    if (!ok) vv[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int e = tid + i * NT;
+    *reinterpret_cast<u32x4*>(&ks_[(e / (KP / 8)) * KSTR + (e % (KP / 8)) * 8]) = kv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int e = tid + i * NT;
+    const int t = e % T, c8 = (e / T) * 8;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      vt[(c8 + j) * VSTR + t] = static_cast<uint16_t>((j & 1) ? (val[j / 2] >> 16) : (val[j / 2] & 0xffffu));
+      vt[(c8 + j) * VSTR + t] = static_cast<uint16_t>((j & 1) ? (vv[i][j / 2] >> 16) : (vv[i][j / 2] & 0xffffu));
   }
   for (int e = tid; e < (NC - DV) * T; e += NT) {
     const int c = DV + e / T;
@@ -563,16 +583,21 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
     vt[c * VSTR + t] = (c == DV && t < nvalid) ? static_cast<uint16_t>(0x3f80) : static_cast<uint16_t>(0);
   }
 
+  // Query group of this wave (64 queries): early groups on waves 0..W/2-1,
+  // late ones (in reverse) on the waves sharing their SIMDs.
+  constexpr int NWV = NT / 64;
+  const int qg = w < NWV / 2 ? w : 3 * NWV / 2 - 1 - w;
   // Query operands (B of X^T): lane holds query 16 qb + lr, dims 32 kst + 8 g ...
   bf16x8 qop[4][KSTEPS];
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
     for (int kst = 0; kst < KSTEPS; ++kst) {
-      const int qi = 64 * w + 16 * qb + lr;
+      const int qi = 64 * qg + 16 * qb + lr;
       const int d0 = 32 * kst + 8 * g;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (qi < nvalid && d0 < DK) val = *reinterpret_cast<const u32x4*>(qh + (tb + qi) * DK + d0);
+      const bool ok = qi < nvalid && d0 < DK;
+      u32x4 val = *reinterpret_cast<const u32x4*>(qh + (tb + (ok ? qi : 0)) * DK + (ok ? d0 : 0));
+      if (!ok) val = u32x4{0u, 0u, 0u, 0u};
       qop[qb][kst] = __builtin_bit_cast(bf16x8, val);
     }
   __syncthreads();
@@ -583,7 +608,7 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) O[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float rcp[4] = {0.f, 1.f, 0.5f, 1.f / 3.f};
-  const int nslice = min(2 * w + 2, (nvalid + 31) / 32);
+  const int nslice = min(2 * qg + 2, (nvalid + 31) / 32);
   for (int sl = 0; sl < nslice; ++sl) {
     f32x4 X[2][4];
 #pragma unroll
@@ -604,14 +629,19 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
     bf16x8 Bm[4], Bw[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const int qi = 64 * w + 16 * qb + lr;
+      const int qi = 64 * qg + 16 * qb + lr;
       float wv[8], mv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int key = 32 * sl + 16 * (j / 4) + 4 * g + (j % 4);
         const float x = X[j / 4][qb][j % 4] * a.inv_c;
+        // Horner's rule over orders P-1..1 (at most three steps, unrolled)
         float h = 0.f;
-        for (int p = a.P - 1; p >= 1; --p) h = x * rcp[p] * (1.f + h);
+#pragma unroll
+        for (int p = 3; p >= 1; --p) {
+          const float hn = x * rcp[p] * (1.f + h);
+          h = p < a.P ? hn : h;
+        }
         const bool ok = key <= qi;
         wv[j] = ok ? h : 0.f;
         mv[j] = ok ? 1.f : 0.f;
@@ -642,7 +672,7 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
   float* rec = a.ws.intra + (static_cast<int64_t>(head) * a.ws.nwp + static_cast<int64_t>(win) * T) * DVP;
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
-    const int qi = 64 * w + 16 * qb + lr;
+    const int qi = 64 * qg + 16 * qb + lr;
     if (qi >= nvalid) continue;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
