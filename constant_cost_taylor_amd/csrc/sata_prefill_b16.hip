@@ -169,20 +169,36 @@ __global__ __launch_bounds__(256) void prefill_amax(ScanArgs a) {
   uint32_t m[3] = {0u, 0u, 0u};
   if (t_begin < t_end) {
     const int64_t e0 = (a.t0 + t_begin) * DK, e1 = (a.t0 + t_end) * DK;   // DK % 8 == 0
-    const void* src[3] = {a.q, a.k, a.v};
+    const int64_t hoff = static_cast<int64_t>(head) * a.n_total * DK;
+    const uint16_t* src[3] = {static_cast<const uint16_t*>(a.q) + hoff, static_cast<const uint16_t*>(a.k) + hoff,
+                              static_cast<const uint16_t*>(a.v) + hoff};
+    auto fold = [&](uint32_t& acc, const u32x4& v) {
 #pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      const uint16_t* p = static_cast<const uint16_t*>(src[x]) + static_cast<int64_t>(head) * a.n_total * DK;
-      uint32_t acc = 0u;
-      for (int64_t e = e0 + 8 * tid; e < e1; e += 8 * 256) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p + e);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w2 = v[j] & 0x7fff7fffu;
-          acc = max(acc, max(w2 & 0xffffu, w2 >> 16));
-        }
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w2 = v[j] & 0x7fff7fffu;
+        acc = max(acc, max(w2 & 0xffffu, w2 >> 16));
       }
-      m[x] = acc;
+    };
+    // q, k and v together, four strides deep: twelve loads in flight
+    constexpr int64_t STR = 8 * 256;
+    int64_t e = e0 + 8 * tid;
+    for (; e + 3 * STR < e1; e += 4 * STR) {
+      u32x4 v[3][4];
+#pragma unroll
+      for (int x = 0; x < 3; ++x)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[x][u] = *reinterpret_cast<const u32x4*>(src[x] + e + u * STR);
+#pragma unroll
+      for (int x = 0; x < 3; ++x)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fold(m[x], v[x][u]);
+    }
+    for (; e < e1; e += STR) {
+      u32x4 v[3];
+#pragma unroll
+      for (int x = 0; x < 3; ++x) v[x] = *reinterpret_cast<const u32x4*>(src[x] + e);
+#pragma unroll
+      for (int x = 0; x < 3; ++x) fold(m[x], v[x]);
     }
   }
 #pragma unroll
@@ -225,13 +241,30 @@ __global__ __launch_bounds__(256) void prefill_stage(ScanArgs a) {
   uint16_t* rec = a.ws.stg + (static_cast<int64_t>(head) * nchp + ch) * (4 * DK * L);
   const uint16_t* src[3] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                             static_cast<const uint16_t*>(a.q)};
-  for (int e = tid; e < 3 * L * NU; e += 256) {
+  // Every load of the chunk first (a token past the window reads the chunk's
+  // first token and is zeroed), then the conversions and LDS writes.
+  constexpr int NI = (3 * L * NU + 255) / 256;
+  u32x4 raws[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int e = tid + 256 * i;
     const int x = e / (L * NU);
     const int r = e % (L * NU);
     const int t = r / NU, u = r % NU;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (t < nvalid)
-      raw = *reinterpret_cast<const u32x4*>(src[x] + (static_cast<int64_t>(head) * a.n_total + tok0 + t) * DK + 8 * u);
+    const bool ok = e < 3 * L * NU && t < nvalid;
+    const uint16_t* sx = !ok || x == 0 ? src[0] : x == 1 ? src[1] : src[2];
+    raws[i] = *reinterpret_cast<const u32x4*>(sx + (static_cast<int64_t>(head) * a.n_total + tok0 + (ok ? t : 0)) * DK +
+                                              (ok ? 8 * u : 0));
+    if (!ok) raws[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int e = tid + 256 * i;
+    if (e >= 3 * L * NU) break;
+    const int x = e / (L * NU);
+    const int r = e % (L * NU);
+    const int t = r / NU, u = r % NU;
+    const u32x4 raw = raws[i];
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -241,7 +274,8 @@ __global__ __launch_bounds__(256) void prefill_stage(ScanArgs a) {
         vraw[t][8 * u + 2 * j] = lo;
         vraw[t][8 * u + 2 * j + 1] = hi;
       }
-      o[j] = hs.safe ? pack_f16(lo * mul[x], hi * mul[x]) : wj;
+      const float mx = x == 0 ? mul[0] : x == 1 ? mul[1] : mul[2];   // no indexed private array
+      o[j] = hs.safe ? pack_f16(lo * mx, hi * mx) : wj;
       tr[x][(8 * u + 2 * j) * TS + t] = static_cast<uint16_t>(o[j] & 0xffffu);
       tr[x][(8 * u + 2 * j + 1) * TS + t] = static_cast<uint16_t>(o[j] >> 16);
     }
