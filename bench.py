@@ -32,7 +32,7 @@ METRIC = "causal SATA tokens/sec/head (prefill, decode) + % of HBM/MFMA roofline
 # FETCH_SIZE / WRITE_SIZE counters scaled by a 1 GiB copy
 # (profiles/decode_update_readout_256x4096_d64_hbm_traffic.txt).  Re-measure after any
 # change to the decode kernel.
-DECODE_TRAFFIC_BYTES = 6.3864e9
+DECODE_TRAFFIC_BYTES = 6.4903e9
 
 
 def parse():
@@ -50,6 +50,10 @@ def parse():
                     help="instead of the step: prefill throughput of the other workloads at their full "
                          "sizes (d8 n256 fp32, d16 n4096 fp32, d64 n16384 bf16), each against the MFMA "
                          "peak of its arithmetic")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the step: what this box sustains with plain library kernels -- a "
+                         "1 GiB device copy, an in-place read-modify-write and a read of 3 GiB, and a "
+                         "bf16 GEMM -- next to the published peaks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB), the "
                          "reference for scaling hardware byte counters")
@@ -190,6 +194,54 @@ def configs(args):
                       "steps": args.steps, "warmup": args.warmup, "points": rows}), flush=True)
 
 
+def ceilings(args):
+    """Measured ceilings of this machine (torch / hipBLASLt kernels, HIP events):
+    the bandwidth a read+write stream, an in-place read-modify-write stream
+    and a read stream reach, and the bf16 matrix rate of a large GEMM."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ms))
+
+    res = {}
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 20)
+    res["copy_1GiB_read_write_gbs"] = 2 * src.numel() * 4 / (t * 1e-3) / 1e9
+    del src, dst
+    big = torch.ones(3 << 28, dtype=torch.float32, device=dev)
+    t = timed(lambda: big.add_(1.0), 10)
+    res["inplace_rmw_3GiB_gbs"] = 2 * big.numel() * 4 / (t * 1e-3) / 1e9
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    t = timed(lambda: torch.sum(big, dim=0, out=acc), 10)
+    res["read_3GiB_sum_gbs"] = big.numel() * 4 / (t * 1e-3) / 1e9
+    del big, acc
+    torch.cuda.empty_cache()
+    n = 8192
+    a = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    t = timed(lambda: torch.matmul(a, b, out=c), 20)
+    res["gemm_bf16_8192_tflops"] = 2 * n ** 3 / (t * 1e-3) / 1e12
+    print(json.dumps({"metric": "measured ceilings of this box", "peaks": {"hbm_gbs": HBM_PEAK_GBS,
+                      "bf16_tflops": BF16_PEAK_TFLOPS, "fp32_tflops": FP32_PEAK_TFLOPS}, "measured": res}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -201,6 +253,9 @@ def main():
         return
     if args.configs:
         configs(args)
+        return
+    if args.ceilings:
+        ceilings(args)
         return
     import torch
     import constant_cost_taylor_amd as sa
@@ -311,7 +366,8 @@ def main():
         "decode": {"head_tokens_per_s": S / (dec * 1e-3), "ms_per_step": dec,
                    "first_last_ratio": float(np.mean(dec_ms[:8]) / np.mean(dec_ms[-8:])),
                    "hbm_gbs": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "decode_update_readout", "achieved": dec_gbs,
+        "roofline": {"bound": "hbm", "kernel": "decode step: decode_update_readout + decode_reduce",
+                     "achieved": dec_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                      "traffic": DECODE_TRAFFIC_BYTES if dsteps else None,
                      "traffic_unit": "bytes per launch (HBM, counter-measured)",

@@ -408,7 +408,8 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
 }
 
 int decode_tiles(const sata_basis* b) {
-  return static_cast<int>((b->D + sata::kDecodeRows - 1) / sata::kDecodeRows);
+  const int rows = sata::decode_rows(b->d);
+  return static_cast<int>((b->D + rows - 1) / rows);
 }
 
 }  // namespace

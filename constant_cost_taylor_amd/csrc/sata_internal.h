@@ -17,9 +17,17 @@ constexpr int kWaves = 4;
 // one wave's LDS traffic and operand building overlap the other's MFMAs.
 constexpr int prefill_waves(bool bf16) { return bf16 ? 8 : kWaves; }
 
-// Rows of one decode tile and threads of every decode / reduce block.
-constexpr int kDecodeRows = 512;
+// Threads of every decode / prefill-reduce block.
 constexpr int kThreads = 256;
+
+// Rows of one decode tile: SATA_DEC_U rows of d_v floats per thread (one
+// float4 per thread and row).  Small one-shot blocks stream a
+// read-modify-write faster than long-running ones on this part.
+#ifndef SATA_DEC_U
+#define SATA_DEC_U 2
+#endif
+constexpr int kDecodeU = SATA_DEC_U;
+constexpr int decode_rows(int dv) { return kDecodeU * kThreads / (dv / 4); }
 
 // Tokens per prefill chunk: 64 for bf16 inputs (the readout operand of the
 // state is refreshed once per chunk, so longer chunks amortise it), 32 for

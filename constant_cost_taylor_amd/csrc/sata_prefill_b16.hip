@@ -991,7 +991,16 @@ __global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
     float s = 0.f;
     if (tt < ntok) {
       const float* rz = a.ws.recz + static_cast<int64_t>(head) * nt * nwp + t0 + tt;
-      for (int tl = qq; tl < nt; tl += 4) s += __builtin_nontemporal_load(rz + static_cast<int64_t>(tl) * nwp);
+      // groups of eight loads in flight, summed in tile order
+      int tl = qq;
+      for (; tl + 28 < nt; tl += 32) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_nontemporal_load(rz + static_cast<int64_t>(tl + 4 * i) * nwp);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += x[i];
+      }
+      for (; tl < nt; tl += 4) s += __builtin_nontemporal_load(rz + static_cast<int64_t>(tl) * nwp);
     }
     dpart[qq][tt] = s;
   }
@@ -1036,6 +1045,23 @@ __global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
       }
     };
     int tl = 0;
+    if constexpr (std::is_same<RedT, uint16_t>::value) {
+      // groups of eight record loads in flight, folded in tile order
+      for (; tl + 7 < nt; tl += 8) {
+        u32x4 x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + (tl + i) * tstride));
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t xj = x[i][j];
+            r[2 * j] += bf16_lo(xj);
+            r[2 * j + 1] += bf16_hi(xj);
+          }
+      }
+    }
 #pragma unroll 4
     for (; tl < nt; ++tl) add_tile(tl);
     const float* ip = intra + static_cast<int64_t>(t) * DVP + 8 * u;
