@@ -8,15 +8,16 @@
 // output from the weighted sum over orders].
 //
 // The step is bound by HBM: every state value is read once and written once.
-// Layout of the work: grid = (row tiles) x (states), tiles of two rows per
-// thread (32 rows of 64 floats at d_v = 64: 8 KB of state per block).  A block
+// Layout of the work: grid = (row tiles) x (states), blocks of 128 threads,
+// tiles of two rows per thread (16 rows of 64 floats at d_v = 64: 4 KB of
+// state per block).  A block
 // issues the loads of its S rows and z values first, builds the features of
 // its rows (phi_k unweighted, phi_q with the row weight) while they are in
 // flight, then applies the rank-1 update, stores, and forms its readout
 // partial sums; a second kernel reduces the per-tile partials in a fixed
 // order and divides.  Small one-shot blocks stream this read-modify-write at
-// 6.1 TB/s where 512-row blocks that loop over their rows reach 5.3 (the
-// partials add 1.6 % to the traffic).  The state is touched once per step and
+// 6.2 TB/s where 512-row blocks that loop over their rows reach 5.3 (the
+// partials add 3.3 % to the traffic).  The state is touched once per step and
 // is far larger than the caches, so its loads and stores carry the
 // non-temporal hint.
 #include <hip/hip_runtime.h>
@@ -43,19 +44,20 @@ __device__ __forceinline__ f4v fma4(float s, f4v v, f4v acc) {
 }
 
 template <int DK, typename IT>
-__global__ __launch_bounds__(kThreads) void decode_update_readout(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeArgs a) {
   constexpr int DV = DK;
   constexpr int TPR = DV / 4;          // threads per S row, one float4 each
-  constexpr int RPP = kThreads / TPR;  // rows per pass of the block
+  constexpr int RPP = kDecodeThreads / TPR;  // rows per pass of the block
   constexpr int DVP = padded_dv(DV);
   constexpr int R = decode_rows(DV);   // rows of the tile
   constexpr int U = R / RPP;           // rows per thread, all in flight at once
-  static_assert(U * RPP == R && R <= kThreads, "decode tile shape");
+  static_assert(U * RPP == R && R <= kDecodeThreads, "decode tile shape");
+  static_assert(DV < kDecodeThreads, "one thread per value column plus one for den");
 
   __shared__ float xq[DK], xk[DK], xv[DV];
   __shared__ float fk[R], fq[R];
   __shared__ float red[RPP * DV];
-  __shared__ float dred[kThreads / 64];
+  __shared__ float dred[kDecodeThreads / 64];
 
   const int tile = blockIdx.x;
   const int s = blockIdx.y;
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void decode_update_readout(DecodeArgs a) 
   }
   if (tid == DV) {
     float sum = 0.f;
-    for (int j = 0; j < kThreads / 64; ++j) sum += dred[j];
+    for (int j = 0; j < kDecodeThreads / 64; ++j) sum += dred[j];
     part[DV] = sum;
   }
 }
@@ -206,9 +208,9 @@ template <int D>
 hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.n_tiles, a.S);
   if (bf16)
-    decode_update_readout<D, uint16_t><<<grid, kThreads, 0, st>>>(a);
+    decode_update_readout<D, uint16_t><<<grid, kDecodeThreads, 0, st>>>(a);
   else
-    decode_update_readout<D, float><<<grid, kThreads, 0, st>>>(a);
+    decode_update_readout<D, float><<<grid, kDecodeThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_reduce<D><<<a.S, kRedThreads, 0, st>>>(a);

@@ -20,14 +20,23 @@ constexpr int prefill_waves(bool bf16) { return bf16 ? 8 : kWaves; }
 // Threads of every decode / prefill-reduce block.
 constexpr int kThreads = 256;
 
-// Rows of one decode tile: SATA_DEC_U rows of d_v floats per thread (one
-// float4 per thread and row).  Small one-shot blocks stream a
-// read-modify-write faster than long-running ones on this part.
+// Decode tiles: blocks of kDecodeThreads threads, kDecodeU rows of d_v
+// floats per thread (one float4 per thread and row).  Small one-shot blocks
+// stream a read-modify-write faster than long-running ones on this part.
 #ifndef SATA_DEC_U
 #define SATA_DEC_U 2
 #endif
+#ifndef SATA_DEC_T
+#define SATA_DEC_T 128
+#endif
 constexpr int kDecodeU = SATA_DEC_U;
-constexpr int decode_rows(int dv) { return kDecodeU * kThreads / (dv / 4); }
+constexpr int kDecodeThreads = SATA_DEC_T;
+constexpr int decode_rows(int dv) {
+  // at most one row per thread (features and z are one row a thread)
+  int u = kDecodeU;
+  while (u > 1 && u * (kDecodeThreads / (dv / 4)) > kDecodeThreads) --u;
+  return u * (kDecodeThreads / (dv / 4));
+}
 
 // Tokens per prefill chunk: 64 for bf16 inputs (the readout operand of the
 // state is refreshed once per chunk, so longer chunks amortise it), 32 for
