@@ -48,7 +48,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
   constexpr int DV = DK;
   constexpr int TPR = DV / 4;          // threads per S row, one float4 each
   constexpr int RPP = kDecodeThreads / TPR;  // rows per pass of the block
-  constexpr int DVP = padded_dv(DV);
   constexpr int R = decode_rows(DV);   // rows of the tile
   constexpr int U = R / RPP;           // rows per thread, all in flight at once
   static_assert(U * RPP == R && R <= kDecodeThreads, "decode tile shape");
@@ -140,35 +139,43 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
   for (int o = 32; o > 0; o >>= 1) dacc += __shfl_xor(dacc, o);
   if ((tid & 63) == 0) dred[tid >> 6] = dacc;
   __syncthreads();
-  float* part = a.part + (static_cast<int64_t>(s) * a.n_tiles + tile) * DVP;
+  const int64_t pi = static_cast<int64_t>(s) * a.n_tiles + tile;
   if (tid < DV) {
     float sum = 0.f;
     for (int j = 0; j < RPP; ++j) sum += red[j * DV + tid];
-    part[tid] = sum;
+    a.part[pi * DV + tid] = sum;
   }
   if (tid == DV) {
     float sum = 0.f;
     for (int j = 0; j < kDecodeThreads / 64; ++j) sum += dred[j];
-    part[DV] = sum;
+    a.partz[pi] = sum;
   }
 }
 
-// One block of kRedThreads per state: groups of DVP/4 threads sum
-// interleaved tiles with float4 loads (eight in flight per thread), then the
-// groups are combined in a fixed order and num / den is written.
+// One block of kRedThreads per state: groups of DV/4 threads sum interleaved
+// tiles of the value partials with float4 loads (eight in flight per thread),
+// every thread sums strided den partials; both are combined in a fixed order
+// and num / den is written.
 constexpr int kRedThreads = 1024;
 template <int DV>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce(DecodeArgs a) {
-  constexpr int DVP = padded_dv(DV);
-  constexpr int Q = DVP / 4;             // float4 columns per tile record
+  constexpr int Q = DV / 4;              // float4 columns per tile record
   constexpr int G = kRedThreads / Q;     // tile groups
   __shared__ float4 red[G * Q];
-  __shared__ float tot[DVP];
+  __shared__ float dz[kRedThreads];
+  __shared__ float dz2[32];
+  __shared__ float tot[DV + 1];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int grp = tid / Q;
   const int c = tid % Q;
-  const float4* part = reinterpret_cast<const float4*>(a.part + static_cast<int64_t>(s) * a.n_tiles * DVP);
+  const float4* part = reinterpret_cast<const float4*>(a.part + static_cast<int64_t>(s) * a.n_tiles * DV);
+  const float* partz = a.partz + static_cast<int64_t>(s) * a.n_tiles;
+  {
+    float z = 0.f;
+    for (int t = tid; t < a.n_tiles; t += kRedThreads) z += partz[t];
+    dz[tid] = z;
+  }
   if (grp < G) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int t = grp;
@@ -194,11 +201,22 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(DecodeArgs a) {
     red[grp * Q + c] = acc;
   }
   __syncthreads();
-  if (tid < DVP) {
+  if (tid < DV) {
     const float* redf = reinterpret_cast<const float*>(red);
     float sum = 0.f;
-    for (int gg = 0; gg < G; ++gg) sum += redf[gg * DVP + tid];
+    for (int gg = 0; gg < G; ++gg) sum += redf[gg * DV + tid];
     tot[tid] = sum;
+  } else if (tid >= 64 && tid < 96) {
+    // den: 32 sums of 32 consecutive thread totals, then their sum (below)
+    float sum = 0.f;
+    for (int j = 0; j < kRedThreads / 32; ++j) sum += dz[(tid - 64) * (kRedThreads / 32) + j];
+    dz2[tid - 64] = sum;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float sum = 0.f;
+    for (int j = 0; j < 32; ++j) sum += dz2[j];
+    tot[DV] = sum;
   }
   __syncthreads();
   if (tid < DV) a.out[static_cast<int64_t>(s) * DV + tid] = tot[tid] / tot[DV];

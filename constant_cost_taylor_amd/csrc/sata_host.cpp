@@ -407,6 +407,15 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
   return pl;
 }
 
+// Decode workspace: value partials [S][tiles][d_v] then den partials
+// [S][tiles], each region 256-byte aligned.
+size_t decode_part_bytes(int S, int tiles, int d_v) {
+  return (static_cast<size_t>(S) * tiles * d_v * sizeof(float) + 255) / 256 * 256;
+}
+size_t decode_partz_bytes(int S, int tiles) {
+  return (static_cast<size_t>(S) * tiles * sizeof(float) + 255) / 256 * 256;
+}
+
 int decode_tiles(const sata_basis* b) {
   const int rows = sata::decode_rows(b->d);
   return static_cast<int>((b->D + rows - 1) / rows);
@@ -616,7 +625,7 @@ int sata_decode_workspace(const sata_basis* b, int S, int d_v, int dtype, size_t
   if (!b || !bytes || S < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
-  *bytes = static_cast<size_t>(S) * decode_tiles(b) * sata::padded_dv(d_v) * sizeof(float);
+  *bytes = decode_part_bytes(S, decode_tiles(b), d_v) + decode_partz_bytes(S, decode_tiles(b));
   return SATA_OK;
 }
 
@@ -637,10 +646,13 @@ int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void*
   if (!ws || ws_bytes < need) return SATA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
   if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  const int tiles = decode_tiles(b);
+  float* part = static_cast<float*>(ws);
+  float* partz = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v));
   sata::DecodeArgs a{q, k, v, state,
                      sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D),
-                     static_cast<float*>(ws), out, b->d_rows, b->d_weight, S,
-                     static_cast<int>(b->D), decode_tiles(b)};
+                     part, partz, out, b->d_rows, b->d_weight, S,
+                     static_cast<int>(b->D), tiles};
   if (sata::launch_decode(b->d, dtype == SATA_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SATA_ERR_HIP;
   return SATA_OK;

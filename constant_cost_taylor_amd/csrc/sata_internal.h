@@ -192,7 +192,8 @@ struct DecodeArgs {
   const void* v;
   float* state;          // [S][stride]
   int64_t stride;        // floats between consecutive states
-  float* part;           // [S][n_tiles][DVP]
+  float* part;           // [S][n_tiles][dv]  readout partials of the value columns
+  float* partz;          // [S][n_tiles]      readout partials of den
   float* out;            // [S][dv]
   const uint32_t* rows;  // packed multiset of every row
   const float* weight;   // w_m of every row

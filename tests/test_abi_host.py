@@ -86,6 +86,10 @@ def test_workspace_sizes():
     small = SA.prefill_workspace_bytes(b, 1, 4, 100, 64, SA.SATA_BF16)
     big = SA.prefill_workspace_bytes(b, 1, 4, 16384, 64, SA.SATA_BF16)
     assert 0 < small < big
-    # decode: one partial (d_v + 1, padded to 68) per tile of 16 rows (two rows of
-    # 64 floats per thread of a 128-thread block) and state
-    assert SA.decode_workspace_bytes(b, 256, 64, SA.SATA_BF16) == 256 * math.ceil(47905 / 16) * 68 * 4
+    # decode: per tile of 16 rows (two rows of 64 floats per thread of a
+    # 128-thread block) and state, d_v value partials and one den partial, in
+    # two 256-byte aligned regions
+    tiles = math.ceil(47905 / 16)
+    up = lambda x: (x + 255) // 256 * 256
+    assert SA.decode_workspace_bytes(b, 256, 64, SA.SATA_BF16) == up(256 * tiles * 64 * 4) + up(256 * tiles * 4)
+    assert SA.decode_workspace_bytes(b, 3, 64, SA.SATA_BF16) == up(3 * tiles * 64 * 4) + up(3 * tiles * 4)
