@@ -80,7 +80,8 @@ def test_device_tables_bit_exact(d, P, c):
 # Decode
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,P,dtype,steps", [(8, 3, W.F32, 80), (16, 4, W.BF16, 40), (64, 4, W.BF16, 12)])
+@pytest.mark.parametrize("d,P,dtype,steps", [(8, 3, W.F32, 80), (16, 4, W.BF16, 40), (32, 4, W.BF16, 24),
+                                             (32, 3, W.F32, 24), (64, 4, W.BF16, 12), (64, 4, W.F32, 8)])
 def test_decode_steps_from_empty_state(d, P, dtype, steps):
     """Token-by-token decode from a zero state reproduces causal attention."""
     note(f"decode from empty d={d} P={P} {dtype} steps={steps}")
@@ -187,7 +188,7 @@ def test_prefill_continuation(d, P, dtype, n1, n2):
         assert O.row_normwise_error(got[0, h], ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("d,P,dtype", [(16, 4, W.F32), (64, 4, W.BF16)])
+@pytest.mark.parametrize("d,P,dtype", [(16, 4, W.F32), (32, 4, W.BF16), (64, 4, W.BF16)])
 def test_prefill_then_decode(d, P, dtype):
     note(f"prefill then decode d={d} P={P} {dtype}")
     n, steps, H = 257, 9, 3
