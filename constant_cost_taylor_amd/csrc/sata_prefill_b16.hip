@@ -970,12 +970,18 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
 // summed in a fixed order.  Block = (64 tokens, head); den per token first
 // (four interleaved tile sums, combined in order), then value items of 8
 // columns.  Records are read once: non-temporal loads, four tiles in flight.
+// Reduce blocks: 32 tokens x 256 threads (64 x 256: 1.5 % slower; 16 x 128
+// and 32 x 128: 5-17 % slower, 64 heads x 4096 tokens at d = 64).
+constexpr int kRedTok = 32;           // tokens per reduce block
+constexpr int kRedThr = 256;          // threads per reduce block
 template <int DK>
-__global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
-  constexpr int DV = DK, DVP = padded_dv(DV), T = prefill_window(true), NU = DV / 8, TB = 64;
+__global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
+  constexpr int DV = DK, DVP = padded_dv(DV), T = prefill_window(true), NU = DV / 8, TB = kRedTok;
+  constexpr int QQ = kRedThr / TB;    // interleaved den sums per token
+  static_assert(QQ >= 1 && QQ * TB == kRedThr, "reduce block shape");
   using RedT = typename std::conditional<prefill_bf16_records(DK, true), uint16_t, float>::type;
   __shared__ float dsh[TB];
-  __shared__ float dpart[4][TB];
+  __shared__ float dpart[QQ][TB];
   const int head = blockIdx.y;
   const int t0 = blockIdx.x * TB;
   const int tid = threadIdx.x;
@@ -987,27 +993,29 @@ __global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
   const float* intra = a.ws.intra + static_cast<int64_t>(head) * nwp * DVP;
   const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + T - 1) / T) * DVP;
   {
-    const int tt = tid % TB, qq = tid / TB;   // 256 threads: 4 interleaved sums
+    const int tt = tid % TB, qq = tid / TB;   // QQ interleaved sums per token
     float s = 0.f;
     if (tt < ntok) {
       const float* rz = a.ws.recz + static_cast<int64_t>(head) * nt * nwp + t0 + tt;
       // groups of eight loads in flight, summed in tile order
       int tl = qq;
-      for (; tl + 28 < nt; tl += 32) {
+      for (; tl + 7 * QQ < nt; tl += 8 * QQ) {
         float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = __builtin_nontemporal_load(rz + static_cast<int64_t>(tl + 4 * i) * nwp);
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_nontemporal_load(rz + static_cast<int64_t>(tl + QQ * i) * nwp);
 #pragma unroll
         for (int i = 0; i < 8; ++i) s += x[i];
       }
-      for (; tl < nt; tl += 4) s += __builtin_nontemporal_load(rz + static_cast<int64_t>(tl) * nwp);
+      for (; tl < nt; tl += QQ) s += __builtin_nontemporal_load(rz + static_cast<int64_t>(tl) * nwp);
     }
     dpart[qq][tt] = s;
   }
   __syncthreads();
   if (tid < TB) {
     const int t = t0 + tid;
-    float s = ((dpart[0][tid] + dpart[1][tid]) + dpart[2][tid]) + dpart[3][tid];
+    float s = dpart[0][tid];
+#pragma unroll
+    for (int j = 1; j < QQ; ++j) s += dpart[j][tid];
     if (tid < ntok) {
       s += intra[static_cast<int64_t>(t) * DVP + DV];
       s += carry[(t / T) * DVP + DV];
@@ -1017,7 +1025,7 @@ __global__ __launch_bounds__(256) void prefill_reduce_b16(ReduceArgs a) {
   __syncthreads();
   const RedT* rec = static_cast<const RedT*>(a.ws.rec) + static_cast<int64_t>(head) * nt * nwp * DV;
   float* out = a.out + (static_cast<int64_t>(head) * a.n_total + a.t0) * DV;
-  for (int e = tid; e < ntok * NU; e += 256) {
+  for (int e = tid; e < ntok * NU; e += kRedThr) {
     const int tt = e / NU, u = e % NU;
     const int t = t0 + tt;
     float r[8];
@@ -1095,7 +1103,7 @@ hipError_t launch_b16_t(int BH, const ScanArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_reduce_b16_t(int BH, const ReduceArgs& a, hipStream_t s) {
-  prefill_reduce_b16<D><<<dim3((a.nw + 63) / 64, BH), 256, 0, s>>>(a);
+  prefill_reduce_b16<D><<<dim3((a.nw + kRedTok - 1) / kRedTok, BH), kRedThr, 0, s>>>(a);
   return hipGetLastError();
 }
 
