@@ -294,6 +294,36 @@ def test_prefill_bf16_large_query_coordinates(d):
         assert O.row_normwise_error(got[0, h], ref) <= TOL[W.BF16], h
 
 
+def test_two_streams_share_a_basis():
+    """Prefill and decode of two state batches on two streams at once, with
+    one basis, give bit for bit what they give one after the other."""
+    note("two streams, one basis")
+    d, P, dtype, n, steps = 32, 4, W.BF16, 300, 6
+    b = SA.build_basis(d, P, 1.0)
+    ins = [W.make_qkv(1, 3, n + steps, d, d, dtype, 15000 + i) for i in range(2)]
+    dev = [tuple(to_dev(x[0], dtype) for x in qkv) for qkv in ins]
+
+    def run(i):
+        q, k, v = dev[i]
+        out, st = SA.prefill(b, q[None, :, :n].contiguous(), k[None, :, :n].contiguous(),
+                             v[None, :, :n].contiguous())
+        dec = [SA.decode_step(b, q[:, n + t].contiguous(), k[:, n + t].contiguous(),
+                              v[:, n + t].contiguous(), st) for t in range(steps)]
+        return out, st, torch.stack(dec)
+
+    ref = [run(0), run(1)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    for i in range(2):
+        with torch.cuda.stream(streams[i]):
+            got[i] = run(i)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for a, r in zip(got[i], ref[i]):
+            assert torch.equal(a, r), i
+
+
 def test_prefill_deterministic():
     note("prefill run-twice bitwise")
     d, P, dtype = 32, 4, W.BF16
