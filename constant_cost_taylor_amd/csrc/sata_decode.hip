@@ -100,9 +100,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
     const int p = static_cast<int>(pk >> 24);
     float fkk = 1.f, fqq = wr;
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
+    for (int t = 0; t < 4; ++t) {
       if (t < p) {
-        const int i = (pk >> (8 * t)) & 0xff;
+        const int i = (pk >> (6 * t)) & 63;
         fkk *= xk[i];
         fqq *= xq[i];
       }

@@ -53,11 +53,13 @@ uint64_t factorial(int n) {
   return f;
 }
 
+// Six bits per index (d_k <= 64), order in bits 24..30.
 uint32_t pack_multiset(const int32_t* m, int p) {
   uint32_t key = static_cast<uint32_t>(p) << 24;
-  for (int r = 0; r < p; ++r) key |= static_cast<uint32_t>(m[r]) << (8 * r);
+  for (int r = 0; r < p; ++r) key |= static_cast<uint32_t>(m[r]) << (6 * r);
   return key;
 }
+int key_index(uint32_t key, int r) { return static_cast<int>((key >> (6 * r)) & 63u); }
 
 // All multisets of size p over [0, d) in lexicographic order.
 std::vector<int32_t> enumerate_multisets(int d, int p, int64_t* count) {
@@ -247,14 +249,17 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
           kside[blk * 16 + 4 * g + j] =
               v2 ? static_cast<uint32_t>(row_ones) | (static_cast<uint32_t>(row_zero) << 16)
                  : static_cast<uint32_t>(xk_zero) << 16;
-        qside[blk * 4 + g] = v2 ? static_cast<uint32_t>(b->d) | (static_cast<uint32_t>(b->d) << 8) : 0u;
+        qside[blk * 4 + g] =
+            v2 ? static_cast<uint32_t>(b->d) | (static_cast<uint32_t>(b->d) << 8) | (static_cast<uint32_t>(b->d) << 24)
+               : 0u;
         continue;
       }
       const Run& run = runs[tiles[t][u]];
       if (v2) {
         const int pp = parent_order(run.parent_key);
-        const int i1 = pp >= 1 ? static_cast<int>(run.parent_key & 0xffu) : b->d;
-        const int i2 = pp >= 2 ? static_cast<int>((run.parent_key >> 8) & 0xffu) : b->d;
+        const int i1 = pp >= 1 ? key_index(run.parent_key, 0) : b->d;
+        const int i2 = pp >= 2 ? key_index(run.parent_key, 1) : b->d;
+        const int i3 = pp >= 3 ? key_index(run.parent_key, 2) : b->d;
         int prow;
         if (pp == 0) {
           prow = row_ones;
@@ -267,14 +272,17 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
             slot = static_cast<int>(slot_of.size());
             slot_of.emplace(run.parent_key, slot);
             const size_t si = static_cast<size_t>(t) * max_slots + slot;
-            parents[si] = static_cast<uint32_t>(i1) | (static_cast<uint32_t>(i2) << 8);
+            // third factor: the ones row for an order-2 parent
+            const int i3r = pp >= 3 ? i3 : row_ones;
+            parents[si] = static_cast<uint32_t>(i1) | (static_cast<uint32_t>(i2) << 8) |
+                          (static_cast<uint32_t>(i3r) << 16);
           } else {
             slot = it->second;
           }
           prow = row_slot + slot;
         }
         qside[blk * 4 + g] = static_cast<uint32_t>(i1) | (static_cast<uint32_t>(i2) << 8) |
-                             (static_cast<uint32_t>(run.c0) << 16);
+                             (static_cast<uint32_t>(run.c0) << 16) | (static_cast<uint32_t>(i3) << 24);
         for (int j = 0; j < 4; ++j) {
           const int xrow = run.row[j] >= 0 ? run.c0 + j : row_zero;
           kside[blk * 16 + 4 * g + j] = static_cast<uint32_t>(prow) | (static_cast<uint32_t>(xrow) << 16);
@@ -291,7 +299,12 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
         slot = static_cast<int>(slot_of.size());
         slot_of.emplace(run.parent_key, slot);
         const size_t si = static_cast<size_t>(t) * max_slots + slot;
-        parents[si] = (run.parent_key & 0xffffu) | (((run.parent_key >> 24) & 3u) << 16);
+        {
+          const int np = parent_order(run.parent_key);
+          uint32_t pw = static_cast<uint32_t>(np) << 24;
+          for (int r = 0; r < np; ++r) pw |= static_cast<uint32_t>(key_index(run.parent_key, r)) << (8 * r);
+          parents[si] = pw;
+        }
         pweight[si] = run.parent_weight;
         kscale[si] = run.kscale;
       } else {
@@ -429,7 +442,7 @@ static int build_basis_impl(int d_k, int P, double c, bool upload_tables, sata_b
   if (!out) return SATA_ERR_INVALID_ARG;
   *out = nullptr;
   if (!(std::isfinite(c) && c > 0.0)) return SATA_ERR_INVALID_ARG;
-  if (!supported_dim(d_k) || P < 1 || P > 4) return SATA_ERR_UNSUPPORTED;
+  if (!supported_dim(d_k) || P < 1 || P > 5) return SATA_ERR_UNSUPPORTED;
   sata_basis* b = new (std::nothrow) sata_basis;
   if (!b) return SATA_ERR_OOM;
   b->d = d_k;
@@ -602,7 +615,7 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
   for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
     const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
     sata::IntraArgs ia{q, k, v, pw, n, t0, w, b->P, inv_c};
-    sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c};
+    sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P};
     sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c};
     if (bf16) {
       if (sata::launch_prefill_b16(b->d, static_cast<int>(BH), sa, s) != hipSuccess) return SATA_ERR_HIP;

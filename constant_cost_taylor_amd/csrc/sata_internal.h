@@ -92,18 +92,20 @@ constexpr int col_blocks(int dv) { return (dv + 1 + 15) / 16; }
 //   qside[tile][wave][rb][4]: parent slot (low 16 bits) and first child index
 //       (high 16 bits) of the run held by lane group g.
 //   rowinfo[tile][wave][rb][16]: (canonical row + 1) | (count << 28), 0 = pad.
-//   parents[tile][slot]: i1 | i2 << 8 | order << 16 of each parent slot;
+//   parents[tile][slot]: i1 | i2 << 8 | i3 << 16 | order << 24 of each
+//       parent slot (order <= 3, unused indices zero);
 //   pweight[tile][slot]: 1 / prod(count!) of that parent (query side);
 //   kscale[tile][slot]: factor of the key-side parent feature (1, or 1/3 for
 //       the slot that feeds the (i, i, i) rows).
 // bfloat16 inputs (key table rows: d key rows, a zero row, a ones row, then
-// one row per order-2 parent slot):
+// one row per parent slot of order 2 or 3):
 //   kside: key-table row of the parent feature (low 16 bits) and of the
 //       child coordinate (high 16 bits) of lane row j;
-//   qside: i1 | i2 << 8 | c0 << 16 of the run of lane group g (index d = the
-//       constant 1);
+//   qside: i1 | i2 << 8 | c0 << 16 | i3 << 24 of the run of lane group g
+//       (index d = the constant 1);
 //   rowinfo: canonical row + 1, 0 = pad;  rweight: w_m of the row, 0 = pad;
-//   parents[tile][slot]: i1 | i2 << 8 of each order-2 parent slot.
+//   parents[tile][slot]: key-table rows r1 | r2 << 8 | r3 << 16 of the
+//       factors of each parent slot (r3 = the ones row for order 2).
 // Both: nslot[tile] = number of parent slots of the tile.
 struct PrefillLayout {
   int rb = 0;
@@ -159,6 +161,7 @@ struct ScanArgs {
   int nw;                // tokens in this window
   int D;                 // total basis rows (incl. order 0)
   float inv_c;           // 1 / c
+  int P;                 // orders 0..P-1
 };
 
 struct IntraArgs {

@@ -295,22 +295,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     }
     __syncthreads();
 
-    // ---- phase B: parent features (order <= 2) and the order-0 carry -----
+    // ---- phase B: parent features (order <= 3) and the order-0 carry -----
     for (int e = tid; e < nslot * L; e += kWaves * 64) {
       const int s = e / L;
       const int t = e % L;
       const uint32_t pw = spar[s];
-      const int np = (pw >> 16) & 3;
-      const int i1 = pw & 255;
-      const int i2 = (pw >> 8) & 255;
+      const int np = pw >> 24;
       float fk = spwk[s], fq = spwq[s];
-      if (np >= 1) {
-        fk *= xk[i1 * KSTR + t];
-        fq *= xq[t * XQSTR + i1];
-      }
-      if (np >= 2) {
-        fk *= xk[i2 * KSTR + t];
-        fq *= xq[t * XQSTR + i2];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        if (r < np) {
+          const int i = (pw >> (8 * r)) & 255;
+          fk *= xk[i * KSTR + t];
+          fq *= xq[t * XQSTR + i];
+        }
       }
       pk[s * KSTR + t] = fk;
       pq[s * QSTR + t] = fq;
@@ -457,7 +455,7 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
   float qi[DK];
 #pragma unroll
   for (int d = 0; d < DK; ++d) qi[d] = i < nvalid ? load_in(qh, (tb + i) * DK + d) * a.inv_c : 0.f;
-  const float rcp[4] = {0.f, 1.f, 0.5f, 1.f / 3.f};
+  const float rcp[5] = {0.f, 1.f, 0.5f, 1.f / 3.f, 0.25f};
   float num[CPG];
 #pragma unroll
   for (int cc = 0; cc < CPG; ++cc) num[cc] = 0.f;
@@ -607,7 +605,7 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) O[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float rcp[4] = {0.f, 1.f, 0.5f, 1.f / 3.f};
+  const float rcp[5] = {0.f, 1.f, 0.5f, 1.f / 3.f, 0.25f};
   const int nslice = min(2 * qg + 2, (nvalid + 31) / 32);
   for (int sl = 0; sl < nslice; ++sl) {
     f32x4 X[2][4];
@@ -635,10 +633,10 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
       for (int j = 0; j < 8; ++j) {
         const int key = 32 * sl + 16 * (j / 4) + 4 * g + (j % 4);
         const float x = X[j / 4][qb][j % 4] * a.inv_c;
-        // Horner's rule over orders P-1..1 (at most three steps, unrolled)
+        // Horner's rule over orders P-1..1 (at most four steps, unrolled)
         float h = 0.f;
 #pragma unroll
-        for (int p = 3; p >= 1; --p) {
+        for (int p = 4; p >= 1; --p) {
           const float hn = x * rcp[p] * (1.f + h);
           h = p < a.P ? hn : h;
         }

@@ -112,7 +112,7 @@ __device__ __forceinline__ void dma_barrier() {
 // max-abs values: k' = k 2^-ek, q' = q 2^ek, v' = v 2^-ev (exact), with ek,
 // ev zero unless |k| is outside [1/16, 2) or |v| outside [2^-8, 2^15).  Then
 // |k'| < 2, and the path is taken when also max |q'| <= 2: every feature (a
-// product of at most three coordinates) is below 8 in magnitude and every
+// product of at most four coordinates) is below 16 in magnitude and every
 // value below 2^15, far inside the f16 range.  Otherwise the head runs with
 // bf16 operands.
 struct HalfScales {
@@ -385,6 +385,25 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Elementwise product of three packed 16-bit 8-vectors: f16, two rounded
+// products; bf16, the exact fp32 product (8 + 8 + 8 significant bits) rounded
+// once.
+template <bool H16>
+__device__ __forceinline__ u32x4 mul8x3(u32x4 x, u32x4 y, u32x4 z) {
+  if constexpr (H16) {
+    return __builtin_bit_cast(
+        u32x4, __builtin_bit_cast(f16x8, x) * __builtin_bit_cast(f16x8, y) * __builtin_bit_cast(f16x8, z));
+  } else {
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t xj = x[j], yj = y[j], zj = z[j];
+      r[j] = pack_bf16(bf16_lo(xj) * bf16_lo(yj) * bf16_lo(zj), bf16_hi(xj) * bf16_hi(yj) * bf16_hi(zj));
+    }
+    return r;
+  }
+}
+
 // Elementwise product of two packed 16-bit 8-vectors (one MFMA operand).
 // f16: packed f16 multiplies; bf16: exact fp32 products rounded once.
 template <bool H16>
@@ -404,7 +423,9 @@ __device__ __forceinline__ u32x4 mul8(u32x4 x, u32x4 y) {
 
 // One head-tile of the scan with one operand type (the kernel below picks it
 // per head).
-template <int DK, bool H16>
+// P5: orders 0..4, whose order-3 parents carry a third coordinate on both
+// sides (a separate instantiation keeps the registers of P <= 4 as they are).
+template <int DK, bool H16, bool P5>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& hs, unsigned char* lds) {
   using C = CfgS<DK>;
   constexpr int DV = C::DV, L = C::L, NW = C::NW, RB = C::RB, NKS = C::NKS, NB = C::NB, NU = C::NU;
@@ -456,6 +477,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   // offset of its four children for token block 0 (block mb: + 2 DK mb, odd
   // blocks also - d4).
   uint32_t oq12[RB], oqc[RB];   // oq12: first | second coordinate offset << 16
+  uint32_t oq3[RB];             // third coordinate offset (P5 only)
   // Token slot lr of token block mb is token 4 lr + (mb ^ (lr & 1)) (rows of
   // both parities in every QN load); QN offsets of odd blocks are d4 lower.
   const bool odd = lr & 1;
@@ -469,9 +491,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       okpc[b] = static_cast<uint32_t>(pr * 128 + 16 * (g ^ swz_row(pr))) |
                 (static_cast<uint32_t>(cr * 128 + 16 * (g ^ swz_row(cr))) << 16);
       const uint32_t qs = a.lay.qside[(lay_base + b) * 4 + g];
-      const int i1 = qs & 255, i2 = (qs >> 8) & 255, c0 = (qs >> 16) & 255;
+      const int i1 = qs & 255, i2 = (qs >> 8) & 255, c0 = (qs >> 16) & 255, i3 = qs >> 24;
       oq12[b] = static_cast<uint32_t>(i1 * 128 + 16 * ((lr >> 1) ^ swz_row(i1)) + 8 * (lr & 1)) |
                 (static_cast<uint32_t>(i2 * 128 + 16 * ((lr >> 1) ^ swz_row(i2)) + 8 * (lr & 1)) << 16);
+      oq3[b] = P5 ? static_cast<uint32_t>(i3 * 128 + 16 * ((lr >> 1) ^ swz_row(i3)) + 8 * (lr & 1)) : 0u;
       oqc[b] = (4 * lr + (odd ? 1 : 0)) * 2 * DK + 16 * ((c0 >> 3) ^ sq) + 8 * ((c0 >> 2) & 1);
     }
   }
@@ -481,18 +504,20 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   // Parent slots: items (slot, 8-token unit), at most one per thread.
   constexpr int NSI = (NSLOT * 8 + NW * 64 - 1) / (NW * 64);
   const int nslot = a.lay.nslot[tile];
-  uint32_t so12[NSI], sod[NSI];
+  uint32_t so12[NSI], sod[NSI], so3[NSI];
 #pragma unroll
   for (int i = 0; i < NSI; ++i) {
     const int e = tid + i * NW * 64;
     sod[i] = 0xffffffffu;
     so12[i] = 0u;
+    so3[i] = 0u;
     if (e < nslot * 8) {
       const int s = e >> 3, u = e & 7;
       const uint32_t par = a.lay.parents[tile * NSLOT + s];
-      const int i1 = par & 255, i2 = (par >> 8) & 255, R = C::ROW_SLOT + s;
+      const int i1 = par & 255, i2 = (par >> 8) & 255, i3 = (par >> 16) & 255, R = C::ROW_SLOT + s;
       so12[i] = static_cast<uint32_t>(i1 * 128 + 16 * (u ^ swz_row(i1))) |
                 (static_cast<uint32_t>(i2 * 128 + 16 * (u ^ swz_row(i2))) << 16);
+      if constexpr (P5) so3[i] = static_cast<uint32_t>(i3 * 128 + 16 * (u ^ swz_row(i3)));
       sod[i] = R * 128 + 16 * (u ^ swz_row(R));
     }
   }
@@ -541,8 +566,9 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   float* st = a.state + static_cast<int64_t>(head) * a.stride;
   const int64_t zoff = static_cast<int64_t>(a.D) * DV;
   const int64_t off2 = 1 + DK, off3 = 1 + DK + static_cast<int64_t>(DK) * (DK + 1) / 2;
+  const int64_t off4 = off3 + static_cast<int64_t>(DK) * (DK + 1) * (DK + 2) / 6;
   auto row_exp = [&](int64_t m, bool value_col) {
-    const int p = m >= off3 ? 3 : m >= off2 ? 2 : m >= 1 ? 1 : 0;
+    const int p = m >= off4 ? 4 : m >= off3 ? 3 : m >= off2 ? 2 : m >= 1 ? 1 : 0;
     return p * hs.ek + (value_col ? hs.ev : 0);
   };
   // Every row index first, then every load with no branch between them (a
@@ -713,7 +739,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     }
   };
 
-  // Parent features of the order-2 parent slots of a chunk (buffer X).
+  // Parent features of the parent slots of a chunk (buffer X): products of
+  // two key rows (order 2) or three (order 3, orders 0..4 only).
   auto slots = [&](int X) {
     unsigned char* kt = lds + C::O_KT + X * C::KT_B;
 #pragma unroll
@@ -721,7 +748,12 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       if (sod[i] != 0xffffffffu) {
         const u32x4 x1 = *reinterpret_cast<const u32x4*>(kt + (so12[i] & 0xffffu));
         const u32x4 x2 = *reinterpret_cast<const u32x4*>(kt + (so12[i] >> 16));
-        *reinterpret_cast<u32x4*>(kt + sod[i]) = mul8<H16>(x1, x2);
+        if constexpr (P5) {
+          const u32x4 x3 = *reinterpret_cast<const u32x4*>(kt + so3[i]);
+          *reinterpret_cast<u32x4*>(kt + sod[i]) = mul8x3<H16>(x1, x2, x3);
+        } else {
+          *reinterpret_cast<u32x4*>(kt + sod[i]) = mul8<H16>(x1, x2);
+        }
       }
     }
   };
@@ -743,13 +775,22 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     for (int b = 0; b < RB; ++b) {
       const u32x2 x1 = *reinterpret_cast<const u32x2*>(qt + (oq12[b] & 0xffffu));
       const u32x2 x2 = *reinterpret_cast<const u32x2*>(qt + (oq12[b] >> 16));
+      // third coordinate (the ones row unless the parent has order 3)
+      const u32x2 x3 = P5 ? *reinterpret_cast<const u32x2*>(qt + oq3[b]) : u32x2{one2, one2};
       if constexpr (H16) {
-        const f16x4 p = __builtin_bit_cast(f16x4, x1) * __builtin_bit_cast(f16x4, x2);
+        f16x4 p = __builtin_bit_cast(f16x4, x1) * __builtin_bit_cast(f16x4, x2);
+        if constexpr (P5) p = p * __builtin_bit_cast(f16x4, x3);
         const u32x2 pw = __builtin_bit_cast(u32x2, p);
         pp[b] = u32x2{__builtin_amdgcn_perm(pw[0], pw[0], psel), __builtin_amdgcn_perm(pw[1], pw[1], psel)};
       } else {
         float v[4] = {bf16_lo(x1[0]) * bf16_lo(x2[0]), bf16_hi(x1[0]) * bf16_hi(x2[0]),
                       bf16_lo(x1[1]) * bf16_lo(x2[1]), bf16_hi(x1[1]) * bf16_hi(x2[1])};
+        if constexpr (P5) {
+          v[0] *= bf16_lo(x3[0]);
+          v[1] *= bf16_hi(x3[0]);
+          v[2] *= bf16_lo(x3[1]);
+          v[3] *= bf16_hi(x3[1]);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) pf[b][j] = odd ? v[j ^ 1] : v[j];
       }
@@ -955,14 +996,14 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   }
 }
 
-template <int DK>
+template <int DK, bool P5>
 __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[CfgS<DK>::LDS_B];
   const HalfScales hs = head_scales(a.ws, blockIdx.y);
   if (hs.safe)
-    scan_tile<DK, true>(a, hs, lds);
+    scan_tile<DK, true, P5>(a, hs, lds);
   else
-    scan_tile<DK, false>(a, hs, lds);
+    scan_tile<DK, false, P5>(a, hs, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1097,7 +1138,10 @@ hipError_t launch_b16_t(int BH, const ScanArgs& a, hipStream_t s) {
   prefill_carry<D><<<BH, 128, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 grid(a.lay.n_tiles, BH);
-  prefill_scan_b16<D><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
+  if (a.P == 5)
+    prefill_scan_b16<D, true><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
+  else
+    prefill_scan_b16<D, false><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@
  *   - No exceptions cross the ABI.  sata_status_string names every status.
  *   - A basis may be shared by several threads and streams; one state buffer
  *     must not be used by two calls in flight at once.
- *   - Supported: d_k = d_v in {8, 16, 32, 64}, P in {1, 2, 3, 4}, c > 0 finite.
+ *   - Supported: d_k = d_v in {8, 16, 32, 64}, P in {1, 2, 3, 4, 5}, c > 0 finite.
  *     Inputs are float32 or bfloat16; state and outputs are float32.
  */
 #ifndef SATA_H
@@ -83,9 +83,9 @@ int sata_basis_rows(const sata_basis* basis, int p, int64_t* rows);
 int sata_basis_copy_tables(const sata_basis* basis, int p, int32_t* idx, uint32_t* mult);
 
 /* Download the device copy of the row table used by the kernels, for every
- * row r in order: packed[r] = i1 | i2 << 8 | i3 << 16 | p << 24 (unused
- * indices zero) and weight[r] = float(mult / (p! c^p)).  Host pointers of
- * total_rows elements; synchronous. */
+ * row r in order: packed[r] = i1 | i2 << 6 | i3 << 12 | i4 << 18 | p << 24
+ * (six bits per index, unused indices zero) and weight[r] =
+ * float(mult / (p! c^p)).  Host pointers of total_rows elements; synchronous. */
 int sata_basis_download_rows(const sata_basis* basis, uint32_t* packed, float* weight);
 
 /* Number of float32 values of one head's state: (d_v + 1) * C(d_k + P - 1, P - 1).

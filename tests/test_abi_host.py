@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
-@pytest.mark.parametrize("d,P", [(8, 1), (8, 3), (16, 4), (32, 4), (64, 4), (64, 2)])
+@pytest.mark.parametrize("d,P", [(8, 1), (8, 3), (16, 4), (32, 4), (64, 4), (64, 2), (16, 5), (64, 5)])
 def test_host_tables_bit_exact(d, P):
     b = SA.build_basis(d, P, 1.0, host_only=True)
     ref = O.enumerate_basis(d, P)
@@ -41,7 +41,7 @@ def test_host_tables_bit_exact(d, P):
         np.testing.assert_array_equal(hm, mult)
 
 
-@pytest.mark.parametrize("d,P", [(8, 3), (16, 4), (64, 4), (32, 4)])
+@pytest.mark.parametrize("d,P", [(8, 3), (16, 4), (64, 4), (32, 4), (8, 5), (64, 5)])
 def test_state_size_matches_closed_form(d, P):
     b = SA.build_basis(d, P, 1.0, host_only=True)
     assert b.state_floats() == O.cost_model(d, d, P)[0]
@@ -52,7 +52,7 @@ def test_invalid_builds():
     h = ctypes.c_void_p()
     L = SA.lib()
     assert L.sata_build_basis_host(7, 3, 1.0, ctypes.byref(h)) == SA.SATA_ERR_UNSUPPORTED
-    assert L.sata_build_basis_host(16, 5, 1.0, ctypes.byref(h)) == SA.SATA_ERR_UNSUPPORTED
+    assert L.sata_build_basis_host(16, 6, 1.0, ctypes.byref(h)) == SA.SATA_ERR_UNSUPPORTED
     assert L.sata_build_basis_host(16, 0, 1.0, ctypes.byref(h)) == SA.SATA_ERR_UNSUPPORTED
     assert L.sata_build_basis_host(16, 3, 0.0, ctypes.byref(h)) == SA.SATA_ERR_INVALID_ARG
     assert L.sata_build_basis_host(16, 3, float("nan"), ctypes.byref(h)) == SA.SATA_ERR_INVALID_ARG

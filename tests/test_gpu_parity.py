@@ -57,7 +57,8 @@ def run_prefill(basis, q, k, v, dtype, state=None):
 # Tables
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,P,c", [(8, 3, 1.0), (16, 4, 1.0), (32, 4, 0.5), (64, 4, 1.0), (64, 1, 2.0)])
+@pytest.mark.parametrize("d,P,c", [(8, 3, 1.0), (16, 4, 1.0), (32, 4, 0.5), (64, 4, 1.0), (64, 1, 2.0),
+                                   (16, 5, 1.0), (64, 5, 0.5)])
 def test_device_tables_bit_exact(d, P, c):
     note(f"device tables d={d} P={P} c={c}")
     b = SA.build_basis(d, P, c)
@@ -67,9 +68,9 @@ def test_device_tables_bit_exact(d, P, c):
     exp_weight = []
     for p, (idx, mult, scale) in enumerate(ref):
         for r in range(idx.shape[0]):
-            key = p << 24
+            key = p << 24   # six bits per index
             for j in range(p):
-                key |= int(idx[r, j]) << (8 * j)
+                key |= int(idx[r, j]) << (6 * j)
             exp_packed.append(key)
         exp_weight.append((mult.astype(np.float64) * scale).astype(np.float32))
     np.testing.assert_array_equal(packed, np.array(exp_packed, dtype=np.uint32))
@@ -81,7 +82,8 @@ def test_device_tables_bit_exact(d, P, c):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("d,P,dtype,steps", [(8, 3, W.F32, 80), (16, 4, W.BF16, 40), (32, 4, W.BF16, 24),
-                                             (32, 3, W.F32, 24), (64, 4, W.BF16, 12), (64, 4, W.F32, 8)])
+                                             (32, 3, W.F32, 24), (64, 4, W.BF16, 12), (64, 4, W.F32, 8),
+                                             (8, 5, W.F32, 40), (32, 5, W.BF16, 16), (64, 5, W.F32, 6)])
 def test_decode_steps_from_empty_state(d, P, dtype, steps):
     """Token-by-token decode from a zero state reproduces causal attention."""
     note(f"decode from empty d={d} P={P} {dtype} steps={steps}")
@@ -120,6 +122,14 @@ CASES = [
     ("d64_bf16_odd_chunks", 1, 1, 1050, 64, 4, 1.0, W.BF16),
     ("d64_bf16_P3", 1, 1, 200, 64, 3, 0.75, W.BF16),
     ("d8_bf16", 1, 1, 97, 8, 4, 1.0, W.BF16),
+    # orders 0..4
+    ("d8_P5", 1, 2, 300, 8, 5, 1.0, W.F32),
+    ("d8_P5_bf16", 1, 1, 200, 8, 5, 1.0, W.BF16),
+    ("d16_P5_bf16", 1, 2, 600, 16, 5, 1.0, W.BF16),
+    ("d32_P5_f32", 1, 1, 200, 32, 5, 1.0, W.F32),
+    ("d32_P5_bf16", 1, 1, 530, 32, 5, 0.75, W.BF16),
+    ("d64_P5_f32", 1, 1, 100, 64, 5, 1.0, W.F32),
+    ("d64_P5_bf16", 1, 2, 300, 64, 5, 1.0, W.BF16),
 ]
 
 
@@ -147,7 +157,7 @@ def test_prefill_empty_is_noop():
 
 
 @pytest.mark.parametrize("d,P,dtype,n", [(16, 4, W.F32, 300), (8, 3, W.F32, 70), (64, 4, W.BF16, 96),
-                                         (32, 4, W.BF16, 150)])
+                                         (32, 4, W.BF16, 150), (16, 5, W.F32, 200), (32, 5, W.BF16, 120)])
 def test_prefill_state_matches_direct_state(d, P, dtype, n):
     """The state written back equals sum_j phi(k_j) v_j and sum_j phi(k_j)
     (unweighted monomials, canonical row order)."""
@@ -174,7 +184,7 @@ def test_prefill_state_matches_direct_state(d, P, dtype, n):
 
 
 @pytest.mark.parametrize("d,P,dtype,n1,n2", [(16, 4, W.F32, 200, 333), (64, 4, W.BF16, 100, 161),
-                                             (8, 3, W.F32, 33, 64)])
+                                             (8, 3, W.F32, 33, 64), (64, 5, W.BF16, 100, 161)])
 def test_prefill_continuation(d, P, dtype, n1, n2):
     """prefill(a) then prefill(b | state) gives the rows of prefill(a + b)."""
     note(f"continuation d={d} P={P} {dtype} {n1}+{n2}")
@@ -188,7 +198,8 @@ def test_prefill_continuation(d, P, dtype, n1, n2):
         assert O.row_normwise_error(got[0, h], ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("d,P,dtype", [(16, 4, W.F32), (32, 4, W.BF16), (64, 4, W.BF16)])
+@pytest.mark.parametrize("d,P,dtype", [(16, 4, W.F32), (32, 4, W.BF16), (64, 4, W.BF16), (32, 5, W.BF16),
+                                       (64, 5, W.F32)])
 def test_prefill_then_decode(d, P, dtype):
     note(f"prefill then decode d={d} P={P} {dtype}")
     n, steps, H = 257, 9, 3
@@ -206,7 +217,7 @@ def test_prefill_then_decode(d, P, dtype):
         assert O.row_normwise_error(got[h], ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("d,P,dtype,n", [(64, 4, W.BF16, 700), (16, 4, W.F32, 530)])
+@pytest.mark.parametrize("d,P,dtype,n", [(64, 4, W.BF16, 700), (16, 4, W.F32, 530), (32, 5, W.BF16, 700)])
 def test_prefill_many_windows(d, P, dtype, n, monkeypatch):
     """A small workspace cap splits the sequence into many windows (the state
     is written back and reloaded between them); results are unchanged."""
