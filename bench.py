@@ -50,6 +50,11 @@ def parse():
                     help="instead of the step: prefill throughput of the other workloads at their full "
                          "sizes (d8 n256 fp32, d16 n4096 fp32, d64 n16384 bf16), each against the MFMA "
                          "peak of its arithmetic")
+    ap.add_argument("--order5", action="store_true",
+                    help="instead of the step: orders 0..4 (P=5) at d_k=d_v=64, 32 states, bf16 -- a "
+                         "4096-token prefill against the MFMA peak, then --order5-steps decode steps "
+                         "against the HBM peak")
+    ap.add_argument("--order5-steps", type=int, default=64)
     ap.add_argument("--ceilings", action="store_true",
                     help="instead of the step: what this box sustains with plain library kernels -- a "
                          "1 GiB device copy, an in-place read-modify-write and a read of 3 GiB, and a "
@@ -194,6 +199,74 @@ def configs(args):
                       "steps": args.steps, "warmup": args.warmup, "points": rows}), flush=True)
 
 
+def order5(args):
+    """Orders 0..4 at d = 64: the prefill leg and the decode leg of a 32-state
+    step, each against its roofline, with a sampled check of the last decode
+    outputs against the oracle."""
+    import torch
+    import constant_cost_taylor_amd as sa
+    import workloads as W
+    from oracle import sata_oracle as O
+    w = W.WORKLOADS["order5_32x4096_d64"]
+    S = w.B * w.H
+    dsteps = args.order5_steps
+    q, k, v = W.workload_inputs(w)
+    qs, ks, vs = W.decode_inputs(w, dsteps)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    basis = sa.build_basis(w.d_k, w.P, w.c)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(dev)
+    Q, K, V = bf(q), bf(k), bf(v)
+    DQ, DK, DV = bf(qs), bf(ks), bf(vs)
+    state = sa.new_state(basis, S, dev)
+    out = torch.empty((w.B, w.H, w.n, w.d_v), dtype=torch.float32, device=dev)
+    dout = torch.empty((dsteps, S, w.d_v), dtype=torch.float32, device=dev)
+    pws = sa.workspace(sa.prefill_workspace_bytes(basis, w.B, w.H, w.n, w.d_v, sa.SATA_BF16), dev)
+    dws = sa.workspace(sa.decode_workspace_bytes(basis, S, w.d_v, sa.SATA_BF16), dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(dsteps + 2)]
+    pre_ms, dec_ms = [], []
+    for it in range(args.warmup + args.steps):
+        state.zero_()
+        ev[0].record(stream)
+        sa.prefill(basis, Q, K, V, state=state, out=out, ws=pws)
+        ev[1].record(stream)
+        for t in range(dsteps):
+            sa.decode_step(basis, DQ[t], DK[t], DV[t], state, out=dout[t], ws=dws)
+            ev[t + 2].record(stream)
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            pre_ms.append(ev[0].elapsed_time(ev[1]))
+            dec_ms.extend(ev[t + 1].elapsed_time(ev[t + 2]) for t in range(dsteps))
+        print(f"order5 step {it}: prefill {ev[0].elapsed_time(ev[1]):.2f} ms", file=sys.stderr, flush=True)
+    got = dout[:, [0, S - 1]].cpu().numpy()
+    qf, kf, vf = (x.reshape(S, w.n, -1) for x in (q, k, v))
+    errs = []
+    for j, s in enumerate([0, S - 1]):
+        rr = np.arange(w.n, w.n + dsteps, max(1, dsteps // 8))
+        ref = O.direct_taylor(np.concatenate([qf[s], qs[:, s]]).astype(np.float64),
+                              np.concatenate([kf[s], ks[:, s]]).astype(np.float64),
+                              np.concatenate([vf[s], vs[:, s]]).astype(np.float64), w.P, w.c, rows=rr)
+        errs.append(O.row_normwise_error(got[rr - w.n, j], ref))
+    pre = float(np.median(pre_ms))
+    dec = float(np.mean(dec_ms))
+    D = basis.total_rows
+    dec_bytes = S * (2 * 4 * (w.d_v + 1) * D + 3 * w.d_k * 2 + w.d_v * 4)
+    _, page_flops = O.cost_model(w.d_k, w.d_v, w.P)
+    pre_tflops = S * w.n * page_flops / (pre * 1e-3) / 1e12
+    dec_gbs = dec_bytes / (dec * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "orders 0..4 (P=5) prefill and decode vs roofline", "unit": "head-tokens/s",
+        "config": {"workload": f"order5: {S} states (batch {w.B} x {w.H} heads), d_k=d_v={w.d_k}, P={w.P}, "
+                               f"D={D}, bf16 inputs, f32 state, {w.n}-token prefill + {dsteps} decode steps"},
+        "steps": args.steps, "warmup": args.warmup,
+        "prefill": {"ms": pre, "head_tokens_per_s": S * w.n / (pre * 1e-3), "page_tflops": pre_tflops,
+                    "mfma_bf16_frac": pre_tflops / BF16_PEAK_TFLOPS},
+        "decode": {"ms_per_step": dec, "head_tokens_per_s": S / (dec * 1e-3), "hbm_gbs": dec_gbs,
+                   "hbm_frac": dec_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dec_bytes},
+        "check": {"decode_row_normwise_err": max(errs)}}), flush=True)
+
+
 def ceilings(args):
     """Measured ceilings of this machine (torch / hipBLASLt kernels, HIP events):
     the bandwidth a read+write stream, an in-place read-modify-write stream
@@ -256,6 +329,9 @@ def main():
         return
     if args.ceilings:
         ceilings(args)
+        return
+    if args.order5:
+        order5(args)
         return
     import torch
     import constant_cost_taylor_amd as sa

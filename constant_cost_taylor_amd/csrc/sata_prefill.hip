@@ -514,7 +514,8 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
 // V' = [v, 1, 0...]: its ones row gives the denominator.  The order-0 term
 // goes through the exact 0/1 mask, so only the small higher-order weights W'
 // are rounded to bf16.
-template <int DK>
+// P5: orders 0..4 (a fourth Horner step; P <= 4 takes three).
+template <int DK, bool P5>
 __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(IntraArgs a) {
   constexpr int DV = DK, T = prefill_window(true);
   constexpr int NT = T;                        // threads: one 64-query wave per 64 tokens
@@ -633,10 +634,10 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
       for (int j = 0; j < 8; ++j) {
         const int key = 32 * sl + 16 * (j / 4) + 4 * g + (j % 4);
         const float x = X[j / 4][qb][j % 4] * a.inv_c;
-        // Horner's rule over orders P-1..1 (at most four steps, unrolled)
+        // Horner's rule over orders P-1..1 (unrolled)
         float h = 0.f;
 #pragma unroll
-        for (int p = 4; p >= 1; --p) {
+        for (int p = P5 ? 4 : 3; p >= 1; --p) {
           const float hn = x * rcp[p] * (1.f + h);
           h = p < a.P ? hn : h;
         }
@@ -732,10 +733,12 @@ template <int D, bool BF16>
 hipError_t launch_intra_t(int BH, const IntraArgs& a, hipStream_t s) {
   constexpr int T = prefill_window(BF16);
   dim3 grid((a.nw + T - 1) / T, BH);
-  if (BF16)
-    prefill_intra_mfma<D><<<grid, T, 0, s>>>(a);
-  else
+  if (!BF16)
     prefill_intra<D><<<grid, 256, 0, s>>>(a);
+  else if (a.P == 5)
+    prefill_intra_mfma<D, true><<<grid, T, 0, s>>>(a);
+  else
+    prefill_intra_mfma<D, false><<<grid, T, 0, s>>>(a);
   return hipGetLastError();
 }
 

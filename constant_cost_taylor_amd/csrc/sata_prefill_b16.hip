@@ -568,7 +568,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   const int64_t off2 = 1 + DK, off3 = 1 + DK + static_cast<int64_t>(DK) * (DK + 1) / 2;
   const int64_t off4 = off3 + static_cast<int64_t>(DK) * (DK + 1) * (DK + 2) / 6;
   auto row_exp = [&](int64_t m, bool value_col) {
-    const int p = m >= off4 ? 4 : m >= off3 ? 3 : m >= off2 ? 2 : m >= 1 ? 1 : 0;
+    const int p = (P5 && m >= off4) ? 4 : m >= off3 ? 3 : m >= off2 ? 2 : m >= 1 ? 1 : 0;
     return p * hs.ek + (value_col ? hs.ev : 0);
   };
   // Every row index first, then every load with no branch between them (a

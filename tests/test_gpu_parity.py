@@ -426,6 +426,35 @@ def test_workload_decode_256x4096_d64():
         assert O.row_normwise_error(got_d[:, s], ref) <= TOL[w.dtype], ("decode", s)
 
 
+def test_workload_order5_32x4096_d64():
+    """Orders 0..4 at d = 64, 32 states: 4096-token prefill (sampled rows of
+    four states), then decode steps (every output checked)."""
+    w = W.WORKLOADS["order5_32x4096_d64"]
+    steps = 8
+    note(f"workload {w.name} states={w.B * w.H} n={w.n} steps={steps}")
+    q, k, v = W.workload_inputs(w)
+    qs, ks, vs = W.decode_inputs(w, steps)
+    b = SA.build_basis(w.d_k, w.P, w.c)
+    out, st = run_prefill(b, q, k, v, w.dtype)
+    S = w.B * w.H
+    got_p = out.cpu().numpy().reshape(S, w.n, w.d_v)
+    del out
+    qd, kd, vd = to_dev(qs, w.dtype), to_dev(ks, w.dtype), to_dev(vs, w.dtype)
+    got_d = np.zeros((steps, S, w.d_v))
+    for s in range(steps):
+        got_d[s] = SA.decode_step(b, qd[s], kd[s], vd[s], st).cpu().numpy()
+    qf, kf, vf = (x.reshape(S, w.n, -1) for x in (q, k, v))
+    g = np.random.Generator(np.random.PCG64(4322))
+    for s in g.choice(S, size=4, replace=False):
+        rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(0, w.n, 127), [w.n - 1]]))
+        ref = oracle_rows(qf[s], kf[s], vf[s], w.P, w.c, rows=rows)
+        assert O.row_normwise_error(got_p[s][rows], ref) <= TOL[w.dtype], ("prefill", s)
+    for s in range(S):
+        qq, kk, vv = (np.concatenate([a[s], b_[:, s]]) for a, b_ in ((qf, qs), (kf, ks), (vf, vs)))
+        ref = oracle_rows(qq, kk, vv, w.P, w.c, rows=np.arange(w.n, w.n + steps))
+        assert O.row_normwise_error(got_d[:, s], ref) <= TOL[w.dtype], ("decode", s)
+
+
 def test_workload_long_d32_n1m_sampled():
     w = W.WORKLOADS["long_d32_n1m"]
     note(f"workload {w.name} H={w.H} n={w.n}")

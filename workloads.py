@@ -27,7 +27,7 @@ BF16 = "bf16"
 class Workload:
     """One named workload: shapes, order count P, logit scale c and input dtype."""
     name: str
-    seed: int         # seed family (1..5): seeds derive from 1000 * seed
+    seed: int         # seed family (1..6): seeds derive from 1000 * seed
     B: int
     H: int
     n: int
@@ -40,7 +40,8 @@ class Workload:
 
 # The five workloads of the causal SATA study (single head n=256 d=8 P=3 fp32,
 # 4x8 heads n=4096 d=16 P=4 fp32, 1x4 heads n=16384 d=64 P=4 bf16, the decode
-# workload with 256 resident d=64 states, and 16 heads of d=32 at n=2^20).
+# workload with 256 resident d=64 states, and 16 heads of d=32 at n=2^20), and
+# an order-5 variant of the decode workload.
 WORKLOADS = {
     "tiny_d8_n256": Workload("tiny_d8_n256", 1, 1, 1, 256, 8, 8, 3, 1.0, F32),
     "d16_n4096": Workload("d16_n4096", 2, 4, 8, 4096, 16, 16, 4, 1.0, F32),
@@ -48,6 +49,9 @@ WORKLOADS = {
     # decode: 8 x 32 = 256 states, 4096-token prefill then 1024 single-token steps
     "decode_256x4096_d64": Workload("decode_256x4096_d64", 4, 8, 32, 4096, 64, 64, 4, 1.0, BF16),
     "long_d32_n1m": Workload("long_d32_n1m", 5, 1, 16, 1 << 20, 32, 32, 4, 1.0, BF16),
+    # orders 0..4 at d = 64 (state 814385 x 65 floats, 211.7 MB a head): 32
+    # states, 4096-token prefill then single-token steps
+    "order5_32x4096_d64": Workload("order5_32x4096_d64", 6, 1, 32, 4096, 64, 64, 5, 1.0, BF16),
 }
 DECODE_STEPS = 1024
 
