@@ -15,7 +15,8 @@
 // its rows (phi_k unweighted, phi_q with the row weight) while they are in
 // flight, then applies the rank-1 update, stores, and forms its readout
 // partial sums; a second kernel reduces the per-tile partials in a fixed
-// order and divides.  Small one-shot blocks stream this read-modify-write at
+// order and divides (with few states and many tiles, in two passes so the
+// reduce still spreads over the chip).  Small one-shot blocks stream this read-modify-write at
 // 6.2 TB/s where 512-row blocks that loop over their rows reach 5.3 (the
 // partials add 3.3 % to the traffic).  The state is touched once per step and
 // is far larger than the caches, so its loads and stores carry the
@@ -152,34 +153,40 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
   }
 }
 
-// One block of kRedThreads per state: groups of DV/4 threads sum interleaved
-// tiles of the value partials with float4 loads (eight in flight per thread),
-// every thread sums strided den partials; both are combined in a fixed order
-// and num / den is written.
+// Sums, in a fixed order, the readout records [t0, t1) of one state: value
+// records part[s][t][DV], den records partz[s][t] (nrec records a state).
+// Block (g, s) takes the range g of length per; FINAL: out[s] = num / den,
+// else the sums become record (s, g) of the next level (nxt, nxtz).  One
+// block of kRedThreads: groups of DV/4 threads sum interleaved records
+// (float4 columns, 8 loads in flight), then a fixed-order combine.
 constexpr int kRedThreads = 1024;
-template <int DV>
-__global__ __launch_bounds__(kRedThreads) void decode_reduce(DecodeArgs a) {
-  constexpr int Q = DV / 4;              // float4 columns per tile record
-  constexpr int G = kRedThreads / Q;     // tile groups
+template <int DV, bool FINAL>
+__global__ __launch_bounds__(kRedThreads) void decode_reduce(const float* __restrict__ part_in,
+                                                             const float* __restrict__ partz_in, int nrec,
+                                                             int per, float* nxt, float* nxtz, float* out) {
+  constexpr int Q = DV / 4;              // float4 columns per record
+  constexpr int G = kRedThreads / Q;     // record groups
   __shared__ float4 red[G * Q];
   __shared__ float dz[kRedThreads];
   __shared__ float dz2[32];
   __shared__ float tot[DV + 1];
-  const int s = blockIdx.x;
+  const int s = blockIdx.y;
+  const int t0 = blockIdx.x * per;
+  const int t1 = min(nrec, t0 + per);
   const int tid = threadIdx.x;
   const int grp = tid / Q;
   const int c = tid % Q;
-  const float4* part = reinterpret_cast<const float4*>(a.part + static_cast<int64_t>(s) * a.n_tiles * DV);
-  const float* partz = a.partz + static_cast<int64_t>(s) * a.n_tiles;
+  const float4* part = reinterpret_cast<const float4*>(part_in + static_cast<int64_t>(s) * nrec * DV);
+  const float* partz = partz_in + static_cast<int64_t>(s) * nrec;
   {
     float z = 0.f;
-    for (int t = tid; t < a.n_tiles; t += kRedThreads) z += partz[t];
+    for (int t = t0 + tid; t < t1; t += kRedThreads) z += partz[t];
     dz[tid] = z;
   }
   if (grp < G) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int t = grp;
-    for (; t + 7 * G < a.n_tiles; t += 8 * G) {
+    int t = t0 + grp;
+    for (; t + 7 * G < t1; t += 8 * G) {
       float4 x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) x[u] = part[static_cast<int64_t>(t + u * G) * Q + c];
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(DecodeArgs a) {
         acc.w += x[u].w;
       }
     }
-    for (; t < a.n_tiles; t += G) {
+    for (; t < t1; t += G) {
       const float4 x = part[static_cast<int64_t>(t) * Q + c];
       acc.x += x.x;
       acc.y += x.y;
@@ -219,7 +226,13 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(DecodeArgs a) {
     tot[DV] = sum;
   }
   __syncthreads();
-  if (tid < DV) a.out[static_cast<int64_t>(s) * DV + tid] = tot[tid] / tot[DV];
+  if constexpr (FINAL) {
+    if (tid < DV) out[static_cast<int64_t>(s) * DV + tid] = tot[tid] / tot[DV];
+  } else {
+    const int64_t r = static_cast<int64_t>(s) * gridDim.x + blockIdx.x;
+    if (tid < DV) nxt[r * DV + tid] = tot[tid];
+    else if (tid == DV) nxtz[r] = tot[DV];
+  }
 }
 
 template <int D>
@@ -231,7 +244,19 @@ hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
     decode_update_readout<D, float><<<grid, kDecodeThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_reduce<D><<<a.S, kRedThreads, 0, st>>>(a);
+  if (a.groups <= 1) {
+    decode_reduce<D, true><<<dim3(1, a.S), kRedThreads, 0, st>>>(a.part, a.partz, a.n_tiles, a.n_tiles, nullptr,
+                                                                 nullptr, a.out);
+    return hipGetLastError();
+  }
+  // Few states: the tiles of a state are split over `groups` blocks, whose
+  // sums a second pass combines (in group order).
+  const int per = (a.n_tiles + a.groups - 1) / a.groups;
+  decode_reduce<D, false><<<dim3(a.groups, a.S), kRedThreads, 0, st>>>(a.part, a.partz, a.n_tiles, per, a.part2,
+                                                                       a.partz2, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  decode_reduce<D, true><<<dim3(1, a.S), kRedThreads, 0, st>>>(a.part2, a.partz2, a.groups, a.groups, nullptr,
+                                                               nullptr, a.out);
   return hipGetLastError();
 }
 

@@ -421,7 +421,8 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
 }
 
 // Decode workspace: value partials [S][tiles][d_v] then den partials
-// [S][tiles], each region 256-byte aligned.
+// [S][tiles]; with more than one reduce group a state, then the second-level
+// partials [S][groups][d_v] and [S][groups].  Each region 256-byte aligned.
 size_t decode_part_bytes(int S, int tiles, int d_v) {
   return (static_cast<size_t>(S) * tiles * d_v * sizeof(float) + 255) / 256 * 256;
 }
@@ -638,7 +639,10 @@ int sata_decode_workspace(const sata_basis* b, int S, int d_v, int dtype, size_t
   if (!b || !bytes || S < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
-  *bytes = decode_part_bytes(S, decode_tiles(b), d_v) + decode_partz_bytes(S, decode_tiles(b));
+  const int tiles = decode_tiles(b);
+  const int groups = sata::decode_groups(S, tiles);
+  *bytes = decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
+  if (groups > 1) *bytes += decode_part_bytes(S, groups, d_v) + decode_partz_bytes(S, groups);
   return SATA_OK;
 }
 
@@ -662,10 +666,14 @@ int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void*
   const int tiles = decode_tiles(b);
   float* part = static_cast<float*>(ws);
   float* partz = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v));
+  const int groups = sata::decode_groups(S, tiles);
+  char* lvl2 = static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
+  float* part2 = groups > 1 ? reinterpret_cast<float*>(lvl2) : nullptr;
+  float* partz2 = groups > 1 ? reinterpret_cast<float*>(lvl2 + decode_part_bytes(S, groups, d_v)) : nullptr;
   sata::DecodeArgs a{q, k, v, state,
                      sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D),
                      part, partz, out, b->d_rows, b->d_weight, S,
-                     static_cast<int>(b->D), tiles};
+                     static_cast<int>(b->D), tiles, groups, part2, partz2};
   if (sata::launch_decode(b->d, dtype == SATA_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SATA_ERR_HIP;
   return SATA_OK;

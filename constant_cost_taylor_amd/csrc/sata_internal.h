@@ -200,7 +200,20 @@ struct DecodeArgs {
   int S;
   int D;
   int n_tiles;
+  int groups;            // reduce blocks per state (1: one pass)
+  float* part2;          // [S][groups][dv]   second-level partials (groups > 1)
+  float* partz2;         // [S][groups]
 };
+
+// Reduce blocks per decode state: enough to give the chip about 256 blocks
+// when there are few states, each summing at least 256 tile records (a
+// second pass then combines the groups); one when S >= 256.
+constexpr int decode_groups(int S, int tiles) {
+  const int want = (256 + S - 1) / S;
+  const int cap = tiles / 256;
+  const int g = want < cap ? want : cap;
+  return g > 1 ? g : 1;
+}
 
 // Launchers (defined in the .hip translation units).  Return hipSuccess or
 // the launch error.

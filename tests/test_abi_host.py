@@ -92,4 +92,9 @@ def test_workspace_sizes():
     tiles = math.ceil(47905 / 16)
     up = lambda x: (x + 255) // 256 * 256
     assert SA.decode_workspace_bytes(b, 256, 64, SA.SATA_BF16) == up(256 * tiles * 64 * 4) + up(256 * tiles * 4)
-    assert SA.decode_workspace_bytes(b, 3, 64, SA.SATA_BF16) == up(3 * tiles * 64 * 4) + up(3 * tiles * 4)
+    # three states: the tile records are reduced in 11 groups (256 records or
+    # more each), whose sums take a second region
+    groups = min(-(-256 // 3), tiles // 256)
+    assert groups == 11
+    assert SA.decode_workspace_bytes(b, 3, 64, SA.SATA_BF16) == (up(3 * tiles * 64 * 4) + up(3 * tiles * 4) +
+                                                                 up(3 * groups * 64 * 4) + up(3 * groups * 4))
