@@ -185,26 +185,49 @@ def workspace(nbytes: int, device="cuda"):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def _check_inputs(basis: Basis, q, k, v):
+    """q, k, v: one dtype, contiguous, on one GPU, q's last dim = the basis d_k
+    (the C calls take d_v only and read d_k coordinates per row)."""
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if q.shape[-1] != basis.d_k:
+        raise ValueError(f"q, k have last dimension {q.shape[-1]}, the basis was built for d_k = {basis.d_k}")
+    if q.device.type != "cuda" or k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one GPU")
+
+
+def _check_buffer(name: str, t, dtype, numel: int, device):
+    """A caller-provided output buffer: dtype, contiguous, on the inputs' GPU and
+    at least numel elements (the C calls see only its address)."""
+    if t.dtype != dtype or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on {device}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call writes {numel}")
+
+
 def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None):
     """Causal prefill. q, k: [B, H, n, d_k], v: [B, H, n, d_v] (float32 or bfloat16,
     contiguous, on the GPU). Returns (out [B, H, n, d_v] float32, state [B*H, stride])."""
     import torch
-    if q.dim() != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B, H, n, d_k] and v [B, H, n, d_v]")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    _check_inputs(basis, q, k, v)
     B, H, n, _ = q.shape
     d_v = v.shape[3]
     code = _dtype_code(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
     if state is None:
         state = new_state(basis, B * H, q.device)
+    _check_buffer("state", state, torch.float32, B * H * basis.state_stride(d_v), q.device)
     if out is None:
         out = torch.empty((B, H, n, d_v), dtype=torch.float32, device=q.device)
+    _check_buffer("out", out, torch.float32, B * H * n * d_v, q.device)
     need = prefill_workspace_bytes(basis, B, H, n, d_v, code)
     if ws is None:
         ws = workspace(need, q.device)
+    if ws.device != q.device:
+        raise ValueError(f"ws must be on {q.device}")
     st = lib().sata_prefill(basis.handle, B, H, n, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             out.data_ptr(), state.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                             _stream_ptr(q.device))
@@ -216,15 +239,20 @@ def decode_step(basis: Basis, q, k, v, state, out=None, ws=None):
     """One decode step for S states: q, k [S, d_k], v [S, d_v]; state [S, stride] in/out.
     Returns out [S, d_v] float32."""
     import torch
-    if q.dim() != 2 or k.shape != q.shape or v.shape[0] != q.shape[0]:
+    if q.dim() != 2 or k.shape != q.shape or v.dim() != 2 or v.shape[0] != q.shape[0]:
         raise ValueError("q, k must be [S, d_k] and v [S, d_v]")
+    _check_inputs(basis, q, k, v)
     S = q.shape[0]
     d_v = v.shape[1]
     code = _dtype_code(q)
+    _check_buffer("state", state, torch.float32, S * basis.state_stride(d_v), q.device)
     if out is None:
         out = torch.empty((S, d_v), dtype=torch.float32, device=q.device)
+    _check_buffer("out", out, torch.float32, S * d_v, q.device)
     if ws is None:
         ws = workspace(decode_workspace_bytes(basis, S, d_v, code), q.device)
+    if ws.device != q.device:
+        raise ValueError(f"ws must be on {q.device}")
     st = lib().sata_decode_step(basis.handle, S, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                 out.data_ptr(), state.data_ptr(), ws.data_ptr(),
                                 ws.numel() * ws.element_size(), _stream_ptr(q.device))

@@ -98,3 +98,21 @@ def test_workspace_sizes():
     assert groups == 11
     assert SA.decode_workspace_bytes(b, 3, 64, SA.SATA_BF16) == (up(3 * tiles * 64 * 4) + up(3 * tiles * 4) +
                                                                  up(3 * groups * 64 * 4) + up(3 * groups * 4))
+
+
+def test_binding_checks_inputs_before_any_call():
+    """Input checks of the Python binding run on the host: mismatched shapes,
+    dtypes, d_k and device are refused before the C library is called."""
+    import torch
+    b = SA.build_basis(16, 3, 1.0, host_only=True)
+    q = torch.zeros((1, 1, 4, 16))
+    with pytest.raises(ValueError):
+        SA.prefill(b, q, q, q[:, :, :3])                       # v length differs
+    with pytest.raises(TypeError):
+        SA.prefill(b, q, q.to(torch.bfloat16), q)              # dtypes differ
+    with pytest.raises(ValueError, match="d_k"):
+        SA.prefill(b, q[..., :8].contiguous(), q[..., :8].contiguous(), q[..., :8].contiguous())
+    with pytest.raises(ValueError, match="GPU"):
+        SA.prefill(b, q, q, q)                                 # host tensors
+    with pytest.raises(ValueError, match="GPU"):
+        SA.decode_step(b, q[0, 0], q[0, 0], q[0, 0], torch.zeros((4, b.state_stride())))

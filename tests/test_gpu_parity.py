@@ -217,6 +217,33 @@ def test_prefill_then_decode(d, P, dtype):
         assert O.row_normwise_error(got[h], ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d,P,dtype", [(64, 4, W.BF16), (16, 4, W.F32), (32, 5, W.BF16)])
+def test_ragged_batched_decode(d, P, dtype):
+    """States at different positions (prefilled to 0, 1, 63, 200 and 517
+    tokens by separate calls) decode together in one batched call per step:
+    the state carries no position, so each row must equal causal attention
+    over its own sequence."""
+    lens = [0, 1, 63, 200, 517]
+    steps = 5
+    note(f"ragged batched decode d={d} P={P} {dtype} lens={lens}")
+    S = len(lens)
+    b = SA.build_basis(d, P, 1.0)
+    st = SA.new_state(b, S)
+    seqs = [W.make_qkv(1, 1, n + steps, d, d, dtype, 18000 + 7 * d + i) for i, n in enumerate(lens)]
+    for i, n in enumerate(lens):
+        if n:
+            q, k, v = (x[:, :, :n] for x in seqs[i])
+            run_prefill(b, q, k, v, dtype, state=st[i:i + 1])
+    got = np.zeros((S, steps, d))
+    for t in range(steps):
+        qt, kt, vt = (np.stack([seqs[i][j][0, 0, lens[i] + t] for i in range(S)]) for j in range(3))
+        got[:, t] = SA.decode_step(b, to_dev(qt, dtype), to_dev(kt, dtype), to_dev(vt, dtype), st).cpu().numpy()
+    for i, n in enumerate(lens):
+        q, k, v = (x[0, 0] for x in seqs[i])
+        ref = oracle_rows(q, k, v, P, 1.0, rows=np.arange(n, n + steps))
+        assert O.row_normwise_error(got[i], ref) <= TOL[dtype], (i, n)
+
+
 @pytest.mark.parametrize("d,P,dtype,n", [(64, 4, W.BF16, 700), (16, 4, W.F32, 530), (32, 5, W.BF16, 700)])
 def test_prefill_many_windows(d, P, dtype, n, monkeypatch):
     """A small workspace cap splits the sequence into many windows (the state
@@ -256,6 +283,32 @@ def test_misaligned_and_host_only_rejected():
                               ws.data_ptr(), ws.numel(), None) == SA.SATA_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert float(st.abs().sum()) == 0.0 and float(out.abs().sum()) == 0.0
+
+
+def test_binding_rejects_bad_buffers():
+    """The binding checks what the C calls cannot see: d_k of the inputs and
+    the size, dtype and device of caller-provided state / out buffers."""
+    note("binding argument checks")
+    b = SA.build_basis(16, 3, 1.0)
+    q = torch.zeros((1, 2, 8, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="d_k"):
+        SA.prefill(b, q[..., :8].contiguous(), q[..., :8].contiguous(), q[..., :8].contiguous())
+    with pytest.raises(ValueError, match="state"):
+        SA.prefill(b, q, q, q, state=SA.new_state(b, 1))
+    with pytest.raises(ValueError, match="state"):
+        SA.prefill(b, q, q, q, state=SA.new_state(b, 2).to(torch.float64))
+    with pytest.raises(ValueError, match="out"):
+        SA.prefill(b, q, q, q, out=torch.zeros((1, 2, 7, 16), device="cuda"))
+    with pytest.raises(TypeError):
+        SA.prefill(b, q, q.float(), q)
+    q1 = torch.zeros((3, 16), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="state"):
+        SA.decode_step(b, q1, q1, q1, SA.new_state(b, 2))
+    with pytest.raises(ValueError, match="out"):
+        SA.decode_step(b, q1, q1, q1, SA.new_state(b, 3), out=torch.zeros((2, 16), device="cuda"))
+    with pytest.raises(ValueError, match="contiguous"):
+        SA.decode_step(b, torch.zeros((16, 3), device="cuda").t(), q1, q1, SA.new_state(b, 3))
+    torch.cuda.synchronize()
 
 
 def _rows_bf16(x):
