@@ -187,10 +187,11 @@ std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32
 //    table and a separate key table; the query side reads a per-slot table
 //    and the scan keeps rows divided by the multiplicity of their last index.
 //  * bfloat16 inputs: one key table (d key rows, a zero row, a ones row, then
-//    one slot row per order-2 parent of the tile); key and query features
-//    are plain monomials (the query side from two coordinates, index d = the
-//    constant 1, and the run's four children) and the row weights w_m are
-//    applied to the state when the scan rounds it to its readout operand.
+//    one slot row per parent of order 2 or 3 of the tile); key and query
+//    features are plain monomials (the query side from two coordinates, three
+//    when P = 5, index d = the constant 1, and the run's four children) and
+//    the row weights w_m are applied to the state when the scan rounds it to
+//    its readout operand.
 int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& rank, bool bf16,
                  bool upload_tables, PrefillLayout* lay) {
   const int rb = sata::prefill_rb(b->d, bf16);

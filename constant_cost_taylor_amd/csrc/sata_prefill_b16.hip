@@ -25,8 +25,9 @@
 //                    barrier-separated segments per chunk, each with MFMA work:
 //                      1  readout  phi_q(Q) Sb  into the cross-wave buffer
 //                      2  cross-wave sum into the tile's records, key
-//                         features of the next chunk's order-2 parents, and
-//                         the update  S += phi_k(K)^T [V 1].
+//                         features of the next chunk's parent slots (order 2,
+//                         and order 3 when P = 5), and the update
+//                         S += phi_k(K)^T [V 1].
 //   prefill_reduce_b16  out = (intra + records + carry) / den per token.
 //
 // Feature map.  Rows of a tile come in runs of four children (P, c..c+3) of
