@@ -315,34 +315,39 @@ def _rows_bf16(x):
     return W.round_bf16(np.asarray(x, dtype=np.float64)).astype(np.float32)
 
 
-@pytest.mark.parametrize("d", [32, 64])
-def test_prefill_bf16_scaled_inputs(d):
+@pytest.mark.parametrize("d,P", [(32, 4), (64, 4), (16, 5), (32, 5)])
+def test_prefill_bf16_scaled_inputs(d, P):
     """bf16 inputs far from unit scale (v x 3000, k x 1/64, q x 64: the logits
-    are unchanged) exercise the per-head power-of-two operand scaling."""
-    note(f"scaled bf16 inputs d={d}")
+    are unchanged) exercise the per-head power-of-two operand scaling (the
+    state of an order-p row carries 2^-(p ek + ev))."""
+    note(f"scaled bf16 inputs d={d} P={P}")
     n = 600
     q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 16000 + d)
     q, k, v = _rows_bf16(q * 64.0), _rows_bf16(k / 64.0), _rows_bf16(v * 3000.0)
-    b = SA.build_basis(d, 4, 1.0)
+    b = SA.build_basis(d, P, 1.0)
     out, st = run_prefill(b, q, k, v, W.BF16)
     got = out.cpu().numpy()
     for h in range(2):
-        ref = oracle_rows(q[0, h], k[0, h], v[0, h], 4, 1.0)
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
         assert O.row_normwise_error(got[0, h], ref) <= TOL[W.BF16], h
-    # the state written back is the canonical one
-    basis = O.enumerate_basis(d, 4)
+    # the state written back is the canonical one, order by order
+    basis = O.enumerate_basis(d, P)
     D = b.total_rows
     S, z = O.direct_state(f64(k[0, 1]), f64(v[0, 1]), basis)
     gS = st.cpu().numpy()[1, :D * d].reshape(D, d)
-    assert np.max(np.abs(gS - S)) <= TOL[W.BF16] * np.max(np.abs(S))
+    off = 0
+    for p in range(P):
+        rows = slice(off, off + math.comb(d + p - 1, p))
+        assert np.max(np.abs(gS[rows] - S[rows])) <= TOL[W.BF16] * np.max(np.abs(S[rows])), p
+        off = rows.stop
 
 
-@pytest.mark.parametrize("d", [32, 64])
-def test_prefill_bf16_large_query_coordinates(d):
+@pytest.mark.parametrize("d,P", [(32, 4), (64, 4), (32, 5)])
+def test_prefill_bf16_large_query_coordinates(d, P):
     """A query coordinate far larger than the keys' scale (first coordinate of
     q = 12, first coordinate of k ~ 1e-3) with moderate logits: outside the
     range of the f16 operand path, so the bf16 operand path runs."""
-    note(f"large query coordinates d={d}")
+    note(f"large query coordinates d={d} P={P}")
     n = 500
     q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 17000 + d)
     q = q.copy()
@@ -350,11 +355,11 @@ def test_prefill_bf16_large_query_coordinates(d):
     q[..., 0] = 12.0
     k[..., 0] *= 1e-2
     q, k, v = _rows_bf16(q), _rows_bf16(k), _rows_bf16(v)
-    b = SA.build_basis(d, 4, 1.0)
+    b = SA.build_basis(d, P, 1.0)
     out, _ = run_prefill(b, q, k, v, W.BF16)
     got = out.cpu().numpy()
     for h in range(2):
-        ref = oracle_rows(q[0, h], k[0, h], v[0, h], 4, 1.0)
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
         assert O.row_normwise_error(got[0, h], ref) <= TOL[W.BF16], h
 
 
