@@ -510,10 +510,10 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
 // the wave's last query:
 //   X^T = K_s Q_w^T                       (bf16 MFMA, fp32 accumulate)
 //   W'  = T_P(X / c) - 1 by Horner's rule in fp32, zero for keys after the query
-//   O^T += V'^T_s M + V'^T_s W'           (M = the 0/1 causal mask)
+//   O^T += V'^T_s M + V'^T_s W_hi + V'^T_s W_lo   (M = the 0/1 causal mask)
 // V' = [v, 1, 0...]: its ones row gives the denominator.  The order-0 term
-// goes through the exact 0/1 mask, so only the small higher-order weights W'
-// are rounded to bf16.
+// goes through the exact 0/1 mask, and the higher-order weights W' as two
+// bf16 parts (W_hi = bf16(W'), W_lo = bf16(W' - W_hi)), about 2^-17 relative.
 // P5: orders 0..4 (a fourth Horner step; P <= 4 takes three).
 template <int DK, bool P5>
 __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(IntraArgs a) {
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
       }
     // Weights in B layout: lane holds query 16 qb + lr and keys
     // 32 sl + 16 (j / 4) + 4 g + j % 4 for j = 0..7.
-    bf16x8 Bm[4], Bw[4];
+    bf16x8 Bm[4], Bw[4], Bl[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int qi = 64 * qg + 16 * qb + lr;
@@ -647,9 +647,20 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
       }
       const u32x4 ww = {pack_bf16(wv[0], wv[1]), pack_bf16(wv[2], wv[3]), pack_bf16(wv[4], wv[5]),
                         pack_bf16(wv[6], wv[7])};
+      // W' = hi + lo: the residual of the bf16 rounding, itself in bf16,
+      // carries W' to about 2^-17 relative
+      float rv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w2 = ww[j / 2];
+        rv[j] = wv[j] - __uint_as_float((j & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+      }
+      const u32x4 wl = {pack_bf16(rv[0], rv[1]), pack_bf16(rv[2], rv[3]), pack_bf16(rv[4], rv[5]),
+                        pack_bf16(rv[6], rv[7])};
       const u32x4 mm = {pack_bf16(mv[0], mv[1]), pack_bf16(mv[2], mv[3]), pack_bf16(mv[4], mv[5]),
                         pack_bf16(mv[6], mv[7])};
       Bw[qb] = __builtin_bit_cast(bf16x8, ww);
+      Bl[qb] = __builtin_bit_cast(bf16x8, wl);
       Bm[qb] = __builtin_bit_cast(bf16x8, mm);
     }
 #pragma unroll
@@ -663,6 +674,7 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
       for (int qb = 0; qb < 4; ++qb) {
         O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bm[qb], O[nb][qb], 0, 0, 0);
         O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bw[qb], O[nb][qb], 0, 0, 0);
+        O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl[qb], O[nb][qb], 0, 0, 0);
       }
     }
   }
