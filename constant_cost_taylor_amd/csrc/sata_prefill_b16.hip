@@ -57,6 +57,16 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kL = 64;   // tokens per chunk
 
+// f16 operand path: the readout operand is scaled per tile and window so that
+// max |Sb| is in [2^(kSbExp-1), 2^kSbExp), and the wave readout partials
+// enter the cross-wave buffer as f16 (11-bit significands; the bf16 operand
+// path keeps bf16 partials).  Range: a query feature is a product of at most
+// four coordinates below 2 and a wave sums 16 RB <= 64 rows, so a partial is
+// below 64 * 16 * 2^kSbExp = 2^15 < 65504.  Entries of Sb below 2^-14 (a
+// factor 2^-19 under the tile's largest) are subnormal: their absolute error
+// is far below that of the largest entries.
+constexpr int kSbExp = 5;
+
 // Two floats rounded (nearest even) to bf16 / f16 and packed in one register.
 // The empty asm pins the conversion here so the fp32 inputs die early.
 __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
@@ -616,7 +626,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     }
 
   // ---- readout operand: Sb = S w 2^-ew, one ew per tile and readout window
-  // (f16: max |S| max(w) 2^-ew in [2^13, 2^14); bf16: ew = 0).  Two steps around a
+  // (f16: max |S| max(w) 2^-ew in [2^(kSbExp-1), 2^kSbExp); bf16: ew = 0).  Two steps around a
   // barrier: each wave posts its max |S|, then every wave derives ew from
   // the tile's max and rounds its slice.
   u32x4 Sb[NKS][NB];
@@ -649,7 +659,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, wmx[ww]);
       int e = 0;
       if (mx > 0.f) (void)frexpf(mx, &e);
-      ew = __builtin_amdgcn_readfirstlane(mx > 0.f ? e - 14 : 0);
+      ew = __builtin_amdgcn_readfirstlane(mx > 0.f ? e - kSbExp : 0);
       sc = ldexpf(1.f, -ew);
     }
     const float* wb = wl + (w * RB) * 16 + 4 * g;
@@ -678,19 +688,25 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   float* reczh = a.ws.recz + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * nwp;
   const uint16_t* red = reinterpret_cast<const uint16_t*>(lds + C::O_RED);
   const float* den = reinterpret_cast<const float*>(lds + C::O_DEN);
-  // Two stacked 16 x 16 identities as an MFMA A operand: lane (lr, g) holds
-  // row lr, K = 8 g .. 8 g + 7; entry 1 where K % 16 == lr (built at use).
+  // Two stacked 16 x 16 identities as an MFMA A operand (16-bit ones of the
+  // partials' type): lane (lr, g) holds row lr, K = 8 g .. 8 g + 7; entry 1
+  // where K % 16 == lr (built at use).
   auto eye2 = [&]() {
-    bf16x8 e;
+    const uint32_t one = H16 ? 0x3c00u : 0x3f80u;
+    u32x4 e;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = static_cast<__bf16>(8 * (g & 1) + j == lr ? 1.f : 0.f);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = 8 * (g & 1) + 2 * j == lr ? one : 0u;
+      const uint32_t hi = 8 * (g & 1) + 2 * j + 1 == lr ? one : 0u;
+      e[j] = lo | (hi << 16);
+    }
     return e;
   };
 
   // Cross-wave sum of chunk ch's readout, times 2^ew, into the records.
   // Value columns on MFMA: for a block of 16 tokens x 16 buffer positions,
   //   sum_w P_w^T = sum over wave pairs p of [I I] [P_2p; P_2p+1]^T,
-  // A = two stacked 16 x 16 identities, B = the bf16 partials of two waves
+  // A = two stacked 16 x 16 identities, B = the 16-bit partials of two waves
   // (K = wave x position); D^T gives lane (lr, g) token slot lr, positions
   // 4 g + r (four consecutive columns).  Red row rho = lr + 16 mb holds token
   // 4 lr + (mb ^ (lr & 1)).  den: fp32 partials summed by the last wave, one
@@ -700,7 +716,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   constexpr int NIW = (NITEM + NW - 1) / NW; // items per wave
   auto red_sum = [&](int ch) {
     const float sc = ldexpf(1.f, ew);
-    const bf16x8 eye = eye2();
+    const u32x4 eye = eye2();
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       const int item = w + NW * i;
@@ -716,7 +732,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
           u32x4 x = {0u, 0u, 0u, 0u};
           if (DV >= 16 || (g & 1) == 0)
             x = *reinterpret_cast<const u32x4*>(&red[ww * L * DV + rho * DV + 8 * upos]);
-          D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(eye, __builtin_bit_cast(bf16x8, x), D, 0, 0, 0);
+          D = mfma16<H16>(eye, x, D);
         }
         const int t = 4 * lr + (tb ^ (lr & 1));
         // positions 4 g .. 4 g + 3 of block cb = units 2 cb + (g >> 1), half g & 1
@@ -757,6 +773,14 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
         }
       }
     }
+  };
+
+  static_assert(RB * 16 * 16 * (1 << kSbExp) <= 32768, "f16 wave partials stay in range");
+  auto pack_red = [&](float x, float y) {
+    if constexpr (H16)
+      return pack_f16(x, y);
+    else
+      return pack_bf16(x, y);
   };
 
   // Readout of chunk X's queries against Sb into the cross-wave buffer.
@@ -846,9 +870,9 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
           // unit 4 P + g = columns 32 P + 4 g .. +3 and 32 P + 16 + 4 g .. +3
 #pragma unroll
           for (int P = 0; P < DV / 32; ++P) {
-            const u32x4 o = {pack_bf16(acc[2 * P][0], acc[2 * P][1]), pack_bf16(acc[2 * P][2], acc[2 * P][3]),
-                             pack_bf16(acc[2 * P + 1][0], acc[2 * P + 1][1]),
-                             pack_bf16(acc[2 * P + 1][2], acc[2 * P + 1][3])};
+            const u32x4 o = {pack_red(acc[2 * P][0], acc[2 * P][1]), pack_red(acc[2 * P][2], acc[2 * P][3]),
+                             pack_red(acc[2 * P + 1][0], acc[2 * P + 1][1]),
+                             pack_red(acc[2 * P + 1][2], acc[2 * P + 1][3])};
             *reinterpret_cast<u32x4*>(&redw[rho * DV + 8 * ((4 * P + g) ^ swz_red<NU>(rho))]) = o;
           }
         } else {
@@ -856,7 +880,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
           for (int nb = 0; nb < NB; ++nb) {
             if (16 * nb < DV && (16 * nb + 16 <= DV || 4 * g < DV % 16)) {
               const int cu = 2 * nb + (g >> 1);
-              const u32x2 o = {pack_bf16(acc[nb][0], acc[nb][1]), pack_bf16(acc[nb][2], acc[nb][3])};
+              const u32x2 o = {pack_red(acc[nb][0], acc[nb][1]), pack_red(acc[nb][2], acc[nb][3])};
               *reinterpret_cast<u32x2*>(&redw[rho * DV + 8 * (cu ^ (swz_row(rho) % NU)) + 4 * (g & 1)]) = o;
             }
           }

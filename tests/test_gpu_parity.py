@@ -122,6 +122,10 @@ CASES = [
     ("d64_bf16_odd_chunks", 1, 1, 1050, 64, 4, 1.0, W.BF16),
     ("d64_bf16_P3", 1, 1, 200, 64, 3, 0.75, W.BF16),
     ("d8_bf16", 1, 1, 97, 8, 4, 1.0, W.BF16),
+    # several readout windows at small head dims: the scan's readout carries
+    # a large share of each output, which averages many values
+    ("d8_bf16_long", 1, 2, 2000, 8, 4, 1.0, W.BF16),
+    ("d16_bf16_long", 1, 2, 2000, 16, 5, 1.0, W.BF16),
     # orders 0..4
     ("d8_P5", 1, 2, 300, 8, 5, 1.0, W.F32),
     ("d8_P5_bf16", 1, 1, 200, 8, 5, 1.0, W.BF16),
