@@ -387,6 +387,7 @@ struct PrefillPlan {
   size_t amax_bytes = 0;
   size_t stg_bytes = 0;   // staged 16-bit tables (bfloat16 inputs)
   size_t vsum_bytes = 0;  // per-chunk sums of v (bfloat16 inputs)
+  size_t recs_bytes = 0;  // per-chunk scales of 16-bit records (bfloat16 inputs, d >= 32)
   size_t total = 0;
 };
 
@@ -399,7 +400,7 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
   const size_t rec_elt = sata::prefill_bf16_records(d, bf16) ? 2 : 4;
   // bytes per token of window: records, intra, staged tables, chunk sums
   const size_t per_token =
-      bf16 ? static_cast<size_t>(BH) * (nt * (d * rec_elt + 4) + dvp * 4 + 8 * d + dvp)
+      bf16 ? static_cast<size_t>(BH) * (nt * (d * rec_elt + 4) + nt / 16 + 1 + dvp * 4 + 8 * d + dvp)
            : static_cast<size_t>(BH) * dvp * (nt * rec_elt + 4);
   int64_t w = static_cast<int64_t>(prefill_ws_cap() / per_token);
   // windows start on readout-window boundaries
@@ -415,9 +416,10 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) 
   pl.amax_bytes = bf16 ? static_cast<size_t>(BH) * sata::kAmaxSplit * 4 * 4 : 0;
   pl.stg_bytes = bf16 ? static_cast<size_t>(BH) * pl.nwp * 4 * d * 2 : 0;
   pl.vsum_bytes = bf16 ? static_cast<size_t>(BH) * (pl.nwp / 64) * dvp * 4 : 0;
+  pl.recs_bytes = rec_elt == 2 ? static_cast<size_t>(BH) * nt * (pl.nwp / 64) * 4 : 0;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   pl.total = up(pl.rec_bytes) + up(pl.recz_bytes) + up(pl.intra_bytes) + up(pl.carry_bytes) +
-             up(pl.amax_bytes) + up(pl.stg_bytes) + up(pl.vsum_bytes);
+             up(pl.amax_bytes) + up(pl.stg_bytes) + up(pl.vsum_bytes) + up(pl.recs_bytes);
   return pl;
 }
 
@@ -613,6 +615,7 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
   pw.recz = reinterpret_cast<float*>(carve(pl.recz_bytes));
   pw.stg = reinterpret_cast<uint16_t*>(carve(pl.stg_bytes));
   pw.vsum = reinterpret_cast<float*>(carve(pl.vsum_bytes));
+  pw.recs = reinterpret_cast<float*>(carve(pl.recs_bytes));
   const float inv_c = static_cast<float>(1.0 / b->c);
   for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
     const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));

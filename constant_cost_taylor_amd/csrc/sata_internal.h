@@ -130,7 +130,11 @@ constexpr int kAmaxSplit = 32;
 //   carry: [BH][nchunks][DVP]       order-0 prefix at each chunk start (fp32)
 // bfloat16 inputs:
 //   rec:   [BH][n_tiles][nwp][DV]   per-tile readout records of the value
-//                                   columns (bf16 at d >= 32, else fp32)
+//                                   columns (16-bit at d >= 32: f16 for heads
+//                                   on the f16 operand path, else bf16; fp32
+//                                   below d = 32)
+//   recs:  [BH][n_tiles][nwp/64]    scale of each 64-token chunk of f16
+//                                   records (d >= 32)
 //   recz:  [BH][n_tiles][nwp]       per-tile den records (fp32)
 //   intra: [BH][nwp][DVP]           intra-window records (fp32)
 //   carry: [BH][nrwin][DVP]         order-0 prefix at each readout window start (fp32)
@@ -146,6 +150,7 @@ struct PrefillWs {
   float* recz;
   uint16_t* stg;
   float* vsum;
+  float* recs;
 };
 
 struct ScanArgs {

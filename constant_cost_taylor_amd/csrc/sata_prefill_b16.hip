@@ -66,6 +66,10 @@ constexpr int kL = 64;   // tokens per chunk
 // factor 2^-19 under the tile's largest) are subnormal: their absolute error
 // is far below that of the largest entries.
 constexpr int kSbExp = 5;
+// Tile records of the f16 operand path (d >= 32): the cross-wave sum of eight
+// partials (below 2^18) times 2^-kRecShift, as f16, with the chunk's scale
+// 2^(ew + kRecShift) in a side array.
+constexpr int kRecShift = 3;
 
 // Two floats rounded (nearest even) to bf16 / f16 and packed in one register.
 // The empty asm pins the conversion here so the fp32 inputs die early.
@@ -83,6 +87,12 @@ __device__ __forceinline__ uint32_t pack_f16(float x, float y) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
 
 // Barrier for LDS traffic only: waits for this wave's LDS operations, not for
 // its global stores.
@@ -686,6 +696,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   const int nwp = a.ws.nwp;
   RedT* rech = static_cast<RedT*>(a.ws.rec) + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * nwp * DV;
   float* reczh = a.ws.recz + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * nwp;
+  float* recsh = a.ws.recs + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * (nwp / L);
+  static_assert(NW * 32768 <= (32768 << kRecShift), "f16 records stay in range");
   const uint16_t* red = reinterpret_cast<const uint16_t*>(lds + C::O_RED);
   const float* den = reinterpret_cast<const float*>(lds + C::O_DEN);
   // Two stacked 16 x 16 identities as an MFMA A operand (16-bit ones of the
@@ -739,14 +751,21 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
         const int col = PAIRED ? 32 * (cb >> 1) + 16 * (g & 1) + 8 * (cb & 1) + 4 * (g >> 1) : 16 * cb + 4 * g;
         if (col < DV) {
           const int64_t ro = (static_cast<int64_t>(ch) * L + t) * DV + col;
-          if constexpr (std::is_same<RedT, uint16_t>::value) {
-            const u32x2 o = {pack_bf16(D[0] * sc, D[1] * sc), pack_bf16(D[2] * sc, D[3] * sc)};
+          if constexpr (std::is_same<RedT, uint16_t>::value && H16) {
+            constexpr float rs = 1.f / (1 << kRecShift);
+            const u32x2 o = {pack_f16(D[0] * rs, D[1] * rs), pack_f16(D[2] * rs, D[3] * rs)};
             __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(&rech[ro]));   // read once, later
+          } else if constexpr (std::is_same<RedT, uint16_t>::value) {
+            const u32x2 o = {pack_bf16(D[0] * sc, D[1] * sc), pack_bf16(D[2] * sc, D[3] * sc)};
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(&rech[ro]));
           } else {
             __builtin_nontemporal_store(D * sc, reinterpret_cast<f32x4*>(&rech[ro]));
           }
         }
       }
+    }
+    if constexpr (std::is_same<RedT, uint16_t>::value && H16) {
+      if (tid == 0) recsh[ch] = ldexpf(1.f, ew + kRecShift);
     }
     if (tid >= (NW - 1) * 64) {
       float sz = 0.f;
@@ -1091,6 +1110,9 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
   __syncthreads();
   const RedT* rec = static_cast<const RedT*>(a.ws.rec) + static_cast<int64_t>(head) * nt * nwp * DV;
   float* out = a.out + (static_cast<int64_t>(head) * a.n_total + a.t0) * DV;
+  // f16 records: scale of this block's chunk (32 | 64) per tile
+  const int nchp = nwp / 64;
+  const float* rsc = a.ws.recs + static_cast<int64_t>(head) * nt * nchp + t0 / 64;
   for (int e = tid; e < ntok * NU; e += kRedThr) {
     const int tt = e / NU, u = e % NU;
     const int t = t0 + tt;
@@ -1099,16 +1121,56 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
     for (int j = 0; j < 8; ++j) r[j] = 0.f;
     const RedT* rp = rec + static_cast<int64_t>(t) * DV + 8 * u;
     const int64_t tstride = static_cast<int64_t>(nwp) * DV;
-    auto add_tile = [&](int tl) {
-      if constexpr (std::is_same<RedT, uint16_t>::value) {
-        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + tl * tstride));
+    int tl = 0;
+    if constexpr (std::is_same<RedT, uint16_t>::value) {
+      // groups of eight record loads in flight, folded in tile order; f16
+      // records (heads on the f16 operand path) times their chunk scale
+      auto sum16 = [&](auto f16c) {
+        constexpr bool F16 = decltype(f16c)::value;
+        for (; tl + 7 < nt; tl += 8) {
+          u32x4 x[8];
+          float sv[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t xj = x[j];
-          r[2 * j] += bf16_lo(xj);
-          r[2 * j + 1] += bf16_hi(xj);
+          for (int i = 0; i < 8; ++i) {
+            x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + (tl + i) * tstride));
+            sv[i] = F16 ? rsc[static_cast<int64_t>(tl + i) * nchp] : 1.f;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t xj = x[i][j];
+              if constexpr (F16) {
+                r[2 * j] = fmaf(f16_lo(xj), sv[i], r[2 * j]);
+                r[2 * j + 1] = fmaf(f16_hi(xj), sv[i], r[2 * j + 1]);
+              } else {
+                r[2 * j] += bf16_lo(xj);
+                r[2 * j + 1] += bf16_hi(xj);
+              }
+            }
         }
-      } else {
+        for (; tl < nt; ++tl) {
+          const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + tl * tstride));
+          const float sv = F16 ? rsc[static_cast<int64_t>(tl) * nchp] : 1.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (F16) {
+              r[2 * j] = fmaf(f16_lo(x[j]), sv, r[2 * j]);
+              r[2 * j + 1] = fmaf(f16_hi(x[j]), sv, r[2 * j + 1]);
+            } else {
+              r[2 * j] += bf16_lo(x[j]);
+              r[2 * j + 1] += bf16_hi(x[j]);
+            }
+          }
+        }
+      };
+      if (hs.safe)
+        sum16(std::true_type{});
+      else
+        sum16(std::false_type{});
+    } else {
+#pragma unroll 4
+      for (; tl < nt; ++tl) {
         const f32x4 x0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rp + tl * tstride));
         const f32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rp + tl * tstride + 4));
 #pragma unroll
@@ -1117,27 +1179,7 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
           r[4 + j] += x1[j];
         }
       }
-    };
-    int tl = 0;
-    if constexpr (std::is_same<RedT, uint16_t>::value) {
-      // groups of eight record loads in flight, folded in tile order
-      for (; tl + 7 < nt; tl += 8) {
-        u32x4 x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + (tl + i) * tstride));
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t xj = x[i][j];
-            r[2 * j] += bf16_lo(xj);
-            r[2 * j + 1] += bf16_hi(xj);
-          }
-      }
     }
-#pragma unroll 4
-    for (; tl < nt; ++tl) add_tile(tl);
     const float* ip = intra + static_cast<int64_t>(t) * DVP + 8 * u;
     const float* cp = carry + (t / T) * DVP + 8 * u;
     const float dinv = 1.f / dsh[tt];
