@@ -70,9 +70,9 @@ constexpr int prefill_slots(int d, bool bf16) {
 // LDS row stride (floats) of the key / parent-feature tables.
 constexpr int prefill_kstride(bool bf16) { return prefill_chunk(bf16) + 4; }
 
-// Readout records are bf16 for bf16 inputs at d >= 32 (the per-tile partial
-// sums there are small next to the order-0 and intra-chunk terms, which stay
-// fp32), fp32 otherwise.
+// Readout records are 16-bit for bf16 inputs at d >= 32 (f16 with a
+// per-chunk scale on the f16 operand path, bf16 on the bf16 operand path;
+// half the record traffic of fp32), fp32 otherwise.
 constexpr bool prefill_bf16_records(int d, bool bf16) { return bf16 && d >= 32; }
 
 // Floats between consecutive heads' states: the state size rounded up to a
