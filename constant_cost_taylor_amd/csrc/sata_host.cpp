@@ -621,7 +621,7 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
     const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
     sata::IntraArgs ia{q, k, v, pw, n, t0, w, b->P, inv_c};
     sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P};
-    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c};
+    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c, b->P};
     if (bf16) {
       if (sata::launch_prefill_b16(b->d, static_cast<int>(BH), sa, s) != hipSuccess) return SATA_ERR_HIP;
       if (sata::launch_prefill_intra(b->d, true, static_cast<int>(BH), ia, s) != hipSuccess)

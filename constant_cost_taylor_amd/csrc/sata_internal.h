@@ -188,7 +188,8 @@ struct ReduceArgs {
   int64_t t0;
   int nw;
   int n_tiles;
-  float inv_c;           // 1 / c (selects the bf16 scan's operand type)
+  float inv_c;           // 1 / c
+  int P;                 // orders 0..P-1 (with the max-abs values, selects the bf16 scan's operand type)
 };
 
 struct DecodeArgs {

@@ -57,15 +57,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kL = 64;   // tokens per chunk
 
-// f16 operand path: the readout operand is scaled per tile and window so that
-// max |Sb| is in [2^(kSbExp-1), 2^kSbExp), and the wave readout partials
-// enter the cross-wave buffer as f16 (11-bit significands; the bf16 operand
-// path keeps bf16 partials).  Range: a query feature is a product of at most
-// four coordinates below 2 and a wave sums 16 RB <= 64 rows, so a partial is
-// below 64 * 16 * 2^kSbExp = 2^15 < 65504.  Entries of Sb below 2^-14 (a
-// factor 2^-19 under the tile's largest) are subnormal: their absolute error
-// is far below that of the largest entries.
-constexpr int kSbExp = 5;
 // Tile records of the f16 operand path (d >= 32): the cross-wave sum of eight
 // partials (below 2^18) times 2^-kRecShift, as f16, with the chunk's scale
 // 2^(ew + kRecShift) in a side array.
@@ -130,19 +121,28 @@ __device__ __forceinline__ void dma_barrier() {
 }
 
 // Per-head scale exponents of the f16 operand path, from the window's
-// max-abs values: k' = k 2^-ek, q' = q 2^ek, v' = v 2^-ev (exact), with ek,
-// ev zero unless |k| is outside [1/16, 2) or |v| outside [2^-8, 2^15).  Then
-// |k'| < 2, and the path is taken when also max |q'| <= 2: every feature (a
-// product of at most four coordinates) is below 16 in magnitude and every
-// value below 2^15, far inside the f16 range.  Otherwise the head runs with
+// max-abs values: k' = k 2^-ek, q' = q 2^ek, v' = v 2^-ev (exact; q'.k' =
+// q.k).  ek splits the magnitude evenly between the two sides: with |q| <
+// 2^eq and |k| < 2^ekk, ek = (ekk - eq) / 2 leaves |q'| < 2^(eq + ek) and
+// |k'| < 2^(ekk - ek), so a query feature (at most P-1 coordinates) is below
+// 2^fq, fq = (P-1) max(eq + ek, 0), and a key feature below 2^fk likewise.
+// ev is zero unless |v| is outside [2^-8, 2^15), so |v'| < 2^15.  The path
+// is taken when fq, fk <= 12 (and every value is finite), far inside the f16
+// range.  The readout operand Sb of a tile is then scaled so that its
+// largest entry lies in [2^(sb-1), 2^sb), sb = min(14, 9 - fq): a wave's
+// readout partial over at most 64 rows stays below 2^6 2^fq 2^sb <= 2^15 <
+// 65504 and goes to the cross-wave sum as f16.  (Entries of Sb more than
+// 2^(sb+14) below the largest are subnormal; their absolute error is
+// negligible next to the largest entries'.)  Otherwise the head runs with
 // bf16 operands.
 struct HalfScales {
   bool safe;
   int ek;
   int ev;
+  int sb;
 };
 
-__device__ __forceinline__ HalfScales half_scales(const float* amax) {
+__device__ __forceinline__ HalfScales half_scales(const float* amax, int P) {
   float mq = 0.f, mk = 0.f, mv = 0.f;
 #pragma unroll 4
   for (int s = 0; s < kAmaxSplit; ++s) {
@@ -151,26 +151,26 @@ __device__ __forceinline__ HalfScales half_scales(const float* amax) {
     mv = fmaxf(mv, amax[4 * s + 2]);
   }
   HalfScales h;
-  h.ek = 0;
+  int eq = 0, ekk = 0, e = 0;
+  if (mq > 0.f) (void)frexpf(mq, &eq);    // mq < 2^eq
+  if (mk > 0.f) (void)frexpf(mk, &ekk);   // mk < 2^ekk
+  h.ek = (ekk - eq) / 2;
   h.ev = 0;
-  int e = 0;
-  if (mk > 0.f) {
-    (void)frexpf(mk, &e);   // mk = m 2^e, m in [0.5, 1)
-    if (e > 1 || e < -3) h.ek = e;
-  }
   if (mv > 0.f) {
     (void)frexpf(mv, &e);
     if (e > 15) h.ev = e - 15;
     else if (e < -7) h.ev = e;
   }
-  const float qmax = ldexpf(mq, h.ek);
-  h.safe = isfinite(mq) && isfinite(mk) && isfinite(mv) && qmax <= 2.f && h.ek > -40 && h.ek < 40 &&
-           h.ev > -40 && h.ev < 40;
+  const int fq = (P - 1) * max(eq + h.ek, 0);
+  const int fk = (P - 1) * max(ekk - h.ek, 0);
+  h.sb = min(14, 9 - fq);
+  h.safe = isfinite(mq) && isfinite(mk) && isfinite(mv) && fq <= 12 && fk <= 12 && h.ek > -40 &&
+           h.ek < 40 && h.ev > -40 && h.ev < 40;
   return h;
 }
 
-__device__ __forceinline__ const HalfScales head_scales(const PrefillWs& ws, int head) {
-  return half_scales(ws.amax + static_cast<int64_t>(head) * kAmaxSplit * 4);
+__device__ __forceinline__ const HalfScales head_scales(const PrefillWs& ws, int head, int P) {
+  return half_scales(ws.amax + static_cast<int64_t>(head) * kAmaxSplit * 4, P);
 }
 
 // ---------------------------------------------------------------------------
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256) void prefill_stage(ScanArgs a) {
   const int ch = blockIdx.x;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
-  const HalfScales hs = head_scales(a.ws, head);
+  const HalfScales hs = head_scales(a.ws, head, a.P);
   const int nvalid = min(L, a.nw - ch * L);
   const int64_t tok0 = a.t0 + static_cast<int64_t>(ch) * L;
   const int nchp = a.ws.nwp / L;
@@ -636,7 +636,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     }
 
   // ---- readout operand: Sb = S w 2^-ew, one ew per tile and readout window
-  // (f16: max |S| max(w) 2^-ew in [2^(kSbExp-1), 2^kSbExp); bf16: ew = 0).  Two steps around a
+  // (f16: max |S| max(w) 2^-ew in [2^(sb-1), 2^sb); bf16: ew = 0).  Two steps around a
   // barrier: each wave posts its max |S|, then every wave derives ew from
   // the tile's max and rounds its slice.
   u32x4 Sb[NKS][NB];
@@ -669,7 +669,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, wmx[ww]);
       int e = 0;
       if (mx > 0.f) (void)frexpf(mx, &e);
-      ew = __builtin_amdgcn_readfirstlane(mx > 0.f ? e - kSbExp : 0);
+      ew = __builtin_amdgcn_readfirstlane(mx > 0.f ? e - hs.sb : 0);
       sc = ldexpf(1.f, -ew);
     }
     const float* wb = wl + (w * RB) * 16 + 4 * g;
@@ -794,7 +794,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     }
   };
 
-  static_assert(RB * 16 * 16 * (1 << kSbExp) <= 32768, "f16 wave partials stay in range");
+  static_assert(RB * 16 <= 64, "the f16 partial bound assumes at most 64 rows a wave");
   auto pack_red = [&](float x, float y) {
     if constexpr (H16)
       return pack_f16(x, y);
@@ -1043,7 +1043,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
 template <int DK, bool P5>
 __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[CfgS<DK>::LDS_B];
-  const HalfScales hs = head_scales(a.ws, blockIdx.y);
+  const HalfScales hs = head_scales(a.ws, blockIdx.y, a.P);
   if (hs.safe)
     scan_tile<DK, true, P5>(a, hs, lds);
   else
@@ -1073,7 +1073,7 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
   const int nwp = a.ws.nwp;
   const int nt = a.n_tiles;
   const int ntok = min(TB, a.nw - t0);
-  const HalfScales hs = head_scales(a.ws, head);
+  const HalfScales hs = head_scales(a.ws, head, a.P);
   const float rscale = hs.safe ? ldexpf(1.f, hs.ev) : 1.f;   // value-column records carry 2^-ev
   const float* intra = a.ws.intra + static_cast<int64_t>(head) * nwp * DVP;
   const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + T - 1) / T) * DVP;

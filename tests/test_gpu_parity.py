@@ -346,17 +346,20 @@ def test_prefill_bf16_scaled_inputs(d, P):
         off = rows.stop
 
 
-@pytest.mark.parametrize("d,P", [(32, 4), (64, 4), (32, 5)])
-def test_prefill_bf16_large_query_coordinates(d, P):
+@pytest.mark.parametrize("d,P,q0", [(32, 4, 12.0), (64, 4, 12.0), (32, 5, 12.0), (32, 4, 40.0), (64, 4, 40.0),
+                                    (16, 4, 40.0)])
+def test_prefill_bf16_large_query_coordinates(d, P, q0):
     """A query coordinate far larger than the keys' scale (first coordinate of
-    q = 12, first coordinate of k ~ 1e-3) with moderate logits: outside the
-    range of the f16 operand path, so the bf16 operand path runs."""
-    note(f"large query coordinates d={d} P={P}")
-    n = 500
+    q = q0, first coordinate of k ~ 1e-3) with moderate logits: the per-head
+    power of two moves magnitude from q to k (q' = q 2^ek, k' = k 2^-ek) so
+    that both sides' features fit the f16 operand path, whose readout operand
+    is then scaled down to keep the wave partials in range."""
+    note(f"large query coordinates d={d} P={P} q0={q0}")
+    n = 1100   # three readout windows: the scan's readout carries the first 512 keys
     q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 17000 + d)
     q = q.copy()
     k = k.copy()
-    q[..., 0] = 12.0
+    q[..., 0] = q0
     k[..., 0] *= 1e-2
     q, k, v = _rows_bf16(q), _rows_bf16(k), _rows_bf16(v)
     b = SA.build_basis(d, P, 1.0)
