@@ -346,21 +346,24 @@ def test_prefill_bf16_scaled_inputs(d, P):
         off = rows.stop
 
 
-@pytest.mark.parametrize("d,P,q0", [(32, 4, 12.0), (64, 4, 12.0), (32, 5, 12.0), (32, 4, 40.0), (64, 4, 40.0),
-                                    (16, 4, 40.0)])
-def test_prefill_bf16_large_query_coordinates(d, P, q0):
+@pytest.mark.parametrize("d,P,q0,kf", [(32, 4, 12.0, 1e-2), (64, 4, 12.0, 1e-2), (32, 5, 12.0, 1e-2),
+                                       (32, 4, 40.0, 1e-2), (64, 4, 40.0, 1e-2), (16, 4, 40.0, 1e-2),
+                                       (32, 4, 1000.0, 1e-4), (64, 5, 1000.0, 1e-4)])
+def test_prefill_bf16_large_query_coordinates(d, P, q0, kf):
     """A query coordinate far larger than the keys' scale (first coordinate of
     q = q0, first coordinate of k ~ 1e-3) with moderate logits: the per-head
     power of two moves magnitude from q to k (q' = q 2^ek, k' = k 2^-ek) so
     that both sides' features fit the f16 operand path, whose readout operand
-    is then scaled down to keep the wave partials in range."""
+    is then scaled down to keep the wave partials in range.  q0 = 1000 (key
+    coordinate x 1e-4) leaves query features beyond 2^12 even after the
+    split, so those heads run the bf16 operand path."""
     note(f"large query coordinates d={d} P={P} q0={q0}")
     n = 1100   # three readout windows: the scan's readout carries the first 512 keys
     q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 17000 + d)
     q = q.copy()
     k = k.copy()
     q[..., 0] = q0
-    k[..., 0] *= 1e-2
+    k[..., 0] *= kf
     q, k, v = _rows_bf16(q), _rows_bf16(k), _rows_bf16(v)
     b = SA.build_basis(d, P, 1.0)
     out, _ = run_prefill(b, q, k, v, W.BF16)
