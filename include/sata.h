@@ -120,6 +120,14 @@ int sata_prefill_workspace(const sata_basis* basis, int B, int H, int n, int d_v
  *         the state after the n tokens is written back.
  *   ws:   device workspace of at least sata_prefill_workspace bytes, 256-byte
  *         aligned; its contents on entry do not matter.
+ * Arithmetic: float32 inputs run in fp32 throughout.  bfloat16 inputs run the
+ * feature products and readout/update contractions on 16-bit MFMA operands
+ * (f16 after exact per-head power-of-two scaling when the inputs' ranges
+ * allow it, else bf16) with fp32 accumulation and an fp32 state; the tests
+ * gate the row-normwise error against the exact truncated polynomial at 1e-5
+ * (float32) and 3e-3 (bfloat16).  Heads whose query/key scales leave the
+ * f16 range (query features beyond 2^12 after the scaling) use bf16 operands
+ * and can exceed 3e-3 at small d_k over sequences of thousands of tokens.
  * n = 0 is a valid no-op. */
 int sata_prefill(const sata_basis* basis, int B, int H, int n, int d_v, int dtype,
                  const void* q, const void* k, const void* v, float* out, float* state,
