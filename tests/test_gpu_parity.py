@@ -126,6 +126,14 @@ CASES = [
     # a large share of each output, which averages many values
     ("d8_bf16_long", 1, 2, 2000, 8, 4, 1.0, W.BF16),
     ("d16_bf16_long", 1, 2, 2000, 16, 5, 1.0, W.BF16),
+    # chunk (64) and readout-window (512) boundaries of the bf16 path
+    ("d64_bf16_n1", 1, 2, 1, 64, 4, 1.0, W.BF16),
+    ("d64_bf16_n63", 1, 1, 63, 64, 4, 1.0, W.BF16),
+    ("d64_bf16_n64", 1, 1, 64, 64, 4, 1.0, W.BF16),
+    ("d64_bf16_n65", 1, 1, 65, 64, 4, 1.0, W.BF16),
+    ("d32_bf16_n511", 1, 1, 511, 32, 4, 1.0, W.BF16),
+    ("d32_bf16_n512", 1, 1, 512, 32, 4, 1.0, W.BF16),
+    ("d32_bf16_n513", 1, 1, 513, 32, 4, 1.0, W.BF16),
     # orders 0..4
     ("d8_P5", 1, 2, 300, 8, 5, 1.0, W.F32),
     ("d8_P5_bf16", 1, 1, 200, 8, 5, 1.0, W.BF16),
@@ -188,7 +196,8 @@ def test_prefill_state_matches_direct_state(d, P, dtype, n):
 
 
 @pytest.mark.parametrize("d,P,dtype,n1,n2", [(16, 4, W.F32, 200, 333), (64, 4, W.BF16, 100, 161),
-                                             (8, 3, W.F32, 33, 64), (64, 5, W.BF16, 100, 161)])
+                                             (8, 3, W.F32, 33, 64), (64, 5, W.BF16, 100, 161),
+                                             (32, 4, W.BF16, 512, 600), (32, 4, W.BF16, 64, 1)])
 def test_prefill_continuation(d, P, dtype, n1, n2):
     """prefill(a) then prefill(b | state) gives the rows of prefill(a + b)."""
     note(f"continuation d={d} P={P} {dtype} {n1}+{n2}")
