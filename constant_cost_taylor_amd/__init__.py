@@ -59,11 +59,17 @@ def _declare(lib):
     lib.sata_prefill.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_sz, c_vp]
     lib.sata_prefill.restype = c_int
+    lib.sata_prefill_strided.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                         c_i64, c_vp, c_sz, c_vp]
+    lib.sata_prefill_strided.restype = c_int
     lib.sata_decode_workspace.argtypes = [c_vp, c_int, c_int, c_int, P(c_sz)]
     lib.sata_decode_workspace.restype = c_int
     lib.sata_decode_step.argtypes = [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                      c_sz, c_vp]
     lib.sata_decode_step.restype = c_int
+    lib.sata_decode_step_strided.argtypes = [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                             c_vp, c_sz, c_vp]
+    lib.sata_decode_step_strided.restype = c_int
     lib.sata_status_string.argtypes = [c_int]
     lib.sata_status_string.restype = ctypes.c_char_p
 
@@ -159,10 +165,25 @@ def _stream_ptr(device) -> int:
     return int(torch.cuda.current_stream(device).cuda_stream)
 
 
-def new_state(basis: Basis, count: int, device="cuda"):
-    """Zero states (empty prefix) for `count` heads: [count, state_stride] float32."""
+def new_state(basis: Basis, count: int, device="cuda", packed: bool = False):
+    """Zero states (empty prefix) for `count` heads: [count, state_stride] float32
+    (rows 256-byte aligned, the layout the decode step streams fastest), or
+    [count, state_floats] with packed=True (heads back to back)."""
     import torch
-    return torch.zeros((count, basis.state_stride()), dtype=torch.float32, device=device)
+    width = basis.state_floats() if packed else basis.state_stride()
+    return torch.zeros((count, width), dtype=torch.float32, device=device)
+
+
+def _state_stride(basis: Basis, state, count: int, d_v: int, device) -> int:
+    """Head stride of a [count, stride] state tensor (stride >= state_floats)."""
+    import torch
+    if state.dtype != torch.float32 or not state.is_contiguous() or state.device != device:
+        raise ValueError(f"state must be a contiguous float32 tensor on {device}")
+    if state.dim() != 2 or state.shape[0] != count:
+        raise ValueError(f"state must be [{count}, stride] (one row per head), got {tuple(state.shape)}")
+    if state.shape[1] < basis.state_floats(d_v):
+        raise ValueError(f"state rows hold {state.shape[1]} floats, a head needs {basis.state_floats(d_v)}")
+    return int(state.shape[1])
 
 
 def prefill_workspace_bytes(basis: Basis, B: int, H: int, n: int, d_v: int, dtype_code: int) -> int:
@@ -209,7 +230,9 @@ def _check_buffer(name: str, t, dtype, numel: int, device):
 
 def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None):
     """Causal prefill. q, k: [B, H, n, d_k], v: [B, H, n, d_v] (float32 or bfloat16,
-    contiguous, on the GPU). Returns (out [B, H, n, d_v] float32, state [B*H, stride])."""
+    contiguous, on the GPU). state: [B*H, stride] float32 with stride >= state_floats
+    (new_state; zeros = empty prefix), read and written. Returns (out [B, H, n, d_v]
+    float32, state)."""
     import torch
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B, H, n, d_k] and v [B, H, n, d_v]")
@@ -219,7 +242,7 @@ def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None):
     code = _dtype_code(q)
     if state is None:
         state = new_state(basis, B * H, q.device)
-    _check_buffer("state", state, torch.float32, B * H * basis.state_stride(d_v), q.device)
+    stride = _state_stride(basis, state, B * H, d_v, q.device)
     if out is None:
         out = torch.empty((B, H, n, d_v), dtype=torch.float32, device=q.device)
     _check_buffer("out", out, torch.float32, B * H * n * d_v, q.device)
@@ -228,10 +251,10 @@ def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None):
         ws = workspace(need, q.device)
     if ws.device != q.device:
         raise ValueError(f"ws must be on {q.device}")
-    st = lib().sata_prefill(basis.handle, B, H, n, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                            out.data_ptr(), state.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
-                            _stream_ptr(q.device))
-    _check(st, "sata_prefill")
+    st = lib().sata_prefill_strided(basis.handle, B, H, n, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    out.data_ptr(), state.data_ptr(), stride, ws.data_ptr(),
+                                    ws.numel() * ws.element_size(), _stream_ptr(q.device))
+    _check(st, "sata_prefill_strided")
     return out, state
 
 
@@ -245,7 +268,7 @@ def decode_step(basis: Basis, q, k, v, state, out=None, ws=None):
     S = q.shape[0]
     d_v = v.shape[1]
     code = _dtype_code(q)
-    _check_buffer("state", state, torch.float32, S * basis.state_stride(d_v), q.device)
+    stride = _state_stride(basis, state, S, d_v, q.device)
     if out is None:
         out = torch.empty((S, d_v), dtype=torch.float32, device=q.device)
     _check_buffer("out", out, torch.float32, S * d_v, q.device)
@@ -253,8 +276,9 @@ def decode_step(basis: Basis, q, k, v, state, out=None, ws=None):
         ws = workspace(decode_workspace_bytes(basis, S, d_v, code), q.device)
     if ws.device != q.device:
         raise ValueError(f"ws must be on {q.device}")
-    st = lib().sata_decode_step(basis.handle, S, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                out.data_ptr(), state.data_ptr(), ws.data_ptr(),
-                                ws.numel() * ws.element_size(), _stream_ptr(q.device))
-    _check(st, "sata_decode_step")
+    st = lib().sata_decode_step_strided(basis.handle, S, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        out.data_ptr(), state.data_ptr(), stride, ws.data_ptr(),
+                                        ws.numel() * ws.element_size(), _stream_ptr(q.device))
+    _check(st, "sata_decode_step_strided")
     return out
+

@@ -36,6 +36,31 @@ __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
 // Four floats as a clang vector (the non-temporal builtins take vector types).
 typedef float f4v __attribute__((ext_vector_type(4)));
 
+// One float4 slot of a state row, non-temporal.  AL: the state base is
+// 16-byte aligned and the head stride a multiple of 4 floats (the padded
+// layout), so the slot is one dwordx4 access; otherwise (the packed layout,
+// heads state_floats apart) four dword accesses.
+template <bool AL>
+__device__ __forceinline__ f4v ld4(const float* p) {
+  if constexpr (AL) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+  } else {
+    return f4v{__builtin_nontemporal_load(p), __builtin_nontemporal_load(p + 1), __builtin_nontemporal_load(p + 2),
+               __builtin_nontemporal_load(p + 3)};
+  }
+}
+template <bool AL>
+__device__ __forceinline__ void st4(f4v x, float* p) {
+  if constexpr (AL) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f4v*>(p));
+  } else {
+    __builtin_nontemporal_store(x.x, p);
+    __builtin_nontemporal_store(x.y, p + 1);
+    __builtin_nontemporal_store(x.z, p + 2);
+    __builtin_nontemporal_store(x.w, p + 3);
+  }
+}
+
 __device__ __forceinline__ f4v fma4(float s, f4v v, f4v acc) {
   acc.x = fmaf(s, v.x, acc.x);
   acc.y = fmaf(s, v.y, acc.y);
@@ -44,7 +69,7 @@ __device__ __forceinline__ f4v fma4(float s, f4v v, f4v acc) {
   return acc;
 }
 
-template <int DK, typename IT>
+template <int DK, typename IT, bool AL>
 __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeArgs a) {
   constexpr int DV = DK;
   constexpr int TPR = DV / 4;          // threads per S row, one float4 each
@@ -69,7 +94,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
   // reads the tile's first row and is not written back); the features are
   // built while they are in flight.
   float* st = a.state + static_cast<int64_t>(s) * a.stride;
-  f4v* S4 = reinterpret_cast<f4v*>(st + static_cast<int64_t>(r0) * DV);
+  float* S4 = st + static_cast<int64_t>(r0) * DV;
   float* z = st + static_cast<int64_t>(a.D) * DV + r0;
   const int c4 = tid % TPR;
   const int rs = tid / TPR;
@@ -77,7 +102,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int row = rs + u * RPP;
-    x[u] = __builtin_nontemporal_load(&S4[(row < nrows ? row : 0) * TPR + c4]);
+    x[u] = ld4<AL>(S4 + ((row < nrows ? row : 0) * TPR + c4) * 4);
   }
   const float zv = __builtin_nontemporal_load(&z[tid < nrows ? tid : 0]);
 
@@ -120,7 +145,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
     const int row = rs + u * RPP;
     if (row < nrows) {
       x[u] = fma4(fk[row], vv, x[u]);
-      __builtin_nontemporal_store(x[u], &S4[row * TPR + c4]);
+      st4<AL>(x[u], S4 + (row * TPR + c4) * 4);
       acc = fma4(fq[row], x[u], acc);
     }
   }
@@ -238,10 +263,15 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(const float* __rest
 template <int D>
 hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.n_tiles, a.S);
-  if (bf16)
-    decode_update_readout<D, uint16_t><<<grid, kDecodeThreads, 0, st>>>(a);
+  const bool al = a.stride % 4 == 0 && reinterpret_cast<uintptr_t>(a.state) % 16 == 0;
+  if (bf16 && al)
+    decode_update_readout<D, uint16_t, true><<<grid, kDecodeThreads, 0, st>>>(a);
+  else if (bf16)
+    decode_update_readout<D, uint16_t, false><<<grid, kDecodeThreads, 0, st>>>(a);
+  else if (al)
+    decode_update_readout<D, float, true><<<grid, kDecodeThreads, 0, st>>>(a);
   else
-    decode_update_readout<D, float><<<grid, kDecodeThreads, 0, st>>>(a);
+    decode_update_readout<D, float, false><<<grid, kDecodeThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.groups <= 1) {

@@ -355,6 +355,7 @@ void release(sata_basis* b) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+
 int check_device(const sata_basis* b) {
   if (b->device < 0 || !b->d_rows) return SATA_ERR_INVALID_ARG;  // host-only handle
   int dev = -1;
@@ -576,17 +577,18 @@ int sata_prefill_workspace(const sata_basis* b, int B, int H, int n, int d_v, in
   return SATA_OK;
 }
 
-int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,
-                 const void* k, const void* v, float* out, float* state, void* ws, size_t ws_bytes,
-                 void* stream) {
+int sata_prefill_strided(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,
+                         const void* k, const void* v, float* out, float* state, int64_t state_stride,
+                         void* ws, size_t ws_bytes, void* stream) {
   if (!b || B < 1 || H < 1 || n < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
   if (n == 0) return SATA_OK;
   if (!q || !k || !v || !out || !state) return SATA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(state, 16))
+      !aligned(state, 4))
     return SATA_ERR_INVALID_ARG;
+  if (state_stride < static_cast<int64_t>(d_v + 1) * b->D) return SATA_ERR_INVALID_ARG;
   const int64_t BH = static_cast<int64_t>(B) * H;
   if (BH > 65535) return SATA_ERR_UNSUPPORTED;  // grid y limit
   const PrefillPlan pl = prefill_plan(b, BH, n, dtype);
@@ -596,7 +598,7 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SATA_BF16;
   const PrefillLayout& lay = b->lay[dtype];
-  const int64_t stride = sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D);
+  const int64_t stride = state_stride;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   char* base = static_cast<char*>(ws);
   size_t off = 0;
@@ -639,6 +641,15 @@ int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, c
   return SATA_OK;
 }
 
+int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,
+                 const void* k, const void* v, float* out, float* state, void* ws, size_t ws_bytes,
+                 void* stream) {
+  if (!b) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  return sata_prefill_strided(b, B, H, n, d_v, dtype, q, k, v, out, state, sata_state_floats(b, d_v), ws,
+                              ws_bytes, stream);
+}
+
 int sata_decode_workspace(const sata_basis* b, int S, int d_v, int dtype, size_t* bytes) {
   if (!b || !bytes || S < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
@@ -650,8 +661,8 @@ int sata_decode_workspace(const sata_basis* b, int S, int d_v, int dtype, size_t
   return SATA_OK;
 }
 
-int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
-                     const void* v, float* out, float* state, void* ws, size_t ws_bytes, void* stream) {
+static int decode_check(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
+                        const void* v, const float* out, const float* state, int64_t state_stride) {
   if (!b || S < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
@@ -660,13 +671,17 @@ int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void*
   const size_t esz = dtype == SATA_BF16 ? 2 : 4;
   if (!q || !k || !v || !out || !state) return SATA_ERR_INVALID_ARG;
   if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) || !aligned(out, 16) ||
-      !aligned(state, 16))
+      !aligned(state, 4))
     return SATA_ERR_INVALID_ARG;
-  size_t need = 0;
-  sata_decode_workspace(b, S, d_v, dtype, &need);
-  if (!ws || ws_bytes < need) return SATA_ERR_WORKSPACE;
-  if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
-  if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  if (state_stride < static_cast<int64_t>(d_v + 1) * b->D) return SATA_ERR_INVALID_ARG;
+  return SATA_OK;
+}
+
+// Launches the decode step with its partial records in ws (already checked
+// to hold sata_decode_workspace bytes and to be 256-byte aligned).
+static int decode_launch(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
+                         const void* v, float* out, float* state, int64_t state_stride, void* ws,
+                         void* stream) {
   const int tiles = decode_tiles(b);
   float* part = static_cast<float*>(ws);
   float* partz = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v));
@@ -674,13 +689,33 @@ int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void*
   char* lvl2 = static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
   float* part2 = groups > 1 ? reinterpret_cast<float*>(lvl2) : nullptr;
   float* partz2 = groups > 1 ? reinterpret_cast<float*>(lvl2 + decode_part_bytes(S, groups, d_v)) : nullptr;
-  sata::DecodeArgs a{q, k, v, state,
-                     sata::state_stride(static_cast<int64_t>(d_v + 1) * b->D),
+  sata::DecodeArgs a{q, k, v, state, state_stride,
                      part, partz, out, b->d_rows, b->d_weight, S,
                      static_cast<int>(b->D), tiles, groups, part2, partz2};
   if (sata::launch_decode(b->d, dtype == SATA_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SATA_ERR_HIP;
   return SATA_OK;
+}
+
+int sata_decode_step_strided(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
+                             const void* v, float* out, float* state, int64_t state_stride, void* ws,
+                             size_t ws_bytes, void* stream) {
+  int st = decode_check(b, S, d_v, dtype, q, k, v, out, state, state_stride);
+  if (st != SATA_OK || S == 0) return st;
+  size_t need = 0;
+  sata_decode_workspace(b, S, d_v, dtype, &need);
+  if (!ws || ws_bytes < need) return SATA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
+  if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  return decode_launch(b, S, d_v, dtype, q, k, v, out, state, state_stride, ws, stream);
+}
+
+int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
+                     const void* v, float* out, float* state, void* ws, size_t ws_bytes, void* stream) {
+  if (!b) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  return sata_decode_step_strided(b, S, d_v, dtype, q, k, v, out, state, sata_state_floats(b, d_v), ws,
+                                  ws_bytes, stream);
 }
 
 const char* sata_status_string(int status) {

@@ -227,6 +227,7 @@ hipError_t launch_prefill_scan(int d, bool bf16, int BH, const ScanArgs& a, hipS
 hipError_t launch_prefill_intra(int d, bool bf16, int BH, const IntraArgs& a, hipStream_t s);
 hipError_t launch_prefill_reduce(int d, bool bf16, int BH, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_decode(int d, bool bf16, const DecodeArgs& a, hipStream_t s);
+
 // bfloat16 inputs: max-abs pre-pass, staging, order-0 carry and the scan of
 // one call window; then the reduce (after the intra-window kernel).
 hipError_t launch_prefill_b16(int d, int BH, const ScanArgs& a, hipStream_t s);

@@ -368,6 +368,8 @@ struct CfgS {
   static constexpr int QT_B = (DK + 1) * 128;
   static constexpr int QN_B = L * 2 * DK;
   static constexpr int RED_B = NW * L * 2 * DV;
+  // bf16 operand path at d <= 16: the low bf16 half of every wave partial
+  static constexpr int REDL_B = DK <= 16 ? RED_B : 0;
   static constexpr int DEN_B = NW * L * 4;
   static constexpr int WL_B = NW * RB * 16 * 4;
   static constexpr int O_KT = 0;
@@ -375,7 +377,8 @@ struct CfgS {
   static constexpr int O_QT = O_VT + 2 * VT_B;
   static constexpr int O_QN = O_QT + 2 * QT_B;
   static constexpr int O_RED = O_QN + 2 * QN_B;
-  static constexpr int O_DEN = O_RED + RED_B;
+  static constexpr int O_REDL = O_RED + RED_B;
+  static constexpr int O_DEN = O_REDL + REDL_B;
   static constexpr int O_WL = O_DEN + DEN_B;
   static constexpr int O_MAX = O_WL + WL_B;
   static constexpr int LDS_B = O_MAX + 16 * NW;
@@ -454,6 +457,11 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   // column blocks (one 16-byte write per block pair)
   constexpr bool PAIRED = DV >= 32;
   constexpr int NSLOT = C::NSLOT;
+  // bf16 operands at d <= 16: the readout operand and the wave partials are
+  // carried as bf16 pairs (value and rounding residual), 16 significant bits,
+  // where a single bf16 (8 bits) would pass its rounding to outputs that
+  // average few rows.
+  constexpr bool LOX = !H16 && DK <= 16;
 
   const int tile = blockIdx.x;
   const int head = blockIdx.y;
@@ -640,6 +648,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   // barrier: each wave posts its max |S|, then every wave derives ew from
   // the tile's max and rounds its slice.
   u32x4 Sb[NKS][NB];
+  u32x4 Sbl[LOX ? NKS : 1][NB];   // residual of Sb (LOX)
   int ew = 0;
   float* wmx = reinterpret_cast<float*>(lds + C::O_MAX);
   // Largest row weight of the lane's rows: max |S| times it bounds max |S w|.
@@ -683,8 +692,13 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
           Sb[b / 2][nb][2 * (b % 2)] = pack_f16(x[0], x[1]);
           Sb[b / 2][nb][2 * (b % 2) + 1] = pack_f16(x[2], x[3]);
         } else {
-          Sb[b / 2][nb][2 * (b % 2)] = pack_bf16(x[0], x[1]);
-          Sb[b / 2][nb][2 * (b % 2) + 1] = pack_bf16(x[2], x[3]);
+          const uint32_t h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
+          Sb[b / 2][nb][2 * (b % 2)] = h0;
+          Sb[b / 2][nb][2 * (b % 2) + 1] = h1;
+          if constexpr (LOX) {
+            Sbl[b / 2][nb][2 * (b % 2)] = pack_bf16(x[0] - bf16_lo(h0), x[1] - bf16_hi(h0));
+            Sbl[b / 2][nb][2 * (b % 2) + 1] = pack_bf16(x[2] - bf16_lo(h1), x[3] - bf16_hi(h1));
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -699,6 +713,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   float* recsh = a.ws.recs + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * (nwp / L);
   static_assert(NW * 32768 <= (32768 << kRecShift), "f16 records stay in range");
   const uint16_t* red = reinterpret_cast<const uint16_t*>(lds + C::O_RED);
+  const uint16_t* redl = reinterpret_cast<const uint16_t*>(lds + C::O_REDL);
   const float* den = reinterpret_cast<const float*>(lds + C::O_DEN);
   // Two stacked 16 x 16 identities as an MFMA A operand (16-bit ones of the
   // partials' type): lane (lr, g) holds row lr, K = 8 g .. 8 g + 7; entry 1
@@ -745,6 +760,12 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
           if (DV >= 16 || (g & 1) == 0)
             x = *reinterpret_cast<const u32x4*>(&red[ww * L * DV + rho * DV + 8 * upos]);
           D = mfma16<H16>(eye, x, D);
+          if constexpr (LOX) {
+            u32x4 xl = {0u, 0u, 0u, 0u};
+            if (DV >= 16 || (g & 1) == 0)
+              xl = *reinterpret_cast<const u32x4*>(&redl[ww * L * DV + rho * DV + 8 * upos]);
+            D = mfma16<H16>(eye, xl, D);
+          }
         }
         const int t = 4 * lr + (tb ^ (lr & 1));
         // positions 4 g .. 4 g + 3 of block cb = units 2 cb + (g >> 1), half g & 1
@@ -810,6 +831,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     const unsigned char* qt = lds + C::O_QT + X * C::QT_B;
     const unsigned char* qn = lds + C::O_QN + X * C::QN_B;
     uint16_t* redw = reinterpret_cast<uint16_t*>(lds + C::O_RED) + w * L * DV;
+    uint16_t* redwl = reinterpret_cast<uint16_t*>(lds + C::O_REDL) + w * L * DV;
     // Parent products for the lane's four tokens, in token-block order
     // (element mb holds token 4 lr + (mb ^ (lr & 1))).
     u32x2 pp[RB];
@@ -878,8 +900,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       const int mb = s_ / NKS, kk = s_ % NKS;
       hook(s_);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
         acc[nb] = mfma16<H16>(Sb[kk][nb], Bcur, kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb]);
+        if constexpr (LOX) acc[nb] = mfma16<H16>(Sbl[kk][nb], Bcur, acc[nb]);
+      }
       u32x4 Bnext = Bcur;
       if (s_ + 1 < NST) Bnext = build((s_ + 1) / NKS, (s_ + 1) % NKS, cr[(s_ + 1) & 1]);
       if (s_ + 3 < NST) load_c((s_ + 3) / NKS, (s_ + 3) % NKS, cr[(s_ + 1) & 1]);
@@ -899,8 +923,14 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
           for (int nb = 0; nb < NB; ++nb) {
             if (16 * nb < DV && (16 * nb + 16 <= DV || 4 * g < DV % 16)) {
               const int cu = 2 * nb + (g >> 1);
-              const u32x2 o = {pack_red(acc[nb][0], acc[nb][1]), pack_red(acc[nb][2], acc[nb][3])};
-              *reinterpret_cast<u32x2*>(&redw[rho * DV + 8 * (cu ^ (swz_row(rho) % NU)) + 4 * (g & 1)]) = o;
+              const uint32_t o0 = pack_red(acc[nb][0], acc[nb][1]), o1 = pack_red(acc[nb][2], acc[nb][3]);
+              const int ro = rho * DV + 8 * (cu ^ (swz_row(rho) % NU)) + 4 * (g & 1);
+              *reinterpret_cast<u32x2*>(&redw[ro]) = u32x2{o0, o1};
+              if constexpr (LOX) {
+                const u32x2 ol = {pack_bf16(acc[nb][0] - bf16_lo(o0), acc[nb][1] - bf16_hi(o0)),
+                                  pack_bf16(acc[nb][2] - bf16_lo(o1), acc[nb][3] - bf16_hi(o1))};
+                *reinterpret_cast<u32x2*>(&redwl[ro]) = ol;
+              }
             }
           }
         }

@@ -74,7 +74,12 @@ void sata_free_basis(sata_basis* basis);
 /* Basic facts of a handle. */
 int sata_basis_info(const sata_basis* basis, int* d_k, int* P, double* c, int64_t* total_rows);
 
-/* Number of rows of order p: C(d_k + p - 1, p). */
+/* Number of rows of order p: C(d_k + p - 1, p), the size of the minimal basis
+ * of the order-p symmetric tensor [SATA page, "Core insight: symmetric tensor
+ * decomposition"]; summed over p = 0..P-1 it is C(d_k + P - 1, P - 1)
+ * [same page, "Engineering of constant compute cost"].  *rows is written on
+ * success; SATA_ERR_INVALID_ARG for a null handle or pointer or p outside
+ * [0, P). */
 int sata_basis_rows(const sata_basis* basis, int p, int64_t* rows);
 
 /* Copy the host tables of order p: idx [rows * p] int32 (row-major, 0-based,
@@ -88,17 +93,20 @@ int sata_basis_copy_tables(const sata_basis* basis, int p, int32_t* idx, uint32_
  * float(mult / (p! c^p)).  Host pointers of total_rows elements; synchronous. */
 int sata_basis_download_rows(const sata_basis* basis, uint32_t* packed, float* weight);
 
-/* Number of float32 values of one head's state: (d_v + 1) * C(d_k + P - 1, P - 1).
+/* Number of float32 values of one head's state: (d_v + 1) * C(d_k + P - 1, P - 1),
+ * the fixed state size of the SATA page, section "Engineering of constant
+ * compute cost" (S_p holds d_v columns and z_p one per basis row; it does not
+ * depend on the sequence length).
  * Layout: S as [D][d_v] row-major, then z as [D]; row order as in
  * sata_build_basis.  Row m holds unweighted monomials (the weights w_m are
- * applied on the query side).  Returns -1 on an invalid argument. */
+ * applied on the query side).  Returns -1 on a null handle or d_v != d_k. */
 int64_t sata_state_floats(const sata_basis* basis, int d_v);
 
-/* Floats between consecutive heads' states in a state buffer: sata_state_floats
- * rounded up to a multiple of 64, so that every head starts 256-byte aligned.
- * A buffer of S states holds S * sata_state_stride floats; the values past
- * sata_state_floats in each head are padding that no call reads or writes.
- * Returns -1 on an invalid argument. */
+/* A head stride (floats) for the *_strided calls: sata_state_floats rounded
+ * up to a multiple of 64, so that every head starts 256-byte aligned and the
+ * decode step streams its rows with 16-byte accesses (the fastest layout).
+ * The values past sata_state_floats in each head are padding that no call
+ * reads or writes.  Returns -1 on a null handle or d_v != d_k. */
 int64_t sata_state_stride(const sata_basis* basis, int d_v);
 
 /* Device workspace in bytes that sata_prefill needs for these sizes.  Long
@@ -109,15 +117,20 @@ int64_t sata_state_stride(const sata_basis* basis, int d_v);
 int sata_prefill_workspace(const sata_basis* basis, int B, int H, int n, int d_v, int dtype,
                            size_t* bytes);
 
-/* Causal prefill of n tokens for B*H independent heads.
+/* Causal prefill of n tokens for B*H independent heads [SATA page, "Engineering
+ * of constant compute cost": each key enters the fixed-size state
+ * S_m += phi_m(k) v, z_m += phi_m(k), and each query reads it out through the
+ * weighted feature map; the sum over j runs to the current token].
  *   q, k: [B, H, n, d_k], v: [B, H, n, d_v], contiguous, dtype as given,
  *         16-byte aligned.
  *   out:  [B, H, n, d_v] float32, 16-byte aligned; row i receives
  *         sum_{j<=i} T_P(q_i.k_j/c) v_j / sum_{j<=i} T_P(q_i.k_j/c), where the
  *         sum also runs over the tokens already folded into `state`.
- *   state:[B*H][sata_state_stride] float32, 16-byte aligned, in/out: the state
- *         of the tokens before this call (all zeros = empty prefix) is read and
- *         the state after the n tokens is written back.
+ *   state:[B*H][sata_state_floats] float32 (heads packed back to back),
+ *         4-byte aligned, in/out: the state of the tokens before this call
+ *         (all zeros = empty prefix) is read and the state after the n tokens
+ *         is written back.  Nothing outside B*H*sata_state_floats floats is
+ *         touched.
  *   ws:   device workspace of at least sata_prefill_workspace bytes, 256-byte
  *         aligned; its contents on entry do not matter.
  * Arithmetic: float32 inputs run in fp32 throughout.  bfloat16 inputs run the
@@ -125,13 +138,23 @@ int sata_prefill_workspace(const sata_basis* basis, int B, int H, int n, int d_v
  * (f16 after exact per-head power-of-two scaling when the inputs' ranges
  * allow it, else bf16) with fp32 accumulation and an fp32 state; the tests
  * gate the row-normwise error against the exact truncated polynomial at 1e-5
- * (float32) and 3e-3 (bfloat16).  Heads whose query/key scales leave the
- * f16 range (query features beyond 2^12 after the scaling) use bf16 operands
- * and can exceed 3e-3 at small d_k over sequences of thousands of tokens.
+ * (float32) and 3e-3 (bfloat16), on both operand paths.
+ * Errors: SATA_ERR_INVALID_ARG (null or misaligned pointer, B, H < 1, n < 0,
+ * bad dtype, a basis of another device or a host-only basis),
+ * SATA_ERR_UNSUPPORTED (d_v != d_k, B*H > 65535), SATA_ERR_WORKSPACE.
  * n = 0 is a valid no-op. */
 int sata_prefill(const sata_basis* basis, int B, int H, int n, int d_v, int dtype,
                  const void* q, const void* k, const void* v, float* out, float* state,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* sata_prefill with heads state_stride floats apart in `state`
+ * (state_stride >= sata_state_floats, else SATA_ERR_INVALID_ARG); the floats
+ * between sata_state_floats and state_stride of each head are not touched.
+ * sata_state_stride gives the aligned stride the decode step streams
+ * fastest. */
+int sata_prefill_strided(const sata_basis* basis, int B, int H, int n, int d_v, int dtype,
+                         const void* q, const void* k, const void* v, float* out, float* state,
+                         int64_t state_stride, void* ws, size_t ws_bytes, void* stream);
 
 /* Device workspace in bytes that sata_decode_step needs for S states. */
 int sata_decode_workspace(const sata_basis* basis, int S, int d_v, int dtype, size_t* bytes);
@@ -141,13 +164,22 @@ int sata_decode_workspace(const sata_basis* basis, int S, int d_v, int dtype, si
  * z_m += phi_m(k)) and then reads out out = sum_m w_m phi_m(q) S_m /
  * sum_m w_m phi_m(q) z_m, so the new token attends to itself
  * [SATA page, "Engineering of constant compute cost"].
- *   q, k: [S, d_k]; v: [S, d_v] (dtype as given); out: [S, d_v] float32;
- *   state: [S][sata_state_stride] float32 in/out; 16-byte aligned out/state,
- *   256-byte aligned ws of at least sata_decode_workspace bytes.
+ *   q, k: [S, d_k]; v: [S, d_v] (dtype as given); out: [S, d_v] float32,
+ *   16-byte aligned; state: [S][sata_state_floats] float32 in/out (packed,
+ *   4-byte aligned); ws: 256-byte aligned, at least sata_decode_workspace
+ *   bytes.  Errors as for sata_prefill.
  * S = 0 is a valid no-op. */
 int sata_decode_step(const sata_basis* basis, int S, int d_v, int dtype, const void* q,
                      const void* k, const void* v, float* out, float* state, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* sata_decode_step with states state_stride floats apart (state_stride >=
+ * sata_state_floats).  With a stride that is a multiple of 4 floats and a
+ * 16-byte aligned state (sata_state_stride), rows stream as 16-byte
+ * accesses; otherwise as 4-byte ones. */
+int sata_decode_step_strided(const sata_basis* basis, int S, int d_v, int dtype, const void* q,
+                             const void* k, const void* v, float* out, float* state,
+                             int64_t state_stride, void* ws, size_t ws_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* sata_status_string(int status);

@@ -98,16 +98,6 @@ def direct_taylor(q, k, v, P: int, c: float = 1.0, rows=None, block: int = 1024,
     return (out, den) if return_den else out
 
 
-def direct_taylor_bh(Q, K, V, P: int, c: float = 1.0):
-    """direct_taylor over [B, H, n, d] inputs."""
-    B, H = Q.shape[:2]
-    out = np.empty(Q.shape[:3] + (V.shape[3],), dtype=np.float64)
-    for b in range(B):
-        for h in range(H):
-            out[b, h] = direct_taylor(Q[b, h], K[b, h], V[b, h], P, c)
-    return out
-
-
 # ----------------------------------------------------------------------------
 # Exact causal softmax (report only)
 # ----------------------------------------------------------------------------

@@ -75,6 +75,12 @@ def test_host_only_handle_rejects_compute():
     assert L.sata_prefill(b.handle, 1, 1, -1, 16, SA.SATA_F32, p, p, p, p, p, p, 1 << 20, None) == SA.SATA_ERR_INVALID_ARG
     assert L.sata_prefill(b.handle, 1, 1, 4, 16, SA.SATA_F32, p, p, p, p, p, p, 8, None) == SA.SATA_ERR_WORKSPACE
     assert L.sata_decode_step(b.handle, 2, 16, SA.SATA_F32, p, p, p, p, p, p, 0, None) == SA.SATA_ERR_WORKSPACE
+    # the strided calls refuse a head stride below the state size
+    F = b.state_floats()
+    assert L.sata_prefill_strided(b.handle, 1, 1, 4, 16, SA.SATA_F32, p, p, p, p, p, F - 1, p, 1 << 20,
+                                  None) == SA.SATA_ERR_INVALID_ARG
+    assert L.sata_decode_step_strided(b.handle, 2, 16, SA.SATA_F32, p, p, p, p, p, F - 1, p, 1 << 20,
+                                      None) == SA.SATA_ERR_INVALID_ARG
     # a host-only handle is refused once everything else checks out
     assert L.sata_decode_step(b.handle, 2, 16, SA.SATA_F32, p, p, p, p, p, p, 1 << 20, None) == SA.SATA_ERR_INVALID_ARG
     assert SA.status_string(SA.SATA_ERR_HIP).startswith("SATA_ERR_HIP")
@@ -116,3 +122,4 @@ def test_binding_checks_inputs_before_any_call():
         SA.prefill(b, q, q, q)                                 # host tensors
     with pytest.raises(ValueError, match="GPU"):
         SA.decode_step(b, q[0, 0], q[0, 0], q[0, 0], torch.zeros((4, b.state_stride())))
+

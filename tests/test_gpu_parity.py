@@ -382,6 +382,96 @@ def test_prefill_bf16_large_query_coordinates(d, P, q0, kf):
         assert O.row_normwise_error(got[0, h], ref) <= TOL[W.BF16], h
 
 
+def _bf16_operand_path(q, k, P):
+    """Whether a head takes the bf16 operand path: the exact power-of-two split
+    of the magnitude between q and k (the same rule as the kernels': |q| < 2^eq,
+    |k| < 2^ekk, ek = (ekk - eq) / 2 truncated) leaves query or key features,
+    products of up to P-1 coordinates, at or beyond 2^13."""
+    eq = math.frexp(float(np.max(np.abs(q))))[1]
+    ekk = math.frexp(float(np.max(np.abs(k))))[1]
+    ek = int((ekk - eq) / 2)
+    return (P - 1) * max(eq + ek, 0) > 12 or (P - 1) * max(ekk - ek, 0) > 12
+
+
+@pytest.mark.parametrize("d,P,n", [(8, 4, 2000), (8, 4, 4096), (8, 5, 2000), (8, 5, 4096),
+                                   (16, 4, 2000), (16, 4, 4096), (16, 5, 2000), (16, 5, 4096)])
+def test_prefill_bf16_operand_path_small_heads(d, P, n):
+    """Small heads forced onto the bf16 operand path (a query coordinate of
+    1000, the matching key coordinate x 1e-4) over several readout windows:
+    few rows per output, so the path carries its readout operand and wave
+    partials as bf16 value + residual pairs."""
+    note(f"bf16 operand path d={d} P={P} n={n}")
+    q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 19000 + d + P)
+    q = q.copy()
+    k = k.copy()
+    q[..., 0] = 1000.0
+    k[..., 0] *= 1e-4
+    q, k, v = _rows_bf16(q), _rows_bf16(k), _rows_bf16(v)
+    for h in range(2):
+        assert _bf16_operand_path(q[0, h], k[0, h], P), h
+    b = SA.build_basis(d, P, 1.0)
+    out, _ = run_prefill(b, q, k, v, W.BF16)
+    got = out.cpu().numpy()
+    for h in range(2):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
+        assert O.row_normwise_error(got[0, h], ref) <= TOL[W.BF16], h
+
+
+@pytest.mark.parametrize("d,P,dtype", [(8, 3, W.F32), (16, 4, W.BF16), (64, 4, W.BF16)])
+def test_packed_state_layout_c_abi(d, P, dtype):
+    """sata_prefill and sata_decode_step with heads packed state_floats apart
+    (an odd count at these sizes, so every other head starts 4 bytes past a
+    16-byte boundary) and the buffer itself 4 bytes off: outputs match the
+    oracle, the state equals the padded layout's bit for bit, and guard words
+    before and after the buffer are untouched."""
+    note(f"packed state layout d={d} P={P} {dtype}")
+    H, n, steps = 3, 200, 4
+    q, k, v = W.make_qkv(1, H, n + steps, d, d, dtype, 21000 + d)
+    b = SA.build_basis(d, P, 1.0)
+    F = b.state_floats()
+    assert F % 2 == 1
+    G = 64
+    code = SA.SATA_BF16 if dtype == W.BF16 else SA.SATA_F32
+    buf = torch.full((H * F + 2 * G + 1,), 1234.5, dtype=torch.float32, device="cuda")
+    st_ptr = buf.data_ptr() + 4 * (G + 1)            # 4-byte aligned, not 16
+    L = SA.lib()
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    qp, kp, vp = (x[:, :, :n].contiguous() for x in (qd, kd, vd))
+    out = torch.empty((1, H, n, d), dtype=torch.float32, device="cuda")
+    ws = SA.workspace(SA.prefill_workspace_bytes(b, 1, H, n, d, code))
+    # the state region starts zeroed (empty prefix)
+    buf[G + 1:G + 1 + H * F] = 0.0
+    st = L.sata_prefill(b.handle, 1, H, n, d, code, qp.data_ptr(), kp.data_ptr(), vp.data_ptr(), out.data_ptr(),
+                        st_ptr, ws.data_ptr(), ws.numel(), SA._stream_ptr(torch.device("cuda")))
+    assert st == SA.SATA_OK, SA.status_string(st)
+    dws = SA.workspace(SA.decode_workspace_bytes(b, H, d, code))
+    dout = torch.empty((steps, H, d), dtype=torch.float32, device="cuda")
+    for t in range(steps):
+        qt, kt, vt = (x[0, :, n + t].contiguous() for x in (qd, kd, vd))
+        st = L.sata_decode_step(b.handle, H, d, code, qt.data_ptr(), kt.data_ptr(), vt.data_ptr(),
+                                dout[t].data_ptr(), st_ptr, dws.data_ptr(), dws.numel(),
+                                SA._stream_ptr(torch.device("cuda")))
+        assert st == SA.SATA_OK, SA.status_string(st)
+    torch.cuda.synchronize()
+    # guard words
+    assert torch.all(buf[:G + 1] == 1234.5) and torch.all(buf[G + 1 + H * F:] == 1234.5)
+    # the same calls on the padded layout give the same bits
+    out2, st2 = SA.prefill(b, qp, kp, vp)
+    dout2 = torch.stack([SA.decode_step(b, *(x[0, :, n + t].contiguous() for x in (qd, kd, vd)), st2)
+                         for t in range(steps)])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(dout, dout2)
+    packed = buf[G + 1:G + 1 + H * F].view(H, F)
+    assert torch.equal(packed, st2[:, :F])
+    tol = TOL[dtype]
+    got = out.cpu().numpy()
+    gd = dout.cpu().numpy()
+    for h in range(H):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
+        assert O.row_normwise_error(got[0, h], ref[:n]) <= tol, h
+        assert O.row_normwise_error(gd[:, h], ref[n:]) <= tol, h
+
+
 def test_two_streams_share_a_basis():
     """Prefill and decode of two state batches on two streams at once, with
     one basis, give bit for bit what they give one after the other."""

@@ -315,6 +315,29 @@ def test_truncation_error_bound_and_decrease():
     assert all(a > b for a, b in zip(errs, errs[1:]))
 
 
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 5])
+def test_taylor_delta_exact_values(P):
+    """delta at logits of +-1 and 1/2 against the partial sums of e written as
+    exact fractions (T_P(1) = 1, 2, 5/2, 8/3, 65/24; T_P(-1) = 1, 0, 1/2, 1/3,
+    3/8), with math.e / math.exp as the exponential; the max runs over the
+    keys j <= i only."""
+    t_plus = [Fraction(1), Fraction(2), Fraction(5, 2), Fraction(8, 3), Fraction(65, 24)][P - 1]
+    t_minus = [Fraction(1), Fraction(0), Fraction(1, 2), Fraction(1, 3), Fraction(3, 8)][P - 1]
+    t_half = sum(Fraction(1, 2 ** p * math.factorial(p)) for p in range(P))
+    d_plus = abs(1.0 - float(t_plus) / math.e)
+    d_minus = abs(1.0 - float(t_minus) * math.e)
+    d_half = abs(1.0 - float(t_half) / math.exp(0.5))
+    q = np.array([[1.0, 0.0], [1.0, 0.0], [0.0, 1.0]])
+    k = np.array([[1.0, 0.0], [-1.0, 0.0], [0.0, 5.0]])   # row 2's own key: x = 5
+    got = O.taylor_delta(q[:2], k[:2], P)
+    np.testing.assert_allclose(got, [d_plus, max(d_plus, d_minus)], rtol=1e-13, atol=1e-15)
+    # c = 2 halves every logit; a later key never enters an earlier row
+    got = O.taylor_delta(q, k, P, c=2.0, rows=[0])
+    np.testing.assert_allclose(got, [d_half], rtol=1e-13, atol=1e-15)
+    # a zero logit is exact for every P
+    assert O.taylor_delta(np.array([[0.0, 1.0]]), np.array([[1.0, 0.0]]), P)[0] == 0.0
+
+
 def test_denominator_positive_on_unit_rows():
     # |x| <= 1 for unit rows; T_3 >= 1/2 and T_4 >= 1/3 there
     xs = np.linspace(-1.01, 1.01, 2001)
