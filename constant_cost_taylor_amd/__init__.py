@@ -21,6 +21,7 @@ SATA_ERR_UNSUPPORTED = -2
 SATA_ERR_WORKSPACE = -3
 SATA_ERR_HIP = -4
 SATA_ERR_OOM = -5
+SATA_ERR_SCRATCH = -6
 SATA_F32 = 0
 SATA_BF16 = 1
 
@@ -70,6 +71,11 @@ def _declare(lib):
     lib.sata_decode_step_strided.argtypes = [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
                                              c_vp, c_sz, c_vp]
     lib.sata_decode_step_strided.restype = c_int
+    lib.sata_decode_step_noalloc.argtypes = [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
+                                             c_vp]
+    lib.sata_decode_step_noalloc.restype = c_int
+    lib.sata_decode_noalloc_max_bytes.argtypes = []
+    lib.sata_decode_noalloc_max_bytes.restype = c_sz
     lib.sata_status_string.argtypes = [c_int]
     lib.sata_status_string.restype = ctypes.c_char_p
 
@@ -282,3 +288,22 @@ def decode_step(basis: Basis, q, k, v, state, out=None, ws=None):
     _check(st, "sata_decode_step_strided")
     return out
 
+
+def decode_step_noalloc(basis: Basis, q, k, v, state, out):
+    """decode_step through sata_decode_step_noalloc: the library allocates
+    nothing (its partial records live in a static device array shared by every
+    call on the device, so calls must not overlap in time).  out [S, d_v]
+    float32 is caller-provided.  Returns out."""
+    import torch
+    if q.dim() != 2 or k.shape != q.shape or v.dim() != 2 or v.shape[0] != q.shape[0]:
+        raise ValueError("q, k must be [S, d_k] and v [S, d_v]")
+    _check_inputs(basis, q, k, v)
+    S = q.shape[0]
+    d_v = v.shape[1]
+    stride = _state_stride(basis, state, S, d_v, q.device)
+    _check_buffer("out", out, torch.float32, S * d_v, q.device)
+    st = lib().sata_decode_step_noalloc(basis.handle, S, d_v, _dtype_code(q), q.data_ptr(), k.data_ptr(),
+                                        v.data_ptr(), out.data_ptr(), state.data_ptr(), stride,
+                                        _stream_ptr(q.device))
+    _check(st, "sata_decode_step_noalloc")
+    return out

@@ -292,6 +292,14 @@ hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Scratch of sata_decode_step_noalloc: the per-tile partial records of a
+// decode step (the same regions as the caller's workspace of
+// sata_decode_step).  Host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch_address(void** ptr) { return hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch)); }
+
 hipError_t launch_decode(int d, bool bf16, const DecodeArgs& a, hipStream_t s) {
   switch (d) {
     case 8: return launch_d<8>(bf16, a, s);

@@ -17,6 +17,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -41,6 +42,7 @@ struct sata_basis {
   float* d_weight = nullptr;
   PrefillLayout lay[2];                      // [0] float32 inputs, [1] bfloat16 inputs
   std::vector<void*> allocations;
+  void* scratch = nullptr;                   // device address of the no-alloc decode scratch
 };
 
 namespace {
@@ -355,6 +357,21 @@ void release(sata_basis* b) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Device address of the no-alloc decode scratch on the current device,
+// resolved once per device (nullptr if the lookup failed).
+void* scratch_for_current_device() {
+  static std::mutex mu;
+  static std::vector<std::pair<int, void*>> known;   // (device, address)
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : known)
+    if (e.first == dev) return e.second;
+  void* p = nullptr;
+  if (sata::noalloc_scratch_address(&p) != hipSuccess) p = nullptr;
+  known.emplace_back(dev, p);
+  return p;
+}
 
 int check_device(const sata_basis* b) {
   if (b->device < 0 || !b->d_rows) return SATA_ERR_INVALID_ARG;  // host-only handle
@@ -503,6 +520,7 @@ static int build_basis_impl(int d_k, int P, double c, bool upload_tables, sata_b
     release(b);
     return st;
   }
+  b->scratch = scratch_for_current_device();
   *out = b;
   return SATA_OK;
 }
@@ -710,6 +728,20 @@ int sata_decode_step_strided(const sata_basis* b, int S, int d_v, int dtype, con
   return decode_launch(b, S, d_v, dtype, q, k, v, out, state, state_stride, ws, stream);
 }
 
+int sata_decode_step_noalloc(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
+                             const void* v, float* out, float* state, int64_t state_stride, void* stream) {
+  int st = decode_check(b, S, d_v, dtype, q, k, v, out, state, state_stride);
+  if (st != SATA_OK || S == 0) return st;
+  size_t need = 0;
+  sata_decode_workspace(b, S, d_v, dtype, &need);
+  if (need > sata::kNoAllocScratchBytes) return SATA_ERR_SCRATCH;
+  if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  if (!b->scratch) return SATA_ERR_HIP;
+  return decode_launch(b, S, d_v, dtype, q, k, v, out, state, state_stride, b->scratch, stream);
+}
+
+size_t sata_decode_noalloc_max_bytes(void) { return sata::kNoAllocScratchBytes; }
+
 int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
                      const void* v, float* out, float* state, void* ws, size_t ws_bytes, void* stream) {
   if (!b) return SATA_ERR_INVALID_ARG;
@@ -726,6 +758,9 @@ const char* sata_status_string(int status) {
     case SATA_ERR_WORKSPACE: return "SATA_ERR_WORKSPACE: workspace too small";
     case SATA_ERR_HIP: return "SATA_ERR_HIP: HIP runtime or launch failure";
     case SATA_ERR_OOM: return "SATA_ERR_OOM: allocation failed";
+    case SATA_ERR_SCRATCH:
+      return "SATA_ERR_SCRATCH: the call needs more scratch than the static array of "
+             "sata_decode_step_noalloc holds (sata_decode_noalloc_max_bytes)";
     default: return "unknown SATA status";
   }
 }

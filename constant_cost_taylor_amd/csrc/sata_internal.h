@@ -228,6 +228,12 @@ hipError_t launch_prefill_intra(int d, bool bf16, int BH, const IntraArgs& a, hi
 hipError_t launch_prefill_reduce(int d, bool bf16, int BH, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_decode(int d, bool bf16, const DecodeArgs& a, hipStream_t s);
 
+// The allocation-free decode entry point keeps its partial records in a
+// file-scope device array of this many bytes (one copy per device, held
+// until the process ends).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+// Device address of that array on the current device (hipGetSymbolAddress).
+hipError_t noalloc_scratch_address(void** ptr);
 // bfloat16 inputs: max-abs pre-pass, staging, order-0 carry and the scan of
 // one call window; then the reduce (after the intra-window kernel).
 hipError_t launch_prefill_b16(int d, int BH, const ScanArgs& a, hipStream_t s);

@@ -49,7 +49,8 @@ enum sata_status {
   SATA_ERR_UNSUPPORTED = -2, /* d_k, d_v or P outside the compiled instances */
   SATA_ERR_WORKSPACE = -3,   /* ws too small (or null while bytes > 0) */
   SATA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
-  SATA_ERR_OOM = -5          /* host or device allocation failed in sata_build_basis */
+  SATA_ERR_OOM = -5,         /* host or device allocation failed in sata_build_basis */
+  SATA_ERR_SCRATCH = -6      /* sata_decode_step_noalloc: the call needs more than its static scratch */
 };
 
 enum sata_dtype { SATA_F32 = 0, SATA_BF16 = 1 }; /* input dtype of q, k, v */
@@ -180,6 +181,26 @@ int sata_decode_step(const sata_basis* basis, int S, int d_v, int dtype, const v
 int sata_decode_step_strided(const sata_basis* basis, int S, int d_v, int dtype, const void* q,
                              const void* k, const void* v, float* out, float* state,
                              int64_t state_stride, void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sata_decode_step_strided without a workspace argument.  The per-tile
+ * partial records live in a file-scope device array of
+ * sata_decode_noalloc_max_bytes() bytes (32 MiB), one per device, held until
+ * the process ends and resolved once per device when a basis is built there.
+ * A call whose sata_decode_workspace exceeds that size returns
+ * SATA_ERR_SCRATCH (at d = 64, P = 4: up to 43 states a call) and launches
+ * nothing.  The call itself allocates and frees nothing.  Every call on one
+ * device shares that device's array: calls that overlap in time on one
+ * device (other streams, other threads) race and must be serialised by the
+ * caller.  Each call overwrites every record it reads, so nothing needs
+ * clearing between calls.  Results are bit-identical to sata_decode_step_strided. */
+int sata_decode_step_noalloc(const sata_basis* basis, int S, int d_v, int dtype, const void* q,
+                             const void* k, const void* v, float* out, float* state,
+                             int64_t state_stride, void* stream);
+
+/* Bytes of the static scratch array behind sata_decode_step_noalloc. */
+size_t sata_decode_noalloc_max_bytes(void);
 
 /* Static, human-readable name of a status code. */
 const char* sata_status_string(int status);

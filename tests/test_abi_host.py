@@ -123,3 +123,25 @@ def test_binding_checks_inputs_before_any_call():
     with pytest.raises(ValueError, match="GPU"):
         SA.decode_step(b, q[0, 0], q[0, 0], q[0, 0], torch.zeros((4, b.state_stride())))
 
+
+def test_noalloc_decode_size_limit_on_host():
+    """The allocation-free decode refuses a call whose partial records exceed
+    its static scratch before touching a GPU (a host-only handle answers the
+    size check first); within the limit the host-only handle is refused."""
+    b = SA.build_basis(64, 4, 1.0, host_only=True)
+    L = SA.lib()
+    cap = L.sata_decode_noalloc_max_bytes()
+    assert cap == 32 << 20
+    buf = (ctypes.c_float * 64)()
+    p = ctypes.c_void_p((ctypes.addressof(buf) + 15) // 16 * 16)
+    F = b.state_floats()
+    S = 1
+    while SA.decode_workspace_bytes(b, S, 64, SA.SATA_BF16) <= cap:
+        S += 1
+    assert S == 44
+    assert L.sata_decode_step_noalloc(b.handle, S, 64, SA.SATA_BF16, p, p, p, p, p, F, None) == SA.SATA_ERR_SCRATCH
+    assert L.sata_decode_step_noalloc(b.handle, S - 1, 64, SA.SATA_BF16, p, p, p, p, p, F,
+                                      None) == SA.SATA_ERR_INVALID_ARG
+    assert L.sata_decode_step_noalloc(b.handle, 0, 64, SA.SATA_BF16, None, None, None, None, None, F,
+                                      None) == SA.SATA_OK
+    assert SA.status_string(SA.SATA_ERR_SCRATCH).startswith("SATA_ERR_SCRATCH")
