@@ -8,7 +8,11 @@ seeded synthetic data (workloads.py), resident in HBM before timing starts.
 Prints one JSON line.  `value` is head-tokens/s over the whole step (every
 prefill and decode token of every state).  The prefill and decode legs are
 also reported on their own, each against its roofline; `roofline` describes
-the dominant kernel (the decode update/readout, bound by HBM).  The CPU
+the dominant kernel (the decode update/readout, bound by HBM).  After the
+timed steps, `configs` reports the other workloads, each against its own
+roofline (a few repetitions each): the d8 / d16 fp32 and d64 bf16 prefills,
+the long-context d32 prefill at 2^16, 2^18 and 2^20 tokens with its per-token
+cost ratio, and the orders 0..4 (P = 5) prefill and decode legs.  The CPU
 baseline is the float64 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -42,6 +46,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (timed after the headline step: the d8/d16/d64 prefills, "
+                         "the long-context sweep at 2^16..2^20 and the orders 0..4 legs)")
+    ap.add_argument("--config-steps", type=int, default=5,
+                    help="timed repetitions of each of the other workloads (one warmup each)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--flatness", action="store_true",
                     help="instead of the step: prefill cost per token of the long-context workload "
@@ -98,22 +107,41 @@ def cpu_baseline(w, q, k, v, qs, ks, vs, budget_s):
                       f"({rows} head-tokens, float64 numpy, {el:.1f} s)"}
 
 
-def flatness(args):
-    """Prefill time per token at growing context: the state is fixed-size, so
-    the per-token cost should not grow with n.  Inputs: seeded unit-norm
-    Gaussian q, k and Gaussian v generated on the device (same distribution as
-    the seeded host generators, which would take minutes at 2^20 tokens)."""
+def _time_prefill(sa, basis, Q, K, V, state, out, ws, stream, reps, warmup):
+    """Median HIP-event time (ms) of a prefill from empty states."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms = []
+    for it in range(warmup + reps):
+        state.zero_()
+        ev[0].record(stream)
+        sa.prefill(basis, Q, K, V, state=state, out=out, ws=ws)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if it >= warmup:
+            ms.append(ev[0].elapsed_time(ev[1]))
+    return float(np.median(ms))
+
+
+def flatness_points(reps, warmup, lgs=(16, 18, 20)):
+    """Prefill time per token of the long-context workload (16 heads, d = 32,
+    P = 4, bf16) at growing context: the state is fixed-size, so the per-token
+    cost should not grow with n.  Inputs: seeded unit-norm Gaussian q, k and
+    Gaussian v generated on the device (same distribution as the seeded host
+    generators, which would take minutes at 2^20 tokens)."""
     import torch
     import constant_cost_taylor_amd as sa
     import workloads as W
+    from oracle import sata_oracle as O
     w = W.WORKLOADS["long_d32_n1m"]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     basis = sa.build_basis(w.d_k, w.P, w.c)
     g = torch.Generator(device=dev)
     g.manual_seed(1000 * w.seed)
+    stream = torch.cuda.current_stream(dev)
+    _, page_flops = O.cost_model(w.d_k, w.d_v, w.P)
     rows = []
-    for lg in (16, 18, 20):
+    for lg in lgs:
         n = 1 << lg
         shape = (w.B, w.H, n, w.d_k)
         q = torch.randn(shape, generator=g, device=dev)
@@ -124,44 +152,41 @@ def flatness(args):
         out = torch.empty(shape, dtype=torch.float32, device=dev)
         state = sa.new_state(basis, w.B * w.H, dev)
         ws = sa.workspace(sa.prefill_workspace_bytes(basis, w.B, w.H, n, w.d_v, sa.SATA_BF16), dev)
-        stream = torch.cuda.current_stream(dev)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ms = []
-        for it in range(args.warmup + args.steps):
-            state.zero_()
-            ev[0].record(stream)
-            sa.prefill(basis, q, k, v, state=state, out=out, ws=ws)
-            ev[1].record(stream)
-            torch.cuda.synchronize()
-            if it >= args.warmup:
-                ms.append(ev[0].elapsed_time(ev[1]))
-        t = float(np.median(ms))
+        t = _time_prefill(sa, basis, q, k, v, state, out, ws, stream, reps, warmup)
         tok = w.B * w.H * n
-        rows.append({"n": n, "ms": t, "ns_per_head_token": 1e6 * t / tok,
-                     "head_tokens_per_s": tok / (t * 1e-3), "finite": bool(torch.isfinite(out).all())})
-        print(f"flatness n=2^{lg}: {t:.2f} ms", file=sys.stderr, flush=True)
+        tf = tok * page_flops / (t * 1e-3) / 1e12
+        rows.append({"n": n, "ms": t, "ns_per_head_token": 1e6 * t / tok, "head_tokens_per_s": tok / (t * 1e-3),
+                     "page_tflops": tf, "mfma_bf16_frac": tf / BF16_PEAK_TFLOPS,
+                     "finite": bool(torch.isfinite(out).all())})
+        print(f"long-context prefill n=2^{lg}: {t:.2f} ms", file=sys.stderr, flush=True)
         del q, k, v, out, state, ws
         torch.cuda.empty_cache()
-    print(json.dumps({"metric": "prefill per-token cost vs context length", "unit": "ns/head-token",
-                      "config": {"workload": f"long-context prefill: batch {w.B} x {w.H} heads, "
-                                             f"d_k=d_v={w.d_k}, P={w.P}, bf16 inputs, f32 state"},
-                      "steps": args.steps, "warmup": args.warmup, "points": rows,
-                      "ratio_2e20_over_2e16": rows[-1]["ns_per_head_token"] / rows[0]["ns_per_head_token"]}),
+    return {"workload": f"long-context prefill: batch {w.B} x {w.H} heads, d_k=d_v={w.d_k}, P={w.P}, bf16 inputs, "
+                        f"f32 state, n = 2^16, 2^18, 2^20 (device-generated inputs)",
+            "steps": reps, "warmup": warmup, "points": rows,
+            "per_token_cost_ratio_last_over_first": rows[-1]["ns_per_head_token"] / rows[0]["ns_per_head_token"]}
+
+
+def flatness(args):
+    torch = __import__("torch")
+    torch.cuda.set_device(0)
+    res = flatness_points(args.steps, args.warmup)
+    print(json.dumps({"metric": "prefill per-token cost vs context length", "unit": "ns/head-token", **res}),
           flush=True)
 
 
-def configs(args):
-    """Prefill of the remaining workloads at their full sizes, from empty
-    states, inputs from the seeded generators (workloads.py)."""
+def config_points(reps, warmup, names=("tiny_d8_n256", "d16_n4096", "d64_n16384")):
+    """Prefill of the other workloads at their full sizes, from empty states,
+    inputs from the seeded generators (workloads.py), each against the MFMA
+    peak of its arithmetic (page FLOPs / time)."""
     import torch
     import constant_cost_taylor_amd as sa
     import workloads as W
     from oracle import sata_oracle as O
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    rows = []
-    for name in ("tiny_d8_n256", "d16_n4096", "d64_n16384"):
+    res = {}
+    for name in names:
         w = W.WORKLOADS[name]
         basis = sa.build_basis(w.d_k, w.P, w.c)
         q, k, v = W.workload_inputs(w)
@@ -172,34 +197,31 @@ def configs(args):
         state = sa.new_state(basis, w.B * w.H, dev)
         ws = sa.workspace(sa.prefill_workspace_bytes(basis, w.B, w.H, w.n, w.d_v,
                                                      sa.SATA_BF16 if bf16 else sa.SATA_F32), dev)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ms = []
-        for it in range(args.warmup + args.steps):
-            state.zero_()
-            ev[0].record(stream)
-            sa.prefill(basis, Q, K, V, state=state, out=out, ws=ws)
-            ev[1].record(stream)
-            torch.cuda.synchronize()
-            if it >= args.warmup:
-                ms.append(ev[0].elapsed_time(ev[1]))
-        t = float(np.median(ms))
+        t = _time_prefill(sa, basis, Q, K, V, state, out, ws, stream, reps, warmup)
         tok = w.B * w.H * w.n
         _, page_flops = O.cost_model(w.d_k, w.d_v, w.P)
         tflops = tok * page_flops / (t * 1e-3) / 1e12
         peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
-        rows.append({"workload": f"{name}: batch {w.B} x {w.H} heads, n={w.n}, d_k=d_v={w.d_k}, P={w.P}, "
-                                 f"{'bf16' if bf16 else 'fp32'} inputs",
+        res[name] = {"workload": f"batch {w.B} x {w.H} heads, n={w.n}, d_k=d_v={w.d_k}, P={w.P}, "
+                                 f"{'bf16' if bf16 else 'fp32'} inputs, f32 state, prefill from empty states",
                      "ms": t, "head_tokens_per_s": tok / (t * 1e-3), "page_tflops": tflops,
                      "mfma_peak_tflops": peak, "mfma_frac": tflops / peak,
-                     "finite": bool(torch.isfinite(out).all())})
-        print(f"configs {name}: {t:.3f} ms", file=sys.stderr, flush=True)
+                     "finite": bool(torch.isfinite(out).all())}
+        print(f"prefill {name}: {t:.3f} ms", file=sys.stderr, flush=True)
         del Q, K, V, out, state, ws
         torch.cuda.empty_cache()
-    print(json.dumps({"metric": "prefill throughput per workload", "unit": "head-tokens/s",
-                      "steps": args.steps, "warmup": args.warmup, "points": rows}), flush=True)
+    return res
 
 
-def order5(args):
+def configs(args):
+    torch = __import__("torch")
+    torch.cuda.set_device(0)
+    res = config_points(args.steps, args.warmup)
+    print(json.dumps({"metric": "prefill throughput per workload", "unit": "head-tokens/s", "steps": args.steps,
+                      "warmup": args.warmup, "points": res}), flush=True)
+
+
+def order5_point(reps, warmup, dsteps):
     """Orders 0..4 at d = 64: the prefill leg and the decode leg of a 32-state
     step, each against its roofline, with a sampled check of the last decode
     outputs against the oracle."""
@@ -209,11 +231,9 @@ def order5(args):
     from oracle import sata_oracle as O
     w = W.WORKLOADS["order5_32x4096_d64"]
     S = w.B * w.H
-    dsteps = args.order5_steps
     q, k, v = W.workload_inputs(w)
     qs, ks, vs = W.decode_inputs(w, dsteps)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     basis = sa.build_basis(w.d_k, w.P, w.c)
     bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(dev)
@@ -226,7 +246,7 @@ def order5(args):
     dws = sa.workspace(sa.decode_workspace_bytes(basis, S, w.d_v, sa.SATA_BF16), dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(dsteps + 2)]
     pre_ms, dec_ms = [], []
-    for it in range(args.warmup + args.steps):
+    for it in range(warmup + reps):
         state.zero_()
         ev[0].record(stream)
         sa.prefill(basis, Q, K, V, state=state, out=out, ws=pws)
@@ -235,7 +255,7 @@ def order5(args):
             sa.decode_step(basis, DQ[t], DK[t], DV[t], state, out=dout[t], ws=dws)
             ev[t + 2].record(stream)
         torch.cuda.synchronize()
-        if it >= args.warmup:
+        if it >= warmup:
             pre_ms.append(ev[0].elapsed_time(ev[1]))
             dec_ms.extend(ev[t + 1].elapsed_time(ev[t + 2]) for t in range(dsteps))
         print(f"order5 step {it}: prefill {ev[0].elapsed_time(ev[1]):.2f} ms", file=sys.stderr, flush=True)
@@ -255,16 +275,24 @@ def order5(args):
     _, page_flops = O.cost_model(w.d_k, w.d_v, w.P)
     pre_tflops = S * w.n * page_flops / (pre * 1e-3) / 1e12
     dec_gbs = dec_bytes / (dec * 1e-3) / 1e9
-    print(json.dumps({
-        "metric": "orders 0..4 (P=5) prefill and decode vs roofline", "unit": "head-tokens/s",
-        "config": {"workload": f"order5: {S} states (batch {w.B} x {w.H} heads), d_k=d_v={w.d_k}, P={w.P}, "
-                               f"D={D}, bf16 inputs, f32 state, {w.n}-token prefill + {dsteps} decode steps"},
-        "steps": args.steps, "warmup": args.warmup,
-        "prefill": {"ms": pre, "head_tokens_per_s": S * w.n / (pre * 1e-3), "page_tflops": pre_tflops,
-                    "mfma_bf16_frac": pre_tflops / BF16_PEAK_TFLOPS},
-        "decode": {"ms_per_step": dec, "head_tokens_per_s": S / (dec * 1e-3), "hbm_gbs": dec_gbs,
-                   "hbm_frac": dec_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dec_bytes},
-        "check": {"decode_row_normwise_err": max(errs)}}), flush=True)
+    del Q, K, V, DQ, DK, DV, state, out, dout, pws, dws
+    torch.cuda.empty_cache()
+    return {"workload": f"order5: {S} states (batch {w.B} x {w.H} heads), d_k=d_v={w.d_k}, P={w.P}, D={D}, bf16 "
+                        f"inputs, f32 state, {w.n}-token prefill + {dsteps} decode steps",
+            "steps": reps, "warmup": warmup,
+            "prefill": {"ms": pre, "head_tokens_per_s": S * w.n / (pre * 1e-3), "page_tflops": pre_tflops,
+                        "mfma_bf16_frac": pre_tflops / BF16_PEAK_TFLOPS},
+            "decode": {"ms_per_step": dec, "head_tokens_per_s": S / (dec * 1e-3), "hbm_gbs": dec_gbs,
+                       "hbm_frac": dec_gbs / HBM_PEAK_GBS, "algorithmic_bytes": dec_bytes},
+            "check": {"decode_row_normwise_err": max(errs)}}
+
+
+def order5(args):
+    torch = __import__("torch")
+    torch.cuda.set_device(0)
+    res = order5_point(args.steps, args.warmup, args.order5_steps)
+    print(json.dumps({"metric": "orders 0..4 (P=5) prefill and decode vs roofline", "unit": "head-tokens/s",
+                      **res}), flush=True)
 
 
 def ceilings(args):
@@ -450,6 +478,13 @@ def main():
                      "algorithmic_bytes": dec_bytes},
         "check": {"decode_row_normwise_err": max(errs)},
     }
+    if not args.no_configs:
+        # the other workloads, timed after the headline step with its buffers freed
+        del Q, K, V, DQ, DK, DV, state, out, dout, pws, dws
+        torch.cuda.empty_cache()
+        res["configs"] = {"prefill": config_points(args.config_steps, 1),
+                          "long_context": flatness_points(args.config_steps, 1),
+                          "order5": order5_point(args.config_steps, 1, 64)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, qs, ks, vs, args.cpu_seconds)
     print(json.dumps(res), flush=True)
