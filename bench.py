@@ -10,7 +10,8 @@ prefill and decode token of every state).  The prefill and decode legs are
 also reported on their own, each against its roofline; `roofline` describes
 the dominant kernel (the decode update/readout, bound by HBM).  After the
 timed steps, `configs` reports the other workloads, each against its own
-roofline (a few repetitions each): the d8 / d16 fp32 and d64 bf16 prefills,
+roofline (a few repetitions each): the same decode on the mixed-precision
+state (orders >= 2 of S in float16), the d8 / d16 fp32 and d64 bf16 prefills,
 the long-context d32 prefill at 2^16, 2^18 and 2^20 tokens with its per-token
 cost ratio, and the orders 0..4 (P = 5) prefill and decode legs.  The CPU
 baseline is the float64 oracle on a bounded sample of the same workload.
@@ -49,6 +50,9 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (timed after the headline step: the d8/d16/d64 prefills, "
                          "the long-context sweep at 2^16..2^20 and the orders 0..4 legs)")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-precision decode-state leg")
+    ap.add_argument("--mixed-steps", type=int, default=256,
+                    help="timed decode steps on the mixed-precision state")
     ap.add_argument("--config-steps", type=int, default=5,
                     help="timed repetitions of each of the other workloads (one warmup each)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -295,6 +299,52 @@ def order5(args):
                       **res}), flush=True)
 
 
+def mixed_leg(sa, basis, w, Q, K, V, DQ, DK, DV, state, out, pws, q, k, v, qs, ks, vs, stream, dsteps, f32_ms):
+    """The same workload's decode on the mixed-precision state (orders >= 2 of
+    S in float16, per-tile scales): prefill on the float32 state, hand-off,
+    then dsteps timed decode steps, against HBM on the mixed state's own
+    bytes."""
+    import torch
+    from oracle import sata_oracle as O
+    S = w.B * w.H
+    D = basis.total_rows
+    state.zero_()
+    sa.prefill(basis, Q, K, V, state=state, out=out, ws=pws)
+    mixed = sa.to_mixed(basis, state)
+    dws = sa.workspace(sa.decode_mixed_workspace_bytes(basis, S, w.d_v, sa.SATA_BF16), Q.device)
+    dout = torch.empty((dsteps, S, w.d_v), dtype=torch.float32, device=Q.device)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(dsteps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for t in range(dsteps):
+        sa.decode_step_mixed(basis, DQ[t], DK[t], DV[t], mixed, out=dout[t], ws=dws)
+        ev[t + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[t].elapsed_time(ev[t + 1]) for t in range(dsteps)]
+    dec = float(np.mean(ms[1:])) if dsteps > 1 else ms[0]
+    lo, r16 = 1 + w.d_k, 2 * (128 // (w.d_v // 8))
+    nt16 = -(-(D - lo) // r16)
+    state_bytes = 2 * (lo * w.d_v * 4 + (D - lo) * w.d_v * 2 + D * 4 + nt16 * 4)
+    io_bytes = 3 * w.d_k * 2 + w.d_v * 4
+    dec_bytes = S * (state_bytes + io_bytes)
+    gbs = dec_bytes / (dec * 1e-3) / 1e9
+    got = dout[:, [0, S - 1]].cpu().numpy()
+    qf, kf, vf = (x.reshape(S, w.n, -1) for x in (q, k, v))
+    errs = []
+    for j, s_ in enumerate([0, S - 1]):
+        rr = np.arange(w.n, w.n + dsteps, max(1, dsteps // 8))
+        ref = O.direct_taylor(np.concatenate([qf[s_], qs[:dsteps, s_]]).astype(np.float64),
+                              np.concatenate([kf[s_], ks[:dsteps, s_]]).astype(np.float64),
+                              np.concatenate([vf[s_], vs[:dsteps, s_]]).astype(np.float64), w.P, w.c, rows=rr)
+        errs.append(O.row_normwise_error(got[rr - w.n, j], ref))
+    del mixed, dws, dout
+    return {"workload": f"same states, orders 0-1 of S and z fp32, orders >= 2 of S float16 with per-tile "
+                        f"power-of-two scales; {dsteps} decode steps after the {w.n}-token prefill",
+            "ms_per_step": dec, "head_tokens_per_s": S / (dec * 1e-3), "algorithmic_bytes": dec_bytes,
+            "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "speedup_vs_f32_state": f32_ms / dec,
+            "check": {"decode_row_normwise_err": max(errs)}}
+
+
 def ceilings(args):
     """Measured ceilings of this machine (torch / hipBLASLt kernels, HIP events):
     the bandwidth a read+write stream, an in-place read-modify-write stream
@@ -478,6 +528,9 @@ def main():
                      "algorithmic_bytes": dec_bytes},
         "check": {"decode_row_normwise_err": max(errs)},
     }
+    if not args.no_mixed:
+        res["decode_mixed_state"] = mixed_leg(sa, basis, w, Q, K, V, DQ, DK, DV, state, out, pws, q, k, v,
+                                              qs, ks, vs, stream, min(dsteps, args.mixed_steps), dec)
     if not args.no_configs:
         # the other workloads, timed after the headline step with its buffers freed
         del Q, K, V, DQ, DK, DV, state, out, dout, pws, dws

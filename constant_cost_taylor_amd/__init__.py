@@ -76,6 +76,17 @@ def _declare(lib):
     lib.sata_decode_step_noalloc.restype = c_int
     lib.sata_decode_noalloc_max_bytes.argtypes = []
     lib.sata_decode_noalloc_max_bytes.restype = c_sz
+    lib.sata_mixed_state_bytes.argtypes = [c_vp, c_int]
+    lib.sata_mixed_state_bytes.restype = c_i64
+    lib.sata_state_to_mixed.argtypes = [c_vp, c_int, c_int, c_vp, c_i64, c_vp, c_vp]
+    lib.sata_state_to_mixed.restype = c_int
+    lib.sata_state_from_mixed.argtypes = [c_vp, c_int, c_int, c_vp, c_vp, c_i64, c_vp]
+    lib.sata_state_from_mixed.restype = c_int
+    lib.sata_decode_mixed_workspace.argtypes = [c_vp, c_int, c_int, c_int, P(c_sz)]
+    lib.sata_decode_mixed_workspace.restype = c_int
+    lib.sata_decode_step_mixed.argtypes = [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                           c_vp]
+    lib.sata_decode_step_mixed.restype = c_int
     lib.sata_status_string.argtypes = [c_int]
     lib.sata_status_string.restype = ctypes.c_char_p
 
@@ -306,4 +317,77 @@ def decode_step_noalloc(basis: Basis, q, k, v, state, out):
                                         v.data_ptr(), out.data_ptr(), state.data_ptr(), stride,
                                         _stream_ptr(q.device))
     _check(st, "sata_decode_step_noalloc")
+    return out
+
+
+# ---- mixed-precision decode state (orders >= 2 of S in float16) ---------------
+
+def mixed_state_bytes(basis: Basis, d_v: Optional[int] = None) -> int:
+    return int(lib().sata_mixed_state_bytes(basis.handle, int(basis.d_k if d_v is None else d_v)))
+
+
+def new_mixed_state(basis: Basis, count: int, device="cuda"):
+    """Uninitialised mixed states: [count, mixed_state_bytes] uint8 (fill with to_mixed)."""
+    import torch
+    return torch.empty((count, mixed_state_bytes(basis)), dtype=torch.uint8, device=device)
+
+
+def _check_mixed(basis: Basis, mixed, count: int, device):
+    import torch
+    if mixed.dtype != torch.uint8 or not mixed.is_contiguous() or mixed.device != device:
+        raise ValueError(f"mixed state must be a contiguous uint8 tensor on {device}")
+    if mixed.dim() != 2 or mixed.shape[0] != count or mixed.shape[1] != mixed_state_bytes(basis):
+        raise ValueError(f"mixed state must be [{count}, {mixed_state_bytes(basis)}]")
+
+
+def to_mixed(basis: Basis, state, mixed=None):
+    """float32 states [S, stride] -> mixed states [S, mixed_state_bytes]."""
+    S = state.shape[0]
+    stride = _state_stride(basis, state, S, basis.d_k, state.device)
+    if mixed is None:
+        mixed = new_mixed_state(basis, S, state.device)
+    _check_mixed(basis, mixed, S, state.device)
+    _check(lib().sata_state_to_mixed(basis.handle, S, basis.d_k, state.data_ptr(), stride, mixed.data_ptr(),
+                                     _stream_ptr(state.device)), "sata_state_to_mixed")
+    return mixed
+
+
+def from_mixed(basis: Basis, mixed, state=None):
+    """mixed states [S, mixed_state_bytes] -> float32 states [S, stride]."""
+    S = mixed.shape[0]
+    if state is None:
+        state = new_state(basis, S, mixed.device)
+    stride = _state_stride(basis, state, S, basis.d_k, mixed.device)
+    _check_mixed(basis, mixed, S, mixed.device)
+    _check(lib().sata_state_from_mixed(basis.handle, S, basis.d_k, mixed.data_ptr(), state.data_ptr(), stride,
+                                       _stream_ptr(mixed.device)), "sata_state_from_mixed")
+    return state
+
+
+def decode_mixed_workspace_bytes(basis: Basis, S: int, d_v: int, dtype_code: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().sata_decode_mixed_workspace(basis.handle, S, d_v, dtype_code, ctypes.byref(b)),
+           "sata_decode_mixed_workspace")
+    return int(b.value)
+
+
+def decode_step_mixed(basis: Basis, q, k, v, mixed, out=None, ws=None):
+    """decode_step on mixed states [S, mixed_state_bytes] (in/out). Returns out [S, d_v]."""
+    import torch
+    if q.dim() != 2 or k.shape != q.shape or v.dim() != 2 or v.shape[0] != q.shape[0]:
+        raise ValueError("q, k must be [S, d_k] and v [S, d_v]")
+    _check_inputs(basis, q, k, v)
+    S = q.shape[0]
+    d_v = v.shape[1]
+    code = _dtype_code(q)
+    _check_mixed(basis, mixed, S, q.device)
+    if out is None:
+        out = torch.empty((S, d_v), dtype=torch.float32, device=q.device)
+    _check_buffer("out", out, torch.float32, S * d_v, q.device)
+    if ws is None:
+        ws = workspace(decode_mixed_workspace_bytes(basis, S, d_v, code), q.device)
+    st = lib().sata_decode_step_mixed(basis.handle, S, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      out.data_ptr(), mixed.data_ptr(), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream_ptr(q.device))
+    _check(st, "sata_decode_step_mixed")
     return out

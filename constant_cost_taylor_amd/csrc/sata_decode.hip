@@ -69,8 +69,51 @@ __device__ __forceinline__ f4v fma4(float s, f4v v, f4v acc) {
   return acc;
 }
 
+// Features of the tile's rows, phi_k = prod k[i_r] and phi_q = w_m prod q[i_r],
+// into fk / fq (thread t < R builds row t; rows past nrows get 0).
+template <int R>
+__device__ __forceinline__ void tile_features(const float* xq, const float* xk, uint32_t pk, float wr, int nrows,
+                                              float* fk, float* fq) {
+  const int tid = threadIdx.x;
+  if (tid < R) {
+    const int p = static_cast<int>(pk >> 24);
+    float fkk = 1.f, fqq = wr;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < p) {
+        const int i = (pk >> (6 * t)) & 63;
+        fkk *= xk[i];
+        fqq *= xq[i];
+      }
+    }
+    fk[tid] = tid < nrows ? fkk : 0.f;
+    fq[tid] = tid < nrows ? fqq : 0.f;
+  }
+}
+
+// Fixed-order reductions of a tile's readout: over the row groups of a
+// column (red[RPP][DV]) and over the block for den (one value per wave), into
+// the tile's partial record.
+template <int DV, int RPP>
+__device__ __forceinline__ void tile_partials(const float* red, const float* dred, float* part, float* partz) {
+  const int tid = threadIdx.x;
+  if (tid < DV) {
+    float sum = 0.f;
+    for (int j = 0; j < RPP; ++j) sum += red[j * DV + tid];
+    *(part + tid) = sum;
+  }
+  if (tid == DV) {
+    float sum = 0.f;
+    for (int j = 0; j < kDecodeThreads / 64; ++j) sum += dred[j];
+    *partz = sum;
+  }
+}
+
+// One tile of fp32 rows [r0, r0 + nrows) of state s: S4 = its first row, z =
+// its first z value.  Rank-1 update, store, readout partial into part/partz.
 template <int DK, typename IT, bool AL>
-__global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeArgs a) {
+__device__ __forceinline__ void f32_tile(const DecodeArgs& a, int s, float* S4, float* z, int r0, int nrows,
+                                         float* part, float* partz) {
   constexpr int DV = DK;
   constexpr int TPR = DV / 4;          // threads per S row, one float4 each
   constexpr int RPP = kDecodeThreads / TPR;  // rows per pass of the block
@@ -84,18 +127,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
   __shared__ float red[RPP * DV];
   __shared__ float dred[kDecodeThreads / 64];
 
-  const int tile = blockIdx.x;
-  const int s = blockIdx.y;
   const int tid = threadIdx.x;
-  const int r0 = tile * R;
-  const int nrows = min(R, a.D - r0);
-
   // The tile's state rows and z values go out first (a row past the tail
   // reads the tile's first row and is not written back); the features are
   // built while they are in flight.
-  float* st = a.state + static_cast<int64_t>(s) * a.stride;
-  float* S4 = st + static_cast<int64_t>(r0) * DV;
-  float* z = st + static_cast<int64_t>(a.D) * DV + r0;
   const int c4 = tid % TPR;
   const int rs = tid / TPR;
   f4v x[U];
@@ -121,21 +156,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
     wr = a.weight[r0 + tid];
   }
   __syncthreads();
-  // Features of this tile's rows: phi_k = prod k[i_r], phi_q = w_m prod q[i_r].
-  if (tid < R) {
-    const int p = static_cast<int>(pk >> 24);
-    float fkk = 1.f, fqq = wr;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (t < p) {
-        const int i = (pk >> (6 * t)) & 63;
-        fkk *= xk[i];
-        fqq *= xq[i];
-      }
-    }
-    fk[tid] = tid < nrows ? fkk : 0.f;
-    fq[tid] = tid < nrows ? fqq : 0.f;
-  }
+  tile_features<R>(xq, xk, pk, wr, nrows, fk, fq);
   __syncthreads();
 
   const f4v vv = {xv[4 * c4], xv[4 * c4 + 1], xv[4 * c4 + 2], xv[4 * c4 + 3]};
@@ -156,7 +177,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
     dacc = fq[tid] * zz;
   }
 
-  // Fixed-order reductions: over the row groups of a column, and over the block for den.
   red[rs * DV + 4 * c4 + 0] = acc.x;
   red[rs * DV + 4 * c4 + 1] = acc.y;
   red[rs * DV + 4 * c4 + 2] = acc.z;
@@ -165,16 +185,243 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
   for (int o = 32; o > 0; o >>= 1) dacc += __shfl_xor(dacc, o);
   if ((tid & 63) == 0) dred[tid >> 6] = dacc;
   __syncthreads();
+  tile_partials<DV, RPP>(red, dred, part, partz);
+}
+
+template <int DK, typename IT, bool AL>
+__global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeArgs a) {
+  constexpr int R = decode_rows(DK);
+  const int tile = blockIdx.x;
+  const int s = blockIdx.y;
+  const int r0 = tile * R;
+  const int nrows = min(R, a.D - r0);
+  float* st = a.state + static_cast<int64_t>(s) * a.stride;
   const int64_t pi = static_cast<int64_t>(s) * a.n_tiles + tile;
-  if (tid < DV) {
-    float sum = 0.f;
-    for (int j = 0; j < RPP; ++j) sum += red[j * DV + tid];
-    a.part[pi * DV + tid] = sum;
+  f32_tile<DK, IT, AL>(a, s, st + static_cast<int64_t>(r0) * DK, st + static_cast<int64_t>(a.D) * DK + r0, r0, nrows,
+                       a.part + pi * DK, a.partz + pi);
+}
+
+// ---------------------------------------------------------------------------
+// Mixed-precision state [SATA page, "Precision/efficiency trade-off
+// parameter" and "Hardware optimisation path and current limitations": a
+// 16-bit state roughly halves the bytes of the memory-bound step].  Rows of
+// orders 0 and 1 of S and all of z stay fp32; rows of order >= 2 of S are
+// f16, each tile of mixed_rows(d_v) rows scaled by a power of two.  The block
+// that owns a tile reads it, updates it in fp32, reads out from the fp32
+// values, and writes it back with a freshly chosen scale that puts the tile's
+// largest entry below 2^15 (so a growing state never overflows f16; entries
+// 2^29 below the tile's largest are subnormal).
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// One f16 tile (t16) of state s: rows [lo + t16 R, ...), record index pi.
+template <int DK, typename IT>
+__device__ __forceinline__ void f16_tile(const MixedDecodeArgs& a, int s, int t16, float* part, float* partz) {
+  constexpr int DV = DK;
+  constexpr int TPR = DV / 8;                 // threads per f16 row, 8 halves (16 bytes) each
+  constexpr int RPP = kDecodeThreads / TPR;   // rows per pass
+  constexpr int R = mixed_rows(DV);
+  constexpr int U = R / RPP;
+  static_assert(U * RPP == R && R <= kDecodeThreads, "mixed tile shape");
+
+  __shared__ float xq[DK], xk[DK], xv[DV];
+  __shared__ float fk[R], fq[R];
+  __shared__ float red[RPP * DV];
+  __shared__ float dred[kDecodeThreads / 64];
+  __shared__ float wmx[kDecodeThreads / 64];
+
+  const int tid = threadIdx.x;
+  unsigned char* base = a.state + static_cast<int64_t>(s) * a.stride_bytes;
+  const int r0 = a.lo + t16 * R;                       // canonical first row
+  const int nrows = min(R, a.D - r0);
+  uint16_t* H = reinterpret_cast<uint16_t*>(base + a.off_h) + static_cast<int64_t>(t16) * R * DV;
+  float* z = reinterpret_cast<float*>(base + a.off_z) + r0;
+  float* sc = reinterpret_cast<float*>(base + a.off_sc) + t16;
+  const int c8 = tid % TPR;
+  const int rs = tid / TPR;
+  u32x4 raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int row = rs + u * RPP;
+    raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(H + (row < nrows ? row : 0) * DV + 8 * c8));
   }
-  if (tid == DV) {
-    float sum = 0.f;
-    for (int j = 0; j < kDecodeThreads / 64; ++j) sum += dred[j];
-    a.partz[pi] = sum;
+  const float zv = __builtin_nontemporal_load(&z[tid < nrows ? tid : 0]);
+  const float scale = *sc;
+
+  const IT* q = static_cast<const IT*>(a.q) + static_cast<int64_t>(s) * DK;
+  const IT* k = static_cast<const IT*>(a.k) + static_cast<int64_t>(s) * DK;
+  const IT* v = static_cast<const IT*>(a.v) + static_cast<int64_t>(s) * DV;
+  if (tid < DK) {
+    xq[tid] = load_in(q, tid);
+    xk[tid] = load_in(k, tid);
+  }
+  if (tid < DV) xv[tid] = load_in(v, tid);
+  uint32_t pk = 0u;
+  float wr = 0.f;
+  if (tid < nrows) {
+    pk = a.rows[r0 + tid];
+    wr = a.weight[r0 + tid];
+  }
+  __syncthreads();
+  tile_features<R>(xq, xk, pk, wr, nrows, fk, fq);
+  __syncthreads();
+
+  float vv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) vv[j] = xv[8 * c8 + j];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float x[U][8];
+  float mx = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int row = rs + u * RPP;
+    const bool live = row < nrows;
+    const float f = live ? fk[row] : 0.f;
+    const float g = live ? fq[row] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = raw[u][j];
+      const f16x2 h = __builtin_bit_cast(f16x2, w);
+      x[u][2 * j] = fmaf(f, vv[2 * j], static_cast<float>(h[0]) * scale);
+      x[u][2 * j + 1] = fmaf(f, vv[2 * j + 1], static_cast<float>(h[1]) * scale);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = fmaf(g, x[u][j], acc[j]);
+      if (live) mx = fmaxf(mx, fabsf(x[u][j]));
+    }
+  }
+  float dacc = 0.f;
+  if (tid < nrows) {
+    const float zz = zv + fk[tid];
+    __builtin_nontemporal_store(zz, &z[tid]);
+    dacc = fq[tid] * zz;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rs * DV + 8 * c8 + j] = acc[j];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    dacc += __shfl_xor(dacc, o);
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if ((tid & 63) == 0) {
+    dred[tid >> 6] = dacc;
+    wmx[tid >> 6] = mx;
+  }
+  __syncthreads();
+  // the tile's new scale: its largest |entry| times 2^-e below 2^15
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < kDecodeThreads / 64; ++j) m = fmaxf(m, wmx[j]);
+  int e = 0;
+  if (m > 0.f) (void)frexpf(m, &e);           // m < 2^e
+  const int es = m > 0.f ? e - 15 : 0;
+  const float inv = ldexpf(1.f, -es);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int row = rs + u * RPP;
+    if (row < nrows) {
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x2 h = {static_cast<_Float16>(x[u][2 * j] * inv), static_cast<_Float16>(x[u][2 * j + 1] * inv)};
+        o[j] = __builtin_bit_cast(uint32_t, h);
+      }
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(H + row * DV + 8 * c8));
+    }
+  }
+  if (tid == 0) *sc = ldexpf(1.f, es);
+  tile_partials<DV, RPP>(red, dred, part, partz);
+}
+
+// Mixed-state decode: blocks [0, nt32) take fp32 tiles of rows [0, lo),
+// blocks [nt32, nt32 + nt16) the f16 tiles; records in block order.
+template <int DK, typename IT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_mixed(MixedDecodeArgs a) {
+  constexpr int R32 = decode_rows(DK);
+  const int tile = blockIdx.x;
+  const int s = blockIdx.y;
+  const int64_t pi = static_cast<int64_t>(s) * a.n_tiles + tile;
+  if (tile < a.nt32) {
+    unsigned char* base = a.state + static_cast<int64_t>(s) * a.stride_bytes;
+    float* st = reinterpret_cast<float*>(base);
+    const int r0 = tile * R32;
+    DecodeArgs d{};
+    d.q = a.q;
+    d.k = a.k;
+    d.v = a.v;
+    d.rows = a.rows;
+    d.weight = a.weight;
+    f32_tile<DK, IT, true>(d, s, st + static_cast<int64_t>(r0) * DK,
+                           reinterpret_cast<float*>(base + a.off_z) + r0, r0, min(R32, a.lo - r0),
+                           a.part + pi * DK, a.partz + pi);
+  } else {
+    f16_tile<DK, IT>(a, s, tile - a.nt32, a.part + pi * DK, a.partz + pi);
+  }
+}
+
+// Conversion between the fp32 state ([S][stride] floats) and the mixed one.
+// Grid x: nt16 f16 tiles, then blocks of kDecodeThreads * 4 floats over the
+// fp32 rows and then over z; grid y: states.
+template <int DK, bool TO_MIXED>
+__global__ __launch_bounds__(kDecodeThreads) void mixed_convert(MixedConvArgs a) {
+  constexpr int DV = DK;
+  constexpr int R = mixed_rows(DV);
+  __shared__ float wmx[kDecodeThreads / 64];
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x;
+  float* st = a.state + static_cast<int64_t>(s) * a.stride;
+  unsigned char* base = a.mixed + static_cast<int64_t>(s) * a.stride_bytes;
+  const int bx = blockIdx.x;
+  if (bx < a.nt16) {
+    const int r0 = a.lo + bx * R;
+    const int nrows = min(R, a.D - r0);
+    const int n = nrows * DV;
+    const float* src = st + static_cast<int64_t>(r0) * DV;
+    uint16_t* H = reinterpret_cast<uint16_t*>(base + a.off_h) + static_cast<int64_t>(bx) * R * DV;
+    float* sc = reinterpret_cast<float*>(base + a.off_sc) + bx;
+    if constexpr (TO_MIXED) {
+      float mx = 0.f;
+      for (int i = tid; i < n; i += kDecodeThreads) mx = fmaxf(mx, fabsf(src[i]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if ((tid & 63) == 0) wmx[tid >> 6] = mx;
+      __syncthreads();
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < kDecodeThreads / 64; ++j) m = fmaxf(m, wmx[j]);
+      int e = 0;
+      if (m > 0.f) (void)frexpf(m, &e);
+      const int es = m > 0.f ? e - 15 : 0;
+      const float inv = ldexpf(1.f, -es);
+      for (int i = tid; i < n; i += kDecodeThreads)
+        H[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(src[i] * inv));
+      if (tid == 0) *sc = ldexpf(1.f, es);
+    } else {
+      const float scale = *sc;
+      float* dst = st + static_cast<int64_t>(r0) * DV;
+      for (int i = tid; i < n; i += kDecodeThreads)
+        dst[i] = static_cast<float>(__builtin_bit_cast(_Float16, H[i])) * scale;
+    }
+    return;
+  }
+  // plain fp32 copies: rows [0, lo) of S, then z
+  const int64_t n32 = static_cast<int64_t>(a.lo) * DV;
+  const int64_t i0 = static_cast<int64_t>(bx - a.nt16) * kDecodeThreads * 4;
+  float* m32 = reinterpret_cast<float*>(base);
+  float* mz = reinterpret_cast<float*>(base + a.off_z);
+  const float* sz = st + static_cast<int64_t>(a.D) * DV;
+  float* szw = st + static_cast<int64_t>(a.D) * DV;
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = i0 + j * kDecodeThreads + tid;
+    if (i < n32) {
+      if constexpr (TO_MIXED) m32[i] = st[i];
+      else st[i] = m32[i];
+    } else if (i < n32 + a.D) {
+      if constexpr (TO_MIXED) mz[i - n32] = sz[i - n32];
+      else szw[i - n32] = mz[i - n32];
+    }
   }
 }
 
@@ -260,6 +507,25 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(const float* __rest
   }
 }
 
+// The fixed-order reduce of a step's partial records (one or two passes).
+template <int D>
+hipError_t launch_reduce(const float* part, const float* partz, float* out, int S, int n_tiles, int groups,
+                         float* part2, float* partz2, hipStream_t st) {
+  if (groups <= 1) {
+    decode_reduce<D, true><<<dim3(1, S), kRedThreads, 0, st>>>(part, partz, n_tiles, n_tiles, nullptr, nullptr, out);
+    return hipGetLastError();
+  }
+  // Few states: the tiles of a state are split over `groups` blocks, whose
+  // sums a second pass combines (in group order).
+  const int per = (n_tiles + groups - 1) / groups;
+  decode_reduce<D, false><<<dim3(groups, S), kRedThreads, 0, st>>>(part, partz, n_tiles, per, part2, partz2,
+                                                                   nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  decode_reduce<D, true><<<dim3(1, S), kRedThreads, 0, st>>>(part2, partz2, groups, groups, nullptr, nullptr, out);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.n_tiles, a.S);
@@ -274,23 +540,53 @@ hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
     decode_update_readout<D, float, false><<<grid, kDecodeThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.groups <= 1) {
-    decode_reduce<D, true><<<dim3(1, a.S), kRedThreads, 0, st>>>(a.part, a.partz, a.n_tiles, a.n_tiles, nullptr,
-                                                                 nullptr, a.out);
-    return hipGetLastError();
-  }
-  // Few states: the tiles of a state are split over `groups` blocks, whose
-  // sums a second pass combines (in group order).
-  const int per = (a.n_tiles + a.groups - 1) / a.groups;
-  decode_reduce<D, false><<<dim3(a.groups, a.S), kRedThreads, 0, st>>>(a.part, a.partz, a.n_tiles, per, a.part2,
-                                                                       a.partz2, nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  decode_reduce<D, true><<<dim3(1, a.S), kRedThreads, 0, st>>>(a.part2, a.partz2, a.groups, a.groups, nullptr,
-                                                               nullptr, a.out);
+  return launch_reduce<D>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, st);
+}
+
+template <int D>
+hipError_t launch_mixed_d(bool bf16, const MixedDecodeArgs& a, hipStream_t st) {
+  dim3 grid(a.n_tiles, a.S);
+  if (bf16)
+    decode_mixed<D, uint16_t><<<grid, kDecodeThreads, 0, st>>>(a);
+  else
+    decode_mixed<D, float><<<grid, kDecodeThreads, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce<D>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, st);
+}
+
+template <int D>
+hipError_t launch_convert_d(bool to_mixed, const MixedConvArgs& a, hipStream_t st) {
+  const int64_t n = static_cast<int64_t>(a.lo) * D + a.D;
+  dim3 grid(a.nt16 + static_cast<int>((n + kDecodeThreads * 4 - 1) / (kDecodeThreads * 4)), a.S);
+  if (to_mixed)
+    mixed_convert<D, true><<<grid, kDecodeThreads, 0, st>>>(a);
+  else
+    mixed_convert<D, false><<<grid, kDecodeThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_decode_mixed(int d, bool bf16, const MixedDecodeArgs& a, hipStream_t s) {
+  switch (d) {
+    case 8: return launch_mixed_d<8>(bf16, a, s);
+    case 16: return launch_mixed_d<16>(bf16, a, s);
+    case 32: return launch_mixed_d<32>(bf16, a, s);
+    case 64: return launch_mixed_d<64>(bf16, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_mixed_convert(int d, bool to_mixed, const MixedConvArgs& a, hipStream_t s) {
+  switch (d) {
+    case 8: return launch_convert_d<8>(to_mixed, a, s);
+    case 16: return launch_convert_d<16>(to_mixed, a, s);
+    case 32: return launch_convert_d<32>(to_mixed, a, s);
+    case 64: return launch_convert_d<64>(to_mixed, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 // Scratch of sata_decode_step_noalloc: the per-tile partial records of a
 // decode step (the same regions as the caller's workspace of

@@ -456,6 +456,26 @@ int decode_tiles(const sata_basis* b) {
   return static_cast<int>((b->D + rows - 1) / rows);
 }
 
+// Mixed-precision state layout of one state (bytes from its base).
+struct MixedPlan {
+  int lo = 0, nt32 = 0, nt16 = 0;
+  int64_t off_h = 0, off_z = 0, off_sc = 0, bytes = 0;
+};
+MixedPlan mixed_plan(const sata_basis* b) {
+  auto up = [](int64_t x, int64_t a) { return (x + a - 1) / a * a; };
+  MixedPlan m;
+  const int64_t d = b->d;
+  m.lo = static_cast<int>(std::min<int64_t>(1 + d, b->D));
+  const int r32 = sata::decode_rows(b->d), r16 = sata::mixed_rows(b->d);
+  m.nt32 = (m.lo + r32 - 1) / r32;
+  m.nt16 = static_cast<int>((b->D - m.lo + r16 - 1) / r16);
+  m.off_h = up(m.lo * d * 4, 256);
+  m.off_z = up(m.off_h + (b->D - m.lo) * d * 2, 256);
+  m.off_sc = up(m.off_z + b->D * 4, 256);
+  m.bytes = up(m.off_sc + static_cast<int64_t>(m.nt16) * 4, 256);
+  return m;
+}
+
 }  // namespace
 
 extern "C" {
@@ -741,6 +761,100 @@ int sata_decode_step_noalloc(const sata_basis* b, int S, int d_v, int dtype, con
 }
 
 size_t sata_decode_noalloc_max_bytes(void) { return sata::kNoAllocScratchBytes; }
+
+int64_t sata_mixed_state_bytes(const sata_basis* b, int d_v) {
+  if (!b || d_v != b->d) return -1;
+  return mixed_plan(b).bytes;
+}
+
+static int mixed_convert(const sata_basis* b, int S, int d_v, float* state, int64_t state_stride, void* mixed,
+                         bool to_mixed, void* stream) {
+  if (!b || S < 0) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  if (S == 0) return SATA_OK;
+  if (S > 65535) return SATA_ERR_UNSUPPORTED;
+  if (!state || !mixed || !aligned(state, 4) || !aligned(mixed, 256)) return SATA_ERR_INVALID_ARG;
+  if (state_stride < static_cast<int64_t>(d_v + 1) * b->D) return SATA_ERR_INVALID_ARG;
+  if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  const MixedPlan m = mixed_plan(b);
+  sata::MixedConvArgs a{state, state_stride, static_cast<unsigned char*>(mixed), m.bytes, m.off_h, m.off_z,
+                        m.off_sc, S, static_cast<int>(b->D), m.lo, m.nt16};
+  if (sata::launch_mixed_convert(b->d, to_mixed, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SATA_ERR_HIP;
+  return SATA_OK;
+}
+
+int sata_state_to_mixed(const sata_basis* b, int S, int d_v, const float* state, int64_t state_stride,
+                        void* mixed, void* stream) {
+  return mixed_convert(b, S, d_v, const_cast<float*>(state), state_stride, mixed, true, stream);
+}
+
+int sata_state_from_mixed(const sata_basis* b, int S, int d_v, const void* mixed, float* state,
+                          int64_t state_stride, void* stream) {
+  return mixed_convert(b, S, d_v, state, state_stride, const_cast<void*>(mixed), false, stream);
+}
+
+int sata_decode_mixed_workspace(const sata_basis* b, int S, int d_v, int dtype, size_t* bytes) {
+  if (!b || !bytes || S < 0) return SATA_ERR_INVALID_ARG;
+  if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  const MixedPlan m = mixed_plan(b);
+  const int tiles = m.nt32 + m.nt16;
+  const int groups = sata::decode_groups(S, tiles);
+  *bytes = decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
+  if (groups > 1) *bytes += decode_part_bytes(S, groups, d_v) + decode_partz_bytes(S, groups);
+  return SATA_OK;
+}
+
+int sata_decode_step_mixed(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
+                           const void* v, float* out, void* mixed, void* ws, size_t ws_bytes, void* stream) {
+  if (!b || S < 0) return SATA_ERR_INVALID_ARG;
+  if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
+  if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
+  if (S == 0) return SATA_OK;
+  if (S > 65535) return SATA_ERR_UNSUPPORTED;
+  const size_t esz = dtype == SATA_BF16 ? 2 : 4;
+  if (!q || !k || !v || !out || !mixed) return SATA_ERR_INVALID_ARG;
+  if (!aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) || !aligned(out, 16) || !aligned(mixed, 256))
+    return SATA_ERR_INVALID_ARG;
+  size_t need = 0;
+  sata_decode_mixed_workspace(b, S, d_v, dtype, &need);
+  if (!ws || ws_bytes < need) return SATA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
+  if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
+  const MixedPlan m = mixed_plan(b);
+  const int tiles = m.nt32 + m.nt16;
+  float* part = static_cast<float*>(ws);
+  float* partz = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v));
+  const int groups = sata::decode_groups(S, tiles);
+  char* lvl2 = static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
+  sata::MixedDecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.state = static_cast<unsigned char*>(mixed);
+  a.stride_bytes = m.bytes;
+  a.off_h = m.off_h;
+  a.off_z = m.off_z;
+  a.off_sc = m.off_sc;
+  a.part = part;
+  a.partz = partz;
+  a.out = out;
+  a.rows = b->d_rows;
+  a.weight = b->d_weight;
+  a.S = S;
+  a.D = static_cast<int>(b->D);
+  a.lo = m.lo;
+  a.nt32 = m.nt32;
+  a.nt16 = m.nt16;
+  a.n_tiles = tiles;
+  a.groups = groups;
+  a.part2 = groups > 1 ? reinterpret_cast<float*>(lvl2) : nullptr;
+  a.partz2 = groups > 1 ? reinterpret_cast<float*>(lvl2 + decode_part_bytes(S, groups, d_v)) : nullptr;
+  if (sata::launch_decode_mixed(b->d, dtype == SATA_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SATA_ERR_HIP;
+  return SATA_OK;
+}
 
 int sata_decode_step(const sata_basis* b, int S, int d_v, int dtype, const void* q, const void* k,
                      const void* v, float* out, float* state, void* ws, size_t ws_bytes, void* stream) {

@@ -228,6 +228,54 @@ hipError_t launch_prefill_intra(int d, bool bf16, int BH, const IntraArgs& a, hi
 hipError_t launch_prefill_reduce(int d, bool bf16, int BH, const ReduceArgs& a, hipStream_t s);
 hipError_t launch_decode(int d, bool bf16, const DecodeArgs& a, hipStream_t s);
 
+// Mixed-precision decode state: rows of orders 0 and 1 of S fp32, rows of
+// order >= 2 f16 in tiles of mixed_rows(dv) rows (two 16-byte slots of eight
+// halves per thread of a kDecodeThreads block, at most one row per thread),
+// each tile with one power-of-two scale; z fp32.  Bytes of one state, from
+// its base: [lo][dv] fp32 rows, then off_h: [D - lo][dv] f16 rows, then
+// off_z: [D] fp32, then off_sc: [nt16] fp32 tile scales; stride_bytes apart.
+constexpr int mixed_rows(int dv) {
+  return 2 * (kDecodeThreads / (dv / 8)) > kDecodeThreads ? kDecodeThreads : 2 * (kDecodeThreads / (dv / 8));
+}
+
+struct MixedDecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  unsigned char* state;  // [S][stride_bytes]
+  int64_t stride_bytes;
+  int64_t off_h, off_z, off_sc;
+  float* part;           // [S][n_tiles][dv]
+  float* partz;          // [S][n_tiles]
+  float* out;            // [S][dv]
+  const uint32_t* rows;
+  const float* weight;
+  int S;
+  int D;
+  int lo;                // rows of orders 0 and 1 (fp32)
+  int nt32;              // fp32 tiles (decode_rows rows each)
+  int nt16;              // f16 tiles (mixed_rows rows each)
+  int n_tiles;           // nt32 + nt16
+  int groups;
+  float* part2;
+  float* partz2;
+};
+
+struct MixedConvArgs {
+  float* state;          // fp32 states [S][stride]
+  int64_t stride;
+  unsigned char* mixed;  // mixed states [S][stride_bytes]
+  int64_t stride_bytes;
+  int64_t off_h, off_z, off_sc;
+  int S;
+  int D;
+  int lo;
+  int nt16;
+};
+
+hipError_t launch_decode_mixed(int d, bool bf16, const MixedDecodeArgs& a, hipStream_t s);
+hipError_t launch_mixed_convert(int d, bool to_mixed, const MixedConvArgs& a, hipStream_t s);
+
 // The allocation-free decode entry point keeps its partial records in a
 // file-scope device array of this many bytes (one copy per device, held
 // until the process ends).

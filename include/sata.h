@@ -182,6 +182,42 @@ int sata_decode_step_strided(const sata_basis* basis, int S, int d_v, int dtype,
                              const void* k, const void* v, float* out, float* state,
                              int64_t state_stride, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Mixed-precision decode state ------------------------------------------
+ * A second state format for the memory-bound decode step [SATA page,
+ * "Precision/efficiency trade-off parameter" (the P = 4 error is of the order
+ * of Float16 precision) and "Hardware optimisation path and current
+ * limitations" (a Float16 state roughly halves the bandwidth)]: rows of
+ * orders 0 and 1 of S and all of z stay float32; rows of order >= 2 of S are
+ * stored as float16, in tiles of rows that each carry one power-of-two scale,
+ * re-chosen by the decode step whenever it writes the tile back so that a
+ * growing state cannot overflow.  At d_k = 64, P = 4 a state is 6.33 MB
+ * instead of 12.46 MB.  The layout inside a state is private to the library;
+ * states are sata_mixed_state_bytes apart (a multiple of 256) in a 256-byte
+ * aligned buffer.  A prefill runs on the float32 state; sata_state_to_mixed
+ * hands it to the decode format, sata_state_from_mixed hands it back (for a
+ * continuation prefill).  Errors as for sata_decode_step. */
+
+/* Bytes of one mixed state (-1 on a null handle or d_v != d_k). */
+int64_t sata_mixed_state_bytes(const sata_basis* basis, int d_v);
+
+/* S float32 states ([S][state_stride] floats) -> S mixed states. */
+int sata_state_to_mixed(const sata_basis* basis, int S, int d_v, const float* state, int64_t state_stride,
+                        void* mixed, void* stream);
+
+/* S mixed states -> S float32 states ([S][state_stride] floats). */
+int sata_state_from_mixed(const sata_basis* basis, int S, int d_v, const void* mixed, float* state,
+                          int64_t state_stride, void* stream);
+
+/* Device workspace in bytes that sata_decode_step_mixed needs for S states. */
+int sata_decode_mixed_workspace(const sata_basis* basis, int S, int d_v, int dtype, size_t* bytes);
+
+/* sata_decode_step on S mixed states: the same update and readout, the
+ * float16 rows read, updated and read out in float32 and rounded (to nearest
+ * even, after their tile's scale) when written back. */
+int sata_decode_step_mixed(const sata_basis* basis, int S, int d_v, int dtype, const void* q,
+                           const void* k, const void* v, float* out, void* mixed, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * sata_decode_step_strided without a workspace argument.  The per-tile

@@ -645,3 +645,81 @@ def test_workload_long_d32_n1m_sampled():
         q, k, v = host[h]
         ref = O.direct_taylor(f64(q), f64(k), f64(v), w.P, w.c, rows=rows, block=8)
         assert O.row_normwise_error(got[h], ref) <= TOL[w.dtype], h
+
+
+# ----------------------------------------------------------------------------
+# Mixed-precision decode state (orders >= 2 of S in float16)
+# ----------------------------------------------------------------------------
+
+def test_mixed_state_decode_workload_1024_steps():
+    """Eight states of the decode workload (d = 64, P = 4, bf16): 4096-token
+    prefill on the float32 state, hand-off to the mixed state, 1024 decode
+    steps; every decode output checked against the oracle."""
+    w = W.WORKLOADS["decode_256x4096_d64"]
+    S, steps = 8, 1024
+    note(f"mixed state: {S} states, n={w.n}, {steps} decode steps")
+    q, k, v = W.make_qkv(1, S, w.n, w.d_k, w.d_v, w.dtype, 1000 * w.seed)
+    qs, ks, vs = W.make_qkv(1, steps, S, w.d_k, w.d_v, w.dtype, 1000 * w.seed + 100)
+    qs, ks, vs = qs[0], ks[0], vs[0]
+    b = SA.build_basis(w.d_k, w.P, w.c)
+    _, st = run_prefill(b, q, k, v, w.dtype)
+    mixed = SA.to_mixed(b, st)
+    qd, kd, vd = to_dev(qs, w.dtype), to_dev(ks, w.dtype), to_dev(vs, w.dtype)
+    dout = torch.empty((steps, S, w.d_v), dtype=torch.float32, device="cuda")
+    ws = SA.workspace(SA.decode_mixed_workspace_bytes(b, S, w.d_v, SA.SATA_BF16))
+    for t in range(steps):
+        SA.decode_step_mixed(b, qd[t], kd[t], vd[t], mixed, out=dout[t], ws=ws)
+    torch.cuda.synchronize()
+    got = dout.cpu().numpy()
+    for s in range(S):
+        qq = np.concatenate([q[0, s], qs[:, s]])
+        kk = np.concatenate([k[0, s], ks[:, s]])
+        vv = np.concatenate([v[0, s], vs[:, s]])
+        ref = oracle_rows(qq, kk, vv, w.P, w.c, rows=np.arange(w.n, w.n + steps))
+        assert O.row_normwise_error(got[:, s], ref) <= TOL[w.dtype], s
+
+
+@pytest.mark.parametrize("d,P,dtype,steps", [(8, 3, W.F32, 60), (16, 4, W.BF16, 40), (32, 4, W.BF16, 30),
+                                             (32, 5, W.BF16, 20), (64, 4, W.F32, 12), (64, 5, W.BF16, 6)])
+def test_mixed_state_decode_from_empty(d, P, dtype, steps):
+    """Mixed decode from an empty state: every tile's scale is re-chosen as
+    the state grows from zero."""
+    note(f"mixed decode from empty d={d} P={P} {dtype} steps={steps}")
+    S = 3
+    q, k, v = W.make_qkv(1, S, steps, d, d, dtype, 24000 + d + P)
+    b = SA.build_basis(d, P, 1.0)
+    mixed = SA.to_mixed(b, SA.new_state(b, S))
+    qd, kd, vd = to_dev(q[0], dtype), to_dev(k[0], dtype), to_dev(v[0], dtype)
+    got = np.zeros((S, steps, d))
+    for t in range(steps):
+        got[:, t] = SA.decode_step_mixed(b, qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(),
+                                         mixed).cpu().numpy()
+    for s in range(S):
+        ref = oracle_rows(q[0, s], k[0, s], v[0, s], P, 1.0)
+        assert O.row_normwise_error(got[s], ref) <= 3e-3, s
+
+
+@pytest.mark.parametrize("d,P", [(16, 4), (64, 4)])
+def test_mixed_state_round_trip(d, P):
+    """fp32 -> mixed -> fp32: rows of orders 0 and 1 and z come back bit for
+    bit; rows of higher order within half an f16 ulp of their tile's scale
+    (relative 2^-11 of each value, absolute 2^-25 of the tile's largest)."""
+    note(f"mixed round trip d={d} P={P}")
+    n, S = 300, 3
+    q, k, v = W.make_qkv(1, S, n, d, d, W.BF16, 25000 + d)
+    v = v * 50.0   # values well away from 1
+    b = SA.build_basis(d, P, 1.0)
+    _, st = run_prefill(b, q, k, _rows_bf16(v), W.BF16)
+    back = SA.from_mixed(b, SA.to_mixed(b, st))
+    torch.cuda.synchronize()
+    a = st.cpu().numpy().astype(np.float64)
+    r = back.cpu().numpy().astype(np.float64)
+    D = b.total_rows
+    lo = 1 + d
+    F = b.state_floats()
+    np.testing.assert_array_equal(r[:, :lo * d], a[:, :lo * d])
+    np.testing.assert_array_equal(r[:, D * d:F], a[:, D * d:F])
+    hi_a = a[:, lo * d:D * d]
+    hi_r = r[:, lo * d:D * d]
+    tile_max = np.max(np.abs(hi_a))
+    assert np.all(np.abs(hi_r - hi_a) <= np.abs(hi_a) * 2.0 ** -11 + tile_max * 2.0 ** -25)
