@@ -63,6 +63,9 @@ def _declare(lib):
     lib.sata_prefill_strided.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
                                          c_i64, c_vp, c_sz, c_vp]
     lib.sata_prefill_strided.restype = c_int
+    lib.sata_prefill_varlen.argtypes = [c_vp, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_vp, c_i64, c_vp, c_sz, c_vp]
+    lib.sata_prefill_varlen.restype = c_int
     lib.sata_decode_workspace.argtypes = [c_vp, c_int, c_int, c_int, P(c_sz)]
     lib.sata_decode_workspace.restype = c_int
     lib.sata_decode_step.argtypes = [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
@@ -245,11 +248,13 @@ def _check_buffer(name: str, t, dtype, numel: int, device):
         raise ValueError(f"{name} holds {t.numel()} elements, the call writes {numel}")
 
 
-def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None):
+def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None, lengths=None):
     """Causal prefill. q, k: [B, H, n, d_k], v: [B, H, n, d_v] (float32 or bfloat16,
     contiguous, on the GPU). state: [B*H, stride] float32 with stride >= state_floats
-    (new_state; zeros = empty prefix), read and written. Returns (out [B, H, n, d_v]
-    float32, state)."""
+    (new_state; zeros = empty prefix), read and written. lengths: optional int32
+    tensor of B*H per-head token counts on the GPU (head h takes its first
+    lengths[h] tokens; its output rows past that are zeros). Returns
+    (out [B, H, n, d_v] float32, state)."""
     import torch
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B, H, n, d_k] and v [B, H, n, d_v]")
@@ -268,6 +273,15 @@ def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None):
         ws = workspace(need, q.device)
     if ws.device != q.device:
         raise ValueError(f"ws must be on {q.device}")
+    if lengths is not None:
+        if lengths.dtype != torch.int32 or not lengths.is_contiguous() or lengths.device != q.device \
+                or lengths.numel() != B * H:
+            raise ValueError(f"lengths must be a contiguous int32 tensor of {B * H} elements on {q.device}")
+        st = lib().sata_prefill_varlen(basis.handle, B, H, n, d_v, code, q.data_ptr(), k.data_ptr(),
+                                       v.data_ptr(), lengths.data_ptr(), out.data_ptr(), state.data_ptr(), stride,
+                                       ws.data_ptr(), ws.numel() * ws.element_size(), _stream_ptr(q.device))
+        _check(st, "sata_prefill_varlen")
+        return out, state
     st = lib().sata_prefill_strided(basis.handle, B, H, n, d_v, code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                     out.data_ptr(), state.data_ptr(), stride, ws.data_ptr(),
                                     ws.numel() * ws.element_size(), _stream_ptr(q.device))

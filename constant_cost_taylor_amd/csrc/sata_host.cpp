@@ -615,9 +615,9 @@ int sata_prefill_workspace(const sata_basis* b, int B, int H, int n, int d_v, in
   return SATA_OK;
 }
 
-int sata_prefill_strided(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,
-                         const void* k, const void* v, float* out, float* state, int64_t state_stride,
-                         void* ws, size_t ws_bytes, void* stream) {
+static int prefill_impl(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,
+                        const void* k, const void* v, const int32_t* lens, float* out, float* state,
+                        int64_t state_stride, void* ws, size_t ws_bytes, void* stream) {
   if (!b || B < 1 || H < 1 || n < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
@@ -659,9 +659,9 @@ int sata_prefill_strided(const sata_basis* b, int B, int H, int n, int d_v, int 
   const float inv_c = static_cast<float>(1.0 / b->c);
   for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
     const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
-    sata::IntraArgs ia{q, k, v, pw, n, t0, w, b->P, inv_c};
-    sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P};
-    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c, b->P};
+    sata::IntraArgs ia{q, k, v, pw, n, t0, w, b->P, inv_c, lens};
+    sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P, lens};
+    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c, b->P, lens};
     if (bf16) {
       if (sata::launch_prefill_b16(b->d, static_cast<int>(BH), sa, s) != hipSuccess) return SATA_ERR_HIP;
       if (sata::launch_prefill_intra(b->d, true, static_cast<int>(BH), ia, s) != hipSuccess)
@@ -677,6 +677,19 @@ int sata_prefill_strided(const sata_basis* b, int B, int H, int n, int d_v, int 
     }
   }
   return SATA_OK;
+}
+
+int sata_prefill_strided(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,
+                         const void* k, const void* v, float* out, float* state, int64_t state_stride,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl(b, B, H, n, d_v, dtype, q, k, v, nullptr, out, state, state_stride, ws, ws_bytes, stream);
+}
+
+int sata_prefill_varlen(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,
+                        const void* k, const void* v, const int32_t* lengths, float* out, float* state,
+                        int64_t state_stride, void* ws, size_t ws_bytes, void* stream) {
+  if (n > 0 && (!lengths || !aligned(lengths, 4))) return SATA_ERR_INVALID_ARG;
+  return prefill_impl(b, B, H, n, d_v, dtype, q, k, v, lengths, out, state, state_stride, ws, ws_bytes, stream);
 }
 
 int sata_prefill(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,

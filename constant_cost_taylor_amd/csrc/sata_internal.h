@@ -167,6 +167,7 @@ struct ScanArgs {
   int D;                 // total basis rows (incl. order 0)
   float inv_c;           // 1 / c
   int P;                 // orders 0..P-1
+  const int32_t* lens;   // [BH] tokens of each head (device), or null: n_total for every head
 };
 
 struct IntraArgs {
@@ -179,6 +180,7 @@ struct IntraArgs {
   int nw;
   int P;
   float inv_c;
+  const int32_t* lens;
 };
 
 struct ReduceArgs {
@@ -190,6 +192,7 @@ struct ReduceArgs {
   int n_tiles;
   float inv_c;           // 1 / c
   int P;                 // orders 0..P-1 (with the max-abs values, selects the bf16 scan's operand type)
+  const int32_t* lens;
 };
 
 struct DecodeArgs {

@@ -42,6 +42,7 @@
 
 #include <type_traits>
 
+#include "sata_device.h"
 #include "sata_internal.h"
 
 namespace sata {
@@ -125,6 +126,9 @@ struct Cfg {
 
 template <int DK>
 __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
+  // tokens of this head in the window; none: the state is left as it is
+  const int nwh = head_tokens(a.lens, blockIdx.y, a.t0, a.nw, a.n_total);
+  if (nwh == 0) return;
   using C = Cfg<DK>;
   constexpr int DV = C::DV, L = C::L, RB = C::RB, NB = C::NB, NC = C::NC, DVP = C::DVP;
   constexpr int NSLOT = C::NSLOT, KSTR = C::KSTR, QSTR = C::QSTR, XQSTR = C::XQSTR;
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   const int nwp = a.ws.nwp;
   RedT* rech = static_cast<RedT*>(a.ws.rec) +
                (static_cast<int64_t>(head) * n_tiles + tile) * DVP * static_cast<int64_t>(nwp);
-  const int nch = (a.nw + L - 1) / L;
+  const int nch = (nwh + L - 1) / L;
   float* carryh = a.ws.carry + static_cast<int64_t>(head) * ((nwp + C::T - 1) / C::T) * DVP;
 
   // Cross-wave sum of one chunk's readout (LDS red) into its records.
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   ChunkRegs<IT, EPT> rq, rk, rv;
   {
     // Tokens past the window read the window's first token (always valid).
-    const bool ok = st_t < min(L, a.nw);
+    const bool ok = st_t < min(L, nwh);
     const int64_t tn = a.t0 + (ok ? st_t : 0);
     rq.load(qh + tn * DK + st_i, ok);
     rk.load(kh + tn * DK + st_i, ok);
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   const int ch_end = min(nch, ch0 + C::SC);
   for (int ch = ch0; ch < ch_end; ++ch) {
     const int64_t tb = a.t0 + static_cast<int64_t>(ch) * L;
-    const int nvalid = min(L, a.nw - ch * L);
+    const int nvalid = min(L, nwh - ch * L);
     // Launder the run metadata so the LDS addresses derived from it are
     // recomputed each chunk (a few integer ops) instead of held live.
 #pragma unroll
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     }
     // Prefetch the next chunk; the loads stay in flight through this chunk.
     if (ch + 1 < nch) {
-      const bool ok = st_t < min(L, a.nw - (ch + 1) * L);
+      const bool ok = st_t < min(L, nwh - (ch + 1) * L);
       const int64_t tn = tb + L + (ok ? st_t : 0);
       rq.load(qh + tn * DK + st_i, ok);
       rk.load(kh + tn * DK + st_i, ok);
@@ -446,7 +450,8 @@ __global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t tb = a.t0 + static_cast<int64_t>(win) * T;
-  const int nvalid = min(T, a.nw - win * T);
+  const int nvalid = min(T, head_tokens(a.lens, head, a.t0, a.nw, a.n_total) - win * T);
+  if (nvalid <= 0) return;
   const IT* qh = static_cast<const IT*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
   const IT* kh = static_cast<const IT*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
   const IT* vh = static_cast<const IT*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
@@ -536,7 +541,8 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
   const int lr = l & 15;
   const int g = l >> 4;
   const int64_t tb = a.t0 + static_cast<int64_t>(win) * T;
-  const int nvalid = min(T, a.nw - win * T);
+  const int nvalid = min(T, head_tokens(a.lens, head, a.t0, a.nw, a.n_total) - win * T);
+  if (nvalid <= 0) return;
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
   const uint16_t* vh = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
@@ -724,10 +730,11 @@ __global__ __launch_bounds__(256) void prefill_reduce(ReduceArgs a) {
   }
   __syncthreads();
   const int ntok = min(TB, a.nw - t0);
+  const int nlive = min(ntok, head_tokens(a.lens, head, a.t0, a.nw, a.n_total) - t0);
   float* out = a.out + (static_cast<int64_t>(head) * a.n_total + a.t0 + t0) * DV;
   for (int e = tid; e < ntok * DV; e += 256) {
     const int t = e / DV, c = e % DV;
-    out[static_cast<int64_t>(t) * DV + c] = acc[c * (TB + 1) + t] / acc[DV * (TB + 1) + t];
+    out[static_cast<int64_t>(t) * DV + c] = t < nlive ? acc[c * (TB + 1) + t] / acc[DV * (TB + 1) + t] : 0.f;
   }
 }
 

@@ -41,6 +41,7 @@
 
 #include <type_traits>
 
+#include "sata_device.h"
 #include "sata_internal.h"
 
 namespace sata {
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(256) void prefill_amax(ScanArgs a) {
   const int tid = threadIdx.x;
   const int64_t per = (a.nw + kAmaxSplit - 1) / kAmaxSplit;
   const int64_t t_begin = static_cast<int64_t>(sp) * per;
-  const int64_t t_end = min(static_cast<int64_t>(a.nw), t_begin + per);
+  const int64_t t_end = min(static_cast<int64_t>(head_tokens(a.lens, head, a.t0, a.nw, a.n_total)), t_begin + per);
   __shared__ uint32_t wmax[3][4];
   uint32_t m[3] = {0u, 0u, 0u};
   if (t_begin < t_end) {
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(256) void prefill_stage(ScanArgs a) {
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
   const HalfScales hs = head_scales(a.ws, head, a.P);
-  const int nvalid = min(L, a.nw - ch * L);
+  const int nvalid = max(0, min(L, head_tokens(a.lens, head, a.t0, a.nw, a.n_total) - ch * L));
   const int64_t tok0 = a.t0 + static_cast<int64_t>(ch) * L;
   const int nchp = a.ws.nwp / L;
   float mul[3] = {1.f, 1.f, 1.f};   // k, v, q
@@ -471,7 +472,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   const int lr = l & 15;
   const int g = l >> 4;
   const int lay_base = (tile * NW + w) * RB;
-  const int nch = (a.nw + L - 1) / L;
+  const int nch = (head_tokens(a.lens, head, a.t0, a.nw, a.n_total) + L - 1) / L;
   const int nchp = a.ws.nwp / L;
 
   // ---- constant rows, row weights -----------------------------------------
@@ -1073,6 +1074,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
 template <int DK, bool P5>
 __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[CfgS<DK>::LDS_B];
+  // no tokens of this head in the window: the state is left as it is
+  if (head_tokens(a.lens, blockIdx.y, a.t0, a.nw, a.n_total) == 0) return;
   const HalfScales hs = head_scales(a.ws, blockIdx.y, a.P);
   if (hs.safe)
     scan_tile<DK, true, P5>(a, hs, lds);
@@ -1102,7 +1105,8 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
   const int tid = threadIdx.x;
   const int nwp = a.ws.nwp;
   const int nt = a.n_tiles;
-  const int ntok = min(TB, a.nw - t0);
+  const int ntok = min(TB, head_tokens(a.lens, head, a.t0, a.nw, a.n_total) - t0);   // may be <= 0
+  const int nout = min(TB, a.nw - t0);   // rows of the block; those past ntok are written as zeros
   const HalfScales hs = head_scales(a.ws, head, a.P);
   const float rscale = hs.safe ? ldexpf(1.f, hs.ev) : 1.f;   // value-column records carry 2^-ev
   const float* intra = a.ws.intra + static_cast<int64_t>(head) * nwp * DVP;
@@ -1222,6 +1226,10 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
     *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(t) * DV + 8 * u) = o0;
     *reinterpret_cast<f32x4*>(out + static_cast<int64_t>(t) * DV + 8 * u + 4) = o1;
   }
+  // rows past the head's length
+  const int nz = max(ntok, 0);
+  for (int e = tid; e < (nout - nz) * DV; e += kRedThr)
+    out[static_cast<int64_t>(t0 + nz) * DV + e] = 0.f;
 }
 
 template <int D>

@@ -157,6 +157,24 @@ int sata_prefill_strided(const sata_basis* basis, int B, int H, int n, int d_v, 
                          const void* q, const void* k, const void* v, float* out, float* state,
                          int64_t state_stride, void* ws, size_t ws_bytes, void* stream);
 
+/* Prefill with a length per head [SATA page, "Engineering of constant
+ * compute cost": the state has the same size whatever a sequence's length, so
+ * sequences of different lengths batch uniformly]: head h (= b * H + h' in
+ * [B, H] order) takes only its first lengths[h] tokens of the n slots of
+ * q, k, v; each of them attends causally to the head's earlier tokens (and
+ * its state), exactly as in sata_prefill_strided over that head alone.  The
+ * state absorbs exactly lengths[h] tokens; output rows past lengths[h] are
+ * written as zeros.  lengths: [B*H] int32 in device memory (read by the
+ * kernels, so the host cannot check it: values are clamped to [0, n]).  A
+ * length of 1 on a head with a state is one decode step, so one call serves
+ * a batch that mixes prefill chunks and decode steps.  Other arguments and
+ * errors as for sata_prefill_strided; the workspace is sata_prefill_workspace
+ * for (B, H, n). */
+int sata_prefill_varlen(const sata_basis* basis, int B, int H, int n, int d_v, int dtype,
+                        const void* q, const void* k, const void* v, const int32_t* lengths,
+                        float* out, float* state, int64_t state_stride, void* ws, size_t ws_bytes,
+                        void* stream);
+
 /* Device workspace in bytes that sata_decode_step needs for S states. */
 int sata_decode_workspace(const sata_basis* basis, int S, int d_v, int dtype, size_t* bytes);
 

@@ -723,3 +723,89 @@ def test_mixed_state_round_trip(d, P):
     hi_r = r[:, lo * d:D * d]
     tile_max = np.max(np.abs(hi_a))
     assert np.all(np.abs(hi_r - hi_a) <= np.abs(hi_a) * 2.0 ** -11 + tile_max * 2.0 ** -25)
+
+
+# ----------------------------------------------------------------------------
+# Per-head lengths (one call for sequences of different lengths)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,P,dtype", [(64, 4, W.BF16), (16, 4, W.F32), (32, 5, W.BF16), (8, 3, W.F32)])
+def test_prefill_varlen(d, P, dtype):
+    """Six heads of lengths 0, 1, 63, 64, 513 and 700 in one [2, 3, 700]
+    call, NaN in every slot past a head's length: each head's rows equal its
+    own causal attention, rows past its length are zero, and its state holds
+    exactly its own tokens."""
+    lens = [0, 1, 63, 64, 513, 700]
+    B, H, n = 2, 3, 700
+    note(f"varlen prefill d={d} P={P} {dtype} lens={lens}")
+    q, k, v = W.make_qkv(B, H, n, d, d, dtype, 26000 + d + P)
+    qn, kn, vn = (x.copy().reshape(B * H, n, -1) for x in (q, k, v))
+    for h, L in enumerate(lens):
+        for x in (qn, kn, vn):
+            x[h, L:] = np.nan
+    qn, kn, vn = (x.reshape(B, H, n, -1) for x in (qn, kn, vn))
+    b = SA.build_basis(d, P, 1.0)
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, st = SA.prefill(b, to_dev(qn, dtype), to_dev(kn, dtype), to_dev(vn, dtype), lengths=lt)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(B * H, n, d)
+    sts = st.cpu().numpy()
+    basis = O.enumerate_basis(d, P)
+    D = b.total_rows
+    qf, kf, vf = (x.reshape(B * H, n, -1) for x in (q, k, v))
+    for h, L in enumerate(lens):
+        assert np.all(got[h, L:] == 0.0), h
+        if L:
+            ref = oracle_rows(qf[h, :L], kf[h, :L], vf[h, :L], P, 1.0)
+            assert O.row_normwise_error(got[h, :L], ref) <= TOL[dtype], (h, L)
+        S_ref, z_ref = O.direct_state(f64(kf[h, :L]), f64(vf[h, :L]), basis)
+        gS = sts[h, :D * d].reshape(D, d)
+        gz = sts[h, D * d:D * (d + 1)]
+        assert np.all(np.isfinite(gS)) and np.all(np.isfinite(gz)), h
+        if L == 0:
+            assert np.all(gS == 0) and np.all(gz == 0), h
+            continue
+        off = 0
+        for p in range(P):
+            rows = slice(off, off + math.comb(d + p - 1, p))
+            assert np.max(np.abs(gS[rows] - S_ref[rows])) <= TOL[dtype] * np.max(np.abs(S_ref[rows])) + 1e-30, (h, p)
+            assert np.max(np.abs(gz[rows] - z_ref[rows])) <= TOL[dtype] * np.max(np.abs(z_ref[rows])) + 1e-30, (h, p)
+            off = rows.stop
+
+
+@pytest.mark.parametrize("d,P,dtype", [(64, 4, W.BF16), (16, 4, W.F32)])
+def test_prefill_varlen_mixes_decode_steps_and_chunks(d, P, dtype):
+    """States prefilled to 0, 5, 200 and 600 tokens continue in one varlen
+    call with lengths 1, 1, 64 and 1 (three decode steps and a 64-token chunk
+    in one batch), then take one sata_decode_step each: every row matches the
+    oracle on the concatenated sequence."""
+    before = [0, 5, 200, 600]
+    now = [1, 1, 64, 1]
+    S = len(before)
+    note(f"varlen continuation d={d} P={P} {dtype} {before} + {now}")
+    total = [a + c + 1 for a, c in zip(before, now)]
+    seqs = [W.make_qkv(1, 1, t, d, d, dtype, 27000 + 7 * d + i) for i, t in enumerate(total)]
+    b = SA.build_basis(d, P, 1.0)
+    st = SA.new_state(b, S)
+    for i, L in enumerate(before):
+        if L:
+            run_prefill(b, *(x[:, :, :L] for x in seqs[i]), dtype, state=st[i:i + 1])
+    nmax = max(now)
+    qb = np.zeros((1, S, nmax, d), dtype=np.float32)
+    kb, vb = qb.copy(), qb.copy()
+    for i in range(S):
+        for x, dst in zip(seqs[i], (qb, kb, vb)):
+            dst[0, i, :now[i]] = x[0, 0, before[i]:before[i] + now[i]]
+    lt = torch.tensor(now, dtype=torch.int32, device="cuda")
+    out, _ = SA.prefill(b, to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), state=st, lengths=lt)
+    last = [np.stack([seqs[i][j][0, 0, total[i] - 1] for i in range(S)]) for j in range(3)]
+    dec = SA.decode_step(b, *(to_dev(x, dtype) for x in last), st)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0]
+    gd = dec.cpu().numpy()
+    for i in range(S):
+        q, k, v = (x[0, 0] for x in seqs[i])
+        ref = oracle_rows(q, k, v, P, 1.0, rows=np.arange(before[i], total[i]))
+        assert O.row_normwise_error(got[i, :now[i]], ref[:now[i]]) <= TOL[dtype], i
+        assert np.all(got[i, now[i]:] == 0.0), i
+        assert O.row_normwise_error(gd[i:i + 1], ref[now[i]:]) <= TOL[dtype], i
