@@ -13,7 +13,8 @@ timed steps, `configs` reports the other workloads, each against its own
 roofline (a few repetitions each): the same decode on the mixed-precision
 state (orders >= 2 of S in float16), the d8 / d16 fp32 and d64 bf16 prefills,
 the long-context d32 prefill at 2^16, 2^18 and 2^20 tokens with its per-token
-cost ratio, and the orders 0..4 (P = 5) prefill and decode legs.  The CPU
+cost ratio, the orders 0..4 (P = 5) prefill and decode legs, and exact causal
+softmax attention beside the SATA prefill over n = 2^12..2^16 (the crossover).  The CPU
 baseline is the float64 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -345,6 +346,67 @@ def mixed_leg(sa, basis, w, Q, K, V, DQ, DK, DV, state, out, pws, q, k, v, qs, k
             "check": {"decode_row_normwise_err": max(errs)}}
 
 
+def crossover_points(reps, warmup, heads=(4, 32), lgs=(12, 13, 14, 15, 16)):
+    """Exact causal softmax attention (sata_softmax_attention, bf16 MFMA)
+    beside the SATA prefill on the same inputs (d = 64, P = 4, bf16,
+    device-generated unit-norm q, k and Gaussian v) over growing n: SATA's
+    cost per token is flat, exact attention's grows with n.  The crossover n
+    is interpolated on log-log axes between the sweep points around it."""
+    import torch
+    import constant_cost_taylor_amd as sa
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    basis = sa.build_basis(64, 4, 1.0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        ms = []
+        for it in range(warmup + reps):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if it >= warmup:
+                ms.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ms))
+
+    res = {}
+    for H in heads:
+        pts = []
+        for lg in lgs:
+            n = 1 << lg
+            g = torch.Generator(device=dev)
+            g.manual_seed(7000 + lg)
+            shape = (1, H, n, 64)
+            q = torch.randn(shape, generator=g, device=dev)
+            q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+            k = torch.randn(shape, generator=g, device=dev)
+            k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+            v = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+            out = torch.empty(shape, dtype=torch.float32, device=dev)
+            t_exact = timed(lambda: sa.softmax_attention(q, k, v, 1.0, out=out))
+            state = sa.new_state(basis, H, dev)
+            ws = sa.workspace(sa.prefill_workspace_bytes(basis, 1, H, n, 64, sa.SATA_BF16), dev)
+            t_sata = timed(lambda: sa.prefill(basis, q, k, v, state=state.zero_(), out=out, ws=ws))
+            pts.append({"n": n, "exact_ms": t_exact, "sata_ms": t_sata,
+                        "exact_ns_per_head_token": 1e6 * t_exact / (H * n),
+                        "sata_ns_per_head_token": 1e6 * t_sata / (H * n)})
+            print(f"crossover H={H} n=2^{lg}: exact {t_exact:.2f} ms, SATA {t_sata:.2f} ms", file=sys.stderr,
+                  flush=True)
+            del q, k, v, out, state, ws
+            torch.cuda.empty_cache()
+        cross = None
+        for a_, b_ in zip(pts, pts[1:]):
+            ra, rb = a_["exact_ms"] / a_["sata_ms"], b_["exact_ms"] / b_["sata_ms"]
+            if ra < 1.0 <= rb:
+                f = np.log(1.0 / ra) / np.log(rb / ra)
+                cross = float(np.exp(np.log(a_["n"]) + f * (np.log(b_["n"]) - np.log(a_["n"]))))
+                break
+        res[f"heads_{H}"] = {"points": pts, "crossover_n": cross}
+    return {"workload": "exact causal softmax (bf16 MFMA) vs SATA prefill, d_k=d_v=64, P=4, bf16 inputs, "
+                        "device-generated inputs", "steps": reps, "warmup": warmup, **res}
+
+
 def ceilings(args):
     """Measured ceilings of this machine (torch / hipBLASLt kernels, HIP events):
     the bandwidth a read+write stream, an in-place read-modify-write stream
@@ -537,7 +599,8 @@ def main():
         torch.cuda.empty_cache()
         res["configs"] = {"prefill": config_points(args.config_steps, 1),
                           "long_context": flatness_points(args.config_steps, 1),
-                          "order5": order5_point(args.config_steps, 1, 64)}
+                          "order5": order5_point(args.config_steps, 1, 64),
+                          "softmax_crossover": crossover_points(3, 1)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, qs, ks, vs, args.cpu_seconds)
     print(json.dumps(res), flush=True)

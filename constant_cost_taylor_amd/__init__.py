@@ -90,6 +90,8 @@ def _declare(lib):
     lib.sata_decode_step_mixed.argtypes = [c_vp, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                            c_vp]
     lib.sata_decode_step_mixed.restype = c_int
+    lib.sata_softmax_attention.argtypes = [c_int, c_int, c_int, c_int, c_int, c_dbl, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.sata_softmax_attention.restype = c_int
     lib.sata_status_string.argtypes = [c_int]
     lib.sata_status_string.restype = ctypes.c_char_p
 
@@ -404,4 +406,28 @@ def decode_step_mixed(basis: Basis, q, k, v, mixed, out=None, ws=None):
                                       out.data_ptr(), mixed.data_ptr(), ws.data_ptr(),
                                       ws.numel() * ws.element_size(), _stream_ptr(q.device))
     _check(st, "sata_decode_step_mixed")
+    return out
+
+
+# ---- exact causal softmax attention (the baseline SATA is measured against) ----
+
+def softmax_attention(q, k, v, c: float = 1.0, out=None):
+    """Exact causal softmax attention of [B, H, n, d] q, k, v (float32 or
+    bfloat16, one GPU): returns out [B, H, n, d] float32."""
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, n, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if q.device.type != "cuda" or k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one GPU")
+    B, H, n, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=q.device)
+    _check_buffer("out", out, torch.float32, B * H * n * d, q.device)
+    _check(lib().sata_softmax_attention(B, H, n, d, _dtype_code(q), float(c), q.data_ptr(), k.data_ptr(),
+                                        v.data_ptr(), out.data_ptr(), _stream_ptr(q.device)),
+           "sata_softmax_attention")
     return out

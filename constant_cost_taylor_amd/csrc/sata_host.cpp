@@ -775,6 +775,23 @@ int sata_decode_step_noalloc(const sata_basis* b, int S, int d_v, int dtype, con
 
 size_t sata_decode_noalloc_max_bytes(void) { return sata::kNoAllocScratchBytes; }
 
+int sata_softmax_attention(int B, int H, int n, int d, int dtype, double c, const void* q, const void* k,
+                           const void* v, float* out, void* stream) {
+  if (B < 1 || H < 1 || n < 0 || !(std::isfinite(c) && c > 0.0)) return SATA_ERR_INVALID_ARG;
+  if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
+  if (!supported_dim(d)) return SATA_ERR_UNSUPPORTED;
+  if (n == 0) return SATA_OK;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (BH > 65535) return SATA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out) return SATA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return SATA_ERR_INVALID_ARG;
+  sata::SoftmaxArgs a{q, k, v, out, n, static_cast<float>(1.0 / c)};
+  if (sata::launch_softmax(d, dtype == SATA_BF16, static_cast<int>(BH), a, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return SATA_ERR_HIP;
+  return SATA_OK;
+}
+
 int64_t sata_mixed_state_bytes(const sata_basis* b, int d_v) {
   if (!b || d_v != b->d) return -1;
   return mixed_plan(b).bytes;

@@ -277,6 +277,17 @@ struct MixedConvArgs {
 };
 
 hipError_t launch_decode_mixed(int d, bool bf16, const MixedDecodeArgs& a, hipStream_t s);
+
+// Exact causal softmax attention (the baseline): q, k, v [BH][n][d], out [BH][n][d] fp32.
+struct SoftmaxArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  int64_t n;
+  float inv_c;
+};
+hipError_t launch_softmax(int d, bool bf16, int BH, const SoftmaxArgs& a, hipStream_t s);
 hipError_t launch_mixed_convert(int d, bool to_mixed, const MixedConvArgs& a, hipStream_t s);
 
 // The allocation-free decode entry point keeps its partial records in a

@@ -236,6 +236,21 @@ int sata_decode_step_mixed(const sata_basis* basis, int S, int d_v, int dtype, c
                            const void* k, const void* v, float* out, void* mixed, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* ---- Exact causal softmax attention (the baseline) -------------------------
+ * out_i = sum_{j<=i} exp(q_i.k_j/c) v_j / sum_{j<=i} exp(q_i.k_j/c), computed
+ * stably with a running maximum [MoA page, section "DNF derivation"]; its
+ * per-token work grows with the position [SATA page, "Scale bottleneck of
+ * conventional self-attention": n (2 d_k + 2 d_v + 3) FLOPs at position n],
+ * which SATA's fixed-size state avoids.  It is here to measure that
+ * crossover on this hardware, not as part of the SATA path.
+ *   q, k, v: [B, H, n, d] contiguous (float32 or bfloat16), out: [B, H, n, d]
+ *   float32, all 16-byte aligned; d in {8, 16, 32, 64}; c > 0.  No basis and
+ *   no workspace.  bfloat16: scores and value sums on bf16 MFMA with fp32
+ *   accumulation, the probabilities as two bf16 parts; float32: fp32
+ *   arithmetic throughout.  Asynchronous on `stream`. */
+int sata_softmax_attention(int B, int H, int n, int d, int dtype, double c, const void* q, const void* k,
+                           const void* v, float* out, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * sata_decode_step_strided without a workspace argument.  The per-tile

@@ -809,3 +809,37 @@ def test_prefill_varlen_mixes_decode_steps_and_chunks(d, P, dtype):
         assert O.row_normwise_error(got[i, :now[i]], ref[:now[i]]) <= TOL[dtype], i
         assert np.all(got[i, now[i]:] == 0.0), i
         assert O.row_normwise_error(gd[i:i + 1], ref[now[i]:]) <= TOL[dtype], i
+
+
+# ----------------------------------------------------------------------------
+# Exact causal softmax attention (the baseline)
+# ----------------------------------------------------------------------------
+
+SOFTMAX_CASES = [
+    # B, H, n, d, c, query scale, dtype
+    (1, 1, 1, 64, 1.0, 1.0, W.F32), (1, 2, 300, 8, 1.0, 1.0, W.F32), (2, 1, 257, 16, 0.5, 1.0, W.F32),
+    (1, 1, 700, 32, 1.0, 1.0, W.F32), (1, 1, 513, 64, 1.0, 100.0, W.F32),
+    (1, 1, 1, 64, 1.0, 1.0, W.BF16), (1, 2, 63, 8, 1.0, 1.0, W.BF16), (1, 1, 64, 16, 1.0, 1.0, W.BF16),
+    (2, 1, 65, 32, 0.5, 1.0, W.BF16), (1, 2, 1100, 64, 1.0, 1.0, W.BF16), (1, 1, 777, 64, 1.0, 100.0, W.BF16),
+    (1, 1, 2048, 32, 1.0, 8.0, W.BF16),
+]
+
+
+@pytest.mark.parametrize("case", SOFTMAX_CASES, ids=[f"{c[6]}-n{c[2]}-d{c[3]}-x{c[5]:g}" for c in SOFTMAX_CASES])
+def test_softmax_attention(case):
+    """Stable causal softmax against the oracle's exact_softmax; logits up to
+    about 100 (query scale 100) would overflow float32 without the running
+    maximum."""
+    B, H, n, d, c, qs, dtype = case
+    note(f"softmax B={B} H={H} n={n} d={d} c={c} q x {qs} {dtype}")
+    q, k, v = W.make_qkv(B, H, n, d, d, W.F32, 28000 + n + d)
+    q = q * qs
+    if dtype == W.BF16:
+        q, k, v = _rows_bf16(q), _rows_bf16(k), _rows_bf16(v)
+    out = SA.softmax_attention(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), c)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for bb in range(B):
+        for h in range(H):
+            ref = O.exact_softmax(f64(q[bb, h]), f64(k[bb, h]), f64(v[bb, h]), c)
+            assert O.row_normwise_error(got[bb, h], ref) <= TOL[dtype], (bb, h)
