@@ -432,80 +432,90 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   }
 }
 
-// Intra-window part: for each token i of a readout window of T tokens, the
-// sum over the window's keys j <= i of T_P(q_i.k_j/c) (v_j, 1), in fp32 with
-// Horner's rule.  Block = (window, head); thread (token i, column group);
-// keys are staged through LDS in tiles of KT tokens and read as broadcasts.
-// Writes record columns [DVP][nwp] (coalesced over tokens).
+// Intra-window part for float32 inputs, on fp32 MFMA (16x16x4): for the
+// window's queries i and keys j <= i, sum T_P(q_i.k_j/c) (v_j, 1).  Block =
+// (window of T = 32 tokens, head), one wave.  With A the 16 x 4 and B the
+// 4 x 16 operand (lane (lr, g) holds A[lr][g] and B[g][lr]) and the 16 x 16
+// result in C layout (lane (lr, g) holds rows 4 g .. 4 g + 3 of column lr):
+//   X^T[key][query] = sum over dims of K Q^T    (tiles of 16 keys x 16 queries)
+//   W^T = T_P(X^T / c) by Horner's rule, zero for keys after the query
+//   O^T[col][query] += V'^T W^T                  (V' = [v, 1, 0...])
+// For K-step s of a key tile, lane (lr, g) feeds key 4 g + s: its own C-layout
+// element s of W^T is the B operand, and the A operand is V' at that key, so
+// no value crosses lanes.  Writes record columns [DVP][nwp].
 template <int DK>
-__global__ __launch_bounds__(256) void prefill_intra(IntraArgs a) {
-  using IT = float;
+__global__ __launch_bounds__(64) void prefill_intra(IntraArgs a) {
   constexpr int DV = DK, T = prefill_window(false);
-  constexpr int KT = T < 64 ? T : 64;         // keys per LDS tile
-  constexpr int NG = 256 / T;                 // column groups
-  constexpr int CPG = (DV + NG - 1) / NG;     // columns per group
-  __shared__ __attribute__((aligned(16))) float sk[KT][DK];
-  __shared__ __attribute__((aligned(16))) float sv[KT][DV];
+  static_assert(T == 32, "two 16-token tiles per window");
+  constexpr int NB = col_blocks(DV), NC = NB * 16;
+  constexpr int KS = DK + 1;                  // LDS row stride of q and k (floats)
+  constexpr int VS = NC + 1;                  // LDS row stride of v'
+  __shared__ float sq[T * KS];
+  __shared__ float sk[T * KS];
+  __shared__ float sv[T * VS];
   const int win = blockIdx.x;
   const int head = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int l = threadIdx.x;
+  const int lr = l & 15;
+  const int g = l >> 4;
   const int64_t tb = a.t0 + static_cast<int64_t>(win) * T;
   const int nvalid = min(T, head_tokens(a.lens, head, a.t0, a.nw, a.n_total) - win * T);
   if (nvalid <= 0) return;
-  const IT* qh = static_cast<const IT*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
-  const IT* kh = static_cast<const IT*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
-  const IT* vh = static_cast<const IT*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
-  const int i = tid % T;
-  const int grp = tid / T;
-  float qi[DK];
-#pragma unroll
-  for (int d = 0; d < DK; ++d) qi[d] = i < nvalid ? load_in(qh, (tb + i) * DK + d) * a.inv_c : 0.f;
+  const float* qh = static_cast<const float*>(a.q) + static_cast<int64_t>(head) * a.n_total * DK;
+  const float* kh = static_cast<const float*>(a.k) + static_cast<int64_t>(head) * a.n_total * DK;
+  const float* vh = static_cast<const float*>(a.v) + static_cast<int64_t>(head) * a.n_total * DV;
+  for (int e = l; e < T * DK; e += 64) {
+    const int t = e / DK, d = e % DK;
+    const bool ok = t < nvalid;
+    sq[t * KS + d] = ok ? qh[(tb + t) * DK + d] * a.inv_c : 0.f;
+    sk[t * KS + d] = ok ? kh[(tb + t) * DK + d] : 0.f;
+  }
+  for (int e = l; e < T * NC; e += 64) {
+    const int t = e / NC, c = e % NC;
+    const bool ok = t < nvalid;
+    sv[t * VS + c] = !ok ? 0.f : c < DV ? vh[(tb + t) * DV + c] : (c == DV ? 1.f : 0.f);
+  }
+  __syncthreads();
   const float rcp[5] = {0.f, 1.f, 0.5f, 1.f / 3.f, 0.25f};
-  float num[CPG];
+  float* rec = a.ws.intra + static_cast<int64_t>(head) * padded_dv(DV) * a.ws.nwp + static_cast<int64_t>(win) * T;
 #pragma unroll
-  for (int cc = 0; cc < CPG; ++cc) num[cc] = 0.f;
-  float den = 0.f;
-  const int ntile = (nvalid + KT - 1) / KT;
-  for (int jt = 0; jt < ntile; ++jt) {
-    __syncthreads();
-    for (int e = tid; e < KT * DK; e += 256) {
-      const int t = e / DK, d = e % DK;
-      const bool ok = jt * KT + t < nvalid;
-      sk[t][d] = ok ? load_in(kh, (tb + jt * KT + t) * DK + d) : 0.f;
-      sv[t][d] = ok ? load_in(vh, (tb + jt * KT + t) * DV + d) : 0.f;
+  for (int qt = 0; qt < 2; ++qt) {
+    f32x4 O[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int qi = 16 * qt + lr;                 // this lane's query (window-relative)
+#pragma unroll
+    for (int kt = 0; kt <= qt; ++kt) {           // key tiles at or before the query tile
+      f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kst = 0; kst < DK / 4; ++kst)
+        X = __builtin_amdgcn_mfma_f32_16x16x4f32(sk[(16 * kt + lr) * KS + 4 * kst + g],
+                                                 sq[(16 * qt + lr) * KS + 4 * kst + g], X, 0, 0, 0);
+      f32x4 Wt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = 16 * kt + 4 * g + r;      // key of element r
+        float wgt = 1.f;
+        for (int p = a.P - 1; p >= 1; --p) wgt = fmaf(wgt, X[r] * rcp[p], 1.f);
+        Wt[r] = (kj <= qi && kj < nvalid) ? wgt : 0.f;
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          O[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv[(16 * kt + 4 * g + st) * VS + 16 * nb + lr], Wt[st], O[nb],
+                                                       0, 0, 0);
     }
-    __syncthreads();
-    const int jend = min(KT, i - jt * KT + 1);   // keys j <= i of this tile
-    if (i >= nvalid) continue;
-    for (int j = 0; j < jend; ++j) {
-      float x = 0.f;
+    if (qi < nvalid) {
 #pragma unroll
-      for (int d = 0; d < DK; d += 4) {
-        const float4 kk = *reinterpret_cast<const float4*>(&sk[j][d]);
-        x = fmaf(qi[d], kk.x, x);
-        x = fmaf(qi[d + 1], kk.y, x);
-        x = fmaf(qi[d + 2], kk.z, x);
-        x = fmaf(qi[d + 3], kk.w, x);
-      }
-      float wgt = 1.f;
-      for (int p = a.P - 1; p >= 1; --p) wgt = fmaf(wgt, x * rcp[p], 1.f);
-      den += wgt;
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int cc = 0; cc < CPG; ++cc) {
-        const int c = grp * CPG + cc;
-        if (c < DV) num[cc] = fmaf(wgt, sv[j][c], num[cc]);
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * nb + 4 * g + r;
+          if (c <= DV) rec[static_cast<int64_t>(c) * a.ws.nwp + qi] = O[nb][r];
+        }
     }
   }
-  if (i >= nvalid) return;
-  constexpr int DVP = padded_dv(DV);
-  float* rec = a.ws.intra + static_cast<int64_t>(head) * DVP * a.ws.nwp + static_cast<int64_t>(win) * T + i;
-#pragma unroll
-  for (int cc = 0; cc < CPG; ++cc) {
-    const int c = grp * CPG + cc;
-    if (c < DV) rec[static_cast<int64_t>(c) * a.ws.nwp] = num[cc];
-  }
-  if (grp == 0) rec[static_cast<int64_t>(DV) * a.ws.nwp] = den;
 }
 
 // Intra-window part on MFMA, for bf16 inputs.  Block = (readout window of T
@@ -753,7 +763,7 @@ hipError_t launch_intra_t(int BH, const IntraArgs& a, hipStream_t s) {
   constexpr int T = prefill_window(BF16);
   dim3 grid((a.nw + T - 1) / T, BH);
   if (!BF16)
-    prefill_intra<D><<<grid, 256, 0, s>>>(a);
+    prefill_intra<D><<<grid, 64, 0, s>>>(a);
   else if (a.P == 5)
     prefill_intra_mfma<D, true><<<grid, T, 0, s>>>(a);
   else
