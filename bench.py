@@ -39,6 +39,8 @@ METRIC = "causal SATA tokens/sec/head (prefill, decode) + % of HBM/MFMA roofline
 # (profiles/decode_update_readout_256x4096_d64_hbm_traffic.txt).  Re-measure after any
 # change to the decode kernel.
 DECODE_TRAFFIC_BYTES = 6.6518e9
+# The same for one decode_mixed launch (mixed-precision state, same workload).
+MIXED_DECODE_TRAFFIC_BYTES = 3.4535e9
 
 
 def parse():
@@ -343,6 +345,7 @@ def mixed_leg(sa, basis, w, Q, K, V, DQ, DK, DV, state, out, pws, q, k, v, qs, k
                         f"power-of-two scales; {dsteps} decode steps after the {w.n}-token prefill",
             "ms_per_step": dec, "head_tokens_per_s": S / (dec * 1e-3), "algorithmic_bytes": dec_bytes,
             "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "speedup_vs_f32_state": f32_ms / dec,
+            "traffic": MIXED_DECODE_TRAFFIC_BYTES, "traffic_unit": "bytes per launch (HBM, counter-measured)",
             "check": {"decode_row_normwise_err": max(errs)}}
 
 
