@@ -369,8 +369,8 @@ struct CfgS {
   static constexpr int QT_B = (DK + 1) * 128;
   static constexpr int QN_B = L * 2 * DK;
   static constexpr int RED_B = NW * L * 2 * DV;
-  // bf16 operand path at d <= 16: the low bf16 half of every wave partial
-  static constexpr int REDL_B = DK <= 16 ? RED_B : 0;
+  // bf16 operand path at d <= 32: the low bf16 half of every wave partial
+  static constexpr int REDL_B = DK <= 32 ? RED_B : 0;
   static constexpr int DEN_B = NW * L * 4;
   static constexpr int WL_B = NW * RB * 16 * 4;
   static constexpr int O_KT = 0;
@@ -458,11 +458,11 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   // column blocks (one 16-byte write per block pair)
   constexpr bool PAIRED = DV >= 32;
   constexpr int NSLOT = C::NSLOT;
-  // bf16 operands at d <= 16: the readout operand and the wave partials are
+  // bf16 operands at d <= 32: the readout operand and the wave partials are
   // carried as bf16 pairs (value and rounding residual), 16 significant bits,
   // where a single bf16 (8 bits) would pass its rounding to outputs that
   // average few rows.
-  constexpr bool LOX = !H16 && DK <= 16;
+  constexpr bool LOX = !H16 && DK <= 32;
 
   const int tile = blockIdx.x;
   const int head = blockIdx.y;
@@ -914,10 +914,18 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
           // unit 4 P + g = columns 32 P + 4 g .. +3 and 32 P + 16 + 4 g .. +3
 #pragma unroll
           for (int P = 0; P < DV / 32; ++P) {
-            const u32x4 o = {pack_red(acc[2 * P][0], acc[2 * P][1]), pack_red(acc[2 * P][2], acc[2 * P][3]),
-                             pack_red(acc[2 * P + 1][0], acc[2 * P + 1][1]),
-                             pack_red(acc[2 * P + 1][2], acc[2 * P + 1][3])};
-            *reinterpret_cast<u32x4*>(&redw[rho * DV + 8 * ((4 * P + g) ^ swz_red<NU>(rho))]) = o;
+            const uint32_t o0 = pack_red(acc[2 * P][0], acc[2 * P][1]), o1 = pack_red(acc[2 * P][2], acc[2 * P][3]);
+            const uint32_t o2 = pack_red(acc[2 * P + 1][0], acc[2 * P + 1][1]);
+            const uint32_t o3 = pack_red(acc[2 * P + 1][2], acc[2 * P + 1][3]);
+            const int ro = rho * DV + 8 * ((4 * P + g) ^ swz_red<NU>(rho));
+            *reinterpret_cast<u32x4*>(&redw[ro]) = u32x4{o0, o1, o2, o3};
+            if constexpr (LOX) {
+              const u32x4 ol = {pack_bf16(acc[2 * P][0] - bf16_lo(o0), acc[2 * P][1] - bf16_hi(o0)),
+                                pack_bf16(acc[2 * P][2] - bf16_lo(o1), acc[2 * P][3] - bf16_hi(o1)),
+                                pack_bf16(acc[2 * P + 1][0] - bf16_lo(o2), acc[2 * P + 1][1] - bf16_hi(o2)),
+                                pack_bf16(acc[2 * P + 1][2] - bf16_lo(o3), acc[2 * P + 1][3] - bf16_hi(o3))};
+              *reinterpret_cast<u32x4*>(&redwl[ro]) = ol;
+            }
           }
         } else {
 #pragma unroll

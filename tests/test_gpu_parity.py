@@ -394,12 +394,13 @@ def _bf16_operand_path(q, k, P):
 
 
 @pytest.mark.parametrize("d,P,n", [(8, 4, 2000), (8, 4, 4096), (8, 5, 2000), (8, 5, 4096),
-                                   (16, 4, 2000), (16, 4, 4096), (16, 5, 2000), (16, 5, 4096)])
+                                   (16, 4, 2000), (16, 4, 4096), (16, 5, 2000), (16, 5, 4096),
+                                   (32, 4, 4096), (32, 5, 2000), (64, 4, 4096)])
 def test_prefill_bf16_operand_path_small_heads(d, P, n):
-    """Small heads forced onto the bf16 operand path (a query coordinate of
-    1000, the matching key coordinate x 1e-4) over several readout windows:
-    few rows per output, so the path carries its readout operand and wave
-    partials as bf16 value + residual pairs."""
+    """Heads forced onto the bf16 operand path (a query coordinate of 1000,
+    the matching key coordinate x 1e-4) over several readout windows; at
+    d <= 32 the path carries its readout operand and wave partials as bf16
+    value + residual pairs (few rows per output at small d)."""
     note(f"bf16 operand path d={d} P={P} n={n}")
     q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 19000 + d + P)
     q = q.copy()
