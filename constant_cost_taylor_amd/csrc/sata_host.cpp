@@ -43,6 +43,7 @@ struct sata_basis {
   PrefillLayout lay[2];                      // [0] float32 inputs, [1] bfloat16 inputs
   std::vector<void*> allocations;
   void* scratch = nullptr;                   // device address of the no-alloc decode scratch
+  int ec = 0;                                // c = c' 2^ec with c' in [1, 2) (bf16 prefill layout)
 };
 
 namespace {
@@ -291,7 +292,11 @@ int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& ran
           kside[blk * 16 + 4 * g + j] = static_cast<uint32_t>(prow) | (static_cast<uint32_t>(xrow) << 16);
           if (run.row[j] >= 0) {
             rowinfo[blk * 16 + 4 * g + j] = static_cast<uint32_t>(run.row[j] + 1);
-            rweight[blk * 16 + 4 * g + j] = b->weight[run.row[j]];
+            // w_m with c' = c 2^-ec (the staged queries carry the 2^-ec)
+            const int po = pp + 1;   // order of the child row
+            rweight[blk * 16 + 4 * g + j] = static_cast<float>(
+                static_cast<double>(b->mult[po][run.row[j] - b->offset[po]]) /
+                (static_cast<double>(factorial(po)) * std::pow(std::ldexp(b->c, -b->ec), po)));
           }
         }
         continue;
@@ -490,6 +495,11 @@ static int build_basis_impl(int d_k, int P, double c, bool upload_tables, sata_b
   b->d = d_k;
   b->P = P;
   b->c = c;
+  {
+    int e = 0;
+    (void)std::frexp(c, &e);   // c = f 2^e, f in [0.5, 1)
+    b->ec = (e - 1 >= -30 && e - 1 <= 30) ? e - 1 : 0;
+  }
   std::unordered_map<uint32_t, int64_t> rank;
   int64_t total = 0;
   for (int p = 0; p < P; ++p) {
@@ -660,8 +670,8 @@ static int prefill_impl(const sata_basis* b, int B, int H, int n, int d_v, int d
   for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
     const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
     sata::IntraArgs ia{q, k, v, pw, n, t0, w, b->P, inv_c, lens};
-    sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P, lens};
-    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c, b->P, lens};
+    sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P, lens, b->ec};
+    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c, b->P, lens, b->ec};
     if (bf16) {
       if (sata::launch_prefill_b16(b->d, static_cast<int>(BH), sa, s) != hipSuccess) return SATA_ERR_HIP;
       if (sata::launch_prefill_intra(b->d, true, static_cast<int>(BH), ia, s) != hipSuccess)

@@ -103,7 +103,9 @@ constexpr int col_blocks(int dv) { return (dv + 1 + 15) / 16; }
 //       child coordinate (high 16 bits) of lane row j;
 //   qside: i1 | i2 << 8 | c0 << 16 | i3 << 24 of the run of lane group g
 //       (index d = the constant 1);
-//   rowinfo: canonical row + 1, 0 = pad;  rweight: w_m of the row, 0 = pad;
+//   rowinfo: canonical row + 1, 0 = pad;  rweight: w_m of the row computed
+//       with c' = c 2^-ec in place of c (0 = pad), the queries being staged
+//       times 2^-ec;
 //   parents[tile][slot]: key-table rows r1 | r2 << 8 | r3 << 16 of the
 //       factors of each parent slot (r3 = the ones row for order 2).
 // Both: nslot[tile] = number of parent slots of the tile.
@@ -168,6 +170,7 @@ struct ScanArgs {
   float inv_c;           // 1 / c
   int P;                 // orders 0..P-1
   const int32_t* lens;   // [BH] tokens of each head (device), or null: n_total for every head
+  int ec;                // c = c' 2^ec, c' in [1, 2): bf16 inputs fold 2^-ec into the staged queries
 };
 
 struct IntraArgs {
@@ -193,6 +196,7 @@ struct ReduceArgs {
   float inv_c;           // 1 / c
   int P;                 // orders 0..P-1 (with the max-abs values, selects the bf16 scan's operand type)
   const int32_t* lens;
+  int ec;                // as in ScanArgs
 };
 
 struct DecodeArgs {

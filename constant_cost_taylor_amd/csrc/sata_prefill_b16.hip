@@ -143,7 +143,7 @@ struct HalfScales {
   int sb;
 };
 
-__device__ __forceinline__ HalfScales half_scales(const float* amax, int P) {
+__device__ __forceinline__ HalfScales half_scales(const float* amax, int P, int ec) {
   float mq = 0.f, mk = 0.f, mv = 0.f;
 #pragma unroll 4
   for (int s = 0; s < kAmaxSplit; ++s) {
@@ -155,6 +155,7 @@ __device__ __forceinline__ HalfScales half_scales(const float* amax, int P) {
   int eq = 0, ekk = 0, e = 0;
   if (mq > 0.f) (void)frexpf(mq, &eq);    // mq < 2^eq
   if (mk > 0.f) (void)frexpf(mk, &ekk);   // mk < 2^ekk
+  eq -= ec;                               // the staged queries carry 2^-ec (the power of two of c)
   h.ek = (ekk - eq) / 2;
   h.ev = 0;
   if (mv > 0.f) {
@@ -170,8 +171,8 @@ __device__ __forceinline__ HalfScales half_scales(const float* amax, int P) {
   return h;
 }
 
-__device__ __forceinline__ const HalfScales head_scales(const PrefillWs& ws, int head, int P) {
-  return half_scales(ws.amax + static_cast<int64_t>(head) * kAmaxSplit * 4, P);
+__device__ __forceinline__ const HalfScales head_scales(const PrefillWs& ws, int head, int P, int ec) {
+  return half_scales(ws.amax + static_cast<int64_t>(head) * kAmaxSplit * 4, P, ec);
 }
 
 // ---------------------------------------------------------------------------
@@ -250,15 +251,17 @@ __global__ __launch_bounds__(256) void prefill_stage(ScanArgs a) {
   const int ch = blockIdx.x;
   const int head = blockIdx.y;
   const int tid = threadIdx.x;
-  const HalfScales hs = head_scales(a.ws, head, a.P);
+  const HalfScales hs = head_scales(a.ws, head, a.P, a.ec);
   const int nvalid = max(0, min(L, head_tokens(a.lens, head, a.t0, a.nw, a.n_total) - ch * L));
   const int64_t tok0 = a.t0 + static_cast<int64_t>(ch) * L;
   const int nchp = a.ws.nwp / L;
-  float mul[3] = {1.f, 1.f, 1.f};   // k, v, q
+  // k, v, q; q also takes 2^-ec, the power of two of c (the row weights
+  // of this layout use c 2^-ec), on both operand paths
+  float mul[3] = {1.f, 1.f, ldexpf(1.f, -a.ec)};
   if (hs.safe) {
     mul[0] = ldexpf(1.f, -hs.ek);
     mul[1] = ldexpf(1.f, -hs.ev);
-    mul[2] = ldexpf(1.f, hs.ek);
+    mul[2] = ldexpf(1.f, hs.ek - a.ec);
   }
   uint16_t* rec = a.ws.stg + (static_cast<int64_t>(head) * nchp + ch) * (4 * DK * L);
   const uint16_t* src[3] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(256) void prefill_stage(ScanArgs a) {
         vraw[t][8 * u + 2 * j + 1] = hi;
       }
       const float mx = x == 0 ? mul[0] : x == 1 ? mul[1] : mul[2];   // no indexed private array
-      o[j] = hs.safe ? pack_f16(lo * mx, hi * mx) : wj;
+      o[j] = hs.safe ? pack_f16(lo * mx, hi * mx) : (x == 2 && a.ec != 0 ? pack_bf16(lo * mx, hi * mx) : wj);
       tr[x][(8 * u + 2 * j) * TS + t] = static_cast<uint16_t>(o[j] & 0xffffu);
       tr[x][(8 * u + 2 * j + 1) * TS + t] = static_cast<uint16_t>(o[j] >> 16);
     }
@@ -1084,7 +1087,7 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
   __shared__ __attribute__((aligned(16))) unsigned char lds[CfgS<DK>::LDS_B];
   // no tokens of this head in the window: the state is left as it is
   if (head_tokens(a.lens, blockIdx.y, a.t0, a.nw, a.n_total) == 0) return;
-  const HalfScales hs = head_scales(a.ws, blockIdx.y, a.P);
+  const HalfScales hs = head_scales(a.ws, blockIdx.y, a.P, a.ec);
   if (hs.safe)
     scan_tile<DK, true, P5>(a, hs, lds);
   else
@@ -1115,7 +1118,7 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
   const int nt = a.n_tiles;
   const int ntok = min(TB, head_tokens(a.lens, head, a.t0, a.nw, a.n_total) - t0);   // may be <= 0
   const int nout = min(TB, a.nw - t0);   // rows of the block; those past ntok are written as zeros
-  const HalfScales hs = head_scales(a.ws, head, a.P);
+  const HalfScales hs = head_scales(a.ws, head, a.P, a.ec);
   const float rscale = hs.safe ? ldexpf(1.f, hs.ev) : 1.f;   // value-column records carry 2^-ev
   const float* intra = a.ws.intra + static_cast<int64_t>(head) * nwp * DVP;
   const float* carry = a.ws.carry + static_cast<int64_t>(head) * ((nwp + T - 1) / T) * DVP;

@@ -473,6 +473,27 @@ def test_packed_state_layout_c_abi(d, P, dtype):
         assert O.row_normwise_error(gd[:, h], ref[n:]) <= tol, h
 
 
+@pytest.mark.parametrize("d,P,s", [(32, 4, 1024.0), (64, 4, 1024.0), (16, 5, 64.0), (64, 4, 1.0 / 64.0),
+                                   (32, 5, 3.0 * 256.0)])
+def test_prefill_bf16_logit_scale(d, P, s):
+    """q scaled by s with c = s (the logits of unit rows): the power of two of
+    c is folded into the staged queries and the row weights, so such heads
+    keep the f16 operand path; parity against the oracle at that c."""
+    note(f"logit scale d={d} P={P} c={s}")
+    n = 1100
+    q, k, v = W.make_qkv(1, 2, n, d, d, W.F32, 29000 + d + P)
+    q = _rows_bf16(q * s)
+    k, v = _rows_bf16(k), _rows_bf16(v)
+    b = SA.build_basis(d, P, s)
+    out, _ = run_prefill(b, q, k, v, W.BF16)
+    got = out.cpu().numpy()
+    for h in range(2):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, s)
+        err = O.row_normwise_error(got[0, h], ref)
+        note(f"  head {h}: {err:.3e}")
+        assert err <= TOL[W.BF16], h
+
+
 def test_two_streams_share_a_basis():
     """Prefill and decode of two state batches on two streams at once, with
     one basis, give bit for bit what they give one after the other."""
