@@ -255,7 +255,11 @@ def prefill(basis: Basis, q, k, v, state=None, out=None, ws=None, lengths=None):
     contiguous, on the GPU). state: [B*H, stride] float32 with stride >= state_floats
     (new_state; zeros = empty prefix), read and written. lengths: optional int32
     tensor of B*H per-head token counts on the GPU (head h takes its first
-    lengths[h] tokens; its output rows past that are zeros). Returns
+    lengths[h] tokens; its output rows past that are zeros). ws: optional
+    workspace, by default prefill_workspace_bytes; a larger one selects the
+    least-time plan, a smaller one (down to prefill_workspace_bytes(basis, 1,
+    1, min(n, 512), ...)) runs the heads in more groups or the tokens in more
+    windows. Returns
     (out [B, H, n, d_v] float32, state)."""
     import torch
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:

@@ -385,11 +385,9 @@ int check_device(const sata_basis* b) {
   return dev == b->device ? SATA_OK : SATA_ERR_INVALID_ARG;
 }
 
-// Tokens per prefill window and the workspace it needs (records of one
-// window; the window is bounded so that they fit the workspace cap: 16 GiB,
-// or the byte count in the environment variable SATA_PREFILL_WS_CAP, read at
-// every call, so the workspace query and the prefill call must see the same
-// value).
+// Upper bound on the prefill workspace: 16 GiB, or the byte count in the
+// environment variable SATA_PREFILL_WS_CAP, read at every call (the workspace
+// query and the prefill call must see the same value).
 size_t prefill_ws_cap() {
   const char* e = std::getenv("SATA_PREFILL_WS_CAP");
   if (e && *e) {
@@ -400,7 +398,13 @@ size_t prefill_ws_cap() {
   return size_t(16) << 30;
 }
 
+// How a prefill call is cut: the heads in `groups` groups of at most `heads`
+// heads each (sizes differ by at most one), each group's tokens in call
+// windows of nw tokens.  Every kernel of the prefill runs once per (group,
+// window); the workspace holds one group's records of one window.
 struct PrefillPlan {
+  int64_t groups = 0;
+  int64_t heads = 0;      // heads of the largest group
   int64_t nw = 0;         // tokens per window
   int64_t nwp = 0;        // nw rounded up to 64
   size_t rec_bytes = 0;   // per-tile records
@@ -412,38 +416,99 @@ struct PrefillPlan {
   size_t vsum_bytes = 0;  // per-chunk sums of v (bfloat16 inputs)
   size_t recs_bytes = 0;  // per-chunk scales of 16-bit records (bfloat16 inputs, d >= 32)
   size_t total = 0;
+  double cost = 0.0;
 };
 
-PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype) {
+// Workspace of G heads and windows of nw tokens.
+PrefillPlan prefill_sizes(const sata_basis* b, int64_t G, int64_t nw, int dtype) {
   const bool bf16 = dtype == SATA_BF16;
   const int nt = b->lay[dtype].n_tiles;
   const int d = b->d;
   const int dvp = sata::padded_dv(d);
   const int T = sata::prefill_window(bf16);
   const size_t rec_elt = sata::prefill_bf16_records(d, bf16) ? 2 : 4;
-  // bytes per token of window: records, intra, staged tables, chunk sums
-  const size_t per_token =
-      bf16 ? static_cast<size_t>(BH) * (nt * (d * rec_elt + 4) + nt / 16 + 1 + dvp * 4 + 8 * d + dvp)
-           : static_cast<size_t>(BH) * dvp * (nt * rec_elt + 4);
-  int64_t w = static_cast<int64_t>(prefill_ws_cap() / per_token);
-  // windows start on readout-window boundaries
-  w = std::max<int64_t>(T, (w / T) * T);
-  const int64_t nround = std::max<int64_t>(64, (n + 63) / 64 * 64);
   PrefillPlan pl;
-  pl.nw = std::min(w, nround);
-  pl.nwp = (pl.nw + 63) / 64 * 64;
-  pl.rec_bytes = static_cast<size_t>(BH) * nt * (bf16 ? d : dvp) * pl.nwp * rec_elt;
-  pl.recz_bytes = bf16 ? static_cast<size_t>(BH) * nt * pl.nwp * 4 : 0;
-  pl.intra_bytes = static_cast<size_t>(BH) * dvp * pl.nwp * 4;
-  pl.carry_bytes = static_cast<size_t>(BH) * ((pl.nwp + T - 1) / T) * dvp * 4;
-  pl.amax_bytes = bf16 ? static_cast<size_t>(BH) * sata::kAmaxSplit * 4 * 4 : 0;
-  pl.stg_bytes = bf16 ? static_cast<size_t>(BH) * pl.nwp * 4 * d * 2 : 0;
-  pl.vsum_bytes = bf16 ? static_cast<size_t>(BH) * (pl.nwp / 64) * dvp * 4 : 0;
-  pl.recs_bytes = rec_elt == 2 ? static_cast<size_t>(BH) * nt * (pl.nwp / 64) * 4 : 0;
+  pl.heads = G;
+  pl.nw = nw;
+  pl.nwp = (nw + 63) / 64 * 64;
+  pl.rec_bytes = static_cast<size_t>(G) * nt * (bf16 ? d : dvp) * pl.nwp * rec_elt;
+  pl.recz_bytes = bf16 ? static_cast<size_t>(G) * nt * pl.nwp * 4 : 0;
+  pl.intra_bytes = static_cast<size_t>(G) * dvp * pl.nwp * 4;
+  pl.carry_bytes = static_cast<size_t>(G) * ((pl.nwp + T - 1) / T) * dvp * 4;
+  pl.amax_bytes = bf16 ? static_cast<size_t>(G) * sata::kAmaxSplit * 4 * 4 : 0;
+  pl.stg_bytes = bf16 ? static_cast<size_t>(G) * pl.nwp * 4 * d * 2 : 0;
+  pl.vsum_bytes = bf16 ? static_cast<size_t>(G) * (pl.nwp / 64) * dvp * 4 : 0;
+  pl.recs_bytes = rec_elt == 2 ? static_cast<size_t>(G) * nt * (pl.nwp / 64) * 4 : 0;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   pl.total = up(pl.rec_bytes) + up(pl.recz_bytes) + up(pl.intra_bytes) + up(pl.carry_bytes) +
              up(pl.amax_bytes) + up(pl.stg_bytes) + up(pl.vsum_bytes) + up(pl.recs_bytes);
   return pl;
+}
+
+// Plans of the prefill, in units of one scan chunk of one workgroup: a scan
+// launch of g heads runs ceil(g * tiles / 256) rounds of workgroups on the
+// 256 compute units; each round costs its chunks plus about 5 for the state
+// tile's load and store (once per window); every (group, window) adds about
+// 10 for its six launches.  Head groups thus cost only the rounding of the
+// rounds, while windows cost a state reload each.  For each group count k the
+// longest window that fits `budget` is taken (groups = 0 when not even one
+// head and one readout window fit).  Of the plans whose modelled time is
+// within (1 + slack) of the least and whose groups each keep the 256 units
+// busy for at least 8 rounds (the model ignores the under-filled kernels of
+// smaller groups: 4 heads at d = 64 in two groups ran 8 % slower), the one
+// with the smallest workspace is returned (ties: the faster); the least-time
+// plan always qualifies.  The workspace query passes slack 0.02, so the
+// default workspace stays small where more groups cost nothing (256 heads of
+// 4096 tokens at d = 64: 2.5 instead of 14.8 GB at the same speed); the call
+// passes 0, so a workspace of the queried size selects the same plan and a
+// larger one the least-time plan.
+PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype, size_t budget, double slack) {
+  const bool bf16 = dtype == SATA_BF16;
+  const int64_t nt = b->lay[dtype].n_tiles;
+  const int64_t T = sata::prefill_window(bf16);
+  const int64_t L = sata::prefill_chunk(bf16);
+  constexpr int64_t kCUs = 256;
+  constexpr double kStateLoad = 5.0, kLaunches = 10.0;
+  const int64_t nround = std::max<int64_t>(64, (n + 63) / 64 * 64);
+  const int64_t chunks = (n + L - 1) / L;
+  const int64_t m = (nround + T - 1) / T;
+  auto window = [&](int64_t i) { return std::min<int64_t>(i * T, nround); };
+  std::vector<PrefillPlan> cands;
+  double least = 0.0;
+  int64_t last_g = -1;
+  for (int64_t k = 1; k <= BH; ++k) {
+    const int64_t G = (BH + k - 1) / k;
+    if (G == last_g) continue;  // same largest group with more launches
+    last_g = G;
+    // the longest window that fits: min(i T, nround) for the largest i (the
+    // workspace grows with the window)
+    if (prefill_sizes(b, G, window(1), dtype).total > budget) continue;
+    int64_t lo = 1, hi = m;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (prefill_sizes(b, G, window(mid), dtype).total <= budget)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int64_t w = window(lo);
+    PrefillPlan pl = prefill_sizes(b, G, w, dtype);
+    const int64_t small = BH / k, nbig = BH - small * k;
+    const int64_t rounds = nbig * ((G * nt + kCUs - 1) / kCUs) + (k - nbig) * ((small * nt + kCUs - 1) / kCUs);
+    const int64_t windows = (n + w - 1) / w;
+    pl.groups = k;
+    pl.cost = static_cast<double>(rounds) * (static_cast<double>(chunks) + kStateLoad * windows) +
+              kLaunches * static_cast<double>(k * windows);
+    least = cands.empty() ? pl.cost : std::min(least, pl.cost);
+    cands.push_back(pl);
+  }
+  PrefillPlan best;
+  for (const PrefillPlan& pl : cands) {
+    const bool filled = pl.groups == 1 || (BH / pl.groups) * nt >= 8 * kCUs;
+    if (pl.cost > least * (1.0 + slack) || (pl.cost > least && !filled)) continue;
+    if (best.groups == 0 || pl.total < best.total || (pl.total == best.total && pl.cost < best.cost)) best = pl;
+  }
+  return best;
 }
 
 // Decode workspace: value partials [S][tiles][d_v] then den partials
@@ -621,7 +686,13 @@ int sata_prefill_workspace(const sata_basis* b, int B, int H, int n, int d_v, in
   if (!b || !bytes || B < 1 || H < 1 || n < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
-  *bytes = n == 0 ? 0 : prefill_plan(b, static_cast<int64_t>(B) * H, n, dtype).total;
+  if (n == 0) {
+    *bytes = 0;
+    return SATA_OK;
+  }
+  const PrefillPlan pl = prefill_plan(b, static_cast<int64_t>(B) * H, n, dtype, prefill_ws_cap(), 0.02);
+  if (pl.groups == 0) return SATA_ERR_WORKSPACE;
+  *bytes = pl.total;
   return SATA_OK;
 }
 
@@ -639,8 +710,9 @@ static int prefill_impl(const sata_basis* b, int B, int H, int n, int d_v, int d
   if (state_stride < static_cast<int64_t>(d_v + 1) * b->D) return SATA_ERR_INVALID_ARG;
   const int64_t BH = static_cast<int64_t>(B) * H;
   if (BH > 65535) return SATA_ERR_UNSUPPORTED;  // grid y limit
-  const PrefillPlan pl = prefill_plan(b, BH, n, dtype);
-  if (!ws || ws_bytes < pl.total) return SATA_ERR_WORKSPACE;
+  if (!ws) return SATA_ERR_WORKSPACE;
+  const PrefillPlan pl = prefill_plan(b, BH, n, dtype, std::min(ws_bytes, prefill_ws_cap()), 0.0);
+  if (pl.groups == 0) return SATA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
   if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -667,24 +739,34 @@ static int prefill_impl(const sata_basis* b, int B, int H, int n, int d_v, int d
   pw.vsum = reinterpret_cast<float*>(carve(pl.vsum_bytes));
   pw.recs = reinterpret_cast<float*>(carve(pl.recs_bytes));
   const float inv_c = static_cast<float>(1.0 / b->c);
-  for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
-    const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
-    sata::IntraArgs ia{q, k, v, pw, n, t0, w, b->P, inv_c, lens};
-    sata::ScanArgs sa{q, k, v, state, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P, lens, b->ec};
-    sata::ReduceArgs ra{pw, out, n, t0, w, lay.n_tiles, inv_c, b->P, lens, b->ec};
-    if (bf16) {
-      if (sata::launch_prefill_b16(b->d, static_cast<int>(BH), sa, s) != hipSuccess) return SATA_ERR_HIP;
-      if (sata::launch_prefill_intra(b->d, true, static_cast<int>(BH), ia, s) != hipSuccess)
-        return SATA_ERR_HIP;
-      if (sata::launch_reduce_b16(b->d, static_cast<int>(BH), ra, s) != hipSuccess) return SATA_ERR_HIP;
-    } else {
-      if (sata::launch_prefill_intra(b->d, false, static_cast<int>(BH), ia, s) != hipSuccess)
-        return SATA_ERR_HIP;
-      if (sata::launch_prefill_scan(b->d, false, static_cast<int>(BH), sa, s) != hipSuccess)
-        return SATA_ERR_HIP;
-      if (sata::launch_prefill_reduce(b->d, false, static_cast<int>(BH), ra, s) != hipSuccess)
-        return SATA_ERR_HIP;
+  const size_t esz = bf16 ? 2 : 4;
+  const int64_t small = BH / pl.groups, nbig = BH - small * pl.groups;
+  int64_t h0 = 0;
+  for (int64_t gi = 0; gi < pl.groups; ++gi) {
+    const int64_t G = small + (gi < nbig ? 1 : 0);
+    const int gh = static_cast<int>(G);
+    const char* qg = static_cast<const char*>(q) + h0 * n * b->d * esz;
+    const char* kg = static_cast<const char*>(k) + h0 * n * b->d * esz;
+    const char* vg = static_cast<const char*>(v) + h0 * n * d_v * esz;
+    float* og = out + h0 * n * d_v;
+    float* sg = state + h0 * stride;
+    const int32_t* lg = lens ? lens + h0 : nullptr;
+    for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
+      const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
+      sata::IntraArgs ia{qg, kg, vg, pw, n, t0, w, b->P, inv_c, lg};
+      sata::ScanArgs sa{qg, kg, vg, sg, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P, lg, b->ec};
+      sata::ReduceArgs ra{pw, og, n, t0, w, lay.n_tiles, inv_c, b->P, lg, b->ec};
+      if (bf16) {
+        if (sata::launch_prefill_b16(b->d, gh, sa, s) != hipSuccess) return SATA_ERR_HIP;
+        if (sata::launch_prefill_intra(b->d, true, gh, ia, s) != hipSuccess) return SATA_ERR_HIP;
+        if (sata::launch_reduce_b16(b->d, gh, ra, s) != hipSuccess) return SATA_ERR_HIP;
+      } else {
+        if (sata::launch_prefill_intra(b->d, false, gh, ia, s) != hipSuccess) return SATA_ERR_HIP;
+        if (sata::launch_prefill_scan(b->d, false, gh, sa, s) != hipSuccess) return SATA_ERR_HIP;
+        if (sata::launch_prefill_reduce(b->d, false, gh, ra, s) != hipSuccess) return SATA_ERR_HIP;
+      }
     }
+    h0 += G;
   }
   return SATA_OK;
 }

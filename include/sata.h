@@ -110,11 +110,22 @@ int64_t sata_state_floats(const sata_basis* basis, int d_v);
  * reads or writes.  Returns -1 on a null handle or d_v != d_k. */
 int64_t sata_state_stride(const sata_basis* basis, int d_v);
 
-/* Device workspace in bytes that sata_prefill needs for these sizes.  Long
- * sequences are processed in windows whose per-token records fit a cap of
- * 16 GiB; the environment variable SATA_PREFILL_WS_CAP (bytes, read at every
- * call: keep it unchanged between this query and the prefill) lowers or
- * raises it, trading workspace for one state reload per window. */
+/* Device workspace in bytes for sata_prefill at these sizes.  A prefill runs
+ * its heads in groups and each group's tokens in call windows (multiples of
+ * 512 tokens for bfloat16 inputs); the workspace holds the records of one
+ * group and window.  The call picks, from the workspace it is given, the cut
+ * of least modelled time that fits: more, smaller groups cost little while
+ * each group still fills the chip's 256 compute units, while every extra
+ * window reloads the state once.  The size returned here is that of the
+ * smallest cut within 2 % of the least modelled time whose groups still fill
+ * the chip (256 heads of 4096 tokens at d = 64, P = 4: 2.5 GB where a single
+ * group needs 14.8 GB, measured as fast); a larger workspace selects the
+ * least-time cut, a smaller one (down to sata_prefill_workspace(basis, 1, 1,
+ * min(n, 512), ...) bytes, which always works) a slower one.  All sizes are
+ * capped at 16 GiB, or at the byte count in the environment variable
+ * SATA_PREFILL_WS_CAP (read at every call: keep it unchanged between this
+ * query and the prefill).  SATA_ERR_WORKSPACE when the cap is below that
+ * minimum. */
 int sata_prefill_workspace(const sata_basis* basis, int B, int H, int n, int d_v, int dtype,
                            size_t* bytes);
 
@@ -132,8 +143,10 @@ int sata_prefill_workspace(const sata_basis* basis, int B, int H, int n, int d_v
  *         (all zeros = empty prefix) is read and the state after the n tokens
  *         is written back.  Nothing outside B*H*sata_state_floats floats is
  *         touched.
- *   ws:   device workspace of at least sata_prefill_workspace bytes, 256-byte
- *         aligned; its contents on entry do not matter.
+ *   ws:   device workspace of ws_bytes bytes, 256-byte aligned: at least
+ *         the one-head, one-window minimum given at sata_prefill_workspace
+ *         (whose returned size is the default); its contents on entry do
+ *         not matter.
  * Arithmetic: float32 inputs run in fp32 throughout.  bfloat16 inputs run the
  * feature products and readout/update contractions on 16-bit MFMA operands
  * (f16 after exact per-head power-of-two scaling when the inputs' ranges

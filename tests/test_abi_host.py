@@ -86,6 +86,21 @@ def test_host_only_handle_rejects_compute():
     assert SA.status_string(SA.SATA_ERR_HIP).startswith("SATA_ERR_HIP")
 
 
+def test_prefill_workspace_plans(monkeypatch):
+    """The fastest plan's workspace is the largest; a cap down to the
+    one-head, one-readout-window minimum still yields a plan, below it none."""
+    b = SA.build_basis(64, 4, 1.0, host_only=True)
+    least = SA.prefill_workspace_bytes(b, 1, 1, 512, 64, SA.SATA_BF16)
+    full = SA.prefill_workspace_bytes(b, 8, 32, 4096, 64, SA.SATA_BF16)
+    assert least < SA.prefill_workspace_bytes(b, 1, 2, 512, 64, SA.SATA_BF16) < full
+    monkeypatch.setenv("SATA_PREFILL_WS_CAP", str(least))
+    assert SA.prefill_workspace_bytes(b, 8, 32, 4096, 64, SA.SATA_BF16) == least
+    monkeypatch.setenv("SATA_PREFILL_WS_CAP", str(least - 1))
+    with pytest.raises(SA.SataError) as e:
+        SA.prefill_workspace_bytes(b, 8, 32, 4096, 64, SA.SATA_BF16)
+    assert e.value.status == SA.SATA_ERR_WORKSPACE
+
+
 def test_workspace_sizes():
     b = SA.build_basis(64, 4, 1.0, host_only=True)
     assert SA.prefill_workspace_bytes(b, 1, 4, 0, 64, SA.SATA_BF16) == 0

@@ -265,7 +265,8 @@ def test_prefill_many_windows(d, P, dtype, n, monkeypatch):
     q, k, v = W.make_qkv(1, 2, n, d, d, dtype, 15000 + d)
     code = SA.SATA_BF16 if dtype == W.BF16 else SA.SATA_F32
     full = SA.prefill_workspace_bytes(b, 1, 2, n, d, code)
-    monkeypatch.setenv("SATA_PREFILL_WS_CAP", str(max(1, full // 6)))
+    least = SA.prefill_workspace_bytes(b, 1, 1, min(n, 512), d, code)
+    monkeypatch.setenv("SATA_PREFILL_WS_CAP", str(max(least, full // 6)))
     small = SA.prefill_workspace_bytes(b, 1, 2, n, d, code)
     note(f"many windows d={d} {dtype} n={n} ws {full} -> {small}")
     assert small < full
@@ -274,6 +275,82 @@ def test_prefill_many_windows(d, P, dtype, n, monkeypatch):
     for h in range(2):
         ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
         assert O.row_normwise_error(got[0, h], ref) <= TOL[dtype], h
+
+
+@pytest.mark.parametrize("d,P,dtype", [(16, 4, W.BF16), (64, 4, W.BF16), (32, 5, W.BF16), (16, 4, W.F32)])
+def test_prefill_head_groups_bitwise(d, P, dtype):
+    """A workspace with room for two heads runs five heads (with and without
+    per-head lengths) as groups of 2, 2 and 1: outputs and states are
+    bit-identical to the one-group call, and the outputs match the oracle."""
+    # one readout window (bf16: 512 tokens, fp32: 64-token records), so that
+    # only head groups can shrink the workspace
+    B, H, n = (1, 5, 480) if dtype == W.BF16 else (1, 5, 64)
+    lens = [480, 1, 300, 0, 417] if dtype == W.BF16 else [64, 1, 37, 0, 63]
+    note(f"head groups d={d} P={P} {dtype} H={H} n={n}")
+    q, k, v = W.make_qkv(B, H, n, d, d, dtype, 28000 + d + P)
+    b = SA.build_basis(d, P, 1.0)
+    code = SA.SATA_BF16 if dtype == W.BF16 else SA.SATA_F32
+    full = SA.prefill_workspace_bytes(b, B, H, n, d, code)
+    two = SA.prefill_workspace_bytes(b, 1, 2, n, d, code)
+    assert two < full
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    res = []
+    for nbytes in (full, two):
+        for lengths in (None, lt):
+            out, st = SA.prefill(b, qd, kd, vd, ws=SA.workspace(nbytes), lengths=lengths)
+            torch.cuda.synchronize()
+            res.append((out.clone(), st.clone()))
+    for i in range(2):
+        assert torch.equal(res[i][0], res[2 + i][0]) and torch.equal(res[i][1], res[2 + i][1]), i
+    got = res[2][0].cpu().numpy()
+    for h in (0, 4):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
+        assert O.row_normwise_error(got[0, h], ref) <= TOL[dtype], h
+    gl = res[3][0].cpu().numpy()
+    for h, L in enumerate(lens):
+        assert np.all(gl[0, h, L:] == 0.0), h
+        if L:
+            ref = oracle_rows(q[0, h, :L], k[0, h, :L], v[0, h, :L], P, 1.0)
+            assert O.row_normwise_error(gl[0, h, :L], ref) <= TOL[dtype], (h, L)
+
+
+@pytest.mark.parametrize("d,P,dtype", [(32, 4, W.BF16), (16, 4, W.F32)])
+def test_prefill_workspace_down_to_minimum(d, P, dtype):
+    """Workspaces from the fastest plan's down to the one-head, one-window
+    minimum (head groups, windows or both): every output matches the oracle,
+    every state the fastest plan's; one byte less than the minimum is refused
+    with nothing written."""
+    B, H, n = 1, 5, 1300
+    note(f"workspace plans d={d} P={P} {dtype} H={H} n={n}")
+    q, k, v = W.make_qkv(B, H, n, d, d, dtype, 29000 + d)
+    b = SA.build_basis(d, P, 1.0)
+    code = SA.SATA_BF16 if dtype == W.BF16 else SA.SATA_F32
+    sizes = [SA.prefill_workspace_bytes(b, B, H, n, d, code), SA.prefill_workspace_bytes(b, 1, 3, n, d, code),
+             SA.prefill_workspace_bytes(b, 1, 2, 700, d, code), SA.prefill_workspace_bytes(b, 1, 1, 512, d, code)]
+    assert sizes == sorted(sizes, reverse=True) and sizes[-1] < sizes[0]
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    refs = {h: oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0) for h in (0, 2, 4)}
+    st0 = None
+    for nbytes in sizes:
+        out, st = SA.prefill(b, qd, kd, vd, ws=SA.workspace(nbytes))
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for h, ref in refs.items():
+            assert O.row_normwise_error(got[0, h], ref) <= TOL[dtype], (nbytes, h)
+        if st0 is None:
+            st0 = st.clone()
+        else:
+            assert torch.allclose(st, st0, rtol=1e-5, atol=1e-6 * float(st0.abs().max())), nbytes
+    # below the minimum (the fp32 minimum is one 64-token record window)
+    least = SA.prefill_workspace_bytes(b, 1, 1, 64, d, code) if dtype == W.F32 else sizes[-1]
+    out = torch.full((B, H, n, d), 7.0, device="cuda")
+    st = SA.new_state(b, B * H)
+    with pytest.raises(SA.SataError) as e:
+        SA.prefill(b, qd, kd, vd, state=st, out=out, ws=SA.workspace(least - 256))
+    assert e.value.status == SA.SATA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert float(out.min()) == 7.0 and float(st.abs().sum()) == 0.0
 
 
 def test_misaligned_and_host_only_rejected():
