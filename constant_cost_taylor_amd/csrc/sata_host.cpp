@@ -41,6 +41,7 @@ struct sata_basis {
   uint32_t* d_rows = nullptr;
   float* d_weight = nullptr;
   PrefillLayout lay[2];                      // [0] float32 inputs, [1] bfloat16 inputs
+  PrefillLayout lay_small;                   // float32 inputs, few heads (rb = 0: none)
   std::vector<void*> allocations;
   void* scratch = nullptr;                   // device address of the no-alloc decode scratch
   int ec = 0;                                // c = c' 2^ec with c' in [1, 2) (bf16 prefill layout)
@@ -196,10 +197,9 @@ std::vector<Run> build_runs(const sata_basis& b, const std::unordered_map<uint32
 //    the row weights w_m are applied to the state when the scan rounds it to
 //    its readout operand.
 int build_layout(sata_basis* b, const std::unordered_map<uint32_t, int64_t>& rank, bool bf16,
-                 bool upload_tables, PrefillLayout* lay) {
-  const int rb = sata::prefill_rb(b->d, bf16);
-  const int per_tile = sata::prefill_runs_per_tile(b->d, bf16);
-  const int max_slots = sata::prefill_slots(b->d, bf16);
+                 bool upload_tables, PrefillLayout* lay, int rb) {
+  const int per_tile = sata::prefill_runs_per_tile_rb(rb, bf16);
+  const int max_slots = sata::prefill_slots_rb(rb, bf16);
   const int kstr = sata::prefill_kstride(bf16);
   const int xk_zero = 2 * b->d * kstr;
   const bool v2 = bf16;
@@ -419,10 +419,19 @@ struct PrefillPlan {
   double cost = 0.0;
 };
 
+// The prefill tiling of a call over BH heads: for float32 inputs, the small
+// tiling when the default one gives too few workgroups to fill the chip.
+const PrefillLayout& prefill_layout(const sata_basis* b, int dtype, int64_t BH) {
+  const PrefillLayout& lay = b->lay[dtype];
+  if (dtype == SATA_F32 && b->lay_small.rb > 0 && BH * lay.n_tiles < sata::kSmallGridWorkgroups)
+    return b->lay_small;
+  return lay;
+}
+
 // Workspace of G heads and windows of nw tokens.
-PrefillPlan prefill_sizes(const sata_basis* b, int64_t G, int64_t nw, int dtype) {
+PrefillPlan prefill_sizes(const sata_basis* b, const PrefillLayout& lay, int64_t G, int64_t nw, int dtype) {
   const bool bf16 = dtype == SATA_BF16;
-  const int nt = b->lay[dtype].n_tiles;
+  const int nt = lay.n_tiles;
   const int d = b->d;
   const int dvp = sata::padded_dv(d);
   const int T = sata::prefill_window(bf16);
@@ -464,7 +473,8 @@ PrefillPlan prefill_sizes(const sata_basis* b, int64_t G, int64_t nw, int dtype)
 // larger one the least-time plan.
 PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype, size_t budget, double slack) {
   const bool bf16 = dtype == SATA_BF16;
-  const int64_t nt = b->lay[dtype].n_tiles;
+  const PrefillLayout& lay = prefill_layout(b, dtype, BH);
+  const int64_t nt = lay.n_tiles;
   const int64_t T = sata::prefill_window(bf16);
   const int64_t L = sata::prefill_chunk(bf16);
   constexpr int64_t kCUs = 256;
@@ -482,17 +492,17 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype, 
     last_g = G;
     // the longest window that fits: min(i T, nround) for the largest i (the
     // workspace grows with the window)
-    if (prefill_sizes(b, G, window(1), dtype).total > budget) continue;
+    if (prefill_sizes(b, lay, G, window(1), dtype).total > budget) continue;
     int64_t lo = 1, hi = m;
     while (lo < hi) {
       const int64_t mid = (lo + hi + 1) / 2;
-      if (prefill_sizes(b, G, window(mid), dtype).total <= budget)
+      if (prefill_sizes(b, lay, G, window(mid), dtype).total <= budget)
         lo = mid;
       else
         hi = mid - 1;
     }
     const int64_t w = window(lo);
-    PrefillPlan pl = prefill_sizes(b, G, w, dtype);
+    PrefillPlan pl = prefill_sizes(b, lay, G, w, dtype);
     const int64_t small = BH / k, nbig = BH - small * k;
     const int64_t rounds = nbig * ((G * nt + kCUs - 1) / kCUs) + (k - nbig) * ((small * nt + kCUs - 1) / kCUs);
     const int64_t windows = (n + w - 1) / w;
@@ -593,8 +603,10 @@ static int build_basis_impl(int d_k, int P, double c, bool upload_tables, sata_b
   }
   b->D = total;
   if (!upload_tables) {
-    int st = build_layout(b, rank, false, false, &b->lay[0]);
-    if (st == SATA_OK) st = build_layout(b, rank, true, false, &b->lay[1]);
+    int st = build_layout(b, rank, false, false, &b->lay[0], sata::prefill_rb(d_k, false));
+    if (st == SATA_OK) st = build_layout(b, rank, true, false, &b->lay[1], sata::prefill_rb(d_k, true));
+    if (st == SATA_OK && sata::prefill_rb_small(d_k) > 0)
+      st = build_layout(b, rank, false, false, &b->lay_small, sata::prefill_rb_small(d_k));
     if (st != SATA_OK) {
       release(b);
       return st;
@@ -609,8 +621,10 @@ static int build_basis_impl(int d_k, int P, double c, bool upload_tables, sata_b
   }
   int st = upload(b, b->packed, &b->d_rows);
   if (st == SATA_OK) st = upload(b, b->weight, &b->d_weight);
-  if (st == SATA_OK) st = build_layout(b, rank, false, true, &b->lay[0]);
-  if (st == SATA_OK) st = build_layout(b, rank, true, true, &b->lay[1]);
+  if (st == SATA_OK) st = build_layout(b, rank, false, true, &b->lay[0], sata::prefill_rb(d_k, false));
+  if (st == SATA_OK) st = build_layout(b, rank, true, true, &b->lay[1], sata::prefill_rb(d_k, true));
+  if (st == SATA_OK && sata::prefill_rb_small(d_k) > 0)
+    st = build_layout(b, rank, false, true, &b->lay_small, sata::prefill_rb_small(d_k));
   if (st != SATA_OK) {
     release(b);
     return st;
@@ -717,7 +731,7 @@ static int prefill_impl(const sata_basis* b, int B, int H, int n, int d_v, int d
   if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SATA_BF16;
-  const PrefillLayout& lay = b->lay[dtype];
+  const PrefillLayout& lay = prefill_layout(b, dtype, BH);
   const int64_t stride = state_stride;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   char* base = static_cast<char*>(ws);

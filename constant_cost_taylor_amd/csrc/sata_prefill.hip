@@ -103,17 +103,17 @@ struct ChunkRegs {
   }
 };
 
-template <int DK>
+template <int DK, int RB_>
 struct Cfg {
   static constexpr int DV = DK;
   static constexpr int L = prefill_chunk(false);
   static constexpr int T = prefill_window(false);    // readout window (tokens)
   static constexpr int SC = T / L;                   // chunks per readout window
-  static constexpr int RB = prefill_rb(DK, false);
+  static constexpr int RB = RB_;                     // 16-row blocks a wave
   static constexpr int NB = col_blocks(DV);        // 16-wide column blocks incl. z
   static constexpr int NC = NB * 16;
   static constexpr int DVP = padded_dv(DV);
-  static constexpr int NSLOT = prefill_slots(DK, false);
+  static constexpr int NSLOT = prefill_slots_rb(RB_, false);
   static constexpr int KSTR = prefill_kstride(false); // xk / pk row stride (floats)
   static constexpr int QSTR = L + 1;                 // pq row stride
   static constexpr int XQSTR = DK + 4;               // xq row stride
@@ -124,12 +124,12 @@ struct Cfg {
   static constexpr int TPG = L / 4;                  // token groups of the cross-wave sum
 };
 
-template <int DK>
+template <int DK, int RB_>
 __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   // tokens of this head in the window; none: the state is left as it is
   const int nwh = head_tokens(a.lens, blockIdx.y, a.t0, a.nw, a.n_total);
   if (nwh == 0) return;
-  using C = Cfg<DK>;
+  using C = Cfg<DK, RB_>;
   constexpr int DV = C::DV, L = C::L, RB = C::RB, NB = C::NB, NC = C::NC, DVP = C::DVP;
   constexpr int NSLOT = C::NSLOT, KSTR = C::KSTR, QSTR = C::QSTR, XQSTR = C::XQSTR;
   constexpr int RSTR = C::RSTR, XK_ZERO = C::XK_ZERO, MB = C::MB, EPT = C::EPT;
@@ -754,7 +754,15 @@ template <int D, bool BF16>
 hipError_t launch_scan_t(int BH, const ScanArgs& a, hipStream_t s) {
   if (BF16) return hipErrorInvalidValue;
   dim3 grid(a.lay.n_tiles, BH);
-  prefill_scan<D><<<grid, kWaves * 64, 0, s>>>(a);
+  constexpr int RB = prefill_rb(D, false), RBS = prefill_rb_small(D);
+  if (a.lay.rb == RB) {
+    prefill_scan<D, RB><<<grid, kWaves * 64, 0, s>>>(a);
+  } else if constexpr (RBS > 0) {
+    if (a.lay.rb != RBS) return hipErrorInvalidValue;
+    prefill_scan<D, RBS><<<grid, kWaves * 64, 0, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -353,6 +353,26 @@ def test_prefill_workspace_down_to_minimum(d, P, dtype):
     assert float(out.min()) == 7.0 and float(st.abs().sum()) == 0.0
 
 
+def test_prefill_f32_both_tilings():
+    """float32 inputs at d = 16 use 64-row tiles when the batch has few heads
+    (32 here) and 128-row tiles otherwise (64 heads): both match the oracle,
+    and the shared heads agree between the two calls to fp32 rounding."""
+    d, P, n = 16, 4, 700
+    note(f"fp32 tilings d={d} P={P} n={n} heads 32 / 64")
+    q, k, v = W.make_qkv(1, 64, n, d, d, W.F32, 30000)
+    b = SA.build_basis(d, P, 1.0)
+    small, _ = run_prefill(b, q[:, :32], k[:, :32], v[:, :32], W.F32)
+    full, _ = run_prefill(b, q, k, v, W.F32)
+    gs, gf = small.cpu().numpy(), full.cpu().numpy()
+    for h in (0, 31):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0)
+        assert O.row_normwise_error(gs[0, h], ref) <= TOL[W.F32], h
+        assert O.row_normwise_error(gf[0, h], ref) <= TOL[W.F32], h
+    ref = oracle_rows(q[0, 63], k[0, 63], v[0, 63], P, 1.0)
+    assert O.row_normwise_error(gf[0, 63], ref) <= TOL[W.F32]
+    assert np.max(np.abs(gs - gf[:, :32])) <= 1e-5 * np.max(np.abs(gf[:, :32]))
+
+
 def test_misaligned_and_host_only_rejected():
     note("misaligned pointers / host-only handle on the GPU")
     b = SA.build_basis(16, 4, 1.0)
