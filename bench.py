@@ -14,7 +14,9 @@ roofline (a few repetitions each): the same decode on the mixed-precision
 state (orders >= 2 of S in float16), the d8 / d16 fp32 and d64 bf16 prefills,
 the long-context d32 prefill at 2^16, 2^18 and 2^20 tokens with its per-token
 cost ratio, the orders 0..4 (P = 5) prefill and decode legs, and exact causal
-softmax attention beside the SATA prefill over n = 2^12..2^16 (the crossover).  The CPU
+softmax attention beside the SATA prefill over n = 2^12..2^16 (the crossover);
+`ceilings` gives the box's own stream and matrix-core rates from the ceiling
+kernels, with the decode and prefill legs as fractions of them.  The CPU
 baseline is the float64 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -410,6 +412,52 @@ def crossover_points(reps, warmup, heads=(4, 32), lgs=(12, 13, 14, 15, 16)):
                         "device-generated inputs", "steps": reps, "warmup": warmup, **res}
 
 
+def box_ceilings(reps=10):
+    """Ceilings of this box from the ceiling kernels (libsata_ceilings.so, HIP
+    events): a 1 GiB read+write copy, a 3 GiB in-place read-modify-write in the
+    decode step's access shape, a 3 GiB read, and the bf16 and fp32 matrix-core
+    loops (eight independent MFMA chains a wave, 1024 workgroups of 8 waves)."""
+    import torch
+    from constant_cost_taylor_amd import ceilings as CL
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def timed(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ms))
+
+    res = {}
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    res["copy_1GiB_read_write_gbs"] = 2 * (1 << 30) / (timed(lambda: CL.copy(src, dst, sp)) * 1e-3) / 1e9
+    del src, dst
+    big = torch.ones(3 << 28, dtype=torch.float32, device=dev)
+    res["rmw_3GiB_gbs"] = 2 * (3 << 30) / (timed(lambda: CL.rmw(big, sp)) * 1e-3) / 1e9
+    part = torch.empty(CL.read_partials(3 << 30), dtype=torch.float32, device=dev)
+    res["read_3GiB_gbs"] = (3 << 30) / (timed(lambda: CL.read(big, part, sp)) * 1e-3) / 1e9
+    del big, part
+    torch.cuda.empty_cache()
+    blocks = 1024
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    for code, name, iters in ((1, "mfma_bf16_tflops", 4000), (0, "mfma_f32_tflops", 2000)):
+        t = timed(lambda: CL.mfma(code, blocks, iters, out, sp))
+        res[name] = CL.mfma_flops(code, blocks, iters) / (t * 1e-3) / 1e12
+    del out
+    torch.cuda.empty_cache()
+    return res
+
+
 def ceilings(args):
     """Measured ceilings of this machine (torch / hipBLASLt kernels, HIP events):
     the bandwidth a read+write stream, an in-place read-modify-write stream
@@ -453,8 +501,11 @@ def ceilings(args):
     c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
     t = timed(lambda: torch.matmul(a, b, out=c), 20)
     res["gemm_bf16_8192_tflops"] = 2 * n ** 3 / (t * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
     print(json.dumps({"metric": "measured ceilings of this box", "peaks": {"hbm_gbs": HBM_PEAK_GBS,
-                      "bf16_tflops": BF16_PEAK_TFLOPS, "fp32_tflops": FP32_PEAK_TFLOPS}, "measured": res}),
+                      "bf16_tflops": BF16_PEAK_TFLOPS, "fp32_tflops": FP32_PEAK_TFLOPS},
+                      "ceiling_kernels": box_ceilings(), "library_kernels": res}),
           flush=True)
 
 
@@ -604,6 +655,12 @@ def main():
                           "long_context": flatness_points(args.config_steps, 1),
                           "order5": order5_point(args.config_steps, 1, 64),
                           "softmax_crossover": crossover_points(3, 1)}
+    if not args.no_configs:
+        # the box's own ceilings (ceiling kernels), and the two legs against them
+        ceil = box_ceilings()
+        ceil["decode_frac_of_rmw"] = dec_gbs / ceil["rmw_3GiB_gbs"]
+        ceil["prefill_frac_of_mfma_bf16"] = pre_tflops / ceil["mfma_bf16_tflops"]
+        res["ceilings"] = ceil
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, qs, ks, vs, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -19,6 +19,9 @@ OUT = os.path.join(PKG, "libsata.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["sata_host.cpp", "sata_decode.hip", "sata_prefill.hip", "sata_prefill_b16.hip", "sata_softmax.hip"]
+# The ceiling kernels (measurement tools) are a library of their own.
+CEIL_SOURCES = ["sata_ceilings.hip"]
+CEIL_OUT = os.path.join(PKG, "libsata_ceilings.so")
 
 # Packed fp32 instructions are disabled for every HIP compile.
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -42,19 +45,27 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build_library(verbose: bool = False, extra: list[str] | None = None) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    extra = list(extra or [])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build_library(verbose: bool = False, extra: list[str] | None = None) -> str:
+    """Compile and link libsata.so and libsata_ceilings.so; returns the first."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    extra = list(extra or [])
+    srcs = SOURCES + CEIL_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], CEIL_OUT)
     if verbose:
         print(f"built {OUT}")
+        print(f"built {CEIL_OUT}")
     return OUT
 
 

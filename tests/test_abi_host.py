@@ -12,11 +12,12 @@ import pytest
 import constant_cost_taylor_amd as SA
 from oracle import sata_oracle as O
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sata.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADER = os.path.join(INCLUDE, "sata.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(sata_[a-z_]+)\s*\(", text)))
 
@@ -27,6 +28,22 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 12
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_ceilings_library_exports_every_declared_symbol():
+    from constant_cost_taylor_amd import ceilings as CL
+    lib = CL.lib()
+    names = _declared_functions(os.path.join(INCLUDE, "sata_ceilings.h"))
+    assert len(names) == 6
+    for name in names:
+        assert hasattr(lib, name), name
+    # host-side checks: argument errors launch nothing; the FLOP count formula
+    assert lib.sata_ceil_copy(None, None, 1024, None) == -1
+    assert lib.sata_ceil_rmw(16, 24, None) == -1          # not a multiple of 16 bytes
+    assert lib.sata_ceil_mfma(2, 1, 1, 16, None) == -1    # no such dtype
+    assert CL.read_partials(1 << 20) == (1 << 20) // (16 * 1024)
+    assert CL.mfma_flops(1, 3, 5) == 2 * 16 * 16 * 32 * 8 * 8 * 3 * 5
+    assert CL.mfma_flops(0, 2, 7) == 2 * 16 * 16 * 4 * 8 * 8 * 2 * 7
 
 
 @pytest.mark.parametrize("d,P", [(8, 1), (8, 3), (16, 4), (32, 4), (64, 4), (64, 2), (16, 5), (64, 5)])
