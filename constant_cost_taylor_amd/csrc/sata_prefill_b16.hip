@@ -325,29 +325,63 @@ __global__ __launch_bounds__(256) void prefill_stage(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Order-0 carry.  Block = head; thread c <= DV runs over the window's chunks
-// in order: carry[r][c] = (order-0 row of the state) + (sum of v[c], or the
-// token count for c = DV, over the chunks before readout window r).  The
-// order-0 row of the state ends as the sum over the whole window.
-template <int DK>
-__global__ __launch_bounds__(128) void prefill_carry(ScanArgs a) {
+// Order-0 carry.  Block = (column c <= DV, head): carry[r][c] = (order-0 entry
+// c of the state) + (sum of v[c], or the token count for c = DV, over the
+// chunks before readout window r); the state's entry ends as the sum over the
+// whole window.  Thread t takes windows [t k, (t + 1) k): the sum of its
+// windows, an exclusive scan of the block's sums in LDS, then the carries of
+// its windows in order.  One wave a block while the window count is small,
+// four waves beyond.
+template <int DK, int kCarryThreads>
+__global__ __launch_bounds__(kCarryThreads) void prefill_carry(ScanArgs a) {
   constexpr int DV = DK, DVP = padded_dv(DV), L = kL, SC = prefill_window(true) / kL;
-  const int head = blockIdx.x;
-  const int c = threadIdx.x;
-  if (c > DV) return;
+  const int c = blockIdx.x;
+  const int head = blockIdx.y;
+  const int tid = threadIdx.x;
   float* st = a.state + static_cast<int64_t>(head) * a.stride;
   const int64_t zoff = static_cast<int64_t>(a.D) * DV;
-  float acc = c < DV ? st[c] : st[zoff];
+  const float s0 = c < DV ? st[c] : st[zoff];
   const int nch = (a.nw + L - 1) / L;
   const int nchp = a.ws.nwp / L;
+  const int R = (nch + SC - 1) / SC;
+  const int k = (R + kCarryThreads - 1) / kCarryThreads;
+  const int r0 = min(R, tid * k), r1 = min(R, r0 + k);
   const float* vs = a.ws.vsum + static_cast<int64_t>(head) * nchp * DVP + c;
   float* carry = a.ws.carry + static_cast<int64_t>(head) * ((a.ws.nwp + SC * L - 1) / (SC * L)) * DVP + c;
-  for (int ch = 0; ch < nch; ++ch) {
-    if (ch % SC == 0) carry[(ch / SC) * DVP] = acc;
-    acc += vs[static_cast<int64_t>(ch) * DVP];
+  auto window_sum = [&](int r) {
+    float v[SC];
+#pragma unroll
+    for (int j = 0; j < SC; ++j) v[j] = r * SC + j < nch ? vs[static_cast<int64_t>(r * SC + j) * DVP] : 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < SC; ++j) s += v[j];
+    return s;
+  };
+  float tot = 0.f;
+  for (int r = r0; r < r1; ++r) tot += window_sum(r);
+  // inclusive scan of the threads' sums (Hillis-Steele over two buffers)
+  __shared__ float sh[2][kCarryThreads];
+  int cur = 0;
+  sh[0][tid] = tot;
+  __syncthreads();
+  for (int o = 1; o < kCarryThreads; o <<= 1) {
+    const float x = sh[cur][tid] + (tid >= o ? sh[cur][tid - o] : 0.f);
+    sh[cur ^ 1][tid] = x;
+    cur ^= 1;
+    __syncthreads();
   }
-  if (c < DV) st[c] = acc;
-  else st[zoff] = acc;
+  float pre = s0 + (sh[cur][tid] - tot);
+  for (int r = r0; r < r1; ++r) {
+    carry[static_cast<int64_t>(r) * DVP] = pre;
+    pre += window_sum(r);
+  }
+  if (tid == kCarryThreads - 1) {
+    const float fin = s0 + sh[cur][tid];
+    if (c < DV)
+      st[c] = fin;
+    else
+      st[zoff] = fin;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1251,7 +1285,11 @@ hipError_t launch_b16_t(int BH, const ScanArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   prefill_stage<D><<<dim3(nch, BH), 256, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  prefill_carry<D><<<BH, 128, 0, s>>>(a);
+  const int windows = (nch + prefill_window(true) / kL - 1) / (prefill_window(true) / kL);
+  if (windows <= 256)
+    prefill_carry<D, 64><<<dim3(D + 1, BH), 64, 0, s>>>(a);
+  else
+    prefill_carry<D, 256><<<dim3(D + 1, BH), 256, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 grid(a.lay.n_tiles, BH);
   if (a.P == 5)
