@@ -170,13 +170,13 @@ def flatness_points(reps, warmup, lgs=(16, 18, 20)):
         print(f"long-context prefill n=2^{lg}: {t:.2f} ms", file=sys.stderr, flush=True)
         del q, k, v, out, state, ws
         torch.cuda.empty_cache()
+    costs = np.array([r["ns_per_head_token"] for r in rows])
     return {"workload": f"long-context prefill: batch {w.B} x {w.H} heads, d_k=d_v={w.d_k}, P={w.P}, bf16 inputs, "
                         f"f32 state, n = 2^16, 2^18, 2^20 (device-generated inputs)",
             "steps": reps, "warmup": warmup, "points": rows,
-            "per_token_cost_ratio_last_over_first": rows[-1]["ns_per_head_token"] / rows[0]["ns_per_head_token"],
+            "per_token_cost_ratio_last_over_first": float(costs[-1] / costs[0]),
             # largest departure of a point's per-token cost from the mean over the points
-            "per_token_cost_max_dev_from_mean": float(max(abs(x / np.mean(costs) - 1.0) for x in costs))
-            if (costs := [r["ns_per_head_token"] for r in rows]) else None}
+            "per_token_cost_max_dev_from_mean": float(np.max(np.abs(costs / costs.mean() - 1.0)))}
 
 
 def flatness(args):
