@@ -13,7 +13,8 @@ timed steps, `configs` reports the other workloads, each against its own
 roofline (a few repetitions each): the same decode on the mixed-precision
 state (orders >= 2 of S in float16), the d8 / d16 fp32 and d64 bf16 prefills,
 the long-context d32 prefill at 2^16, 2^18 and 2^20 tokens with its per-token
-cost ratio, the orders 0..4 (P = 5) prefill and decode legs, and exact causal
+cost ratio, the orders 0..4 (P = 5) prefill and decode legs, few-head long
+prefills with and without sequence segments, and exact causal
 softmax attention beside the SATA prefill over n = 2^12..2^16 (the crossover);
 `ceilings` gives the box's own stream and matrix-core rates from the ceiling
 kernels, with the decode and prefill legs as fractions of them.  The CPU
@@ -185,6 +186,52 @@ def flatness(args):
     res = flatness_points(args.steps, args.warmup)
     print(json.dumps({"metric": "prefill per-token cost vs context length", "unit": "ns/head-token", **res}),
           flush=True)
+
+
+def segment_points(reps, warmup, cases=((1, 20, 32), (4, 18, 32), (1, 16, 64))):
+    """Prefill of few heads over long sequences, with the sequence segments
+    the library takes for such batches and with them turned off
+    (SATA_PREFILL_SEGMENTS=0): (heads, log2 n, d) each, P = 4, bf16 inputs
+    generated on the device (seeded unit-norm Gaussian q, k; Gaussian v)."""
+    import torch
+    import constant_cost_taylor_amd as sa
+    from oracle import sata_oracle as O
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for H, lg, d in cases:
+        n = 1 << lg
+        basis = sa.build_basis(d, 4, 1.0)
+        _, page_flops = O.cost_model(d, d, 4)
+        g = torch.Generator(device=dev)
+        g.manual_seed(7000 + lg + d)
+        shape = (1, H, n, d)
+        q = torch.randn(shape, generator=g, device=dev)
+        q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        k = torch.randn(shape, generator=g, device=dev)
+        k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        v = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+        state = sa.new_state(basis, H, dev)
+        row = {"heads": H, "n": n, "d": d}
+        for mode in ("segments", "no_segments"):
+            if mode == "no_segments":
+                os.environ["SATA_PREFILL_SEGMENTS"] = "0"
+            ws = sa.workspace(sa.prefill_workspace_bytes(basis, 1, H, n, d, sa.SATA_BF16), dev)
+            t = _time_prefill(sa, basis, q, k, v, state, out, ws, stream, reps, warmup)
+            os.environ.pop("SATA_PREFILL_SEGMENTS", None)
+            tf = H * n * page_flops / (t * 1e-3) / 1e12
+            row[mode] = {"ms": t, "head_tokens_per_s": H * n / (t * 1e-3), "page_tflops": tf,
+                         "mfma_bf16_frac": tf / BF16_PEAK_TFLOPS, "finite": bool(torch.isfinite(out).all())}
+            del ws
+            torch.cuda.empty_cache()
+        row["speedup"] = row["no_segments"]["ms"] / row["segments"]["ms"]
+        rows.append(row)
+        del q, k, v, out, state
+        torch.cuda.empty_cache()
+    return {"workload": "prefill of few heads over long sequences, P=4, bf16 inputs, f32 state, from empty "
+                        "states, with and without sequence segments (device-generated inputs)",
+            "steps": reps, "warmup": warmup, "points": rows}
 
 
 def config_points(reps, warmup, names=("tiny_d8_n256", "d16_n4096", "d64_n16384")):
@@ -657,6 +704,7 @@ def main():
         res["configs"] = {"prefill": config_points(args.config_steps, 1),
                           "long_context": flatness_points(args.config_steps, 1),
                           "order5": order5_point(args.config_steps, 1, 64),
+                          "segments": segment_points(args.config_steps, 1),
                           "softmax_crossover": crossover_points(3, 1)}
     if not args.no_configs:
         # the box's own ceilings (ceiling kernels), and the two legs against them

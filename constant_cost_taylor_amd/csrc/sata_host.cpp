@@ -521,6 +521,167 @@ PrefillPlan prefill_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype, 
   return best;
 }
 
+// The prefill kernels of BH heads of n tokens under plan pl (every head
+// group and call window), workspace at ws.  state_only (bf16 inputs): the
+// state update alone, no outputs.
+static int run_plan(const sata_basis* b, const PrefillPlan& pl, const PrefillLayout& lay, int64_t BH, int64_t n,
+                    int d_v, bool bf16, const char* q, const char* k, const char* v, const int32_t* lens,
+                    float* out, float* state, int64_t stride, char* ws, bool state_only, hipStream_t s) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t off = 0;
+  auto carve = [&](size_t bytes) -> char* {
+    if (bytes == 0) return nullptr;
+    char* p = ws + off;
+    off += up(bytes);
+    return p;
+  };
+  sata::PrefillWs pw{};
+  pw.rec = carve(pl.rec_bytes);
+  pw.intra = reinterpret_cast<float*>(carve(pl.intra_bytes));
+  pw.carry = reinterpret_cast<float*>(carve(pl.carry_bytes));
+  pw.amax = reinterpret_cast<float*>(carve(pl.amax_bytes));
+  pw.nwp = static_cast<int>(pl.nwp);
+  pw.recz = reinterpret_cast<float*>(carve(pl.recz_bytes));
+  pw.stg = reinterpret_cast<uint16_t*>(carve(pl.stg_bytes));
+  pw.vsum = reinterpret_cast<float*>(carve(pl.vsum_bytes));
+  pw.recs = reinterpret_cast<float*>(carve(pl.recs_bytes));
+  const float inv_c = static_cast<float>(1.0 / b->c);
+  const size_t esz = bf16 ? 2 : 4;
+  const int64_t small = BH / pl.groups, nbig = BH - small * pl.groups;
+  int64_t h0 = 0;
+  for (int64_t gi = 0; gi < pl.groups; ++gi) {
+    const int64_t G = small + (gi < nbig ? 1 : 0);
+    if (G == 0) continue;   // a plan made for more heads than this call has
+    const int gh = static_cast<int>(G);
+    const char* qg = q + h0 * n * b->d * esz;
+    const char* kg = k + h0 * n * b->d * esz;
+    const char* vg = v + h0 * n * d_v * esz;
+    float* og = out ? out + h0 * n * d_v : nullptr;
+    float* sg = state + h0 * stride;
+    const int32_t* lg = lens ? lens + h0 : nullptr;
+    for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
+      const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
+      sata::IntraArgs ia{qg, kg, vg, pw, n, t0, w, b->P, inv_c, lg};
+      sata::ScanArgs sa{qg, kg, vg, sg, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P, lg, b->ec,
+                        state_only ? 1 : 0};
+      sata::ReduceArgs ra{pw, og, n, t0, w, lay.n_tiles, inv_c, b->P, lg, b->ec};
+      if (bf16) {
+        if (sata::launch_prefill_b16(b->d, gh, sa, s) != hipSuccess) return SATA_ERR_HIP;
+        if (state_only) continue;
+        if (sata::launch_prefill_intra(b->d, true, gh, ia, s) != hipSuccess) return SATA_ERR_HIP;
+        if (sata::launch_reduce_b16(b->d, gh, ra, s) != hipSuccess) return SATA_ERR_HIP;
+      } else {
+        if (sata::launch_prefill_intra(b->d, false, gh, ia, s) != hipSuccess) return SATA_ERR_HIP;
+        if (sata::launch_prefill_scan(b->d, false, gh, sa, s) != hipSuccess) return SATA_ERR_HIP;
+        if (sata::launch_prefill_reduce(b->d, false, gh, ra, s) != hipSuccess) return SATA_ERR_HIP;
+      }
+    }
+    h0 += G;
+  }
+  return SATA_OK;
+}
+
+// Sequence segments for batches of few heads (bfloat16 inputs, one length for
+// every head).  The scan gives each workgroup a tile of one head's basis rows
+// for the whole sequence, so a batch of few heads leaves CUs idle however long
+// the sequence.  The state composes over token ranges [SATA page, "Engineering
+// of constant compute cost": the state is a plain sum over the keys], so each
+// head runs as G segments of Ls tokens in parallel:
+//   pass 1  state-only scans of segments 0 .. G-2, the first from the head's
+//           state, the others from zero: P_1 and the increments dS_s;
+//   prefix  P_s = P_{s-1} + dS_{s-1};
+//   pass 2  the full prefill of the G segments, segment s from P_s (P_0 the
+//           head's state); the last segment's state is the head's new state;
+//   tail    the n - G Ls tokens past the segments, a plain continuation.
+// Pass 1 repeats the update of all but the last segment (about half a scan's
+// cost a token), so segments pay only where they fill idle CUs.  Model, in
+// chunk units as in prefill_plan, per head: ceil((G-1) tiles / 256) rounds of
+// state-only chunks (0.5 each) and ceil(G tiles / 256) rounds of full chunks
+// over Ls tokens, 5 per round for the state tiles, 30 for the launches, plus
+// the tail; taken when it beats one launch of all heads by 20 %.  The
+// environment variable SATA_PREFILL_SEGMENTS=0 turns segments off.
+struct SegPlan {
+  int G = 1;              // segments per head (1: none)
+  int64_t Ls = 0;         // tokens a segment (a multiple of the 512-token readout window)
+  int64_t rest = 0;       // tokens after the G segments
+  int64_t ts = 0;         // floats between segment states
+  size_t tmp_bytes = 0;   // G segment states
+  PrefillPlan inner;      // G segments as heads of Ls tokens
+  PrefillPlan tail;       // one head of `rest` tokens
+  size_t total = 0;
+};
+
+bool segments_enabled() {
+  const char* e = std::getenv("SATA_PREFILL_SEGMENTS");
+  return !(e && e[0] == '0' && e[1] == 0);
+}
+
+SegPlan segment_plan(const sata_basis* b, int64_t BH, int64_t n, int dtype, bool varlen, size_t budget,
+                     double slack) {
+  SegPlan sp;
+  if (dtype != SATA_BF16 || varlen || !segments_enabled()) return sp;
+  constexpr int64_t kCUs = 256, T = sata::prefill_window(true), L = sata::prefill_chunk(true);
+  const int64_t nt = b->lay[SATA_BF16].n_tiles;
+  if (nt < 1 || BH * nt >= kCUs) return sp;
+  const double plain = static_cast<double>((BH * nt + kCUs - 1) / kCUs) * ((n + L - 1) / L + 5) + 10;
+  double best = 0.8 * plain;
+  for (int64_t G = 2; G <= std::min<int64_t>(kCUs / nt, n / T); ++G) {
+    const int64_t Ls = T * (n / (T * G));
+    const int64_t rest = n - G * Ls;
+    const double ch = static_cast<double>(Ls / L);
+    double c = static_cast<double>(((G - 1) * nt + kCUs - 1) / kCUs) * (0.5 * ch + 5) +
+               static_cast<double>((G * nt + kCUs - 1) / kCUs) * (ch + 5) + 30;
+    if (rest > 0) c += static_cast<double>((nt + kCUs - 1) / kCUs) * ((rest + L - 1) / L + 5) + 10;
+    c *= static_cast<double>(BH);
+    if (c < best) {
+      best = c;
+      sp.G = static_cast<int>(G);
+      sp.Ls = Ls;
+      sp.rest = rest;
+    }
+  }
+  if (sp.G == 1) return sp;
+  sp.ts = sata::state_stride(static_cast<int64_t>(b->d + 1) * b->D);
+  sp.tmp_bytes = (static_cast<size_t>(sp.G) * sp.ts * 4 + 255) / 256 * 256;
+  if (sp.tmp_bytes >= budget) return SegPlan{};
+  sp.inner = prefill_plan(b, sp.G, sp.Ls, dtype, budget - sp.tmp_bytes, slack);
+  if (sp.rest > 0) sp.tail = prefill_plan(b, 1, sp.rest, dtype, budget - sp.tmp_bytes, slack);
+  if (sp.inner.groups == 0 || (sp.rest > 0 && sp.tail.groups == 0)) return SegPlan{};
+  sp.total = sp.tmp_bytes + std::max(sp.inner.total, sp.rest > 0 ? sp.tail.total : size_t(0));
+  return sp;
+}
+
+// One head through segments (see segment_plan); q, k, v, out and state point
+// at the head.
+static int run_segments(const sata_basis* b, const SegPlan& sp, int64_t n, int d_v, const char* q, const char* k,
+                        const char* v, float* out, float* state, char* ws, hipStream_t s) {
+  const PrefillLayout& lay = b->lay[SATA_BF16];
+  const int64_t nf = static_cast<int64_t>(d_v + 1) * b->D;
+  float* T = reinterpret_cast<float*>(ws);
+  char* inner_ws = ws + sp.tmp_bytes;
+  const int G = sp.G;
+  // pass 1: segment 0 from the head's state into T[1], segments 1..G-2 from
+  // zero into T[2..G-1]
+  if (sata::launch_state_copy(T + sp.ts, state, nf, s) != hipSuccess) return SATA_ERR_HIP;
+  if (G > 2 && sata::launch_state_zero(T + 2 * sp.ts, sp.ts, G - 2, nf, s) != hipSuccess) return SATA_ERR_HIP;
+  PrefillPlan p1 = sp.inner;   // G - 1 of the G segment heads fit the same plan
+  int st = run_plan(b, p1, lay, G - 1, sp.Ls, d_v, true, q, k, v, nullptr, nullptr, T + sp.ts, sp.ts, inner_ws,
+                    true, s);
+  if (st != SATA_OK) return st;
+  // prefix: T[s] = P_s for s >= 1
+  if (G > 2 && sata::launch_state_prefix(T, sp.ts, G, nf, s) != hipSuccess) return SATA_ERR_HIP;
+  // pass 2 from P_0 = the head's state
+  if (sata::launch_state_copy(T, state, nf, s) != hipSuccess) return SATA_ERR_HIP;
+  st = run_plan(b, sp.inner, lay, G, sp.Ls, d_v, true, q, k, v, nullptr, out, T, sp.ts, inner_ws, false, s);
+  if (st != SATA_OK) return st;
+  if (sata::launch_state_copy(state, T + static_cast<int64_t>(G - 1) * sp.ts, nf, s) != hipSuccess)
+    return SATA_ERR_HIP;
+  if (sp.rest == 0) return SATA_OK;
+  const int64_t t = static_cast<int64_t>(G) * sp.Ls;
+  return run_plan(b, sp.tail, lay, 1, sp.rest, d_v, true, q + t * b->d * 2, k + t * b->d * 2, v + t * d_v * 2,
+                  nullptr, out + t * d_v, state, 0, inner_ws, false, s);
+}
+
 // Decode workspace: value partials [S][tiles][d_v] then den partials
 // [S][tiles]; with more than one reduce group a state, then the second-level
 // partials [S][groups][d_v] and [S][groups].  Each region 256-byte aligned.
@@ -704,7 +865,13 @@ int sata_prefill_workspace(const sata_basis* b, int B, int H, int n, int d_v, in
     *bytes = 0;
     return SATA_OK;
   }
-  const PrefillPlan pl = prefill_plan(b, static_cast<int64_t>(B) * H, n, dtype, prefill_ws_cap(), 0.02);
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  const SegPlan sp = segment_plan(b, BH, n, dtype, false, prefill_ws_cap(), 0.02);
+  if (sp.G > 1) {
+    *bytes = sp.total;
+    return SATA_OK;
+  }
+  const PrefillPlan pl = prefill_plan(b, BH, n, dtype, prefill_ws_cap(), 0.02);
   if (pl.groups == 0) return SATA_ERR_WORKSPACE;
   *bytes = pl.total;
   return SATA_OK;
@@ -725,64 +892,32 @@ static int prefill_impl(const sata_basis* b, int B, int H, int n, int d_v, int d
   const int64_t BH = static_cast<int64_t>(B) * H;
   if (BH > 65535) return SATA_ERR_UNSUPPORTED;  // grid y limit
   if (!ws) return SATA_ERR_WORKSPACE;
-  const PrefillPlan pl = prefill_plan(b, BH, n, dtype, std::min(ws_bytes, prefill_ws_cap()), 0.0);
-  if (pl.groups == 0) return SATA_ERR_WORKSPACE;
+  const size_t budget = std::min(ws_bytes, prefill_ws_cap());
+  const SegPlan sp = segment_plan(b, BH, n, dtype, lens != nullptr, budget, 0.0);
+  PrefillPlan pl;
+  if (sp.G == 1) {
+    pl = prefill_plan(b, BH, n, dtype, budget, 0.0);
+    if (pl.groups == 0) return SATA_ERR_WORKSPACE;
+  }
   if (!aligned(ws, 256)) return SATA_ERR_INVALID_ARG;
   if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SATA_BF16;
-  const PrefillLayout& lay = prefill_layout(b, dtype, BH);
-  const int64_t stride = state_stride;
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  char* base = static_cast<char*>(ws);
-  size_t off = 0;
-  auto carve = [&](size_t bytes) -> char* {
-    if (bytes == 0) return nullptr;
-    char* p = base + off;
-    off += up(bytes);
-    return p;
-  };
-  sata::PrefillWs pw{};
-  pw.rec = carve(pl.rec_bytes);
-  pw.intra = reinterpret_cast<float*>(carve(pl.intra_bytes));
-  pw.carry = reinterpret_cast<float*>(carve(pl.carry_bytes));
-  pw.amax = reinterpret_cast<float*>(carve(pl.amax_bytes));
-  pw.nwp = static_cast<int>(pl.nwp);
-  pw.recz = reinterpret_cast<float*>(carve(pl.recz_bytes));
-  pw.stg = reinterpret_cast<uint16_t*>(carve(pl.stg_bytes));
-  pw.vsum = reinterpret_cast<float*>(carve(pl.vsum_bytes));
-  pw.recs = reinterpret_cast<float*>(carve(pl.recs_bytes));
-  const float inv_c = static_cast<float>(1.0 / b->c);
-  const size_t esz = bf16 ? 2 : 4;
-  const int64_t small = BH / pl.groups, nbig = BH - small * pl.groups;
-  int64_t h0 = 0;
-  for (int64_t gi = 0; gi < pl.groups; ++gi) {
-    const int64_t G = small + (gi < nbig ? 1 : 0);
-    const int gh = static_cast<int>(G);
-    const char* qg = static_cast<const char*>(q) + h0 * n * b->d * esz;
-    const char* kg = static_cast<const char*>(k) + h0 * n * b->d * esz;
-    const char* vg = static_cast<const char*>(v) + h0 * n * d_v * esz;
-    float* og = out + h0 * n * d_v;
-    float* sg = state + h0 * stride;
-    const int32_t* lg = lens ? lens + h0 : nullptr;
-    for (int64_t t0 = 0; t0 < n; t0 += pl.nw) {
-      const int w = static_cast<int>(std::min<int64_t>(pl.nw, n - t0));
-      sata::IntraArgs ia{qg, kg, vg, pw, n, t0, w, b->P, inv_c, lg};
-      sata::ScanArgs sa{qg, kg, vg, sg, stride, pw, lay, n, t0, w, static_cast<int>(b->D), inv_c, b->P, lg, b->ec};
-      sata::ReduceArgs ra{pw, og, n, t0, w, lay.n_tiles, inv_c, b->P, lg, b->ec};
-      if (bf16) {
-        if (sata::launch_prefill_b16(b->d, gh, sa, s) != hipSuccess) return SATA_ERR_HIP;
-        if (sata::launch_prefill_intra(b->d, true, gh, ia, s) != hipSuccess) return SATA_ERR_HIP;
-        if (sata::launch_reduce_b16(b->d, gh, ra, s) != hipSuccess) return SATA_ERR_HIP;
-      } else {
-        if (sata::launch_prefill_intra(b->d, false, gh, ia, s) != hipSuccess) return SATA_ERR_HIP;
-        if (sata::launch_prefill_scan(b->d, false, gh, sa, s) != hipSuccess) return SATA_ERR_HIP;
-        if (sata::launch_prefill_reduce(b->d, false, gh, ra, s) != hipSuccess) return SATA_ERR_HIP;
-      }
+  const char* qc = static_cast<const char*>(q);
+  const char* kc = static_cast<const char*>(k);
+  const char* vc = static_cast<const char*>(v);
+  char* wsc = static_cast<char*>(ws);
+  if (sp.G > 1) {
+    const size_t esz = 2;
+    for (int64_t h = 0; h < BH; ++h) {
+      const int st = run_segments(b, sp, n, d_v, qc + h * n * b->d * esz, kc + h * n * b->d * esz,
+                                  vc + h * n * d_v * esz, out + h * n * d_v, state + h * state_stride, wsc, s);
+      if (st != SATA_OK) return st;
     }
-    h0 += G;
+    return SATA_OK;
   }
-  return SATA_OK;
+  return run_plan(b, pl, prefill_layout(b, dtype, BH), BH, n, d_v, bf16, qc, kc, vc, lens, out, state,
+                  state_stride, wsc, false, s);
 }
 
 int sata_prefill_strided(const sata_basis* b, int B, int H, int n, int d_v, int dtype, const void* q,

@@ -182,6 +182,7 @@ struct ScanArgs {
   int P;                 // orders 0..P-1
   const int32_t* lens;   // [BH] tokens of each head (device), or null: n_total for every head
   int ec;                // c = c' 2^ec, c' in [1, 2): bf16 inputs fold 2^-ec into the staged queries
+  int state_only;        // bf16 scan: update the state only (no readout, no records)
 };
 
 struct IntraArgs {
@@ -314,6 +315,12 @@ hipError_t noalloc_scratch_address(void** ptr);
 // bfloat16 inputs: max-abs pre-pass, staging, order-0 carry and the scan of
 // one call window; then the reduce (after the intra-window kernel).
 hipError_t launch_prefill_b16(int d, int BH, const ScanArgs& a, hipStream_t s);
+// Segment states of a prefill over sequence segments: nf floats each, T[s]
+// at T + s * ts.  copy: dst = src; zero: T[0 .. count) = 0; prefix: T[s] +=
+// T[s - 1] for s = 2 .. G - 1, in order.
+hipError_t launch_state_copy(float* dst, const float* src, int64_t nf, hipStream_t s);
+hipError_t launch_state_zero(float* T, int64_t ts, int count, int64_t nf, hipStream_t s);
+hipError_t launch_state_prefix(float* T, int64_t ts, int G, int64_t nf, hipStream_t s);
 hipError_t launch_reduce_b16(int d, int BH, const ReduceArgs& a, hipStream_t s);
 
 }  // namespace sata

@@ -487,7 +487,9 @@ __device__ __forceinline__ u32x4 mul8(u32x4 x, u32x4 y) {
 // per head).
 // P5: orders 0..4, whose order-3 parents carry a third coordinate on both
 // sides (a separate instantiation keeps the registers of P <= 4 as they are).
-template <int DK, bool H16, bool P5>
+// SO (state only): the state update alone, for the first pass of a prefill
+// over sequence segments; no readout operand, readout or records.
+template <int DK, bool H16, bool P5, bool SO>
 __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& hs, unsigned char* lds) {
   using C = CfgS<DK>;
   constexpr int DV = C::DV, L = C::L, NW = C::NW, RB = C::RB, NKS = C::NKS, NB = C::NB, NU = C::NU;
@@ -1042,10 +1044,10 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   };
 
   // ---- prologue: chunk 0's parent slots, the first Sb ---------------------------
-  post_max();
+  if constexpr (!SO) post_max();
   dma_barrier();
   slots(0);
-  refresh();
+  if constexpr (!SO) refresh();
   lds_barrier();
 
   // ---- chunks -------------------------------------------------------------------
@@ -1056,6 +1058,16 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     constexpr int X = decltype(Xc)::value;
 #pragma unroll
     for (int b = 0; b < RB; ++b) asm volatile("" : "+v"(okpc[b]));
+    if constexpr (SO) {
+      // the next chunk's tables, then this chunk's update and the next
+      // chunk's parent slots
+      dma(ch + 1 < nch ? ch + 1 : ch, X ^ 1);
+      update(X, [](int) {});
+      dma_barrier();
+      if (ch + 1 < nch) slots(X ^ 1);
+      lds_barrier();
+      return;
+    }
     // segment 1: read out this chunk; the next chunk's DMA goes out one
     // block per readout step
     if (ch > 0 && ch % C::SC == 0) refresh();
@@ -1116,16 +1128,16 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   }
 }
 
-template <int DK, bool P5>
+template <int DK, bool P5, bool SO>
 __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[CfgS<DK>::LDS_B];
   // no tokens of this head in the window: the state is left as it is
   if (head_tokens(a.lens, blockIdx.y, a.t0, a.nw, a.n_total) == 0) return;
   const HalfScales hs = head_scales(a.ws, blockIdx.y, a.P, a.ec);
   if (hs.safe)
-    scan_tile<DK, true, P5>(a, hs, lds);
+    scan_tile<DK, true, P5, SO>(a, hs, lds);
   else
-    scan_tile<DK, false, P5>(a, hs, lds);
+    scan_tile<DK, false, P5, SO>(a, hs, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1292,10 +1304,18 @@ hipError_t launch_b16_t(int BH, const ScanArgs& a, hipStream_t s) {
     prefill_carry<D, 256><<<dim3(D + 1, BH), 256, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 grid(a.lay.n_tiles, BH);
-  if (a.P == 5)
-    prefill_scan_b16<D, true><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
-  else
-    prefill_scan_b16<D, false><<<grid, prefill_waves(true) * 64, 0, s>>>(a);
+  constexpr int NT = prefill_waves(true) * 64;
+  if (a.state_only) {
+    if (a.P == 5)
+      prefill_scan_b16<D, true, true><<<grid, NT, 0, s>>>(a);
+    else
+      prefill_scan_b16<D, false, true><<<grid, NT, 0, s>>>(a);
+  } else {
+    if (a.P == 5)
+      prefill_scan_b16<D, true, false><<<grid, NT, 0, s>>>(a);
+    else
+      prefill_scan_b16<D, false, false><<<grid, NT, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -1306,6 +1326,48 @@ hipError_t launch_reduce_b16_t(int BH, const ReduceArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+namespace {
+constexpr int kStateThreads = 256;
+// Elementwise kernels over segment states (grid-stride over nf floats).
+__global__ __launch_bounds__(kStateThreads) void state_copy(float* dst, const float* src, int64_t nf) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kStateThreads + threadIdx.x; i < nf;
+       i += static_cast<int64_t>(gridDim.x) * kStateThreads)
+    dst[i] = src[i];
+}
+__global__ __launch_bounds__(kStateThreads) void state_zero(float* T, int64_t ts, int64_t nf) {
+  float* t = T + static_cast<int64_t>(blockIdx.y) * ts;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kStateThreads + threadIdx.x; i < nf;
+       i += static_cast<int64_t>(gridDim.x) * kStateThreads)
+    t[i] = 0.f;
+}
+__global__ __launch_bounds__(kStateThreads) void state_prefix(float* T, int64_t ts, int G, int64_t nf) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kStateThreads + threadIdx.x; i < nf;
+       i += static_cast<int64_t>(gridDim.x) * kStateThreads) {
+    float acc = T[ts + i];
+    for (int s = 2; s < G; ++s) {
+      acc += T[s * ts + i];
+      T[s * ts + i] = acc;
+    }
+  }
+}
+unsigned state_blocks(int64_t nf) {
+  return static_cast<unsigned>(std::min<int64_t>((nf + kStateThreads - 1) / kStateThreads, 4096));
+}
+}  // namespace
+
+hipError_t launch_state_copy(float* dst, const float* src, int64_t nf, hipStream_t s) {
+  state_copy<<<state_blocks(nf), kStateThreads, 0, s>>>(dst, src, nf);
+  return hipGetLastError();
+}
+hipError_t launch_state_zero(float* T, int64_t ts, int count, int64_t nf, hipStream_t s) {
+  state_zero<<<dim3(state_blocks(nf), count), kStateThreads, 0, s>>>(T, ts, nf);
+  return hipGetLastError();
+}
+hipError_t launch_state_prefix(float* T, int64_t ts, int G, int64_t nf, hipStream_t s) {
+  state_prefix<<<state_blocks(nf), kStateThreads, 0, s>>>(T, ts, G, nf);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_b16(int d, int BH, const ScanArgs& a, hipStream_t s) {
   switch (d) {

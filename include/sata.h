@@ -113,7 +113,15 @@ int64_t sata_state_stride(const sata_basis* basis, int d_v);
 /* Device workspace in bytes for sata_prefill at these sizes.  A prefill runs
  * its heads in groups and each group's tokens in call windows (multiples of
  * 512 tokens for bfloat16 inputs); the workspace holds the records of one
- * group and window.  The call picks, from the workspace it is given, the cut
+ * group and window.  With bfloat16 inputs, one length for every head and
+ * too few heads to fill the chip, each head instead runs as parallel
+ * sequence segments [SATA page, "Engineering of constant compute cost": the
+ * state is a sum over the keys, so it composes over token ranges]: a
+ * state-only pass over all but the last segment, a prefix sum of the segment
+ * states, then every segment in full from its prefix state; the workspace
+ * then also holds one state per segment.  The environment variable
+ * SATA_PREFILL_SEGMENTS=0 (read at every call, like the cap below) turns
+ * segments off.  The call picks, from the workspace it is given, the cut
  * of least modelled time that fits: more, smaller groups cost little while
  * each group still fills the chip's 256 compute units, while every extra
  * window reloads the state once.  The size returned here is that of the

@@ -373,6 +373,50 @@ def test_prefill_f32_both_tilings():
     assert np.max(np.abs(gs - gf[:, :32])) <= 1e-5 * np.max(np.abs(gf[:, :32]))
 
 
+@pytest.mark.parametrize("d,P,n,cont", [(32, 4, 5000, False), (64, 4, 36864, False), (16, 5, 3584, False),
+                                        (32, 4, 4608, True), (8, 4, 6000, False)])
+def test_prefill_sequence_segments(d, P, n, cont, monkeypatch):
+    """One head of a long sequence runs as parallel sequence segments (state
+    passes, prefix, full passes, tail): outputs match the oracle, the state
+    matches the direct state, and both agree with the call that has segments
+    turned off; `cont`: from a state that already holds 700 tokens."""
+    n0 = 700 if cont else 0
+    note(f"sequence segments d={d} P={P} n={n} from {n0} tokens")
+    q, k, v = W.make_qkv(1, 1, n0 + n, d, d, W.BF16, 32000 + d + P + n)
+    b = SA.build_basis(d, P, 1.0)
+    seg_ws = SA.prefill_workspace_bytes(b, 1, 1, n, d, SA.SATA_BF16)
+    monkeypatch.setenv("SATA_PREFILL_SEGMENTS", "0")
+    plain_ws = SA.prefill_workspace_bytes(b, 1, 1, n, d, SA.SATA_BF16)
+    monkeypatch.delenv("SATA_PREFILL_SEGMENTS")
+    assert seg_ws != plain_ws, "this shape should take segments"
+    res = {}
+    for mode in ("seg", "plain"):
+        if mode == "plain":
+            monkeypatch.setenv("SATA_PREFILL_SEGMENTS", "0")
+        st = SA.new_state(b, 1)
+        if n0:
+            run_prefill(b, q[:, :, :n0], k[:, :, :n0], v[:, :, :n0], W.BF16, state=st)
+        out, st = run_prefill(b, q[:, :, n0:], k[:, :, n0:], v[:, :, n0:], W.BF16, state=st)
+        res[mode] = (out.cpu().numpy()[0, 0], st.cpu().numpy()[0])
+        monkeypatch.delenv("SATA_PREFILL_SEGMENTS", raising=False)
+    rows = np.unique(np.concatenate([np.arange(0, n, 97), np.arange(n - 40, n)]))
+    ref = oracle_rows(q[0, 0], k[0, 0], v[0, 0], P, 1.0, rows=n0 + rows)
+    for mode in ("seg", "plain"):
+        assert O.row_normwise_error(res[mode][0][rows], ref) <= TOL[W.BF16], mode
+    assert O.row_normwise_error(res["seg"][0], res["plain"][0]) <= TOL[W.BF16]
+    basis = O.enumerate_basis(d, P)
+    S_ref, z_ref = O.direct_state(f64(k[0, 0]), f64(v[0, 0]), basis)
+    D = b.total_rows
+    gS = res["seg"][1][:D * d].reshape(D, d)
+    gz = res["seg"][1][D * d:D * (d + 1)]
+    off = 0
+    for p in range(P):
+        r = slice(off, off + math.comb(d + p - 1, p))
+        assert np.max(np.abs(gS[r] - S_ref[r])) <= TOL[W.BF16] * np.max(np.abs(S_ref[r])), p
+        assert np.max(np.abs(gz[r] - z_ref[r])) <= TOL[W.BF16] * np.max(np.abs(z_ref[r])), p
+        off = r.stop
+
+
 def test_misaligned_and_host_only_rejected():
     note("misaligned pointers / host-only handle on the GPU")
     b = SA.build_basis(16, 4, 1.0)
