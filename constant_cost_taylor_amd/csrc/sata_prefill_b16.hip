@@ -601,7 +601,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
     const int beta = w + NW * i;
     ldst[i] = -1;
     lstep[i] = 0;
-    if (beta < C::NBLK) {
+    // the state-only scan reads the key and value tables only
+    if (beta < C::NBLK && (!SO || beta / NU < 2)) {
       const int tau = beta / NU, bb = beta % NU;
       const int p = 64 * bb + l;   // 16-byte unit of the table
       if (tau < 3) {
@@ -620,7 +621,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
                              static_cast<int64_t>(head) * nchp * (8 * DK * L);
   // Block i of this wave's share of chunk ch into buffer X.
   auto dma_one = [&](int i, int ch, int X) {
-    if (C::NBLK % NW == 0 || ldst[i] >= 0)
+    if ((!SO && C::NBLK % NW == 0) || ldst[i] >= 0)
       dma16(stg + static_cast<int64_t>(ch) * (8 * DK * L) + ((gofs[i / 2] >> (16 * (i & 1))) & 0xffffu),
             lds + __builtin_amdgcn_readfirstlane(ldst[i] + X * lstep[i]));
   };
