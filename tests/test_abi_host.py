@@ -118,6 +118,28 @@ def test_prefill_workspace_plans(monkeypatch):
     assert e.value.status == SA.SATA_ERR_WORKSPACE
 
 
+def test_prefill_segment_workspace(monkeypatch):
+    """One bf16 head of 2^20 tokens at d = 32 runs as sequence segments: its
+    workspace holds the segment states on top of the segment prefill's; four
+    heads fill the chip at d = 64 and 256 heads at d = 32 take no segments,
+    nor does float32; SATA_PREFILL_SEGMENTS=0 turns them off."""
+    def sizes(d, H, n, code):
+        b = SA.build_basis(d, 4, 1.0, host_only=True)
+        monkeypatch.delenv("SATA_PREFILL_SEGMENTS", raising=False)
+        seg = SA.prefill_workspace_bytes(b, 1, H, n, d, code)
+        monkeypatch.setenv("SATA_PREFILL_SEGMENTS", "0")
+        plain = SA.prefill_workspace_bytes(b, 1, H, n, d, code)
+        monkeypatch.delenv("SATA_PREFILL_SEGMENTS")
+        return b, seg, plain
+    b, seg, plain = sizes(32, 1, 1 << 20, SA.SATA_BF16)
+    assert seg > plain
+    assert seg - plain >= 2 * b.state_stride(32) * 4     # at least two segment states
+    for d, H, n, code in ((64, 4, 16384, SA.SATA_BF16), (32, 256, 4096, SA.SATA_BF16), (32, 1, 1 << 20, SA.SATA_F32),
+                          (32, 1, 1000, SA.SATA_BF16)):
+        _, seg, plain = sizes(d, H, n, code)
+        assert seg == plain, (d, H, n, code)
+
+
 def test_workspace_sizes():
     b = SA.build_basis(64, 4, 1.0, host_only=True)
     assert SA.prefill_workspace_bytes(b, 1, 4, 0, 64, SA.SATA_BF16) == 0
