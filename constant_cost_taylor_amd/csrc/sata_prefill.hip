@@ -524,12 +524,13 @@ __global__ __launch_bounds__(64) void prefill_intra(IntraArgs a) {
 // one late group (equal causal work per SIMD).  For every 32-key slice up to
 // the wave's last query:
 //   X^T = K_s Q_w^T                       (bf16 MFMA, fp32 accumulate)
-//   W'  = T_P(X / c) - 1 by Horner's rule in fp32, zero for keys after the query
+//   W'  = T_P(X / c) - 1 in fp32 (nested with the coefficients 1/(p! c^p),
+//         zero past order P - 1), zero for keys after the query
 //   O^T += V'^T_s M + V'^T_s W_hi + V'^T_s W_lo   (M = the 0/1 causal mask)
 // V' = [v, 1, 0...]: its ones row gives the denominator.  The order-0 term
 // goes through the exact 0/1 mask, and the higher-order weights W' as two
 // bf16 parts (W_hi = bf16(W'), W_lo = bf16(W' - W_hi)), about 2^-17 relative.
-// P5: orders 0..4 (a fourth Horner step; P <= 4 takes three).
+// P5: orders 0..4 (a fourth nesting step; P <= 4 takes three).
 template <int DK, bool P5>
 __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(IntraArgs a) {
   constexpr int DV = DK, T = prefill_window(true);
@@ -622,7 +623,13 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) O[nb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float rcp[5] = {0.f, 1.f, 0.5f, 1.f / 3.f, 0.25f};
+  // W' = T_P(x/c) - 1 = x (a1 + x (a2 + x (a3 + x a4))), a_p = 1 / (p! c^p)
+  // for p < P and 0 beyond: the same nesting for every P, no per-order select
+  const float ic = a.inv_c;
+  const float a1 = a.P > 1 ? ic : 0.f;
+  const float a2 = a.P > 2 ? ic * ic * 0.5f : 0.f;
+  const float a3 = a.P > 3 ? ic * ic * ic * (1.f / 6.f) : 0.f;
+  const float a4 = P5 && a.P > 4 ? ic * ic * ic * ic * (1.f / 24.f) : 0.f;
   const int nslice = min(2 * qg + 2, (nvalid + 31) / 32);
   for (int sl = 0; sl < nslice; ++sl) {
     f32x4 X[2][4];
@@ -649,14 +656,11 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int key = 32 * sl + 16 * (j / 4) + 4 * g + (j % 4);
-        const float x = X[j / 4][qb][j % 4] * a.inv_c;
-        // Horner's rule over orders P-1..1 (unrolled)
-        float h = 0.f;
-#pragma unroll
-        for (int p = P5 ? 4 : 3; p >= 1; --p) {
-          const float hn = x * rcp[p] * (1.f + h);
-          h = p < a.P ? hn : h;
-        }
+        const float x = X[j / 4][qb][j % 4];
+        float h = P5 ? fmaf(x, a4, a3) : a3;
+        h = fmaf(x, h, a2);
+        h = fmaf(x, h, a1);
+        h *= x;
         const bool ok = key <= qi;
         wv[j] = ok ? h : 0.f;
         mv[j] = ok ? 1.f : 0.f;
