@@ -690,12 +690,13 @@ __global__ __launch_bounds__(prefill_window(true)) void prefill_intra_mfma(Intra
       const u32x2 hi = *reinterpret_cast<const u32x2*>(__builtin_assume_aligned(vr + 16, 8));
       const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
       const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+      // the three products of one accumulator four instructions apart
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bm[qb], O[nb][qb], 0, 0, 0);
-        O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bw[qb], O[nb][qb], 0, 0, 0);
-        O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl[qb], O[nb][qb], 0, 0, 0);
-      }
+      for (int qb = 0; qb < 4; ++qb) O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bm[qb], O[nb][qb], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bw[qb], O[nb][qb], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) O[nb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl[qb], O[nb][qb], 0, 0, 0);
     }
   }
   // O^T in C layout: lane holds query 16 qb + lr, value columns 16 nb + 4 g + r;
