@@ -16,7 +16,8 @@
 //                    index-major, queries index-major and token-major; plus
 //                    exact fp32 sums of v per chunk.
 //   prefill_carry    order-0 prefix at each readout-window start, and the
-//                    order-0 row of the state.
+//                    order-0 row of the state (a parallel scan over the
+//                    readout windows, one block per column and head).
 //   prefill_scan_b16 grid = (row tiles) x (heads), 8 waves.  Per chunk the
 //                    staged tables arrive in LDS by DMA (global_load_lds,
 //                    double-buffered, one chunk ahead; the loop runs chunk
@@ -29,6 +30,10 @@
 //                         and order 3 when P = 5), and the update
 //                         S += phi_k(K)^T [V 1].
 //   prefill_reduce_b16  out = (intra + records + carry) / den per token.
+// The state-only scan (the first pass over sequence segments) keeps the
+// update, the key/value DMA and the parent slots, and drops the readout,
+// its 16-bit operand and the records; no intra-window or reduce kernel runs.
+// state_copy, state_zero and state_prefix move the segment states.
 //
 // Feature map.  Rows of a tile come in runs of four children (P, c..c+3) of
 // one parent multiset P (the nested i1 <= ... <= ip index structure); a
