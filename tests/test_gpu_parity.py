@@ -417,6 +417,43 @@ def test_prefill_sequence_segments(d, P, n, cont, monkeypatch):
         off = r.stop
 
 
+def test_prefill_seeded_shapes_and_workspaces():
+    """Seeded shapes (head dim, orders, dtype, heads, length, per-head lengths
+    or not) each run with a workspace drawn between the minimum and the
+    default size (so head groups, windows and segments mix): sampled rows match
+    the oracle."""
+    rng = np.random.default_rng(33000)
+    for case in range(8):
+        d = int(rng.choice([8, 16, 32, 64]))
+        P = int(rng.integers(1, 6)) if d < 64 else int(rng.integers(1, 5))
+        dtype = W.BF16 if rng.random() < 0.7 else W.F32
+        H = int(rng.integers(1, 6))
+        n = int(rng.integers(1, 3000))
+        varlen = bool(rng.random() < 0.3)
+        note(f"seeded case {case}: d={d} P={P} {dtype} H={H} n={n} varlen={varlen}")
+        q, k, v = W.make_qkv(1, H, n, d, d, dtype, 33100 + case)
+        b = SA.build_basis(d, P, 1.0)
+        code = SA.SATA_BF16 if dtype == W.BF16 else SA.SATA_F32
+        full = SA.prefill_workspace_bytes(b, 1, H, n, d, code)
+        least = SA.prefill_workspace_bytes(b, 1, 1, min(n, 512), d, code)
+        nbytes = int(least + rng.random() * max(0, full - least)) // 256 * 256
+        lens = [int(rng.integers(0, n + 1)) for _ in range(H)] if varlen else [n] * H
+        lt = torch.tensor(lens, dtype=torch.int32, device="cuda") if varlen else None
+        out, _ = SA.prefill(b, to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), ws=SA.workspace(max(nbytes, least)),
+                            lengths=lt)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()[0]
+        for h in range(H):
+            L = lens[h]
+            if L == 0:
+                assert np.all(got[h] == 0.0)
+                continue
+            rows = np.unique(np.concatenate([np.arange(0, L, max(1, L // 40)), [L - 1]]))
+            ref = oracle_rows(q[0, h, :L], k[0, h, :L], v[0, h, :L], P, 1.0, rows=rows)
+            assert O.row_normwise_error(got[h, rows], ref) <= TOL[dtype], (case, h)
+            assert np.all(got[h, L:] == 0.0), (case, h)
+
+
 def test_misaligned_and_host_only_rejected():
     note("misaligned pointers / host-only handle on the GPU")
     b = SA.build_basis(16, 4, 1.0)
