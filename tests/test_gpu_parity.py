@@ -373,7 +373,7 @@ def test_prefill_f32_both_tilings():
     assert np.max(np.abs(gs - gf[:, :32])) <= 1e-5 * np.max(np.abs(gf[:, :32]))
 
 
-@pytest.mark.parametrize("d,P,n,cont", [(32, 4, 5000, False), (64, 4, 36864, False), (16, 5, 3584, False),
+@pytest.mark.parametrize("d,P,n,cont", [(32, 4, 5000, False), (64, 4, 36864, False), (16, 5, 3584, False), (16, 4, 8192, True),
                                         (32, 4, 4608, True), (8, 4, 6000, False)])
 def test_prefill_sequence_segments(d, P, n, cont, monkeypatch):
     """One head of a long sequence runs as parallel sequence segments (state
