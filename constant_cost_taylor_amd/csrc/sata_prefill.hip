@@ -132,6 +132,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   using C = Cfg<DK, RB_>;
   constexpr int DV = C::DV, L = C::L, RB = C::RB, NB = C::NB, NC = C::NC, DVP = C::DVP;
   constexpr int NSLOT = C::NSLOT, KSTR = C::KSTR, QSTR = C::QSTR, XQSTR = C::XQSTR;
+  // d_v a multiple of 16: the denominator column would fill a 16-wide MFMA
+  // block of its own (half the blocks at d = 16), so z and phi_q.z run on
+  // VALU instead; the MFMA blocks hold value columns only.
+  constexpr bool VDEN = DV % 16 == 0;
+  constexpr int NBM = VDEN ? NB - 1 : NB;
   constexpr int RSTR = C::RSTR, XK_ZERO = C::XK_ZERO, MB = C::MB, EPT = C::EPT;
   using IT = float;
   using RedT = float;
@@ -192,28 +197,32 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
   for (int b = 0; b < RB; ++b)
 #pragma unroll
     for (int r = 0; r < 4; ++r) info[b][r] = a.lay.rowinfo[(lay_base + b) * 16 + 4 * g + r];
-  f32x4 S[RB][NB];
+  f32x4 S[RB][NBM];
+  // VDEN: z of rows 4 g + r of block b, the same in every lane of group g
+  float zr[VDEN ? RB : 1][4];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t m = info[b][r] ? (info[b][r] & 0x0fffffffu) - 1 : 0u;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
+      for (int nb = 0; nb < NBM; ++nb) {
         const int col = nb * 16 + lr;
         S[b][nb][r] = st[col < DV ? m * DV + col : static_cast<uint32_t>(zoff) + m];
       }
+      if constexpr (VDEN) zr[b][r] = st[static_cast<uint32_t>(zoff) + m];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float inv_cnt = info[b][r] ? 1.f / static_cast<float>(info[b][r] >> 28) : 0.f;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) S[b][nb][r] = (nb * 16 + lr <= DV) ? S[b][nb][r] * inv_cnt : 0.f;
+      for (int nb = 0; nb < NBM; ++nb) S[b][nb][r] = (nb * 16 + lr <= DV) ? S[b][nb][r] * inv_cnt : 0.f;
+      if constexpr (VDEN) zr[b][r] *= inv_cnt;
     }
     // Move the block into accumulator registers right away, so the whole
     // tile is never held in VGPRs at once.
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(S[b][nb]));
+    for (int nb = 0; nb < NBM; ++nb) asm volatile("" : "+a"(S[b][nb]));
     __builtin_amdgcn_sched_barrier(0);
   }
   if (tile == 0 && tid < NC) carry[tid] = tid < DV ? st[tid] : (tid == DV ? st[zoff] : 0.f);
@@ -339,11 +348,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     // (two 16-token blocks at a time), written to the reduction buffer.
 #pragma unroll
     for (int half = 0; half < MB / 2; ++half) {
-      f32x4 acc[2][NB];
+      f32x4 acc[2][NBM];
+      float dn[2] = {0.f, 0.f};   // VDEN: phi_q.z over the lane's rows, token 16 mb + lr
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NBM; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         const int slot = qs[b] & 0xffff;
@@ -357,17 +367,31 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NBM; ++nb)
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], S[b][nb][r], acc[mb][nb], 0, 0, 0);
+          if constexpr (VDEN) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dn[mb] = fmaf(av[r], zr[b][r], dn[mb]);
+          }
         }
       }
-    
+      if constexpr (VDEN) {
+        // over the four lane groups (rows 4 g + r), then one store a token
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          float d = dn[mb];
+          d += __shfl_xor(d, 16);
+          d += __shfl_xor(d, 32);
+          if (g == 0) red[(w * (DV + 1) + DV) * RSTR + (2 * half + mb) * 16 + lr] = d;
+        }
+      }
+
       // C layout: lane holds column nb*16 + lr of tokens 4g..4g+3 -> one
       // 4-token vector store per (block, column block).
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int nb = 0; nb < NBM; ++nb) {
           const int col = nb * 16 + lr;
           if (col <= DV) {
             RedT* dst = &red[(w * (DV + 1) + col) * RSTR + (2 * half + mb) * 16 + 4 * g];
@@ -378,20 +402,36 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
     }
 
     // ---- phase C: state update S += phi_k(K)^T [V 1] ----------------------
+    float zinc[VDEN ? RB : 1];   // VDEN: sum of phi_k(row lr) over the lane's tokens
+#pragma unroll
+    for (int b = 0; b < (VDEN ? RB : 1); ++b) zinc[b] = 0.f;
 #pragma unroll
     for (int kst = 0; kst < L / 4; ++kst) {
       const int t = 4 * kst + g;
-      float bv[NB];
+      float bv[NBM];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bv[nb] = vv[t * NC + nb * 16 + lr];
+      for (int nb = 0; nb < NBM; ++nb) bv[nb] = vv[t * NC + nb * 16 + lr];
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         const int pko = ks[b] & 0xffff;
         const int xko = ks[b] >> 16;
         const float av = pk[pko + t] * xk[xko + t];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NBM; ++nb)
           S[b][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[nb], S[b][nb], 0, 0, 0);
+        if constexpr (VDEN) zinc[b] += av;
+      }
+    }
+    if constexpr (VDEN) {
+      // z of row lr gains the sum over the four token groups; lane (lr, g)
+      // keeps rows 4 g + r, found in lanes 4 g + r of group 0
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        float x = zinc[b];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zr[b][r] += __shfl(x, 4 * g + r);
       }
     }
   
@@ -418,10 +458,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefill_scan(ScanArgs a) {
       const uint32_t m = (info2[b][r] & 0x0fffffffu) - 1;
       const float cnt = static_cast<float>(info2[b][r] >> 28);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
+      for (int nb = 0; nb < NBM; ++nb) {
         const int col = nb * 16 + lr;
         if (info2[b][r] != 0u && col <= DV)
           stw[col < DV ? m * DV + col : static_cast<uint32_t>(zoff) + m] = S[b][nb][r] * cnt;
+      }
+      if constexpr (VDEN) {
+        if (info2[b][r] != 0u && lr == 0) stw[static_cast<uint32_t>(zoff) + m] = zr[b][r] * cnt;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
