@@ -20,6 +20,8 @@
 //                  nested i1 <= ... <= ip structure of the index matrices),
 //                  reads out  phi_q(Q_t) S  and updates  S += phi_k(K_t)^T [V_t 1]
 //                  on fp32 MFMA, and writes one readout record per token.
+//                  Where d_v is a multiple of 16, z and phi_q.z run on VALU
+//                  (the den column would take an MFMA block of its own).
 //                  Tile 0 also records the exact order-0 prefix of every chunk.
 //   prefill_intra  grid = (chunks) x (heads): the intra-chunk part, fp32.
 //   prefill_reduce sums the records in a fixed order and divides.
