@@ -146,7 +146,7 @@ constexpr int kAmaxSplit = 32;
 //                                   columns (16-bit at d >= 32: f16 for heads
 //                                   on the f16 operand path, else bf16; fp32
 //                                   below d = 32)
-//   recs:  [BH][n_tiles][nwp/64]    scale of each 64-token chunk of f16
+//   recs:  [BH][nwp/64][n_tiles]    scale of each 64-token chunk of f16
 //                                   records (d >= 32)
 //   recz:  [BH][n_tiles][nwp]       per-tile den records (fp32)
 //   intra: [BH][nwp][DVP]           intra-window records (fp32)

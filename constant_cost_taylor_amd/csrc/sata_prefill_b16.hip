@@ -756,7 +756,8 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
   const int nwp = a.ws.nwp;
   RedT* rech = static_cast<RedT*>(a.ws.rec) + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * nwp * DV;
   float* reczh = a.ws.recz + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * nwp;
-  float* recsh = a.ws.recs + (static_cast<int64_t>(head) * a.lay.n_tiles + tile) * (nwp / L);
+  // chunk scales [head][chunk][tile]: a reduce block reads its chunk's tiles contiguously
+  float* recsh = a.ws.recs + static_cast<int64_t>(head) * (nwp / L) * a.lay.n_tiles + tile;
   static_assert(NW * 32768 <= (32768 << kRecShift), "f16 records stay in range");
   const uint16_t* red = reinterpret_cast<const uint16_t*>(lds + C::O_RED);
   const uint16_t* redl = reinterpret_cast<const uint16_t*>(lds + C::O_REDL);
@@ -832,7 +833,7 @@ __device__ __forceinline__ void scan_tile(const ScanArgs& a, const HalfScales& h
       }
     }
     if constexpr (std::is_same<RedT, uint16_t>::value && H16) {
-      if (tid == 0) recsh[ch] = ldexpf(1.f, ew + kRecShift);
+      if (tid == 0) recsh[static_cast<int64_t>(ch) * a.lay.n_tiles] = ldexpf(1.f, ew + kRecShift);
     }
     if (tid >= (NW - 1) * 64) {
       float sz = 0.f;
@@ -1148,9 +1149,10 @@ __global__ __launch_bounds__(prefill_waves(true) * 64, 1) void prefill_scan_b16(
 
 // ---------------------------------------------------------------------------
 // out = (intra + sum over tiles of the records + carry) for num / for den,
-// summed in a fixed order.  Block = (64 tokens, head); den per token first
-// (four interleaved tile sums, combined in order), then value items of 8
-// columns.  Records are read once: non-temporal loads, four tiles in flight.
+// summed in a fixed order.  Block = (32 tokens, head); den per token first
+// (eight interleaved tile sums, combined in order), then value items of 8
+// columns.  Records are read once: non-temporal loads, sixteen (or eight)
+// tiles in flight a thread.
 // Reduce blocks: 32 tokens x 256 threads (64 x 256: 1.5 % slower; 16 x 128
 // and 32 x 128: 5-17 % slower, 64 heads x 4096 tokens at d = 64).
 constexpr int kRedTok = 32;           // tokens per reduce block
@@ -1209,7 +1211,7 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
   float* out = a.out + (static_cast<int64_t>(head) * a.n_total + a.t0) * DV;
   // f16 records: scale of this block's chunk (32 | 64) per tile
   const int nchp = nwp / 64;
-  const float* rsc = a.ws.recs + static_cast<int64_t>(head) * nt * nchp + t0 / 64;
+  const float* rsc = a.ws.recs + (static_cast<int64_t>(head) * nchp + t0 / 64) * nt;
   for (int e = tid; e < ntok * NU; e += kRedThr) {
     const int tt = e / NU, u = e % NU;
     const int t = t0 + tt;
@@ -1220,20 +1222,24 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
     const int64_t tstride = static_cast<int64_t>(nwp) * DV;
     int tl = 0;
     if constexpr (std::is_same<RedT, uint16_t>::value) {
-      // groups of eight record loads in flight, folded in tile order; f16
-      // records (heads on the f16 operand path) times their chunk scale
-      auto sum16 = [&](auto f16c) {
+      // groups of G record loads in flight, folded in tile order; f16
+      // records (heads on the f16 operand path) times their chunk scale.
+      // G = 16 up to 256 tiles (eight: 4 % slower at d = 64, P = 4, 101
+      // tiles), else 8 (sixteen: 25-40 % slower at d = 64, P = 5, 1745 tiles
+      // whose records lie 512 KB apart)
+      auto sum16 = [&](auto f16c, auto gc) {
         constexpr bool F16 = decltype(f16c)::value;
-        for (; tl + 7 < nt; tl += 8) {
-          u32x4 x[8];
-          float sv[8];
+        constexpr int G = decltype(gc)::value;
+        for (; tl + G - 1 < nt; tl += G) {
+          u32x4 x[G];
+          float sv[G];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < G; ++i) {
             x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + (tl + i) * tstride));
-            sv[i] = F16 ? rsc[static_cast<int64_t>(tl + i) * nchp] : 1.f;
+            sv[i] = F16 ? rsc[tl + i] : 1.f;
           }
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
+          for (int i = 0; i < G; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const uint32_t xj = x[i][j];
@@ -1248,7 +1254,7 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
         }
         for (; tl < nt; ++tl) {
           const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + tl * tstride));
-          const float sv = F16 ? rsc[static_cast<int64_t>(tl) * nchp] : 1.f;
+          const float sv = F16 ? rsc[tl] : 1.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if constexpr (F16) {
@@ -1261,10 +1267,19 @@ __global__ __launch_bounds__(kRedThr) void prefill_reduce_b16(ReduceArgs a) {
           }
         }
       };
-      if (hs.safe)
-        sum16(std::true_type{});
-      else
-        sum16(std::false_type{});
+      using G16 = std::integral_constant<int, 16>;
+      using G8 = std::integral_constant<int, 8>;
+      if (nt <= 256) {
+        if (hs.safe)
+          sum16(std::true_type{}, G16{});
+        else
+          sum16(std::false_type{}, G16{});
+      } else {
+        if (hs.safe)
+          sum16(std::true_type{}, G8{});
+        else
+          sum16(std::false_type{}, G8{});
+      }
     } else {
 #pragma unroll 4
       for (; tl < nt; ++tl) {
