@@ -41,7 +41,7 @@ METRIC = "causal SATA tokens/sec/head (prefill, decode) + % of HBM/MFMA roofline
 # FETCH_SIZE / WRITE_SIZE counters scaled by a 1 GiB copy
 # (profiles/decode_update_readout_256x4096_d64_hbm_traffic.txt).  Re-measure after any
 # change to the decode kernel.
-DECODE_TRAFFIC_BYTES = 6.6518e9
+DECODE_TRAFFIC_BYTES = 6.5784e9
 # The same for one decode_mixed launch (mixed-precision state, same workload).
 MIXED_DECODE_TRAFFIC_BYTES = 3.4535e9
 

@@ -17,12 +17,17 @@
 // partial sums; a second kernel reduces the per-tile partials in a fixed
 // order and divides (with few states and many tiles, in two passes so the
 // reduce still spreads over the chip).  Small one-shot blocks stream this read-modify-write at
-// 6.2 TB/s where 512-row blocks that loop over their rows reach 5.3 (the
-// partials add 3.3 % to the traffic).  The state is touched once per step and
+// 6.2 TB/s where 512-row blocks that loop over their rows reach 5.3.  With
+// bf16 inputs the value partials go out as 16-bit records (f16 with a
+// power-of-two scale per tile; fp32 for the tiles of the order-0 and order-1
+// rows), half the bytes the reduce reads.  The state is touched once per step and
 // is far larger than the caches, so its loads and stores carry the
 // non-temporal hint.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
+#include "sata_device.h"
 #include "sata_internal.h"
 
 namespace sata {
@@ -109,11 +114,45 @@ __device__ __forceinline__ void tile_partials(const float* red, const float* dre
   }
 }
 
+// The same sums as 16-bit records (bf16 inputs): the value partials of tile
+// `tile` of state s as f16 times a power of two that puts the tile's largest
+// below 2^15 (the first lo_t tiles, the rows of orders 0 and 1, keep fp32
+// records), den as fp32.
+template <int DV, int RPP>
+__device__ __forceinline__ void tile_partials_c16(const float* red, const float* dred, const DecodeArgs& a, int s,
+                                                  int tile) {
+  static_assert(DV <= 64, "the value columns fit one wave");
+  const int tid = threadIdx.x;
+  const int64_t pi = static_cast<int64_t>(s) * a.n_tiles + tile;
+  if (tid < 64) {
+    float sum = 0.f;
+    if (tid < DV)
+      for (int j = 0; j < RPP; ++j) sum += red[j * DV + tid];
+    if (tile < a.lo_t) {
+      if (tid < DV) a.partlo[(static_cast<int64_t>(s) * a.lo_t + tile) * DV + tid] = sum;
+    } else {
+      const float m = wave_max(fabsf(sum));
+      int e = 0;
+      if (m > 0.f) (void)frexpf(m, &e);     // m < 2^e
+      const int es = m > 0.f ? max(e - 15, -100) : 0;
+      if (tid < DV)
+        a.part16[pi * DV + tid] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sum * ldexpf(1.f, -es)));
+      if (tid == 0) a.psc[pi] = ldexpf(1.f, es);
+    }
+  }
+  if (tid == DV) {
+    float sum = 0.f;
+    for (int j = 0; j < kDecodeThreads / 64; ++j) sum += dred[j];
+    a.partz[pi] = sum;
+  }
+}
+
 // One tile of fp32 rows [r0, r0 + nrows) of state s: S4 = its first row, z =
-// its first z value.  Rank-1 update, store, readout partial into part/partz.
-template <int DK, typename IT, bool AL>
+// its first z value.  Rank-1 update, store, readout partial into part/partz
+// (C16: the 16-bit records of tile `tile`).
+template <int DK, typename IT, bool AL, bool C16>
 __device__ __forceinline__ void f32_tile(const DecodeArgs& a, int s, float* S4, float* z, int r0, int nrows,
-                                         float* part, float* partz) {
+                                         float* part, float* partz, int tile) {
   constexpr int DV = DK;
   constexpr int TPR = DV / 4;          // threads per S row, one float4 each
   constexpr int RPP = kDecodeThreads / TPR;  // rows per pass of the block
@@ -185,9 +224,13 @@ __device__ __forceinline__ void f32_tile(const DecodeArgs& a, int s, float* S4, 
   for (int o = 32; o > 0; o >>= 1) dacc += __shfl_xor(dacc, o);
   if ((tid & 63) == 0) dred[tid >> 6] = dacc;
   __syncthreads();
-  tile_partials<DV, RPP>(red, dred, part, partz);
+  if constexpr (C16)
+    tile_partials_c16<DV, RPP>(red, dred, a, s, tile);
+  else
+    tile_partials<DV, RPP>(red, dred, part, partz);
 }
 
+// bf16 inputs write 16-bit records, fp32 inputs fp32 ones.
 template <int DK, typename IT, bool AL>
 __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeArgs a) {
   constexpr int R = decode_rows(DK);
@@ -197,8 +240,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_update_readout(DecodeAr
   const int nrows = min(R, a.D - r0);
   float* st = a.state + static_cast<int64_t>(s) * a.stride;
   const int64_t pi = static_cast<int64_t>(s) * a.n_tiles + tile;
-  f32_tile<DK, IT, AL>(a, s, st + static_cast<int64_t>(r0) * DK, st + static_cast<int64_t>(a.D) * DK + r0, r0, nrows,
-                       a.part + pi * DK, a.partz + pi);
+  constexpr bool C16 = std::is_same<IT, uint16_t>::value;
+  f32_tile<DK, IT, AL, C16>(a, s, st + static_cast<int64_t>(r0) * DK, st + static_cast<int64_t>(a.D) * DK + r0, r0,
+                            nrows, C16 ? nullptr : a.part + pi * DK, C16 ? nullptr : a.partz + pi, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -353,9 +397,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mixed(MixedDecodeArgs a
     d.v = a.v;
     d.rows = a.rows;
     d.weight = a.weight;
-    f32_tile<DK, IT, true>(d, s, st + static_cast<int64_t>(r0) * DK,
-                           reinterpret_cast<float*>(base + a.off_z) + r0, r0, min(R32, a.lo - r0),
-                           a.part + pi * DK, a.partz + pi);
+    f32_tile<DK, IT, true, false>(d, s, st + static_cast<int64_t>(r0) * DK,
+                                  reinterpret_cast<float*>(base + a.off_z) + r0, r0, min(R32, a.lo - r0),
+                                  a.part + pi * DK, a.partz + pi, tile);
   } else {
     f16_tile<DK, IT>(a, s, tile - a.nt32, a.part + pi * DK, a.partz + pi);
   }
@@ -432,10 +476,15 @@ __global__ __launch_bounds__(kDecodeThreads) void mixed_convert(MixedConvArgs a)
 // block of kRedThreads: groups of DV/4 threads sum interleaved records
 // (float4 columns, 8 loads in flight), then a fixed-order combine.
 constexpr int kRedThreads = 1024;
-template <int DV, bool FINAL>
+// C16: value records as written by tile_partials_c16 (p16: f16 records, psc
+// their scales, plo the fp32 records of the first lo_t tiles).
+template <int DV, bool FINAL, bool C16>
 __global__ __launch_bounds__(kRedThreads) void decode_reduce(const float* __restrict__ part_in,
                                                              const float* __restrict__ partz_in, int nrec,
-                                                             int per, float* nxt, float* nxtz, float* out) {
+                                                             int per, float* nxt, float* nxtz, float* out,
+                                                             const uint16_t* __restrict__ p16,
+                                                             const float* __restrict__ psc,
+                                                             const float* __restrict__ plo, int lo_t) {
   constexpr int Q = DV / 4;              // float4 columns per record
   constexpr int G = kRedThreads / Q;     // record groups
   __shared__ float4 red[G * Q];
@@ -448,7 +497,7 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(const float* __rest
   const int tid = threadIdx.x;
   const int grp = tid / Q;
   const int c = tid % Q;
-  const float4* part = reinterpret_cast<const float4*>(part_in + static_cast<int64_t>(s) * nrec * DV);
+  const float4* part = C16 ? nullptr : reinterpret_cast<const float4*>(part_in + static_cast<int64_t>(s) * nrec * DV);
   const float* partz = partz_in + static_cast<int64_t>(s) * nrec;
   {
     float z = 0.f;
@@ -458,24 +507,62 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(const float* __rest
   if (grp < G) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int t = t0 + grp;
-    for (; t + 7 * G < t1; t += 8 * G) {
-      float4 x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = part[static_cast<int64_t>(t + u * G) * Q + c];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc.x += x[u].x;
-        acc.y += x[u].y;
-        acc.z += x[u].z;
-        acc.w += x[u].w;
+    if constexpr (C16) {
+      // the records in the same order as fp32 ones: an fp32 record of a
+      // low-order tile first (t < lo_t <= G happens only for t = grp of the
+      // first block), then f16 records times their scales
+      if (t < lo_t && t < t1) {
+        const float4 x = reinterpret_cast<const float4*>(plo + (static_cast<int64_t>(s) * lo_t + t) * DV)[c];
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+        t += G;
       }
-    }
-    for (; t < t1; t += G) {
-      const float4 x = part[static_cast<int64_t>(t) * Q + c];
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+      const uint2* q16 = reinterpret_cast<const uint2*>(p16 + static_cast<int64_t>(s) * nrec * DV);
+      const float* sc = psc + static_cast<int64_t>(s) * nrec;
+      auto add16 = [&](uint2 x, float f) {
+        const _Float16 h0 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(x.x & 0xffffu));
+        const _Float16 h1 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(x.x >> 16));
+        const _Float16 h2 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(x.y & 0xffffu));
+        const _Float16 h3 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(x.y >> 16));
+        acc.x += static_cast<float>(h0) * f;
+        acc.y += static_cast<float>(h1) * f;
+        acc.z += static_cast<float>(h2) * f;
+        acc.w += static_cast<float>(h3) * f;
+      };
+      for (; t + 7 * G < t1; t += 8 * G) {
+        uint2 x[8];
+        float f[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          x[u] = q16[static_cast<int64_t>(t + u * G) * Q + c];
+          f[u] = sc[t + u * G];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) add16(x[u], f[u]);
+      }
+      for (; t < t1; t += G) add16(q16[static_cast<int64_t>(t) * Q + c], sc[t]);
+    } else {
+      for (; t + 7 * G < t1; t += 8 * G) {
+        float4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = part[static_cast<int64_t>(t + u * G) * Q + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          acc.x += x[u].x;
+          acc.y += x[u].y;
+          acc.z += x[u].z;
+          acc.w += x[u].w;
+        }
+      }
+      for (; t < t1; t += G) {
+        const float4 x = part[static_cast<int64_t>(t) * Q + c];
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+      }
     }
     red[grp * Q + c] = acc;
   }
@@ -508,21 +595,28 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(const float* __rest
 }
 
 // The fixed-order reduce of a step's partial records (one or two passes).
-template <int D>
+// C16: the step's records are 16-bit ones (a.part16, a.psc, a.partlo).
+template <int D, bool C16>
 hipError_t launch_reduce(const float* part, const float* partz, float* out, int S, int n_tiles, int groups,
-                         float* part2, float* partz2, hipStream_t st) {
+                         float* part2, float* partz2, const DecodeArgs* c16, hipStream_t st) {
+  const uint16_t* p16 = C16 ? c16->part16 : nullptr;
+  const float* psc = C16 ? c16->psc : nullptr;
+  const float* plo = C16 ? c16->partlo : nullptr;
+  const int lo_t = C16 ? c16->lo_t : 0;
   if (groups <= 1) {
-    decode_reduce<D, true><<<dim3(1, S), kRedThreads, 0, st>>>(part, partz, n_tiles, n_tiles, nullptr, nullptr, out);
+    decode_reduce<D, true, C16><<<dim3(1, S), kRedThreads, 0, st>>>(part, partz, n_tiles, n_tiles, nullptr, nullptr,
+                                                                     out, p16, psc, plo, lo_t);
     return hipGetLastError();
   }
   // Few states: the tiles of a state are split over `groups` blocks, whose
   // sums a second pass combines (in group order).
   const int per = (n_tiles + groups - 1) / groups;
-  decode_reduce<D, false><<<dim3(groups, S), kRedThreads, 0, st>>>(part, partz, n_tiles, per, part2, partz2,
-                                                                   nullptr);
+  decode_reduce<D, false, C16><<<dim3(groups, S), kRedThreads, 0, st>>>(part, partz, n_tiles, per, part2, partz2,
+                                                                         nullptr, p16, psc, plo, lo_t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_reduce<D, true><<<dim3(1, S), kRedThreads, 0, st>>>(part2, partz2, groups, groups, nullptr, nullptr, out);
+  decode_reduce<D, true, false><<<dim3(1, S), kRedThreads, 0, st>>>(part2, partz2, groups, groups, nullptr, nullptr,
+                                                                     out, nullptr, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -540,7 +634,8 @@ hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
     decode_update_readout<D, float, false><<<grid, kDecodeThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_reduce<D>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, st);
+  if (bf16) return launch_reduce<D, true>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, &a, st);
+  return launch_reduce<D, false>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, nullptr, st);
 }
 
 template <int D>
@@ -552,7 +647,7 @@ hipError_t launch_mixed_d(bool bf16, const MixedDecodeArgs& a, hipStream_t st) {
     decode_mixed<D, float><<<grid, kDecodeThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_reduce<D>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, st);
+  return launch_reduce<D, false>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, nullptr, st);
 }
 
 template <int D>

@@ -697,6 +697,45 @@ int decode_tiles(const sata_basis* b) {
   return static_cast<int>((b->D + rows - 1) / rows);
 }
 
+// Decode workspace regions.  fp32 inputs: value records [S][tiles][d_v] and
+// den records [S][tiles], fp32.  bf16 inputs (16-bit records): f16 value
+// records [S][tiles][d_v], their scales [S][tiles], the fp32 value records of
+// the first lo_t tiles [S][lo_t][d_v], den records [S][tiles].  Then, with
+// more than one reduce group a state, the fp32 second-level partials
+// [S][groups][d_v] and [S][groups].  Each region 256-byte aligned.
+struct DecodeWs {
+  size_t part = 0, p16 = 0, psc = 0, plo = 0, partz = 0, part2 = 0, partz2 = 0, total = 0;
+};
+DecodeWs decode_ws(const sata_basis* b, int S, int d_v, bool c16) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const int tiles = decode_tiles(b);
+  const int groups = sata::decode_groups(S, tiles);
+  const size_t ST = static_cast<size_t>(S) * tiles;
+  DecodeWs w;
+  size_t off = 0;
+  if (c16) {
+    w.p16 = off;
+    off += up(ST * d_v * 2);
+    w.psc = off;
+    off += up(ST * 4);
+    w.plo = off;
+    off += up(static_cast<size_t>(S) * sata::decode_lo_tiles(b->d) * d_v * 4);
+  } else {
+    w.part = off;
+    off += up(ST * d_v * 4);
+  }
+  w.partz = off;
+  off += up(ST * 4);
+  if (groups > 1) {
+    w.part2 = off;
+    off += up(static_cast<size_t>(S) * groups * d_v * 4);
+    w.partz2 = off;
+    off += up(static_cast<size_t>(S) * groups * 4);
+  }
+  w.total = off;
+  return w;
+}
+
 // Mixed-precision state layout of one state (bytes from its base).
 struct MixedPlan {
   int lo = 0, nt32 = 0, nt16 = 0;
@@ -946,10 +985,7 @@ int sata_decode_workspace(const sata_basis* b, int S, int d_v, int dtype, size_t
   if (!b || !bytes || S < 0) return SATA_ERR_INVALID_ARG;
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
-  const int tiles = decode_tiles(b);
-  const int groups = sata::decode_groups(S, tiles);
-  *bytes = decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
-  if (groups > 1) *bytes += decode_part_bytes(S, groups, d_v) + decode_partz_bytes(S, groups);
+  *bytes = decode_ws(b, S, d_v, dtype == SATA_BF16).total;
   return SATA_OK;
 }
 
@@ -975,15 +1011,17 @@ static int decode_launch(const sata_basis* b, int S, int d_v, int dtype, const v
                          const void* v, float* out, float* state, int64_t state_stride, void* ws,
                          void* stream) {
   const int tiles = decode_tiles(b);
-  float* part = static_cast<float*>(ws);
-  float* partz = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v));
   const int groups = sata::decode_groups(S, tiles);
-  char* lvl2 = static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
-  float* part2 = groups > 1 ? reinterpret_cast<float*>(lvl2) : nullptr;
-  float* partz2 = groups > 1 ? reinterpret_cast<float*>(lvl2 + decode_part_bytes(S, groups, d_v)) : nullptr;
+  const bool c16 = dtype == SATA_BF16;
+  const DecodeWs w = decode_ws(b, S, d_v, c16);
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   sata::DecodeArgs a{q, k, v, state, state_stride,
-                     part, partz, out, b->d_rows, b->d_weight, S,
-                     static_cast<int>(b->D), tiles, groups, part2, partz2};
+                     c16 ? nullptr : at(w.part), at(w.partz), out, b->d_rows, b->d_weight, S,
+                     static_cast<int>(b->D), tiles, groups,
+                     groups > 1 ? at(w.part2) : nullptr, groups > 1 ? at(w.partz2) : nullptr,
+                     c16 ? reinterpret_cast<uint16_t*>(base + w.p16) : nullptr, c16 ? at(w.psc) : nullptr,
+                     c16 ? at(w.plo) : nullptr, c16 ? sata::decode_lo_tiles(b->d) : 0};
   if (sata::launch_decode(b->d, dtype == SATA_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SATA_ERR_HIP;
   return SATA_OK;

@@ -217,7 +217,7 @@ struct DecodeArgs {
   const void* v;
   float* state;          // [S][stride]
   int64_t stride;        // floats between consecutive states
-  float* part;           // [S][n_tiles][dv]  readout partials of the value columns
+  float* part;           // [S][n_tiles][dv]  readout partials of the value columns (fp32 records)
   float* partz;          // [S][n_tiles]      readout partials of den
   float* out;            // [S][dv]
   const uint32_t* rows;  // packed multiset of every row
@@ -228,7 +228,19 @@ struct DecodeArgs {
   int groups;            // reduce blocks per state (1: one pass)
   float* part2;          // [S][groups][dv]   second-level partials (groups > 1)
   float* partz2;         // [S][groups]
+  // 16-bit records (bf16 inputs): value partials of tiles >= lo_t as f16
+  // times a per-tile power of two, those of the first lo_t tiles (the rows
+  // of orders 0 and 1) in fp32; part is unused then.
+  uint16_t* part16;      // [S][n_tiles][dv]  (tiles < lo_t unused)
+  float* psc;            // [S][n_tiles]      scale of each f16 record
+  float* partlo;         // [S][lo_t][dv]
+  int lo_t;
 };
+
+// Decode tiles whose rows include orders 0 and 1 (rows [0, 1 + d)): their
+// readout partials carry most of the output and stay fp32 in the 16-bit
+// record format.
+constexpr int decode_lo_tiles(int d) { return (1 + d + decode_rows(d) - 1) / decode_rows(d); }
 
 // Reduce blocks per decode state: enough to give the chip about 256 blocks
 // when there are few states, each summing at least 256 tile records (a

@@ -98,22 +98,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-// Max over the wave (DPP: prefix maxima within rows of 16, then across rows;
-// lane 63 ends with the total).
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float x) {
-  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false);
-  return fmaxf(x, __int_as_float(y));
-}
-__device__ __forceinline__ float wave_max(float x) {
-  x = dpp_max<0x111>(x);   // row_shr:1
-  x = dpp_max<0x112>(x);   // row_shr:2
-  x = dpp_max<0x114>(x);   // row_shr:4
-  x = dpp_max<0x118>(x);   // row_shr:8
-  x = dpp_max<0x142>(x);   // row_bcast:15
-  x = dpp_max<0x143>(x);   // row_bcast:31
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
 
 // 16 bytes a lane from global memory straight into LDS (lane l writes bytes
 // [16 l, 16 l + 16) after the wave-uniform LDS address).

@@ -279,7 +279,8 @@ int sata_softmax_attention(int B, int H, int n, int d, int dtype, double c, cons
  * sata_decode_noalloc_max_bytes() bytes (32 MiB), one per device, held until
  * the process ends and resolved once per device when a basis is built there.
  * A call whose sata_decode_workspace exceeds that size returns
- * SATA_ERR_SCRATCH (at d = 64, P = 4: up to 43 states a call) and launches
+ * SATA_ERR_SCRATCH (at d = 64, P = 4: up to 81 states a call with bf16
+ * inputs, 43 with fp32 inputs) and launches
  * nothing.  The call itself allocates and frees nothing.  Every call on one
  * device shares that device's array: calls that overlap in time on one
  * device (other streams, other threads) race and must be serialised by the

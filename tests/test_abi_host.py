@@ -147,16 +147,24 @@ def test_workspace_sizes():
     big = SA.prefill_workspace_bytes(b, 1, 4, 16384, 64, SA.SATA_BF16)
     assert 0 < small < big
     # decode: per tile of 16 rows (two rows of 64 floats per thread of a
-    # 128-thread block) and state, d_v value partials and one den partial, in
-    # two 256-byte aligned regions
+    # 128-thread block) and state, d_v value partials and one den partial.
+    # fp32 inputs: fp32 records in two 256-byte aligned regions.  bf16
+    # inputs: f16 value records, one scale a record, fp32 value records for
+    # the 5 tiles holding rows 0..64 (orders 0 and 1), fp32 den records.
     tiles = math.ceil(47905 / 16)
+    lo_t = math.ceil(65 / 16)
     up = lambda x: (x + 255) // 256 * 256
-    assert SA.decode_workspace_bytes(b, 256, 64, SA.SATA_BF16) == up(256 * tiles * 64 * 4) + up(256 * tiles * 4)
+    assert SA.decode_workspace_bytes(b, 256, 64, SA.SATA_F32) == up(256 * tiles * 64 * 4) + up(256 * tiles * 4)
+    assert SA.decode_workspace_bytes(b, 256, 64, SA.SATA_BF16) == (up(256 * tiles * 64 * 2) + up(256 * tiles * 4) +
+                                                                   up(256 * lo_t * 64 * 4) + up(256 * tiles * 4))
     # three states: the tile records are reduced in 11 groups (256 records or
-    # more each), whose sums take a second region
+    # more each), whose fp32 sums take two more regions
     groups = min(-(-256 // 3), tiles // 256)
     assert groups == 11
-    assert SA.decode_workspace_bytes(b, 3, 64, SA.SATA_BF16) == (up(3 * tiles * 64 * 4) + up(3 * tiles * 4) +
+    assert SA.decode_workspace_bytes(b, 3, 64, SA.SATA_F32) == (up(3 * tiles * 64 * 4) + up(3 * tiles * 4) +
+                                                                up(3 * groups * 64 * 4) + up(3 * groups * 4))
+    assert SA.decode_workspace_bytes(b, 3, 64, SA.SATA_BF16) == (up(3 * tiles * 64 * 2) + up(3 * tiles * 4) +
+                                                                 up(3 * lo_t * 64 * 4) + up(3 * tiles * 4) +
                                                                  up(3 * groups * 64 * 4) + up(3 * groups * 4))
 
 
@@ -192,7 +200,7 @@ def test_noalloc_decode_size_limit_on_host():
     S = 1
     while SA.decode_workspace_bytes(b, S, 64, SA.SATA_BF16) <= cap:
         S += 1
-    assert S == 44
+    assert S == 82
     assert L.sata_decode_step_noalloc(b.handle, S, 64, SA.SATA_BF16, p, p, p, p, p, F, None) == SA.SATA_ERR_SCRATCH
     assert L.sata_decode_step_noalloc(b.handle, S - 1, 64, SA.SATA_BF16, p, p, p, p, p, F,
                                       None) == SA.SATA_ERR_INVALID_ARG

@@ -63,7 +63,7 @@ def test_decode_noalloc_matches_workspace_call(d, P, S1, S2):
     big = S1
     while SA.decode_workspace_bytes(b, big, d, SA.SATA_BF16) <= cap:
         big += 1
-    if big <= 64:
+    if big <= 128:
         qb = torch.zeros((big, d), dtype=torch.bfloat16, device="cuda")
         ob = torch.zeros((big, d), device="cuda")
         sb = SA.new_state(b, big)
