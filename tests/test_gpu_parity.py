@@ -230,6 +230,33 @@ def test_prefill_then_decode(d, P, dtype):
         assert O.row_normwise_error(got[h], ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d,P", [(64, 4), (16, 4), (32, 5)])
+def test_decode_16bit_records_extreme_value_scales(d, P):
+    """bf16 decode writes its per-tile readout records as f16 with a
+    power-of-two scale per tile (fp32 for the tiles of the order-0/1 rows):
+    values scaled by 2^-90 and 2^60 (exact in bf16) keep the relative error
+    of unit-scale values, and a state whose values are all zero (every
+    record zero) reads out exact zeros."""
+    note(f"decode 16-bit records, value scales 2^-90 / 2^60 / 0, d={d} P={P}")
+    n, steps, H = 300, 6, 4
+    q, k, v = W.make_qkv(1, H, n + steps, d, d, W.BF16, 31000 + d + P)
+    scale = np.array([2.0 ** -90, 2.0 ** 60, 0.0, 1.0])
+    v = (v.astype(np.float64) * scale[None, :, None, None]).astype(np.float32)
+    b = SA.build_basis(d, P, 1.0)
+    _, st = run_prefill(b, q[:, :, :n], k[:, :, :n], v[:, :, :n], W.BF16)
+    qd, kd, vd = to_dev(q[0], W.BF16), to_dev(k[0], W.BF16), to_dev(v[0], W.BF16)
+    got = np.zeros((H, steps, d))
+    for s in range(steps):
+        t = n + s
+        got[:, s] = SA.decode_step(b, qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(),
+                                   st).cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.all(got[2] == 0.0)
+    for h in (0, 1, 3):
+        ref = oracle_rows(q[0, h], k[0, h], v[0, h], P, 1.0, rows=np.arange(n, n + steps))
+        assert O.row_normwise_error(got[h], ref) <= TOL[W.BF16], h
+
+
 @pytest.mark.parametrize("d,P,dtype", [(64, 4, W.BF16), (16, 4, W.F32), (32, 5, W.BF16)])
 def test_ragged_batched_decode(d, P, dtype):
     """States at different positions (prefilled to 0, 1, 63, 200 and 517
