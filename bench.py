@@ -43,7 +43,7 @@ METRIC = "causal SATA tokens/sec/head (prefill, decode) + % of HBM/MFMA roofline
 # change to the decode kernel.
 DECODE_TRAFFIC_BYTES = 6.5784e9
 # The same for one decode_mixed launch (mixed-precision state, same workload).
-MIXED_DECODE_TRAFFIC_BYTES = 3.4535e9
+MIXED_DECODE_TRAFFIC_BYTES = 3.4166e9
 
 
 def parse():

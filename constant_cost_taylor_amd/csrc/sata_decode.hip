@@ -118,9 +118,8 @@ __device__ __forceinline__ void tile_partials(const float* red, const float* dre
 // `tile` of state s as f16 times a power of two that puts the tile's largest
 // below 2^15 (the first lo_t tiles, the rows of orders 0 and 1, keep fp32
 // records), den as fp32.
-template <int DV, int RPP>
-__device__ __forceinline__ void tile_partials_c16(const float* red, const float* dred, const DecodeArgs& a, int s,
-                                                  int tile) {
+template <int DV, int RPP, typename A>
+__device__ __forceinline__ void tile_partials_c16(const float* red, const float* dred, const A& a, int s, int tile) {
   static_assert(DV <= 64, "the value columns fit one wave");
   const int tid = threadIdx.x;
   const int64_t pi = static_cast<int64_t>(s) * a.n_tiles + tile;
@@ -260,7 +259,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // One f16 tile (t16) of state s: rows [lo + t16 R, ...), record index pi.
-template <int DK, typename IT>
+template <int DK, typename IT, bool C16>
 __device__ __forceinline__ void f16_tile(const MixedDecodeArgs& a, int s, int t16, float* part, float* partz) {
   constexpr int DV = DK;
   constexpr int TPR = DV / 8;                 // threads per f16 row, 8 halves (16 bytes) each
@@ -376,17 +375,24 @@ __device__ __forceinline__ void f16_tile(const MixedDecodeArgs& a, int s, int t1
     }
   }
   if (tid == 0) *sc = ldexpf(1.f, es);
-  tile_partials<DV, RPP>(red, dred, part, partz);
+  if constexpr (C16)
+    tile_partials_c16<DV, RPP>(red, dred, a, s, a.nt32 + t16);
+  else
+    tile_partials<DV, RPP>(red, dred, part, partz);
 }
 
 // Mixed-state decode: blocks [0, nt32) take fp32 tiles of rows [0, lo),
-// blocks [nt32, nt32 + nt16) the f16 tiles; records in block order.
+// blocks [nt32, nt32 + nt16) the f16 tiles; records in block order (bf16
+// inputs: 16-bit records, fp32 ones for the fp32 tiles).
 template <int DK, typename IT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mixed(MixedDecodeArgs a) {
   constexpr int R32 = decode_rows(DK);
+  constexpr bool C16 = std::is_same<IT, uint16_t>::value;
   const int tile = blockIdx.x;
   const int s = blockIdx.y;
   const int64_t pi = static_cast<int64_t>(s) * a.n_tiles + tile;
+  float* part = C16 ? nullptr : a.part + pi * DK;
+  float* partz = C16 ? nullptr : a.partz + pi;
   if (tile < a.nt32) {
     unsigned char* base = a.state + static_cast<int64_t>(s) * a.stride_bytes;
     float* st = reinterpret_cast<float*>(base);
@@ -397,11 +403,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mixed(MixedDecodeArgs a
     d.v = a.v;
     d.rows = a.rows;
     d.weight = a.weight;
-    f32_tile<DK, IT, true, false>(d, s, st + static_cast<int64_t>(r0) * DK,
-                                  reinterpret_cast<float*>(base + a.off_z) + r0, r0, min(R32, a.lo - r0),
-                                  a.part + pi * DK, a.partz + pi, tile);
+    d.partz = a.partz;
+    d.n_tiles = a.n_tiles;
+    d.part16 = a.part16;
+    d.psc = a.psc;
+    d.partlo = a.partlo;
+    d.lo_t = a.lo_t;
+    f32_tile<DK, IT, true, C16>(d, s, st + static_cast<int64_t>(r0) * DK,
+                                reinterpret_cast<float*>(base + a.off_z) + r0, r0, min(R32, a.lo - r0), part, partz,
+                                tile);
   } else {
-    f16_tile<DK, IT>(a, s, tile - a.nt32, a.part + pi * DK, a.partz + pi);
+    f16_tile<DK, IT, C16>(a, s, tile - a.nt32, part, partz);
   }
 }
 
@@ -596,13 +608,13 @@ __global__ __launch_bounds__(kRedThreads) void decode_reduce(const float* __rest
 
 // The fixed-order reduce of a step's partial records (one or two passes).
 // C16: the step's records are 16-bit ones (a.part16, a.psc, a.partlo).
-template <int D, bool C16>
+template <int D, bool C16, typename A>
 hipError_t launch_reduce(const float* part, const float* partz, float* out, int S, int n_tiles, int groups,
-                         float* part2, float* partz2, const DecodeArgs* c16, hipStream_t st) {
-  const uint16_t* p16 = C16 ? c16->part16 : nullptr;
-  const float* psc = C16 ? c16->psc : nullptr;
-  const float* plo = C16 ? c16->partlo : nullptr;
-  const int lo_t = C16 ? c16->lo_t : 0;
+                         float* part2, float* partz2, const A& a, hipStream_t st) {
+  const uint16_t* p16 = C16 ? a.part16 : nullptr;
+  const float* psc = C16 ? a.psc : nullptr;
+  const float* plo = C16 ? a.partlo : nullptr;
+  const int lo_t = C16 ? a.lo_t : 0;
   if (groups <= 1) {
     decode_reduce<D, true, C16><<<dim3(1, S), kRedThreads, 0, st>>>(part, partz, n_tiles, n_tiles, nullptr, nullptr,
                                                                      out, p16, psc, plo, lo_t);
@@ -634,8 +646,8 @@ hipError_t launch_d(bool bf16, const DecodeArgs& a, hipStream_t st) {
     decode_update_readout<D, float, false><<<grid, kDecodeThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (bf16) return launch_reduce<D, true>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, &a, st);
-  return launch_reduce<D, false>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, nullptr, st);
+  if (bf16) return launch_reduce<D, true>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, a, st);
+  return launch_reduce<D, false>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, a, st);
 }
 
 template <int D>
@@ -647,7 +659,8 @@ hipError_t launch_mixed_d(bool bf16, const MixedDecodeArgs& a, hipStream_t st) {
     decode_mixed<D, float><<<grid, kDecodeThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_reduce<D, false>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, nullptr, st);
+  if (bf16) return launch_reduce<D, true>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, a, st);
+  return launch_reduce<D, false>(a.part, a.partz, a.out, a.S, a.n_tiles, a.groups, a.part2, a.partz2, a, st);
 }
 
 template <int D>

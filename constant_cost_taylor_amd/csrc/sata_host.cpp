@@ -682,22 +682,13 @@ static int run_segments(const sata_basis* b, const SegPlan& sp, int64_t n, int d
                   nullptr, out + t * d_v, state, 0, inner_ws, false, s);
 }
 
-// Decode workspace: value partials [S][tiles][d_v] then den partials
-// [S][tiles]; with more than one reduce group a state, then the second-level
-// partials [S][groups][d_v] and [S][groups].  Each region 256-byte aligned.
-size_t decode_part_bytes(int S, int tiles, int d_v) {
-  return (static_cast<size_t>(S) * tiles * d_v * sizeof(float) + 255) / 256 * 256;
-}
-size_t decode_partz_bytes(int S, int tiles) {
-  return (static_cast<size_t>(S) * tiles * sizeof(float) + 255) / 256 * 256;
-}
-
 int decode_tiles(const sata_basis* b) {
   const int rows = sata::decode_rows(b->d);
   return static_cast<int>((b->D + rows - 1) / rows);
 }
 
-// Decode workspace regions.  fp32 inputs: value records [S][tiles][d_v] and
+// Decode workspace regions (sata_decode_step and, with tiles = nt32 + nt16 and
+// lo_t = nt32, sata_decode_step_mixed).  fp32 inputs: value records [S][tiles][d_v] and
 // den records [S][tiles], fp32.  bf16 inputs (16-bit records): f16 value
 // records [S][tiles][d_v], their scales [S][tiles], the fp32 value records of
 // the first lo_t tiles [S][lo_t][d_v], den records [S][tiles].  Then, with
@@ -706,9 +697,8 @@ int decode_tiles(const sata_basis* b) {
 struct DecodeWs {
   size_t part = 0, p16 = 0, psc = 0, plo = 0, partz = 0, part2 = 0, partz2 = 0, total = 0;
 };
-DecodeWs decode_ws(const sata_basis* b, int S, int d_v, bool c16) {
+DecodeWs decode_ws_tiles(int S, int tiles, int lo_t, int d_v, bool c16) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const int tiles = decode_tiles(b);
   const int groups = sata::decode_groups(S, tiles);
   const size_t ST = static_cast<size_t>(S) * tiles;
   DecodeWs w;
@@ -719,7 +709,7 @@ DecodeWs decode_ws(const sata_basis* b, int S, int d_v, bool c16) {
     w.psc = off;
     off += up(ST * 4);
     w.plo = off;
-    off += up(static_cast<size_t>(S) * sata::decode_lo_tiles(b->d) * d_v * 4);
+    off += up(static_cast<size_t>(S) * lo_t * d_v * 4);
   } else {
     w.part = off;
     off += up(ST * d_v * 4);
@@ -734,6 +724,9 @@ DecodeWs decode_ws(const sata_basis* b, int S, int d_v, bool c16) {
   }
   w.total = off;
   return w;
+}
+DecodeWs decode_ws(const sata_basis* b, int S, int d_v, bool c16) {
+  return decode_ws_tiles(S, decode_tiles(b), sata::decode_lo_tiles(b->d), d_v, c16);
 }
 
 // Mixed-precision state layout of one state (bytes from its base).
@@ -1108,10 +1101,7 @@ int sata_decode_mixed_workspace(const sata_basis* b, int S, int d_v, int dtype, 
   if (dtype != SATA_F32 && dtype != SATA_BF16) return SATA_ERR_INVALID_ARG;
   if (d_v != b->d) return SATA_ERR_UNSUPPORTED;
   const MixedPlan m = mixed_plan(b);
-  const int tiles = m.nt32 + m.nt16;
-  const int groups = sata::decode_groups(S, tiles);
-  *bytes = decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
-  if (groups > 1) *bytes += decode_part_bytes(S, groups, d_v) + decode_partz_bytes(S, groups);
+  *bytes = decode_ws_tiles(S, m.nt32 + m.nt16, m.nt32, d_v, dtype == SATA_BF16).total;
   return SATA_OK;
 }
 
@@ -1133,10 +1123,11 @@ int sata_decode_step_mixed(const sata_basis* b, int S, int d_v, int dtype, const
   if (check_device(b) != SATA_OK) return SATA_ERR_INVALID_ARG;
   const MixedPlan m = mixed_plan(b);
   const int tiles = m.nt32 + m.nt16;
-  float* part = static_cast<float*>(ws);
-  float* partz = reinterpret_cast<float*>(static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v));
   const int groups = sata::decode_groups(S, tiles);
-  char* lvl2 = static_cast<char*>(ws) + decode_part_bytes(S, tiles, d_v) + decode_partz_bytes(S, tiles);
+  const bool c16 = dtype == SATA_BF16;
+  const DecodeWs w = decode_ws_tiles(S, tiles, m.nt32, d_v, c16);
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   sata::MixedDecodeArgs a{};
   a.q = q;
   a.k = k;
@@ -1146,8 +1137,8 @@ int sata_decode_step_mixed(const sata_basis* b, int S, int d_v, int dtype, const
   a.off_h = m.off_h;
   a.off_z = m.off_z;
   a.off_sc = m.off_sc;
-  a.part = part;
-  a.partz = partz;
+  a.part = c16 ? nullptr : at(w.part);
+  a.partz = at(w.partz);
   a.out = out;
   a.rows = b->d_rows;
   a.weight = b->d_weight;
@@ -1158,8 +1149,12 @@ int sata_decode_step_mixed(const sata_basis* b, int S, int d_v, int dtype, const
   a.nt16 = m.nt16;
   a.n_tiles = tiles;
   a.groups = groups;
-  a.part2 = groups > 1 ? reinterpret_cast<float*>(lvl2) : nullptr;
-  a.partz2 = groups > 1 ? reinterpret_cast<float*>(lvl2 + decode_part_bytes(S, groups, d_v)) : nullptr;
+  a.part2 = groups > 1 ? at(w.part2) : nullptr;
+  a.partz2 = groups > 1 ? at(w.partz2) : nullptr;
+  a.part16 = c16 ? reinterpret_cast<uint16_t*>(base + w.p16) : nullptr;
+  a.psc = c16 ? at(w.psc) : nullptr;
+  a.partlo = c16 ? at(w.plo) : nullptr;
+  a.lo_t = c16 ? m.nt32 : 0;
   if (sata::launch_decode_mixed(b->d, dtype == SATA_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SATA_ERR_HIP;
   return SATA_OK;

@@ -290,6 +290,11 @@ struct MixedDecodeArgs {
   int groups;
   float* part2;
   float* partz2;
+  // 16-bit records (bf16 inputs), as for DecodeArgs; lo_t = nt32
+  uint16_t* part16;
+  float* psc;
+  float* partlo;
+  int lo_t;
 };
 
 struct MixedConvArgs {
