@@ -230,7 +230,7 @@ def test_prefill_then_decode(d, P, dtype):
         assert O.row_normwise_error(got[h], ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("d,P", [(64, 4), (16, 4), (32, 5)])
+@pytest.mark.parametrize("d,P", [(64, 4), (16, 4), (32, 5), (8, 3)])
 def test_decode_16bit_records_extreme_value_scales(d, P):
     """bf16 decode writes its per-tile readout records as f16 with a
     power-of-two scale per tile (fp32 for the tiles of the order-0/1 rows):
@@ -906,7 +906,7 @@ def test_mixed_state_decode_workload_1024_steps():
         assert O.row_normwise_error(got[:, s], ref) <= TOL[w.dtype], s
 
 
-@pytest.mark.parametrize("d,P,dtype,steps", [(8, 3, W.F32, 60), (16, 4, W.BF16, 40), (32, 4, W.BF16, 30),
+@pytest.mark.parametrize("d,P,dtype,steps", [(8, 3, W.F32, 60), (8, 3, W.BF16, 40), (16, 4, W.BF16, 40), (32, 4, W.BF16, 30),
                                              (32, 5, W.BF16, 20), (64, 4, W.F32, 12), (64, 5, W.BF16, 6)])
 def test_mixed_state_decode_from_empty(d, P, dtype, steps):
     """Mixed decode from an empty state: every tile's scale is re-chosen as
